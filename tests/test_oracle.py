@@ -1,0 +1,320 @@
+"""Pins for the fp64 CPU oracle (no GPU).
+
+Each test ties the oracle to something other than itself: torch's float64
+scaled_dot_product_attention on dense, never-paged inputs; closed forms;
+invariances the mathematics fixes; hand-derived worked examples.  The set is
+chosen so that a dropped term, a wrong sign, a wrong index (causal offset,
+GQA head mapping, page / slot / layout index, split range) or a transposed
+operand fails at least one test; `test_oracle_mutants.py` checks that claim by
+planting such mistakes in a copy of the oracle.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from pa_testutil import dense_request, scatter_pages, sdpa_reference
+
+TOL = 1e-12
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _build_case(seed, specs, Hq, Hkv, Dqk, Dv, P, dtype=torch.float32, layout="mha", spare=1):
+    """specs: list of (nq, ctx).  Returns dense tensors plus the paged inputs."""
+    gen = torch.Generator().manual_seed(seed)
+    qs, Ks, Vs = [], [], []
+    for nq, ctx in specs:
+        if layout == "mla":
+            q, K, _ = dense_request(gen, nq, ctx, Hq, 1, Dqk, Dv, dtype)
+            V = K[:, :, :Dv]
+        else:
+            q, K, V = dense_request(gen, nq, ctx, Hq, Hkv, Dqk, Dv, dtype)
+        qs.append(q)
+        Ks.append(K)
+        Vs.append(V)
+    kc, vc, bt = scatter_pages(Ks, Vs, P, gen, spare=spare, layout=layout)
+    qsl = np.zeros(len(specs) + 1, dtype=np.int32)
+    qsl[1:] = np.cumsum([s[0] for s in specs])
+    seq = np.array([s[0] + s[1] for s in specs], dtype=np.int32)
+    qcat = torch.cat(qs, 0) if sum(s[0] for s in specs) else torch.zeros(0, Hq, Dqk, dtype=dtype)
+    return dict(q=qcat, qs=qs, Ks=Ks, Vs=Vs, kc=kc, vc=vc, bt=bt, qsl=qsl, seq=seq)
+
+
+def _run(c, scale, Hkv, Dv, layout="mha", rows=None):
+    lay = oracle.LAYOUT_MLA if layout == "mla" else oracle.LAYOUT_MHA
+    return oracle.attention(c["q"], c["kc"], c["vc"], c["bt"], c["seq"], c["qsl"], scale,
+                            Hkv, head_dim_v=Dv, layout=lay, rows=rows)
+
+
+CASES = [
+    # seed, specs (nq, ctx), Hq, Hkv, Dqk, Dv, P
+    (1, [(1, 0), (1, 9), (5, 0), (3, 7)], 4, 2, 8, 8, 4),
+    (2, [(2, 30), (1, 39), (7, 3)], 6, 2, 8, 5, 16),
+    (3, [(4, 0), (1, 1)], 3, 1, 4, 4, 1),
+    (4, [(0, 5), (6, 10), (1, 0)], 2, 2, 16, 16, 4),
+    (5, [(16, 17), (1, 31)], 8, 4, 8, 8, 16),
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("case", CASES)
+def test_bruteforce_against_torch_sdpa(case, dtype):
+    """Paged fp64 oracle == float64 torch SDPA on the dense, unpaged inputs."""
+    seed, specs, Hq, Hkv, Dqk, Dv, P = case
+    c = _build_case(seed, specs, Hq, Hkv, Dqk, Dv, P, dtype)
+    scale = 1.0 / math.sqrt(Dqk) * 1.3
+    out, lse = _run(c, scale, Hkv, Dv)
+    i0 = 0
+    for (nq, ctx), q, K, V in zip(specs, c["qs"], c["Ks"], c["Vs"]):
+        if nq == 0:
+            continue
+        ro, rl = sdpa_reference(q, K, V, float(np.float32(scale)))
+        np.testing.assert_allclose(out[i0:i0 + nq], ro, atol=TOL, rtol=0)
+        np.testing.assert_allclose(lse[i0:i0 + nq], rl, atol=TOL, rtol=0)
+        i0 += nq
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+
+
+def test_page_permutation_is_bitwise_invariant():
+    specs = [(3, 20), (1, 44), (6, 0)]
+    a = _build_case(11, specs, 4, 2, 8, 8, 4)
+    out_a, lse_a = _run(a, 0.4, 2, 8)
+    # same dense tensors, different physical page order and pool size
+    gen = torch.Generator().manual_seed(999)
+    kc, vc, bt = scatter_pages(a["Ks"], a["Vs"], 4, gen, spare=5)
+    b = dict(a, kc=kc, vc=vc, bt=bt)
+    out_b, lse_b = _run(b, 0.4, 2, 8)
+    assert not np.array_equal(a["bt"].numpy(), bt.numpy()[:, :a["bt"].shape[1]])
+    assert np.array_equal(out_a, out_b) and np.array_equal(lse_a, lse_b)
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 7, 64])
+def test_split_then_merge_equals_unsplit(S):
+    specs = [(1, 0), (1, 12), (1, 37), (1, 63)]
+    c = _build_case(21, specs, 4, 2, 8, 8, 4)
+    out, lse = _run(c, 0.35, 2, 8)
+    q = c["q"].reshape(len(specs), 4, 8)
+    po, pl = oracle.decode_split(q, c["kc"], c["vc"], c["bt"], c["seq"], 0.35, S, 2, head_dim_v=8)
+    mo, ml = oracle.merge_lse(po, pl)
+    np.testing.assert_allclose(mo, out, atol=TOL, rtol=0)
+    np.testing.assert_allclose(ml, lse, atol=TOL, rtol=0)
+    for b, L in enumerate(c["seq"]):
+        pages = (int(L) + 3) // 4
+        for s in range(S):
+            if s >= pages:  # more partitions than pages: the extra ones are empty
+                assert np.all(np.isneginf(pl[b, :, s])) and np.all(po[b, :, s] == 0)
+
+
+def test_split_partials_match_sdpa_on_their_ranges():
+    """Each partial is plain attention over its own key range (checked with SDPA on
+    the dense keys), and the ranges tile [0, L) contiguously on page boundaries."""
+    specs = [(1, 40), (1, 9)]
+    c = _build_case(23, specs, 4, 1, 8, 8, 4)
+    S = 3
+    q = c["q"].reshape(2, 4, 8)
+    po, pl = oracle.decode_split(q, c["kc"], c["vc"], c["bt"], c["seq"], 0.5, S, 1, head_dim_v=8)
+    for b, L in enumerate(c["seq"]):
+        L = int(L)
+        prev = 0
+        for s in range(S):
+            t0, t1 = oracle.split_range(L, 4, S, s)
+            assert t0 == prev and t0 % 4 == 0 and t0 <= t1 <= L
+            prev = t1
+            if t1 > t0:
+                K = c["Ks"][b][t0:t1]
+                V = c["Vs"][b][t0:t1]
+                ro, rl = sdpa_reference(c["qs"][b], K, V, 0.5)
+                np.testing.assert_allclose(po[b, :, s], ro[0], atol=TOL, rtol=0)
+                np.testing.assert_allclose(pl[b, :, s], rl[0], atol=TOL, rtol=0)
+        assert prev == L
+        sizes = [oracle.split_range(L, 4, S, s) for s in range(S)]
+        nonempty = [t1 - t0 for t0, t1 in sizes if t1 > t0]
+        assert all(n == nonempty[0] for n in nonempty[:-1])
+
+
+def test_constant_value_rows_sum_to_one():
+    """V = const => out = const for every row (softmax rows sum to 1)."""
+    specs = [(1, 30), (4, 5), (9, 0)]
+    c = _build_case(31, specs, 4, 2, 8, 8, 4)
+    vc = torch.where(torch.isnan(c["vc"]), c["vc"], torch.full_like(c["vc"], 2.5))
+    out, _ = _run(dict(c, vc=vc), 0.7, 2, 8)
+    np.testing.assert_allclose(out, 2.5, atol=1e-14, rtol=0)
+
+
+def test_length_one_context_returns_v0():
+    specs = [(1, 0)]
+    c = _build_case(41, specs, 4, 2, 8, 8, 16)
+    out, lse = _run(c, 0.25, 2, 8)
+    q, K, V = c["qs"][0].double(), c["Ks"][0].double(), c["Vs"][0].double()
+    for h in range(4):
+        kvh = h // 2
+        assert np.array_equal(out[0, h], V[0, kvh].numpy())
+        s0 = 0.25 * float(np.dot(q[0, h].numpy(), K[0, kvh].numpy()))
+        assert abs(lse[0, h] - s0) <= 1e-15 * max(1.0, abs(s0))
+    # the first token of a prefill also sees only key 0
+    c = _build_case(42, [(5, 0)], 4, 2, 8, 8, 4)
+    out, _ = _run(c, 0.25, 2, 8)
+    for h in range(4):
+        assert np.array_equal(out[0, h], c["Vs"][0][0, h // 2].double().numpy())
+
+
+def test_equal_keys_give_mean_of_visible_values():
+    specs = [(3, 6)]
+    c = _build_case(51, specs, 2, 1, 8, 8, 4)
+    K = c["Ks"][0]
+    Keq = K[:1].expand_as(K).clone()
+    gen = torch.Generator().manual_seed(52)
+    kc, vc, bt = scatter_pages([Keq], c["Vs"], 4, gen)
+    out, lse = _run(dict(c, kc=kc, vc=vc, bt=bt), 0.3, 1, 8)
+    V = c["Vs"][0].double().numpy()
+    q = c["qs"][0].double().numpy()
+    for j in range(3):
+        pos = 6 + j
+        for h in range(2):
+            np.testing.assert_allclose(out[j, h], V[:pos + 1, 0].mean(0), atol=1e-14, rtol=0)
+            s = float(np.float32(0.3)) * float(np.dot(q[j, h], Keq[0, 0].double().numpy()))
+            assert abs(lse[j, h] - (s + math.log(pos + 1))) <= 1e-13
+
+
+def test_zero_query_gives_mean_and_log_count():
+    specs = [(4, 3), (1, 10)]
+    c = _build_case(61, specs, 4, 2, 8, 8, 4)
+    q0 = torch.zeros_like(c["q"])
+    out, lse = _run(dict(c, q=q0), 0.9, 2, 8)
+    i0 = 0
+    for (nq, ctx), V in zip(specs, c["Vs"]):
+        Vd = V.double().numpy()
+        for j in range(nq):
+            n = ctx + j + 1
+            for h in range(4):
+                np.testing.assert_allclose(out[i0 + j, h], Vd[:n, h // 2].mean(0), atol=1e-14)
+                assert abs(lse[i0 + j, h] - math.log(n)) <= 1e-14
+        i0 += nq
+
+
+def test_decode_equals_last_prefill_row_and_extend_matches_prefill():
+    gen = torch.Generator().manual_seed(71)
+    Hq, Hkv, D, P = 4, 2, 8, 4
+    q, K, V = dense_request(gen, 10, 0, Hq, Hkv, D, D, torch.float32)
+    kc, vc, bt = scatter_pages([K], [V], P, gen)
+
+    def run(qpart, nq, L):
+        return oracle.attention(qpart, kc, vc, bt, np.array([L], np.int32),
+                                np.array([0, nq], np.int32), 0.4, Hkv)
+
+    full_o, full_l = run(q, 10, 10)
+    dec_o, dec_l = run(q[9:], 1, 10)               # decode: last token over 10 keys
+    assert np.array_equal(dec_o[0], full_o[9]) and np.array_equal(dec_l[0], full_l[9])
+    ext_o, ext_l = run(q[6:], 4, 10)               # extend: 4 new tokens on 6 cached
+    assert np.array_equal(ext_o, full_o[6:]) and np.array_equal(ext_l, full_l[6:])
+    pre_o, _ = run(q[:7], 7, 7)                    # a shorter prefill = leading rows
+    assert np.array_equal(pre_o, full_o[:7])
+
+
+def test_gqa_equals_replicated_mha():
+    specs = [(3, 9), (1, 20)]
+    c = _build_case(81, specs, 8, 2, 8, 8, 4)
+    out_g, lse_g = _run(c, 0.3, 2, 8)
+    Ks = [K.repeat_interleave(4, dim=1) for K in c["Ks"]]
+    Vs = [V.repeat_interleave(4, dim=1) for V in c["Vs"]]
+    gen = torch.Generator().manual_seed(82)
+    kc, vc, bt = scatter_pages(Ks, Vs, 4, gen)
+    out_m, lse_m = _run(dict(c, kc=kc, vc=vc, bt=bt), 0.3, 8, 8)
+    assert np.array_equal(out_g, out_m) and np.array_equal(lse_g, lse_m)
+
+
+def test_request_order_permutation():
+    specs = [(1, 14), (5, 3), (2, 0), (1, 30)]
+    c = _build_case(91, specs, 4, 2, 8, 8, 4)
+    out, lse = _run(c, 0.3, 2, 8)
+    order = [2, 0, 3, 1]
+    specs2 = [specs[i] for i in order]
+    gen = torch.Generator().manual_seed(92)
+    kc, vc, bt = scatter_pages([c["Ks"][i] for i in order], [c["Vs"][i] for i in order], 4, gen)
+    q2 = torch.cat([c["qs"][i] for i in order], 0)
+    qsl = np.zeros(5, np.int32)
+    qsl[1:] = np.cumsum([s[0] for s in specs2])
+    seq = np.array([a + b for a, b in specs2], np.int32)
+    out2, lse2 = oracle.attention(q2, kc, vc, bt, seq, qsl, 0.3, 2)
+    starts = np.concatenate([[0], np.cumsum([s[0] for s in specs])])
+    i0 = 0
+    for i in order:
+        n = specs[i][0]
+        assert np.array_equal(out2[i0:i0 + n], out[starts[i]:starts[i] + n])
+        assert np.array_equal(lse2[i0:i0 + n], lse[starts[i]:starts[i] + n])
+        i0 += n
+
+
+def test_mla_latent_layout_matches_sdpa_and_mha_layout():
+    """MLA: keys are the full latent rows, values their first Dv columns."""
+    specs = [(1, 20), (1, 0), (1, 64)]
+    Hq, Dqk, Dv, P = 8, 12, 8, 8
+    c = _build_case(101, specs, Hq, 1, Dqk, Dv, P, torch.bfloat16, layout="mla")
+    out, lse = _run(c, 0.2, 1, Dv, layout="mla")
+    for b, (q, K) in enumerate(zip(c["qs"], c["Ks"])):
+        ro, rl = sdpa_reference(q, K, K[:, :, :Dv], float(np.float32(0.2)))
+        np.testing.assert_allclose(out[b:b + 1], ro, atol=TOL, rtol=0)
+        np.testing.assert_allclose(lse[b:b + 1], rl, atol=TOL, rtol=0)
+    gen = torch.Generator().manual_seed(102)
+    kc, vc, bt = scatter_pages(c["Ks"], [K[:, :, :Dv] for K in c["Ks"]], P, gen)
+    out_m, lse_m = _run(dict(c, kc=kc, vc=vc, bt=bt), 0.2, 1, Dv)
+    np.testing.assert_allclose(out_m, out, atol=1e-14, rtol=0)
+    np.testing.assert_allclose(lse_m, lse, atol=1e-14, rtol=0)
+
+
+def test_merge_closed_forms():
+    o = np.array([[[1.0, 2.0], [5.0, -3.0]]])          # [rows=1, S=2, Dv=2]
+    l = np.array([[0.0, math.log(3.0)]])                # weights 1 : 3
+    out, lse = oracle.merge_lse(o, l)
+    np.testing.assert_allclose(out[0], [(1 + 15) / 4, (2 - 9) / 4], atol=1e-15)
+    assert abs(lse[0] - math.log(4.0)) < 1e-15
+    # one empty partition: the other passes through
+    out, lse = oracle.merge_lse(o, np.array([[-np.inf, 0.5]]))
+    np.testing.assert_array_equal(out[0], [5.0, -3.0])
+    assert lse[0] == 0.5
+    # all empty: zeros and -inf, never NaN
+    out, lse = oracle.merge_lse(o, np.array([[-np.inf, -np.inf]]))
+    assert np.all(out == 0) and np.isneginf(lse[0])
+    # large equal lse values do not overflow
+    out, lse = oracle.merge_lse(o, np.array([[800.0, 800.0]]))
+    np.testing.assert_allclose(out[0], [3.0, -0.5], atol=1e-15)
+    assert abs(lse[0] - (800.0 + math.log(2.0))) < 1e-12
+
+
+def test_invalid_inputs_are_rejected():
+    c = _build_case(111, [(2, 3)], 4, 2, 8, 8, 4)
+    bad = c["seq"].copy()
+    bad[0] = 1  # seq_len < q_len
+    with pytest.raises(ValueError):
+        oracle.attention(c["q"], c["kc"], c["vc"], c["bt"], bad, c["qsl"], 0.3, 2)
+    bt = c["bt"].clone()
+    bt[0, 0] = 10 ** 6
+    with pytest.raises(ValueError):
+        oracle.attention(c["q"], c["kc"], c["vc"], bt, c["seq"], c["qsl"], 0.3, 2)
+    with pytest.raises(ValueError):
+        oracle.attention(c["q"], c["kc"], c["vc"], c["bt"], c["seq"], c["qsl"], 0.3, 3)
+
+
+def _load_golden():
+    with open(os.path.join(HERE, "golden", "worked_examples.json")) as f:
+        return json.load(f)["examples"]
+
+
+@pytest.mark.parametrize("ex", _load_golden(), ids=lambda e: e["name"])
+def test_hand_worked_examples(ex):
+    """Tiny cases whose results were derived by hand (see the fixture's notes)."""
+    P, Hq, Hkv = ex["page_size"], ex["num_q_heads"], ex["num_kv_heads"]
+    q = np.array(ex["q"], dtype=np.float32)
+    kc = np.array(ex["k_cache"], dtype=np.float32)
+    vc = np.array(ex["v_cache"], dtype=np.float32)
+    bt = np.array(ex["block_table"], dtype=np.int32)
+    seq = np.array(ex["seq_lens"], dtype=np.int32)
+    qsl = np.array(ex["query_start_loc"], dtype=np.int32)
+    out, lse = oracle.attention(q, kc, vc, bt, seq, qsl, ex["scale"], Hkv,
+                                head_dim_v=vc.shape[2])
+    np.testing.assert_allclose(out, np.array(ex["expected_out"]), atol=1e-12, rtol=0)
+    np.testing.assert_allclose(lse, np.array(ex["expected_lse"]), atol=1e-12, rtol=0)
