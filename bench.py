@@ -1,0 +1,228 @@
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+Step = one pa_forward call (planner kernel + persistent attention kernel +
+split merge) over one batch of synthetic Llama-3.1-8B-shaped decode requests:
+64 sequences, context lengths uniform in [500, 8192], 32 query / 8 KV heads,
+head dim 128, page size 16, bf16, pages in random physical order.  Inputs are
+resident in HBM before the timed region.
+
+Printed (one JSON line): decode HBM GB/s of the whole step (algorithmic bytes
+/ step time), the roofline entry of the attention kernel timed alone with HIP
+events recorded by the library around that launch, the prefill half of the
+metric (TFLOP/s of the Qwen3-235B-shaped prefill + extend requests of the
+mixed batch, same method), and the fp64 CPU oracle timed on the host.
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode attn HBM GB/s (% of peak) + prefill attn TFLOP/s (% MFMA peak), 1 GPU"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+KERNEL_SRC = os.path.join(ROOT, "paged_attention_kv_pa_amd", "csrc", "pa_mha.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+class HipEvents:
+    """Raw hipEvent_t pairs (the library records them on its own launch stream)."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.pairs = []
+        for _ in range(n):
+            a, b = ctypes.c_void_p(), ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(a)) == 0
+            assert self.hip.hipEventCreate(ctypes.byref(b)) == 0
+            self.pairs.append((a, b))
+
+    def elapsed_ms(self, i):
+        t = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(t), self.pairs[i][0], self.pairs[i][1])
+        assert rc == 0, rc
+        return float(t.value)
+
+    def close(self):
+        for a, b in self.pairs:
+            self.hip.hipEventDestroy(a)
+            self.hip.hipEventDestroy(b)
+
+
+def time_steps(call, steps, warmup, lib):
+    """Run `call` warmup + steps times; returns (ms per step, mean attention-kernel ms)."""
+    import torch
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = HipEvents(steps)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        lib.pa_set_kernel_events(ev.pairs[i][0], ev.pairs[i][1])
+        call()
+    lib.pa_set_kernel_events(None, None)
+    t1.record()
+    torch.cuda.synchronize()
+    step_ms = t0.elapsed_time(t1) / steps
+    kern_ms = sum(ev.elapsed_ms(i) for i in range(steps)) / steps
+    ev.close()
+    return step_ms, kern_ms
+
+
+def traffic_entry(kernel_name):
+    """HBM traffic per launch from committed counter runs, if taken on this kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+        e = t.get(kernel_name)
+        if e and e.get("source_sha256") == src:
+            return e.get("bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+    return None
+
+
+def cpu_baseline(b, nbytes):
+    import oracle
+    h = b.to("cpu")
+    threads = oracle.max_threads()
+    t = time.perf_counter()
+    reps = 0
+    while True:
+        oracle.attention(h.q, h.k_cache, h.v_cache, h.block_table, h.seq_lens, h.query_start_loc,
+                         h.scale, h.num_kv_heads, nthreads=threads)
+        reps += 1
+        el = time.perf_counter() - t
+        if el >= 10.0 or reps >= 20:
+            break
+    per = el / reps
+    return {"value": round(nbytes / per / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "the whole timed batch (64 decode requests), %d pass(es), %.2f s each" % (reps, per)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_attention_kv_pa_amd as pa
+    from paged_attention_kv_pa_amd import workload
+
+    if not os.path.exists(pa.library_path()):
+        from paged_attention_kv_pa_amd import build as pbuild
+        pbuild.build()
+    lib = pa.library()
+    lib.pa_set_kernel_events.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    lib.pa_set_kernel_events.restype = ctypes.c_int32
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---- decode: Llama-3.1-8B shapes, B = 64, L ~ U[500, 8192]
+    b = workload.llama_decode(3, device=dev)
+    T, Hq = b.num_tokens, b.num_q_heads
+    out = torch.empty(T, Hq, b.head_dim_v, dtype=b.dtype, device=dev)
+    lse = torch.empty(T, Hq, dtype=torch.float32, device=dev)
+    maxL, maxq = max(b.seq_lens_list), max(b.q_lens)
+    dims = pa.make_dims(b.q, b.k_cache, b.v_cache, b.block_table, b.seq_lens, T,
+                        max_seq_len=maxL, max_q_len=maxq)
+    ws = torch.empty(pa.pa_workspace_size(dims), dtype=torch.uint8, device=dev)
+
+    def step():
+        pa.pa_forward(b.q, b.k_cache, b.v_cache, b.block_table, b.seq_lens, b.query_start_loc,
+                      b.scale, out=out, lse=lse, workspace=ws, max_seq_len=maxL, max_q_len=maxq)
+
+    step_ms, kern_ms = time_steps(step, args.steps, args.warmup, lib)
+    nbytes = workload.algorithmic_bytes(b)
+    value = nbytes / (step_ms * 1e-3) / 1e9
+    achieved = nbytes / (kern_ms * 1e-3) / 1e9
+    tr = traffic_entry("mha_forward_kernel<128, decode>")
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Llama-3.1-8B-shaped paged decode", "batch": 64,
+                   "context": "uniform [500, 8192]", "q_heads": 32, "kv_heads": 8,
+                   "head_dim": 128, "page_size": 16, "total_keys": int(sum(b.seq_lens_list)),
+                   "algorithmic_bytes": nbytes},
+        "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
+        "roofline": {"kernel": "mha_forward_kernel<128, decode-only>", "bound": "hbm",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "kernel_ms": round(kern_ms, 5),
+                     "traffic": tr},
+    }
+    del ws, out, lse
+    b_host_needed = not args.no_cpu_baseline
+
+    # ---- prefill half of the metric: the prefill + extend requests of the Qwen3-235B
+    # mixed batch (requests 48..63), and the whole mixed batch in one call
+    if not args.no_prefill:
+        full = workload.qwen3_mixed(0, device=dev)
+
+        def timed_forward(m, steps):
+            Tm = m.num_tokens
+            mo = torch.empty(Tm, m.num_q_heads, m.head_dim_v, dtype=m.dtype, device=dev)
+            mmaxL, mmaxq = max(m.seq_lens_list), max(m.q_lens)
+            mdims = pa.make_dims(m.q, m.k_cache, m.v_cache, m.block_table, m.seq_lens, Tm,
+                                 max_seq_len=mmaxL, max_q_len=mmaxq)
+            mws = torch.empty(pa.pa_workspace_size(mdims), dtype=torch.uint8, device=dev)
+
+            def pstep():
+                pa.pa_forward(m.q, m.k_cache, m.v_cache, m.block_table, m.seq_lens,
+                              m.query_start_loc, m.scale, out=mo, workspace=mws,
+                              max_seq_len=mmaxL, max_q_len=mmaxq)
+
+            return time_steps(pstep, steps, 2, lib)
+
+        psteps = max(3, args.steps // 3)
+        pre = workload.sub_batch(full, range(48, 64))
+        p_step_ms, p_kern_ms = timed_forward(pre, psteps)
+        flops = workload.algorithmic_flops(pre)
+        tf = flops / (p_kern_ms * 1e-3) / 1e12
+        result["prefill"] = {
+            "workload": "Qwen3-235B-shaped mixed batch, its 8 extend (q~U[256,2048] on "
+                        "c~U[4096,32768]) + 8 prefill (q~U[512,8192]) requests; 64/4 heads, "
+                        "d=128, page 16, causal",
+            "value": round(tf, 2), "unit": "TFLOP/s", "peak": BF16_PEAK_TFLOPS,
+            "frac": round(tf / BF16_PEAK_TFLOPS, 4), "kernel_ms": round(p_kern_ms, 4),
+            "ms_per_step": round(p_step_ms, 4), "algorithmic_flops": flops, "steps": psteps}
+        m_step_ms, m_kern_ms = timed_forward(full, psteps)
+        result["mixed_batch"] = {
+            "workload": "Qwen3-235B-shaped mixed batch, all 64 requests [48 decode : 8 extend : "
+                        "8 prefill] in one pa_forward call",
+            "ms_per_step": round(m_step_ms, 4), "kernel_ms": round(m_kern_ms, 4),
+            "new_tokens_per_s": round(full.num_tokens / (m_step_ms * 1e-3), 1),
+            "tflops": round(workload.algorithmic_flops(full) / (m_step_ms * 1e-3) / 1e12, 2),
+            "hbm_gbs": round(workload.algorithmic_bytes(full) / (m_step_ms * 1e-3) / 1e9, 2)}
+        del full, pre
+
+    if b_host_needed:
+        result["cpu_baseline"] = cpu_baseline(b, nbytes)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,222 @@
+/*
+ * pa.h — C ABI of the MI355X (gfx950) paged-attention engine (libpa.so).
+ *
+ * The engine computes causal softmax(scale * Q K^T) V for a continuous batch
+ * of requests whose keys and values live in fixed-size pages of a KV cache.
+ * Sources of the operations (web pages the method is described on):
+ *   [TDD] "vLLM Triton Attention Backend Deep Dive"
+ *   [ROC] "vLLM AMD ROCm Attention Backend Optimization"
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every pointer argument except the `pa_dims` descriptor and the stream is
+ *    a DEVICE pointer owned by the caller.  The library never allocates,
+ *    frees or synchronises on these calls; work is enqueued on `stream`
+ *    (a hipStream_t; NULL means the null stream) and the call returns at
+ *    once.  Scratch memory comes from the caller as `workspace`, sized with
+ *    the matching *_workspace_size() function (contents need no
+ *    initialisation and are overwritten).
+ *  - Sizes, dtypes and capacities are checked on the host before anything is
+ *    launched; a failed check returns an error code and launches nothing.
+ *    A launch failure returns PA_ERR_HIP (pa_last_hip_error() gives the
+ *    hipError_t).  Nothing throws across this boundary.
+ *  - DEVICE CONTENTS ARE NOT CHECKED by the compute calls (a block-table entry
+ *    outside [0, num_pages), seq_len < q_len, a non-monotone
+ *    query_start_loc ...): they are undefined behaviour there.  pa_validate()
+ *    checks them synchronously.
+ *  - Calls are graph-capture safe: each call is a fixed sequence of kernel
+ *    launches whose grids depend only on the pa_dims capacities, never on
+ *    device contents, and no call issues a memset or a host synchronisation.
+ *    A captured call may be replayed after the caller rewrites seq_lens,
+ *    query_start_loc and block_table in place (within the capacities).
+ *
+ * Data layouts (row-major, element strides in brackets)
+ * -----------------------------------------------------
+ *  q            [T, Hq, Dqk]            T >= query_start_loc[B]; rows past
+ *               query_start_loc[B] are neither read nor written
+ *  k_cache      [num_pages, Hkv, P, Dqk]      key of (page, head, slot)
+ *  v_cache      [num_pages, Hkv, Dv, P]       value, stored column-major per
+ *               page so that consecutive slots of one column are adjacent
+ *               (a layout chosen for the matrix cores: [ROC] section
+ *               "ROCM_AITER_FA", bullet on the hardware-optimised cache layout)
+ *  MLA latent   [num_pages, P, 576]           key = the whole row,
+ *               value = its first 512 columns
+ *  block_table  int32 [B, max_pages_per_seq]  logical page -> physical page;
+ *               token t of request b is at page block_table[b][t / P], slot
+ *               t % P.  Entries past ceil(seq_len / P) are never read.
+ *  seq_lens     int32 [B]     total keys of request b INCLUDING its new tokens
+ *  query_start_loc int32 [B + 1]  request b owns query rows
+ *               [qsl[b], qsl[b+1]); q_len = qsl[b+1] - qsl[b] may be 0.
+ *  out          [T, Hq, Dv]   same dtype as q
+ *  lse          float32 [T, Hq]   natural-log log-sum-exp of the scaled
+ *               scores of the row (optional: NULL skips it)
+ *
+ * Causality: the q_len new tokens of a request are its LAST q_len positions;
+ * new token j (0-based) sees keys 0 .. seq_len - q_len + j.  The new tokens'
+ * keys and values must already be written into the cache.
+ * GQA: query head h reads KV head h / (Hq / Hkv).
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define PA_API __attribute__((visibility("default")))
+#else
+#define PA_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1,  /* null pointer, inconsistent sizes, bad range       */
+  PA_ERR_UNSUPPORTED = 2,  /* valid but not implemented (head dim, page size ...) */
+  PA_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than required            */
+  PA_ERR_HIP = 4,          /* a HIP call or kernel launch failed                 */
+  PA_ERR_DEVICE_DATA = 5   /* pa_validate only: device contents are invalid      */
+} pa_status;
+
+typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Shapes and host-side capacities of one call.  Capacities (max_*) size the
+ * workspace and the launch grids without reading device memory. */
+typedef struct pa_dims {
+  int32_t num_seqs;          /* B                                              */
+  int32_t num_tokens;        /* T, rows of q / out (>= query_start_loc[B])      */
+  int32_t num_q_heads;       /* Hq, a multiple of num_kv_heads                 */
+  int32_t num_kv_heads;      /* Hkv                                            */
+  int32_t head_dim_qk;       /* Dqk                                            */
+  int32_t head_dim_v;        /* Dv                                             */
+  int32_t page_size;         /* P                                              */
+  int32_t num_pages;         /* pages in the cache pool                        */
+  int32_t max_pages_per_seq; /* block_table row stride                         */
+  int32_t max_seq_len;       /* >= every seq_len                               */
+  int32_t max_q_len;         /* >= every q_len                                 */
+  int32_t dtype;             /* pa_dtype of q, caches and out                  */
+} pa_dims;
+
+/*
+ * Bytes of workspace pa_forward needs for these dims (0 if the dims are
+ * invalid).  Pure host function.
+ */
+PA_API size_t pa_workspace_size(const pa_dims* dims);
+
+/*
+ * pa_forward — paged causal attention over a varlen continuous batch of
+ * prefill, extend and decode requests in one call ([TDD] sections
+ * "Technical implementation of paged attention", "Q-block optimization",
+ * "Persistent kernels and CUDA graphs"; [ROC] section "The challenge of
+ * mixed inference workloads").  A planner kernel turns seq_lens and
+ * query_start_loc into work items (query tokens x the query heads of one KV
+ * head, over a key range); one persistent kernel with a fixed grid runs them;
+ * decode rows whose key range was split are then merged by log-sum-exp
+ * ([TDD] section "Parallel tiled softmax (3D kernel)").
+ *
+ * Supported: bf16 with Dqk == Dv in {64, 128}, P a multiple of 8 up to 256;
+ * fp32 with Dqk, Dv <= 256 and any P >= 1.  Requires Hq % Hkv == 0.
+ * Returns PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE or
+ * PA_ERR_HIP.
+ */
+PA_API pa_status pa_forward(const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_table, const int32_t* seq_lens,
+                     const int32_t* query_start_loc, float scale, void* out,
+                     float* lse, const pa_dims* dims, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_split — first launch of split-KV decode ([TDD] section
+ * "Parallel tiled softmax (3D kernel)"): every request has exactly one query
+ * token (T == B, q is [B, Hq, Dqk]; query_start_loc is not taken).  The keys
+ * of request b are cut into num_splits contiguous, page-aligned partitions of
+ * P * ceil(ceil(L / P) / num_splits) keys each (L = seq_lens[b]; trailing
+ * partitions may be short or empty).  Partition s yields
+ *   part_out[b, h, s, :]  float32 [B, Hq, S, Dv]  softmax-normalised within
+ *                         the partition (zeros if empty)
+ *   part_lse[b, h, s]     float32 [B, Hq, S]      its log-sum-exp (-inf if empty)
+ * num_splits in [1, 256].  Same dtype / shape support as pa_forward.
+ * Every seq_len must be >= 1.
+ */
+PA_API pa_status pa_decode_split(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, const int32_t* seq_lens,
+                          float scale, int32_t num_splits, float* part_out,
+                          float* part_lse, const pa_dims* dims, void* stream);
+
+/*
+ * pa_merge_lse — second launch: log-sum-exp merge of split partials ([TDD]
+ * section "Parallel tiled softmax (3D kernel)"; [ROC] bullet "Chunked context
+ * processing").  For each of num_rows rows:
+ *   M = max_s lse_s,  w_s = exp(lse_s - M) (0 for lse_s = -inf),
+ *   out = sum_s w_s o_s / sum_s w_s,  lse = M + ln sum_s w_s;
+ * a row whose partitions are all empty gives zeros and -inf.
+ *   part_out float32 [num_rows, S, Dv], part_lse float32 [num_rows, S]
+ *   out      [num_rows, Dv] in out_dtype (pa_dtype), lse float32 [num_rows] or NULL
+ * num_splits in [1, 256], head_dim_v in [1, 1024].
+ */
+PA_API pa_status pa_merge_lse(const float* part_out, const float* part_lse, int32_t num_rows,
+                       int32_t num_splits, int32_t head_dim_v, void* out, float* lse,
+                       int32_t out_dtype, void* stream);
+
+/*
+ * Bytes of workspace mla_decode needs for these dims and num_splits
+ * (0 = the automatic choice mla_decode makes); 0 if the dims are invalid.
+ */
+PA_API size_t mla_workspace_size(const pa_dims* dims, int32_t num_splits);
+
+/*
+ * mla_decode — absorbed multi-head latent attention decode ([ROC] sections
+ * "AITER MLA backend" and "Hybrid processing strategy"): one query token per
+ * request; all Hq heads share one cached 576-wide latent row per token, which
+ * is the key (576 columns) and, through its first 512 columns, the value.
+ *   q        bf16 [B, Hq, 576]
+ *   kv_cache bf16 [num_pages, P, 576]
+ *   out      bf16 [B, Hq, 512];  lse float32 [B, Hq] or NULL
+ * The keys of each request are split into num_splits page-aligned partitions
+ * (as in pa_decode_split; 0 picks a count from B and the capacities) and
+ * merged by log-sum-exp.  Requires bf16, Hkv == 1, Dqk == 576, Dv == 512,
+ * Hq a multiple of 16 up to 128, P a multiple of 8 up to 256, seq_len >= 1.
+ */
+PA_API pa_status mla_decode(const void* q, const void* kv_cache, const int32_t* block_table,
+                     const int32_t* seq_lens, float scale, void* out, float* lse,
+                     int32_t num_splits, const pa_dims* dims, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
+ * pa_validate — synchronous debug check of the device contents a pa_forward
+ * call would read: query_start_loc[0] == 0, non-decreasing, query_start_loc[B]
+ * <= num_tokens, 0 <= q_len <= max_q_len, q_len <= seq_len <= max_seq_len,
+ * ceil(seq_len / P) <= max_pages_per_seq and every used block-table entry in
+ * [0, num_pages).  query_start_loc may be NULL (then every q_len is 1).
+ * Returns PA_OK, PA_ERR_DEVICE_DATA (with the first bad request in
+ * *bad_seq when bad_seq is not NULL), PA_ERR_INVALID_ARG or PA_ERR_HIP.
+ * Copies the three index arrays to the host and waits for `stream`.
+ */
+PA_API pa_status pa_validate(const int32_t* block_table, const int32_t* seq_lens,
+                      const int32_t* query_start_loc, const pa_dims* dims,
+                      int32_t* bad_seq, void* stream);
+
+/*
+ * pa_set_kernel_events — measurement hook.  When both events are non-NULL
+ * (hipEvent_t, created by the caller), every later pa_forward, pa_decode_split
+ * and mla_decode call made from THIS thread records `start` on its stream
+ * immediately before launching its attention kernel and `stop` immediately
+ * after it, so the caller can time that one kernel without the planner or the
+ * merge.  Passing NULL for either turns the hook off.  Returns PA_OK.
+ */
+PA_API pa_status pa_set_kernel_events(void* start, void* stop);
+
+/* Static, human-readable name of a status code. */
+PA_API const char* pa_status_string(pa_status status);
+
+/* hipError_t of the last PA_ERR_HIP returned on this thread (0 if none). */
+PA_API int32_t pa_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,428 @@
+// pa_api.hip — the C ABI declared in include/pa.h: host-side argument checks,
+// workspace sizing, per-device launch configuration and the launch sequences.
+// Nothing here synchronises, allocates or touches device memory except
+// pa_validate, which is documented as a synchronous debug call.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <map>
+#include <mutex>
+#include <vector>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+thread_local hipEvent_t g_ev_start = nullptr;
+thread_local hipEvent_t g_ev_stop = nullptr;
+
+// Records the measurement hook's event (if set) on stream s.
+hipError_t mark(hipEvent_t ev, hipStream_t s) {
+  return (g_ev_start && g_ev_stop) ? hipEventRecord(ev, s) : hipSuccess;
+}
+
+pa_status hip_fail(hipError_t e) {
+  g_last_hip_error = (int32_t)e;
+  return PA_ERR_HIP;
+}
+
+struct DevCfg {
+  int cu_count = 0;
+  int occ[2][2] = {{0, 0}, {0, 0}};  // [D == 128][decode_only]
+};
+
+std::mutex g_mu;
+std::map<int, DevCfg> g_cfg;
+
+pa_status device_config(DevCfg* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_cfg.find(dev);
+  if (it == g_cfg.end()) {
+    DevCfg c;
+    e = hipDeviceGetAttribute(&c.cu_count, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e);
+    for (int di = 0; di < 2; ++di)
+      for (int dd = 0; dd < 2; ++dd) {
+        e = pa::mha_occupancy(di ? 128 : 64, dd != 0, &c.occ[di][dd]);
+        if (e != hipSuccess) return hip_fail(e);
+        if (c.occ[di][dd] < 1) c.occ[di][dd] = 1;
+      }
+    it = g_cfg.emplace(dev, c).first;
+  }
+  *out = it->second;
+  return PA_OK;
+}
+
+// Shape checks common to every call.  Returns PA_OK or PA_ERR_INVALID_ARG.
+pa_status check_dims(const pa_dims* d) {
+  if (!d) return PA_ERR_INVALID_ARG;
+  if (d->num_seqs < 0 || d->num_tokens < 0 || d->num_q_heads <= 0 || d->num_kv_heads <= 0 ||
+      d->head_dim_qk <= 0 || d->head_dim_v <= 0 || d->page_size <= 0 || d->num_pages <= 0 ||
+      d->max_pages_per_seq <= 0 || d->max_seq_len < 0 || d->max_q_len < 0)
+    return PA_ERR_INVALID_ARG;
+  if (d->num_q_heads % d->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (d->dtype != PA_F32 && d->dtype != PA_BF16) return PA_ERR_INVALID_ARG;
+  if ((int64_t)d->max_pages_per_seq * d->page_size < d->max_seq_len) return PA_ERR_INVALID_ARG;
+  if (d->max_q_len > d->max_seq_len) return PA_ERR_INVALID_ARG;
+  if ((int64_t)d->num_tokens * d->num_q_heads > INT32_MAX) return PA_ERR_INVALID_ARG;
+  return PA_OK;
+}
+
+// Support check for the MHA kernels (pa_forward / pa_decode_split).
+pa_status check_mha_support(const pa_dims* d) {
+  if (d->dtype == PA_BF16) {
+    if (d->head_dim_qk != d->head_dim_v) return PA_ERR_UNSUPPORTED;
+    if (d->head_dim_qk != 64 && d->head_dim_qk != 128) return PA_ERR_UNSUPPORTED;
+    if (d->page_size % 8 != 0 || d->page_size > 256) return PA_ERR_UNSUPPORTED;
+  } else {
+    if (d->head_dim_qk > 256 || d->head_dim_v > 256) return PA_ERR_UNSUPPORTED;
+  }
+  return PA_OK;
+}
+
+int mla_auto_splits(const pa_dims* d, int cu_count) {
+  const int B = std::max(1, d->num_seqs);
+  int s = (2 * cu_count + B - 1) / B;
+  const int max_pages = (d->max_seq_len + d->page_size - 1) / d->page_size;
+  s = std::min(s, std::max(1, max_pages));
+  return std::max(1, std::min(s, 64));
+}
+
+size_t mla_ws_bytes(const pa_dims* d, int S) {
+  if (S <= 1) return 256;  // nothing needed; keep a non-zero size
+  const size_t rows = (size_t)d->num_seqs * d->num_q_heads;
+  const size_t lse_bytes = ((rows * S * sizeof(float)) + 255) & ~(size_t)255;
+  return lse_bytes + rows * S * 512 * sizeof(float);
+}
+
+pa_status check_mla(const pa_dims* d) {
+  pa_status st = check_dims(d);
+  if (st != PA_OK) return st;
+  if (d->dtype != PA_BF16 || d->num_kv_heads != 1 || d->head_dim_qk != 576 ||
+      d->head_dim_v != 512)
+    return PA_ERR_UNSUPPORTED;
+  if (d->num_q_heads % 16 != 0 || d->num_q_heads > 128) return PA_ERR_UNSUPPORTED;
+  if (d->page_size % 8 != 0 || d->page_size > 256) return PA_ERR_UNSUPPORTED;
+  if (d->num_tokens != d->num_seqs) return PA_ERR_INVALID_ARG;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_HIP: return "HIP error";
+    case PA_ERR_DEVICE_DATA: return "invalid device data";
+  }
+  return "unknown status";
+}
+
+int32_t pa_last_hip_error(void) { return g_last_hip_error; }
+
+pa_status pa_set_kernel_events(void* start, void* stop) {
+  g_ev_start = (start && stop) ? (hipEvent_t)start : nullptr;
+  g_ev_stop = (start && stop) ? (hipEvent_t)stop : nullptr;
+  return PA_OK;
+}
+
+size_t pa_workspace_size(const pa_dims* d) {
+  if (check_dims(d) != PA_OK) return 0;
+  if (d->dtype == PA_F32) return 256;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  return pa::fwd_workspace_layout(d->num_seqs, d->num_tokens, d->num_kv_heads, G, d->head_dim_v)
+      .total;
+}
+
+pa_status pa_forward(const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_table, const int32_t* seq_lens,
+                     const int32_t* query_start_loc, float scale, void* out, float* lse,
+                     const pa_dims* d, void* workspace, size_t workspace_bytes, void* stream) {
+  pa_status st = check_dims(d);
+  if (st != PA_OK) return st;
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !query_start_loc || !out)
+    return PA_ERR_INVALID_ARG;
+  st = check_mha_support(d);
+  if (st != PA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if (d->num_seqs == 0 || d->num_tokens == 0) return PA_OK;
+
+  if (d->dtype == PA_F32) {
+    pa::F32Args a{};
+    a.q = (const float*)q;
+    a.k_cache = (const float*)k_cache;
+    a.v_cache = (const float*)v_cache;
+    a.block_table = block_table;
+    a.seq_lens = seq_lens;
+    a.qsl = query_start_loc;
+    a.out = (float*)out;
+    a.lse = lse;
+    a.scale = scale;
+    a.B = d->num_seqs;
+    a.T = d->num_tokens;
+    a.Hq = d->num_q_heads;
+    a.Hkv = d->num_kv_heads;
+    a.G = G;
+    a.Dqk = d->head_dim_qk;
+    a.Dv = d->head_dim_v;
+    a.P = d->page_size;
+    a.max_pages = d->max_pages_per_seq;
+    a.num_splits = 1;
+    hipError_t e = mark(g_ev_start, s);
+    if (e == hipSuccess) e = pa::launch_f32_forward(a, s);
+    if (e == hipSuccess) e = mark(g_ev_stop, s);
+    return e == hipSuccess ? PA_OK : hip_fail(e);
+  }
+
+  const int D = d->head_dim_qk;
+  const pa::FwdWorkspace w = pa::fwd_workspace_layout(d->num_seqs, d->num_tokens,
+                                                      d->num_kv_heads, G, D);
+  if (!workspace || workspace_bytes < w.total) return PA_ERR_WORKSPACE;
+  DevCfg cfg;
+  st = device_config(&cfg);
+  if (st != PA_OK) return st;
+  const bool decode_only = (int64_t)d->max_q_len * G <= pa::kDecodeRows;
+  const int grid = cfg.cu_count * cfg.occ[D == 128][decode_only ? 1 : 0];
+
+  char* ws = (char*)workspace;
+  pa::Control* ctrl = (pa::Control*)(ws + w.ctrl_off);
+  pa::WorkItem* items = (pa::WorkItem*)(ws + w.items_off);
+  pa::MergeItem* merges = (pa::MergeItem*)(ws + w.merges_off);
+
+  pa::PlanArgs pl{};
+  pl.seq_lens = seq_lens;
+  pl.qsl = query_start_loc;
+  pl.items = items;
+  pl.merges = merges;
+  pl.ctrl = ctrl;
+  pl.B = d->num_seqs;
+  pl.Hkv = d->num_kv_heads;
+  pl.G = G;
+  pl.P = d->page_size;
+  pl.max_pages = d->max_pages_per_seq;
+  pl.target_items = std::max(1, 2 * grid);
+  hipError_t e = pa::launch_plan(pl, s);
+  if (e != hipSuccess) return hip_fail(e);
+
+  pa::MhaArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.qsl = query_start_loc;
+  a.out = out;
+  a.lse = lse;
+  a.part_o = (float*)(ws + w.po_off);
+  a.part_lse = (float*)(ws + w.plse_off);
+  a.items = items;
+  a.merges = merges;
+  a.ctrl = ctrl;
+  a.scale = scale;
+  a.num_seqs = d->num_seqs;
+  a.Hq = d->num_q_heads;
+  a.Hkv = d->num_kv_heads;
+  a.G = G;
+  a.P = d->page_size;
+  a.max_pages = d->max_pages_per_seq;
+  a.num_splits = 1;
+  if ((e = mark(g_ev_start, s)) != hipSuccess) return hip_fail(e);
+  e = pa::launch_mha_forward(a, D, decode_only, grid, s);
+  if (e != hipSuccess) return hip_fail(e);
+  if ((e = mark(g_ev_stop, s)) != hipSuccess) return hip_fail(e);
+  e = pa::launch_mha_forward_merge(a, D, std::max(1, cfg.cu_count * 2), s);
+  if (e != hipSuccess) return hip_fail(e);
+  return PA_OK;
+}
+
+pa_status pa_decode_split(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, const int32_t* seq_lens, float scale,
+                          int32_t num_splits, float* part_out, float* part_lse,
+                          const pa_dims* d, void* stream) {
+  pa_status st = check_dims(d);
+  if (st != PA_OK) return st;
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !part_out || !part_lse)
+    return PA_ERR_INVALID_ARG;
+  if (num_splits < 1 || num_splits > pa::kMaxSplits) return PA_ERR_INVALID_ARG;
+  if (d->num_tokens != d->num_seqs) return PA_ERR_INVALID_ARG;
+  st = check_mha_support(d);
+  if (st != PA_OK) return st;
+  if (d->num_seqs == 0) return PA_OK;
+  if ((int64_t)d->num_seqs * d->num_q_heads * num_splits > INT32_MAX) return PA_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  hipError_t e = mark(g_ev_start, s);
+  if (e != hipSuccess) return hip_fail(e);
+  if (d->dtype == PA_F32) {
+    pa::F32Args a{};
+    a.q = (const float*)q;
+    a.k_cache = (const float*)k_cache;
+    a.v_cache = (const float*)v_cache;
+    a.block_table = block_table;
+    a.seq_lens = seq_lens;
+    a.qsl = nullptr;
+    a.part_o = part_out;
+    a.part_lse = part_lse;
+    a.scale = scale;
+    a.B = d->num_seqs;
+    a.T = d->num_seqs;
+    a.Hq = d->num_q_heads;
+    a.Hkv = d->num_kv_heads;
+    a.G = G;
+    a.Dqk = d->head_dim_qk;
+    a.Dv = d->head_dim_v;
+    a.P = d->page_size;
+    a.max_pages = d->max_pages_per_seq;
+    a.num_splits = num_splits;
+    e = pa::launch_f32_split(a, s);
+  } else {
+    pa::MhaArgs a{};
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_table = block_table;
+    a.seq_lens = seq_lens;
+    a.qsl = nullptr;
+    a.part_o = part_out;
+    a.part_lse = part_lse;
+    a.scale = scale;
+    a.num_seqs = d->num_seqs;
+    a.Hq = d->num_q_heads;
+    a.Hkv = d->num_kv_heads;
+    a.G = G;
+    a.P = d->page_size;
+    a.max_pages = d->max_pages_per_seq;
+    a.num_splits = num_splits;
+    e = pa::launch_mha_split(a, d->head_dim_qk, s);
+  }
+  if (e == hipSuccess) e = mark(g_ev_stop, s);
+  return e == hipSuccess ? PA_OK : hip_fail(e);
+}
+
+pa_status pa_merge_lse(const float* part_out, const float* part_lse, int32_t num_rows,
+                       int32_t num_splits, int32_t head_dim_v, void* out, float* lse,
+                       int32_t out_dtype, void* stream) {
+  if (!part_out || !part_lse || !out) return PA_ERR_INVALID_ARG;
+  if (num_rows < 0 || num_splits < 1 || num_splits > pa::kMaxSplits || head_dim_v < 1 ||
+      head_dim_v > 1024)
+    return PA_ERR_INVALID_ARG;
+  if (out_dtype != PA_F32 && out_dtype != PA_BF16) return PA_ERR_INVALID_ARG;
+  hipError_t e = pa::launch_merge(part_out, part_lse, num_rows, num_splits, head_dim_v, out,
+                                  out_dtype == PA_BF16, lse, (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : hip_fail(e);
+}
+
+size_t mla_workspace_size(const pa_dims* d, int32_t num_splits) {
+  if (check_mla(d) != PA_OK || num_splits < 0 || num_splits > 64) return 0;
+  int S = num_splits;
+  if (S == 0) {
+    DevCfg cfg;
+    if (device_config(&cfg) != PA_OK) return 0;
+    S = mla_auto_splits(d, cfg.cu_count);
+  }
+  return mla_ws_bytes(d, S);
+}
+
+pa_status mla_decode(const void* q, const void* kv_cache, const int32_t* block_table,
+                     const int32_t* seq_lens, float scale, void* out, float* lse,
+                     int32_t num_splits, const pa_dims* d, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  pa_status st = check_mla(d);
+  if (st != PA_OK) return st;
+  if (!q || !kv_cache || !block_table || !seq_lens || !out) return PA_ERR_INVALID_ARG;
+  if (num_splits < 0 || num_splits > 64) return PA_ERR_INVALID_ARG;
+  if (d->num_seqs == 0) return PA_OK;
+  int S = num_splits;
+  if (S == 0) {
+    DevCfg cfg;
+    st = device_config(&cfg);
+    if (st != PA_OK) return st;
+    S = mla_auto_splits(d, cfg.cu_count);
+  }
+  if ((int64_t)d->num_seqs * S > INT32_MAX) return PA_ERR_INVALID_ARG;
+  const size_t need = mla_ws_bytes(d, S);
+  if (S > 1 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+  const size_t rows = (size_t)d->num_seqs * d->num_q_heads;
+  const size_t lse_bytes = ((rows * S * sizeof(float)) + 255) & ~(size_t)255;
+  pa::MlaArgs a{};
+  a.q = q;
+  a.kv = kv_cache;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.lse = lse;
+  a.part_lse = S > 1 ? (float*)workspace : nullptr;
+  a.part_o = S > 1 ? (float*)((char*)workspace + lse_bytes) : nullptr;
+  a.scale = scale;
+  a.B = d->num_seqs;
+  a.Hq = d->num_q_heads;
+  a.P = d->page_size;
+  a.max_pages = d->max_pages_per_seq;
+  a.num_splits = S;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = mark(g_ev_start, s);
+  if (e == hipSuccess) e = pa::launch_mla_split(a, s);
+  if (e == hipSuccess) e = mark(g_ev_stop, s);
+  if (e != hipSuccess) return hip_fail(e);
+  if (S > 1) {
+    e = pa::launch_merge(a.part_o, a.part_lse, (int)rows, S, 512, out, true, lse, s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return PA_OK;
+}
+
+pa_status pa_validate(const int32_t* block_table, const int32_t* seq_lens,
+                      const int32_t* query_start_loc, const pa_dims* d, int32_t* bad_seq,
+                      void* stream) {
+  pa_status st = check_dims(d);
+  if (st != PA_OK) return st;
+  if (!block_table || !seq_lens) return PA_ERR_INVALID_ARG;
+  if (bad_seq) *bad_seq = -1;
+  const int B = d->num_seqs;
+  if (B == 0) return PA_OK;
+  hipStream_t s = (hipStream_t)stream;
+  std::vector<int32_t> bt((size_t)B * d->max_pages_per_seq), sl(B), qs(B + 1);
+  hipError_t e = hipMemcpyAsync(bt.data(), block_table, bt.size() * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(sl.data(), seq_lens, sl.size() * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess && query_start_loc)
+    e = hipMemcpyAsync(qs.data(), query_start_loc, qs.size() * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e);
+  if (!query_start_loc)
+    for (int b = 0; b <= B; ++b) qs[b] = b;
+  int bad = -1;
+  if (qs[0] != 0) bad = 0;
+  for (int b = 0; b < B && bad < 0; ++b) {
+    const int nq = qs[b + 1] - qs[b], L = sl[b];
+    bool ok = nq >= 0 && nq <= d->max_q_len && L >= nq && L <= d->max_seq_len;
+    if (!query_start_loc && L < 1) ok = false;
+    if (ok) {
+      const int64_t np = ((int64_t)L + d->page_size - 1) / d->page_size;
+      if (np > d->max_pages_per_seq) ok = false;
+      for (int64_t i = 0; i < np && ok; ++i) {
+        const int32_t pg = bt[(size_t)b * d->max_pages_per_seq + i];
+        if (pg < 0 || pg >= d->num_pages) ok = false;
+      }
+    }
+    if (!ok) bad = b;
+  }
+  if (bad < 0 && qs[B] > d->num_tokens) bad = B - 1;
+  if (bad >= 0) {
+    if (bad_seq) *bad_seq = bad;
+    return PA_ERR_DEVICE_DATA;
+  }
+  return PA_OK;
+}
+
+}  // extern "C"

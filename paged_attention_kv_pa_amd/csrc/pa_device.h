@@ -1,0 +1,135 @@
+// pa_device.h — device-side building blocks shared by the gfx950 kernels:
+// vector types, the bf16 MFMA, 16-byte loads, bf16 packing, wave reductions.
+//
+// Lane layout of v_mfma_f32_16x16x32_bf16 (64 lanes, lane l, group g = l / 16,
+// r = l % 16):  A[m][k] (16 x 32): lane holds A[r][8g .. 8g+7];
+//               B[k][n] (32 x 16): lane holds B[8g .. 8g+7][r];
+//               D[m][n] (16 x 16): lane holds D[4g .. 4g+3][r].
+// The contraction index only has to be laid out the same way in A and B, so
+// the kernels are free to permute which key / column a K-slot stands for.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float floatx4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ floatx4 mfma_bf16(const bf16x8& a, const bf16x8& b,
+                                             const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ void store16(void* p, const u32x4& v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ u32x4 as_u32x4(const bf16x8& v) {
+  return __builtin_bit_cast(u32x4, v);
+}
+
+// bf16 (raw 16-bit pattern) -> float, exact.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two floats -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  bf16x2 v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Butterfly reductions across the 4 lane groups (lanes l, l^16, l^32, l^48)
+// that hold the same MFMA row.
+__device__ __forceinline__ float group_max4(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float group_sum4(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+// Full 64-lane reductions.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Zero the bf16 elements i (0..7) of a 16-byte group whose key index
+// key0 + i is >= limit.
+__device__ __forceinline__ u32x4 zero_tail8(u32x4 v, int key0, int limit) {
+  int n = limit - key0;  // number of valid leading elements
+  if (n >= 8) return v;
+  uint32_t w[4] = {v[0], v[1], v[2], v[3]};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t m = 0;
+    if (2 * j < n) m |= 0x0000ffffu;
+    if (2 * j + 1 < n) m |= 0xffff0000u;
+    w[j] &= m;
+  }
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+// One unit of work of the persistent MHA kernel: rows = (new token x query
+// head of one KV head) of one request over the key range [kv_begin, kv_end).
+struct WorkItem {
+  int32_t seq;       // request
+  int32_t kvh;       // KV head
+  int32_t row0;      // first row; row index = token_in_request * G + head_in_group
+  int32_t nrows;     // rows in the item
+  int32_t kv_begin;  // first key (multiple of 8)
+  int32_t kv_end;    // one past the last key any row of the item may see
+  int32_t part;      // < 0: write the final output; >= 0: partial slot
+  int32_t pad;
+};
+
+// Merge of the partial slots of one split (request, KV head): the rows of
+// slots [slot0, slot0 + nsplit) are combined into the final output.
+struct MergeItem {
+  int32_t seq;
+  int32_t kvh;
+  int32_t slot0;
+  int32_t nsplit;
+  int32_t nrows;
+  int32_t pad[3];
+};
+
+// Control block at the start of the pa_forward workspace.
+struct Control {
+  int32_t n_items;
+  int32_t n_merge;
+  int32_t work_counter;
+  int32_t pad[61];
+};
+
+}  // namespace pa

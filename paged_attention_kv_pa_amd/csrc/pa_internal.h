@@ -1,0 +1,106 @@
+// pa_internal.h — host-side interface between the C ABI (pa_api.hip) and the
+// kernel files.  Each kernel file owns its kernels and the launcher that
+// starts them; launchers only enqueue work and return the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_device.h"
+
+namespace pa {
+
+// Tunables shared by the planner, the workspace sizing and the kernels.
+constexpr int kThreads = 256;          // threads of an MHA workgroup (4 waves)
+constexpr int kDecodeRows = 16;        // rows of one decode-mode item (one MFMA tile)
+constexpr int kPrefillRowTiles = 2;    // 16-row tiles per wave in prefill mode
+constexpr int kPrefillRows = 4 * 16 * kPrefillRowTiles;  // rows of a prefill-mode item
+constexpr int kMaxFwdSplits = 64;      // key partitions per decode row in pa_forward
+constexpr int kMinChunk = 256;         // smallest key partition pa_forward makes
+constexpr int kMaxSplits = 256;        // pa_decode_split / pa_merge_lse / mla_decode limit
+
+struct MhaArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const int32_t* qsl;        // NULL: one query token per request (token index == request)
+  void* out;
+  float* lse;                // may be NULL
+  float* part_o;             // partial outputs (split items)
+  float* part_lse;
+  const WorkItem* items;
+  const MergeItem* merges;
+  Control* ctrl;
+  float scale;
+  int32_t num_seqs;
+  int32_t Hq, Hkv, G, P, max_pages;
+  int32_t num_splits;        // pa_decode_split only
+};
+
+struct PlanArgs {
+  const int32_t* seq_lens;
+  const int32_t* qsl;
+  WorkItem* items;
+  MergeItem* merges;
+  Control* ctrl;
+  int32_t B, Hkv, G;
+  int32_t P, max_pages;
+  int32_t target_items;
+};
+
+struct F32Args {
+  const float* q;
+  const float* k_cache;
+  const float* v_cache;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const int32_t* qsl;        // NULL in split mode
+  float* out;                // forward mode
+  float* lse;
+  float* part_o;             // split mode [B, Hq, S, Dv]
+  float* part_lse;
+  float scale;
+  int32_t B, T, Hq, Hkv, G, Dqk, Dv, P, max_pages, num_splits;
+};
+
+struct MlaArgs {
+  const void* q;             // bf16 [B, Hq, 576]
+  const void* kv;            // bf16 [pages, P, 576]
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  void* out;                 // bf16 [B, Hq, 512] (num_splits == 1)
+  float* lse;
+  float* part_o;             // [B, Hq, S, 512] (num_splits > 1)
+  float* part_lse;           // [B, Hq, S]
+  float scale;
+  int32_t B, Hq, P, max_pages, num_splits;
+};
+
+// Device properties cached per device by the ABI layer.
+struct DeviceInfo {
+  int cu_count;
+  int fwd_blocks_per_cu_mixed[2];   // [D == 128] persistent kernel occupancy
+  int fwd_blocks_per_cu_decode[2];
+};
+
+// Workspace layout of pa_forward.
+struct FwdWorkspace {
+  size_t ctrl_off, items_off, merges_off, plse_off, po_off, total;
+  int64_t cap_items, cap_merges, cap_slots;
+};
+FwdWorkspace fwd_workspace_layout(int B, int T, int Hkv, int G, int D);
+
+hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+hipError_t launch_mha_forward(const MhaArgs& a, int D, bool decode_only, int grid, hipStream_t s);
+hipError_t launch_mha_forward_merge(const MhaArgs& a, int D, int grid, hipStream_t s);
+hipError_t launch_mha_split(const MhaArgs& a, int D, hipStream_t s);
+hipError_t mha_occupancy(int D, bool decode_only, int* blocks_per_cu);
+hipError_t launch_merge(const float* po, const float* pl, int rows, int S, int Dv, void* out,
+                        bool out_bf16, float* lse, hipStream_t s);
+hipError_t launch_f32_forward(const F32Args& a, hipStream_t s);
+hipError_t launch_f32_split(const F32Args& a, hipStream_t s);
+hipError_t launch_mla_split(const MlaArgs& a, hipStream_t s);
+
+}  // namespace pa

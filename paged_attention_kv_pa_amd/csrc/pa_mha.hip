@@ -1,0 +1,797 @@
+// pa_mha.hip — bf16 paged attention on gfx950 matrix cores (MHA / GQA).
+//
+// Method (sources: "vLLM Triton Attention Backend Deep Dive" [TDD] and
+// "vLLM AMD ROCm Attention Backend Optimization" [ROC]):
+//   * paged attention: keys and values are fetched page by page through the
+//     block table ([TDD] "Technical implementation of paged attention");
+//   * Q-block: the rows of one work item are (new token x query head of one KV
+//     head), so one KV load serves every query head of the group
+//     ([TDD] "Q-block optimization");
+//   * split KV + second-launch log-sum-exp merge for decode rows
+//     ([TDD] "Parallel tiled softmax (3D kernel)"; [ROC] "Chunked context
+//     processing");
+//   * persistent kernel: a fixed grid pulls work items that a planner kernel
+//     wrote to device memory, so the launch is graph-capturable
+//     ([TDD] "Persistent kernels and CUDA graphs").
+//
+// Both matrix products run on v_mfma_f32_16x16x32_bf16 with fp32 accumulation
+// and are formed transposed, S^T = K Q^T and O^T = V^T P^T, so that every row
+// statistic of the online softmax stays inside one lane:
+//   * lane l (group g = l / 16, r = l % 16) owns query row r of a 16-row tile;
+//   * in S^T the A operand is K with its 16 M-rows permuted so that, for the two
+//     16-key M-tiles of a 32-key step, lane group g receives keys 8g .. 8g+7 —
+//     exactly the 8 contraction slots it must supply as the B operand (P^T) of
+//     the value product;
+//   * in O^T the A operand is V^T, read 16 bytes at a time straight from the
+//     column-major value page ([dim][slot]); the lane's accumulator holds
+//     O[r][16 dt + 4g + i].
+// Softmax runs in base 2 on fp32 scores (scale * log2 e folded into one FMA);
+// the probabilities are rounded to bf16 for the value product.
+#include <type_traits>
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kTK = 64;  // keys per LDS tile in prefill mode
+
+// Key that M-row m of M-tile mt (0, 1) of a 32-key step stands for.
+__device__ __forceinline__ int kperm(int mt, int m) { return 8 * (m >> 2) + 4 * mt + (m & 3); }
+
+// Where the rows of an item go.
+struct Dest {
+  bool partial;
+  int64_t po_base, po_row;  // partial output offsets (elements)
+  int64_t pl_base, pl_row;
+};
+
+struct RowMap {
+  int q0;    // first query row of the request in q / out
+  int ctx;   // cached keys before the new tokens
+};
+
+__device__ __forceinline__ RowMap row_map(const MhaArgs& a, int b) {
+  RowMap m;
+  const int L = a.seq_lens[b];
+  if (a.qsl) {
+    m.q0 = a.qsl[b];
+    m.ctx = L - (a.qsl[b + 1] - m.q0);
+  } else {
+    m.q0 = b;
+    m.ctx = L - 1;
+  }
+  return m;
+}
+
+template <int D>
+struct alignas(16) LdsDecode {
+  static constexpr int kOStride = D + 4;  // floats per row of the merge buffer
+  float m[4][16];
+  float l[4][16];
+  float o[4][16][kOStride];
+};
+
+template <int D>
+struct alignas(16) LdsPrefill {
+  static constexpr int kKRow = D + 8;    // bf16 per K row (16 B pad)
+  static constexpr int kVRow = kTK + 8;  // bf16 per V^T row (16 B pad)
+  __bf16 k[2][kTK * kKRow];
+  __bf16 v[2][D * kVRow];
+};
+
+// Write one finished row: o[] are this thread's `n` consecutive columns
+// starting at column c0, already divided by the row sum.
+template <int D, int N>
+__device__ __forceinline__ void store_row_chunk(const MhaArgs& a, const Dest& dst, int row,
+                                                int64_t out_row, int c0, const float* o) {
+  if (dst.partial) {
+    float* p = a.part_o + dst.po_base + (int64_t)row * dst.po_row + c0;
+#pragma unroll
+    for (int e = 0; e < N; e += 4) store16(p + e, __builtin_bit_cast(u32x4, floatx4{o[e], o[e + 1], o[e + 2], o[e + 3]}));
+  } else {
+    __bf16* p = (__bf16*)a.out + out_row * D + c0;
+    if constexpr (N == 8) {
+      store16(p, u32x4{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                       pack_bf16x2(o[6], o[7])});
+    } else {
+      *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    }
+  }
+}
+
+__device__ __forceinline__ void store_lse(const MhaArgs& a, const Dest& dst, int row,
+                                          int64_t out_row, float v) {
+  if (dst.partial) {
+    a.part_lse[dst.pl_base + (int64_t)row * dst.pl_row] = v;
+  } else if (a.lse) {
+    a.lse[out_row] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode mode: an item of at most 16 rows.  The 4 waves take interleaved
+// 32-key steps of the item's key range straight from global memory into MFMA
+// operands (no LDS staging: nothing is shared between waves), then merge their
+// partial softmax states through LDS.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ void run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest& dst,
+                                LdsDecode<D>& sm) {
+  constexpr int KS = D / 32, DT = D / 16;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
+  const int b = it.seq, kvh = it.kvh, G = a.G, P = a.P;
+  const RowMap rm = row_map(a, b);
+  const int kv_end = it.kv_end;
+
+  // this lane's query row
+  const bool row_ok = r < it.nrows;
+  const int ridx = it.row0 + r;
+  const int tok = ridx / G;
+  const int head = kvh * G + (ridx - tok * G);
+  const int lim = row_ok ? min(rm.ctx + tok + 1, kv_end) : it.kv_begin;
+
+  bf16x8 qf[KS];
+  {
+    const __bf16* qp = (const __bf16*)a.q + ((int64_t)(rm.q0 + tok) * a.Hq + head) * D + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = row_ok ? as_bf16x8(load16(qp + 32 * ks)) : as_bf16x8(u32x4{0, 0, 0, 0});
+  }
+
+  const float sc = a.scale * kLog2e;
+  float m = kNegInf, l = 0.f;
+  floatx4 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
+  const int64_t page_elems = (int64_t)a.Hkv * P * D;
+  const __bf16* kbase = (const __bf16*)a.k_cache + (int64_t)kvh * P * D + 8 * g;
+  const __bf16* vbase = (const __bf16*)a.v_cache + (int64_t)kvh * D * P + (int64_t)r * P;
+  const int last8 = (kv_end - 1) & ~7;
+
+  for (int t0 = it.kv_begin + 32 * wave; t0 < kv_end; t0 += 128) {
+    // K operand rows (clamped into the valid range; masked below)
+    bf16x8 kf[2][KS];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int key = min(t0 + kperm(mt, r), kv_end - 1);
+      const int page = bt[key / P];
+      const __bf16* kp = kbase + (int64_t)page * page_elems + (key % P) * D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kf[mt][ks] = as_bf16x8(load16(kp + 32 * ks));
+    }
+    // V^T operand: keys t0+8g .. t0+8g+7 of column 16dt + r
+    bf16x8 vf[DT];
+    {
+      const int key8 = min(t0 + 8 * g, last8);
+      const int page = bt[key8 / P];
+      const __bf16* vp = vbase + (int64_t)page * page_elems + (key8 % P);
+      const bool tail = t0 + 32 > kv_end;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        u32x4 raw = load16(vp + (int64_t)16 * dt * P);
+        if (tail) raw = zero_tail8(raw, t0 + 8 * g, kv_end);
+        vf[dt] = as_bf16x8(raw);
+      }
+    }
+    // S^T = K Q^T
+    floatx4 s[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s[0] = mfma_bf16(kf[0][ks], qf[ks], s[0]);
+      s[1] = mfma_bf16(kf[1][ks], qf[ks], s[1]);
+    }
+    // online softmax on keys t0 + 8g + j, j = 0..7
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int key = t0 + 8 * g + j;
+      const float v = s[j >> 2][j & 3];
+      x[j] = key < lim ? v : kNegInf;
+    }
+    float tmax = x[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) tmax = fmaxf(tmax, x[j]);
+    tmax = group_max4(tmax);
+    const float mnew = fmaxf(m, tmax);
+    const float muse = mnew == kNegInf ? 0.f : mnew;
+    const float alpha = fast_exp2((m - muse) * sc);
+    const float msc = muse * sc;
+    float p[8], psum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      p[j] = fast_exp2(fmaf(x[j], sc, -msc));
+      psum += p[j];
+    }
+    l = fmaf(l, alpha, psum);
+    m = mnew;
+    const bf16x8 pf = __builtin_bit_cast(
+        bf16x8, u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                      pack_bf16x2(p[6], p[7])});
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      acc[dt] *= alpha;
+      acc[dt] = mfma_bf16(vf[dt], pf, acc[dt]);
+    }
+  }
+
+  // merge the 4 waves' states
+  const float lrow = group_sum4(l);
+  if (g == 0) {
+    sm.m[wave][r] = m;
+    sm.l[wave][r] = lrow;
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+    store16(&sm.o[wave][r][16 * dt + 4 * g], __builtin_bit_cast(u32x4, acc[dt]));
+  __syncthreads();
+  {
+    constexpr int NC = D / 16;  // columns per thread
+    const int row = tid >> 4, c0 = (tid & 15) * NC;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm.m[w][row]);
+    float o[NC];
+#pragma unroll
+    for (int e = 0; e < NC; ++e) o[e] = 0.f;
+    float wsum = 0.f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = fast_exp2((sm.m[w][row] - M) * sc);
+        wsum = fmaf(f, sm.l[w][row], wsum);
+#pragma unroll
+        for (int e = 0; e < NC; ++e) o[e] = fmaf(f, sm.o[w][row][c0 + e], o[e]);
+      }
+    }
+    if (row < it.nrows) {
+      const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+      for (int e = 0; e < NC; ++e) o[e] *= inv;
+      const int rid = it.row0 + row;
+      const int t = rid / G;
+      const int64_t out_row = (int64_t)(rm.q0 + t) * a.Hq + kvh * G + (rid - t * G);
+      store_row_chunk<D, NC>(a, dst, row, out_row, c0, o);
+      if ((tid & 15) == 0)
+        store_lse(a, dst, row, out_row, wsum > 0.f ? M * a.scale + __log2f(wsum) * kLn2 : kNegInf);
+    }
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// Prefill mode: an item of up to 64 * NT rows; wave w owns rows
+// [16 NT w, 16 NT (w + 1)).  64-key tiles of K ([key][dim]) and V^T ([dim][key])
+// are staged in LDS, double buffered, and shared by the 4 waves.
+// ---------------------------------------------------------------------------
+template <int D, int NT>
+__device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Dest& dst,
+                                 LdsPrefill<D>& sm) {
+  constexpr int KS = D / 32, DT = D / 16;
+  constexpr int KROW = LdsPrefill<D>::kKRow, VROW = LdsPrefill<D>::kVRow;
+  constexpr int KCH = kTK * D / 8 / kThreads;  // 16-byte K chunks per thread per tile
+  constexpr int VCH = D * kTK / 8 / kThreads;  // 16-byte V chunks per thread per tile
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
+  const int b = it.seq, kvh = it.kvh, G = a.G, P = a.P;
+  const RowMap rm = row_map(a, b);
+  const int kv_begin = it.kv_begin, kv_end = it.kv_end;
+
+  // rows of this lane, one per row tile
+  int lim[NT];
+  int64_t out_row[NT];
+  bool row_ok[NT];
+  bf16x8 qf[NT][KS];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int row = 16 * (NT * wave + nt) + r;
+    row_ok[nt] = row < it.nrows;
+    const int rid = it.row0 + row;
+    const int t = rid / G;
+    const int head = kvh * G + (rid - t * G);
+    out_row[nt] = (int64_t)(rm.q0 + t) * a.Hq + head;
+    lim[nt] = row_ok[nt] ? min(rm.ctx + t + 1, kv_end) : kv_begin;
+    const __bf16* qp = (const __bf16*)a.q + out_row[nt] * D + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[nt][ks] = row_ok[nt] ? as_bf16x8(load16(qp + 32 * ks)) : as_bf16x8(u32x4{0, 0, 0, 0});
+  }
+  // largest key limit of the wave's rows (wave-uniform)
+  int wave_lim = kv_begin;
+  {
+    const int last_row = min(16 * NT * (wave + 1), it.nrows) - 1;
+    if (last_row >= 16 * NT * wave) {
+      const int t = (it.row0 + last_row) / G;
+      wave_lim = min(rm.ctx + t + 1, kv_end);
+    }
+  }
+
+  const float sc = a.scale * kLog2e;
+  float m[NT], l[NT];
+  floatx4 acc[NT][DT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    m[nt] = kNegInf;
+    l[nt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[nt][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
+  const int64_t page_elems = (int64_t)a.Hkv * P * D;
+  const __bf16* kbase = (const __bf16*)a.k_cache + (int64_t)kvh * P * D;
+  const __bf16* vbase = (const __bf16*)a.v_cache + (int64_t)kvh * D * P;
+  const int last8 = (kv_end - 1) & ~7;
+
+  u32x4 kreg[KCH], vreg[VCH];
+  auto gload = [&](int t0) {
+#pragma unroll
+    for (int j = 0; j < KCH; ++j) {
+      const int c = j * kThreads + tid;
+      const int key = min(t0 + c / (D / 8), kv_end - 1);
+      const int page = bt[key / P];
+      kreg[j] = load16(kbase + (int64_t)page * page_elems + (key % P) * D + (c % (D / 8)) * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < VCH; ++j) {
+      const int c = j * kThreads + tid;
+      const int dim = c / (kTK / 8);
+      const int key8 = t0 + 8 * (c % (kTK / 8));
+      const int kk = min(key8, last8);
+      const int page = bt[kk / P];
+      u32x4 raw = load16(vbase + (int64_t)page * page_elems + (int64_t)dim * P + (kk % P));
+      vreg[j] = zero_tail8(raw, key8, kv_end);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < KCH; ++j) {
+      const int c = j * kThreads + tid;
+      store16(&sm.k[buf][(c / (D / 8)) * KROW + (c % (D / 8)) * 8], kreg[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < VCH; ++j) {
+      const int c = j * kThreads + tid;
+      store16(&sm.v[buf][(c / (kTK / 8)) * VROW + (c % (kTK / 8)) * 8], vreg[j]);
+    }
+  };
+
+  const int ntiles = (kv_end - kv_begin + kTK - 1) / kTK;
+  if (ntiles > 0) {
+    gload(kv_begin);
+    lstore(0);
+  }
+  __syncthreads();
+  for (int ti = 0; ti < ntiles; ++ti) {
+    const int t0 = kv_begin + ti * kTK;
+    const int buf = ti & 1;
+    if (ti + 1 < ntiles) gload(t0 + kTK);
+    if (t0 < wave_lim) {
+      const __bf16* kt = sm.k[buf];
+      const __bf16* vt = sm.v[buf];
+      floatx4 s[NT][2][2];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) s[nt][kh][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 kf =
+                as_bf16x8(load16(kt + (32 * kh + kperm(mt, r)) * KROW + 32 * ks + 8 * g));
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) s[nt][kh][mt] = mfma_bf16(kf, qf[nt][ks], s[nt][kh][mt]);
+          }
+      bf16x8 pf[NT][2];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float x[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int kh = j >> 3, jj = j & 7;
+          const int key = t0 + 32 * kh + 8 * g + jj;
+          const float v = s[nt][kh][jj >> 2][jj & 3];
+          x[j] = key < lim[nt] ? v : kNegInf;
+        }
+        float tmax = x[0];
+#pragma unroll
+        for (int j = 1; j < 16; ++j) tmax = fmaxf(tmax, x[j]);
+        tmax = group_max4(tmax);
+        const float mnew = fmaxf(m[nt], tmax);
+        const float muse = mnew == kNegInf ? 0.f : mnew;
+        const float alpha = fast_exp2((m[nt] - muse) * sc);
+        const float msc = muse * sc;
+        float p[16], psum = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          p[j] = fast_exp2(fmaf(x[j], sc, -msc));
+          psum += p[j];
+        }
+        l[nt] = fmaf(l[nt], alpha, psum);
+        m[nt] = mnew;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[nt][dt] *= alpha;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+          pf[nt][kh] = __builtin_bit_cast(
+              bf16x8, u32x4{pack_bf16x2(p[8 * kh + 0], p[8 * kh + 1]),
+                            pack_bf16x2(p[8 * kh + 2], p[8 * kh + 3]),
+                            pack_bf16x2(p[8 * kh + 4], p[8 * kh + 5]),
+                            pack_bf16x2(p[8 * kh + 6], p[8 * kh + 7])});
+      }
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const bf16x8 vf = as_bf16x8(load16(vt + (16 * dt + r) * VROW + 32 * kh + 8 * g));
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) acc[nt][dt] = mfma_bf16(vf, pf[nt][kh], acc[nt][dt]);
+        }
+    }
+    if (ti + 1 < ntiles) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds O[row][16 dt + 4g + i]
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const float lrow = group_sum4(l[nt]);
+    if (!row_ok[nt]) continue;
+    const float inv = lrow > 0.f ? 1.f / lrow : 0.f;
+    const int row = 16 * (NT * wave + nt) + r;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const float o[4] = {acc[nt][dt][0] * inv, acc[nt][dt][1] * inv, acc[nt][dt][2] * inv,
+                          acc[nt][dt][3] * inv};
+      if (dst.partial) {
+        float* p = a.part_o + dst.po_base + (int64_t)row * dst.po_row + 16 * dt + 4 * g;
+        store16(p, __builtin_bit_cast(u32x4, floatx4{o[0], o[1], o[2], o[3]}));
+      } else {
+        __bf16* p = (__bf16*)a.out + out_row[nt] * D + 16 * dt + 4 * g;
+        *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+      }
+    }
+    if (g == 0)
+      store_lse(a, dst, row, out_row[nt],
+                lrow > 0.f ? m[nt] * a.scale + __log2f(lrow) * kLn2 : kNegInf);
+  }
+}
+
+template <int D, bool DECODE_ONLY>
+struct FwdLds {
+  union U {
+    LdsDecode<D> dec;
+    LdsPrefill<D> pre;
+  };
+  typedef typename std::conditional<DECODE_ONLY, LdsDecode<D>, U>::type type;
+};
+
+template <int D, bool DECODE_ONLY>
+__device__ __forceinline__ LdsDecode<D>& dec_lds(typename FwdLds<D, DECODE_ONLY>::type& s) {
+  if constexpr (DECODE_ONLY) return s; else return s.dec;
+}
+
+// Persistent forward kernel: a fixed grid; each workgroup takes the next item
+// index from a device counter until the planner's list is exhausted.
+template <int D, bool DECODE_ONLY>
+__global__ __launch_bounds__(kThreads) void mha_forward_kernel(MhaArgs a) {
+  __shared__ typename FwdLds<D, DECODE_ONLY>::type sm;
+  __shared__ int s_idx;
+  const int n_items = a.ctrl->n_items;
+  for (;;) {
+    if (threadIdx.x == 0) s_idx = atomicAdd(&a.ctrl->work_counter, 1);
+    __syncthreads();
+    const int idx = s_idx;
+    __syncthreads();
+    if (idx >= n_items) break;
+    const WorkItem it = a.items[idx];
+    Dest dst;
+    dst.partial = it.part >= 0;
+    dst.po_base = (int64_t)it.part * kDecodeRows * D;
+    dst.po_row = D;
+    dst.pl_base = (int64_t)it.part * kDecodeRows;
+    dst.pl_row = 1;
+    if constexpr (DECODE_ONLY) {
+      run_decode_item<D>(a, it, dst, sm);
+    } else {
+      if (it.nrows <= kDecodeRows) run_decode_item<D>(a, it, dst, sm.dec);
+      else run_prefill_item<D, kPrefillRowTiles>(a, it, dst, sm.pre);
+    }
+  }
+}
+
+// pa_decode_split: one workgroup per (request, KV head, partition).
+template <int D, bool DEC>
+__global__ __launch_bounds__(kThreads) void mha_split_kernel(MhaArgs a) {
+  __shared__ typename std::conditional<DEC, LdsDecode<D>, LdsPrefill<D>>::type sm;
+  const int S = a.num_splits;
+  const int s = blockIdx.x % S;
+  const int bk = blockIdx.x / S;
+  const int kvh = bk % a.Hkv, b = bk / a.Hkv;
+  const int L = a.seq_lens[b];
+  const int pages = (L + a.P - 1) / a.P;
+  const int per = a.P * ((pages + S - 1) / S);
+  const long long a0 = (long long)s * per, a1 = a0 + per;
+  const int t0 = a0 < L ? (int)a0 : L, t1 = a1 < L ? (int)a1 : L;
+  Dest dst;
+  dst.partial = true;
+  dst.po_base = ((int64_t)(b * a.Hq + kvh * a.G) * S + s) * D;
+  dst.po_row = (int64_t)S * D;
+  dst.pl_base = (int64_t)(b * a.Hq + kvh * a.G) * S + s;
+  dst.pl_row = S;
+  if (t1 <= t0) {  // empty partition: zeros and -inf
+    for (int i = threadIdx.x; i < a.G * D; i += kThreads)
+      a.part_o[dst.po_base + (int64_t)(i / D) * dst.po_row + (i % D)] = 0.f;
+    for (int i = threadIdx.x; i < a.G; i += kThreads)
+      a.part_lse[dst.pl_base + (int64_t)i * dst.pl_row] = kNegInf;
+    return;
+  }
+  WorkItem it;
+  it.seq = b;
+  it.kvh = kvh;
+  it.row0 = 0;
+  it.nrows = a.G;
+  it.kv_begin = t0;
+  it.kv_end = t1;
+  it.part = 0;
+  it.pad = 0;
+  if constexpr (DEC) run_decode_item<D>(a, it, dst, sm);
+  else run_prefill_item<D, kPrefillRowTiles>(a, it, dst, sm);
+}
+
+// Planner: one workgroup of 1024 threads turns (seq_lens, query_start_loc)
+// into the work list and the merge list.  Prefill-mode items come first
+// (heaviest rows of a request first), decode-mode items after them.
+constexpr int kPlanThreads = 1024;
+
+__device__ int4 block_exclusive_scan4(int4 v, int4* sh, int4* total) {
+  const int tid = threadIdx.x;
+  sh[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < kPlanThreads; off <<= 1) {
+    int4 u = tid >= off ? sh[tid - off] : int4{0, 0, 0, 0};
+    __syncthreads();
+    int4 w = sh[tid];
+    sh[tid] = int4{w.x + u.x, w.y + u.y, w.z + u.z, w.w + u.w};
+    __syncthreads();
+  }
+  int4 incl = sh[tid];
+  *total = sh[kPlanThreads - 1];
+  __syncthreads();
+  return int4{incl.x - v.x, incl.y - v.y, incl.z - v.z, incl.w - v.w};
+}
+
+// New-token count and key count of request b.  Requests whose lengths are
+// inconsistent (seq_len < q_len) get no work; seq_len is capped at the
+// block-table capacity so no item can index past a table row.
+__device__ __forceinline__ void request_shape(const PlanArgs& a, int b, int* nq, int* L) {
+  int q = a.qsl[b + 1] - a.qsl[b];
+  int l = a.seq_lens[b];
+  const long long cap = (long long)a.max_pages * a.P;
+  if (l > cap) l = (int)cap;
+  if (q < 0 || l < q || l < 1) q = 0;
+  *nq = q;
+  *L = l;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
+  __shared__ int4 sh[kPlanThreads];
+  __shared__ unsigned long long s_dec_keys;
+  __shared__ int s_pre_items;
+  const int tid = threadIdx.x;
+  const int G = a.G, Hkv = a.Hkv;
+  if (tid == 0) {
+    s_dec_keys = 0;
+    s_pre_items = 0;
+  }
+  __syncthreads();
+  // pass 1: totals
+  unsigned long long my_keys = 0;
+  int my_pre = 0;
+  for (int b = tid; b < a.B; b += kPlanThreads) {
+    int nq, L;
+    request_shape(a, b, &nq, &L);
+    if (nq <= 0) continue;
+    const int rows = nq * G;
+    if (rows <= kDecodeRows) my_keys += (unsigned long long)L;
+    else my_pre += Hkv * ((rows + kPrefillRows - 1) / kPrefillRows);
+  }
+  atomicAdd(&s_dec_keys, my_keys);
+  atomicAdd(&s_pre_items, my_pre);
+  __syncthreads();
+  const unsigned long long dec_work = s_dec_keys * (unsigned long long)Hkv;
+  long long chunk = (long long)((dec_work + a.target_items - 1) / (unsigned long long)a.target_items);
+  chunk = chunk < kMinChunk ? kMinChunk : chunk;
+  chunk = (chunk + 63) & ~63LL;
+  const int pre_total = s_pre_items;
+
+  // pass 2: scan and write
+  int4 run = int4{0, pre_total, 0, 0};  // prefill offset, decode offset, slot offset, merge offset
+  for (int base = 0; base < a.B; base += kPlanThreads) {
+    const int b = base + tid;
+    int nq = 0, L = 0, rows = 0, nsplit = 0, per = 0, nblk = 0;
+    int4 cnt = int4{0, 0, 0, 0};
+    if (b < a.B) {
+      request_shape(a, b, &nq, &L);
+      rows = nq * G;
+      if (nq > 0 && rows <= kDecodeRows) {
+        long long s = (L + chunk - 1) / chunk;
+        s = s < 1 ? 1 : (s > kMaxFwdSplits ? kMaxFwdSplits : s);
+        per = 64 * (int)(((L + 63) / 64 + s - 1) / s);
+        nsplit = (L + per - 1) / per;
+        if (nsplit < 1) nsplit = 1;
+        cnt.y = Hkv * nsplit;
+        if (nsplit > 1) {
+          cnt.z = Hkv * nsplit;
+          cnt.w = Hkv;
+        }
+      } else if (nq > 0) {
+        nblk = (rows + kPrefillRows - 1) / kPrefillRows;
+        cnt.x = Hkv * nblk;
+      }
+    }
+    int4 tot;
+    const int4 ex = block_exclusive_scan4(cnt, sh, &tot);
+    if (b < a.B && nq > 0) {
+      const int ctx = L - nq;
+      if (nblk > 0) {
+        for (int h = 0; h < Hkv; ++h)
+          for (int k = 0; k < nblk; ++k) {
+            const int blk = nblk - 1 - k;  // last (heaviest) row block first
+            WorkItem it;
+            it.seq = b;
+            it.kvh = h;
+            it.row0 = blk * kPrefillRows;
+            it.nrows = min(kPrefillRows, rows - it.row0);
+            it.kv_begin = 0;
+            it.kv_end = ctx + (it.row0 + it.nrows - 1) / G + 1;
+            it.part = -1;
+            it.pad = 0;
+            a.items[run.x + ex.x + h * nblk + k] = it;
+          }
+      } else {
+        const int slot0 = run.z + ex.z;
+        for (int h = 0; h < Hkv; ++h) {
+          for (int s = 0; s < nsplit; ++s) {
+            WorkItem it;
+            it.seq = b;
+            it.kvh = h;
+            it.row0 = 0;
+            it.nrows = rows;
+            it.kv_begin = s * per;
+            it.kv_end = min(L, (s + 1) * per);
+            it.part = nsplit > 1 ? slot0 + h * nsplit + s : -1;
+            it.pad = 0;
+            a.items[run.y + ex.y + h * nsplit + s] = it;
+          }
+          if (nsplit > 1) {
+            MergeItem mi;
+            mi.seq = b;
+            mi.kvh = h;
+            mi.slot0 = slot0 + h * nsplit;
+            mi.nsplit = nsplit;
+            mi.nrows = rows;
+            mi.pad[0] = mi.pad[1] = mi.pad[2] = 0;
+            a.merges[run.w + ex.w + h] = mi;
+          }
+        }
+      }
+    }
+    run = int4{run.x + tot.x, run.y + tot.y, run.z + tot.z, run.w + tot.w};
+  }
+  if (tid == 0) {
+    a.ctrl->n_items = run.y;  // decode items are placed after all prefill items
+    a.ctrl->n_merge = run.w;
+    a.ctrl->work_counter = 0;
+  }
+}
+
+// Merge of pa_forward's split decode rows: one wave per (merge item, row).
+template <int D>
+__global__ __launch_bounds__(kThreads) void mha_forward_merge_kernel(MhaArgs a) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int n_units = a.ctrl->n_merge * kDecodeRows;
+  const int stride = gridDim.x * (kThreads / 64);
+  for (int u = blockIdx.x * (kThreads / 64) + wv; u < n_units; u += stride) {
+    const MergeItem mi = a.merges[u / kDecodeRows];
+    const int row = u % kDecodeRows;
+    if (row >= mi.nrows) continue;
+    const int S = mi.nsplit;  // <= 64: one lane per partition
+    const float ls = lane < S ? a.part_lse[(int64_t)(mi.slot0 + lane) * kDecodeRows + row] : kNegInf;
+    const float M = wave_max(ls);
+    const float w = (lane < S && ls != kNegInf) ? __expf(ls - M) : 0.f;
+    const float wsum = wave_sum(w);
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    const int t = row / a.G;
+    const int64_t out_row = (int64_t)(a.qsl[mi.seq] + t) * a.Hq + mi.kvh * a.G + (row - t * a.G);
+    float o[D / 64];
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) o[e] = 0.f;
+    for (int s = 0; s < S; ++s) {
+      const float ws = __shfl(w, s);
+      const float* po = a.part_o + ((int64_t)(mi.slot0 + s) * kDecodeRows + row) * D;
+#pragma unroll
+      for (int e = 0; e < D / 64; ++e) o[e] = fmaf(ws, po[lane + 64 * e], o[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) ((__bf16*)a.out)[out_row * D + lane + 64 * e] = (__bf16)(o[e] * inv);
+    if (lane == 0 && a.lse) a.lse[out_row] = wsum > 0.f ? M + __logf(wsum) : kNegInf;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t mha_occupancy(int D, bool decode_only, int* blocks_per_cu) {
+  const void* f;
+  if (D == 128) f = decode_only ? (const void*)mha_forward_kernel<128, true> : (const void*)mha_forward_kernel<128, false>;
+  else f = decode_only ? (const void*)mha_forward_kernel<64, true> : (const void*)mha_forward_kernel<64, false>;
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, f, kThreads, 0);
+}
+
+hipError_t launch_mha_forward(const MhaArgs& a, int D, bool decode_only, int grid, hipStream_t s) {
+  if (D == 128) {
+    if (decode_only) hipLaunchKernelGGL((mha_forward_kernel<128, true>), dim3(grid), dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((mha_forward_kernel<128, false>), dim3(grid), dim3(kThreads), 0, s, a);
+  } else {
+    if (decode_only) hipLaunchKernelGGL((mha_forward_kernel<64, true>), dim3(grid), dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((mha_forward_kernel<64, false>), dim3(grid), dim3(kThreads), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_mha_forward_merge(const MhaArgs& a, int D, int grid, hipStream_t s) {
+  if (D == 128) hipLaunchKernelGGL(mha_forward_merge_kernel<128>, dim3(grid), dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL(mha_forward_merge_kernel<64>, dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_mha_split(const MhaArgs& a, int D, hipStream_t s) {
+  const int64_t blocks = (int64_t)a.num_seqs * a.Hkv * a.num_splits;
+  if (blocks <= 0) return hipSuccess;
+  const bool dec = a.G <= kDecodeRows;
+  if (D == 128) {
+    if (dec) hipLaunchKernelGGL((mha_split_kernel<128, true>), dim3(blocks), dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((mha_split_kernel<128, false>), dim3(blocks), dim3(kThreads), 0, s, a);
+  } else {
+    if (dec) hipLaunchKernelGGL((mha_split_kernel<64, true>), dim3(blocks), dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((mha_split_kernel<64, false>), dim3(blocks), dim3(kThreads), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+FwdWorkspace fwd_workspace_layout(int B, int T, int Hkv, int G, int D) {
+  FwdWorkspace w;
+  auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  w.cap_items = (int64_t)Hkv * ((int64_t)B * kMaxFwdSplits +
+                                ((int64_t)T * G + kPrefillRows - 1) / kPrefillRows + B);
+  w.cap_merges = (int64_t)Hkv * B;
+  w.cap_slots = (int64_t)Hkv * B * kMaxFwdSplits;
+  size_t off = 0;
+  w.ctrl_off = off;
+  off = align(off + sizeof(Control));
+  w.items_off = off;
+  off = align(off + (size_t)w.cap_items * sizeof(WorkItem));
+  w.merges_off = off;
+  off = align(off + (size_t)w.cap_merges * sizeof(MergeItem));
+  w.plse_off = off;
+  off = align(off + (size_t)w.cap_slots * kDecodeRows * sizeof(float));
+  w.po_off = off;
+  off = align(off + (size_t)w.cap_slots * kDecodeRows * D * sizeof(float));
+  w.total = off;
+  return w;
+}
+
+}  // namespace pa

@@ -181,6 +181,20 @@ def make_batch(q_lens: Sequence[int], ctx_lens: Sequence[int], *, num_q_heads: i
                  layout=layout, q_lens=q_lens, ctx_lens=ctx_lens, name=name)
 
 
+def sub_batch(b: Batch, requests: Sequence[int]) -> Batch:
+    """The given consecutive requests of `b` as a batch of their own (same cache pool)."""
+    r = list(requests)
+    assert r == list(range(r[0], r[-1] + 1)), "requests must be consecutive"
+    qsl = b.query_start_loc
+    t0, t1 = int(qsl[r[0]]), int(qsl[r[-1] + 1])
+    return dataclasses.replace(
+        b, q=b.q[t0:t1], block_table=b.block_table[r[0]:r[-1] + 1].contiguous(),
+        seq_lens=b.seq_lens[r[0]:r[-1] + 1].contiguous(),
+        query_start_loc=(qsl[r[0]:r[-1] + 2] - t0).contiguous(),
+        q_lens=b.q_lens[r[0]:r[-1] + 1], ctx_lens=b.ctx_lens[r[0]:r[-1] + 1],
+        name=b.name + "[%d:%d]" % (r[0], r[-1] + 1))
+
+
 def _randint(gen, lo, hi, n):
     """n integers uniform in [lo, hi] (inclusive)."""
     return [int(x) for x in torch.randint(int(lo), int(hi) + 1, (n,), generator=gen)]

@@ -1,0 +1,206 @@
+"""Host-side tests of the C ABI (no GPU): the library loads, exports every
+entry point include/pa.h declares, and rejects bad arguments on the host
+before any HIP call; plus checks of the seeded input generator."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import paged_attention_kv_pa_amd as pa
+from paged_attention_kv_pa_amd import binding, workload
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return re.findall(r"PA_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def test_header_declares_the_entry_points():
+    names = set(_declared())
+    assert {"pa_forward", "pa_decode_split", "pa_merge_lse", "mla_decode", "pa_workspace_size",
+            "mla_workspace_size", "pa_validate", "pa_status_string", "pa_last_hip_error"} <= names
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = ctypes.CDLL(pa.library_path())
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code in range(6):
+        s = pa.pa_status_string(code)
+        assert isinstance(s, str) and s and s != "unknown status"
+    assert pa.pa_status_string(99) == "unknown status"
+
+
+def _dims(**kw):
+    d = binding.PaDims()
+    base = dict(num_seqs=4, num_tokens=4, num_q_heads=32, num_kv_heads=8, head_dim_qk=128,
+                head_dim_v=128, page_size=16, num_pages=100, max_pages_per_seq=20,
+                max_seq_len=320, max_q_len=1, dtype=binding.PA_BF16)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(d, k, v)
+    return d
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its host checks
+
+
+def _fwd(d, ws_bytes=1 << 40, q=FAKE, lse=None):
+    lib = pa.library()
+    return lib.pa_forward(q, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, lse, ctypes.byref(d), FAKE,
+                          ws_bytes, None)
+
+
+def test_workspace_size_host_function():
+    assert pa.library().pa_workspace_size(None) == 0
+    d = _dims()
+    s1 = pa.pa_workspace_size(d)
+    assert s1 > 0
+    s2 = pa.pa_workspace_size(_dims(num_seqs=64, num_tokens=64))
+    assert s2 > s1
+    assert pa.pa_workspace_size(_dims(dtype=binding.PA_F32)) > 0
+    assert pa.pa_workspace_size(_dims(num_q_heads=30)) == 0  # Hq % Hkv != 0
+
+
+@pytest.mark.parametrize("field,value", [
+    ("num_seqs", -1), ("num_q_heads", 0), ("num_kv_heads", 0), ("num_q_heads", 30),
+    ("head_dim_qk", 0), ("page_size", 0), ("num_pages", 0), ("max_pages_per_seq", 0),
+    ("dtype", 7), ("max_seq_len", 10 ** 6), ("max_q_len", 10 ** 6)])
+def test_forward_rejects_bad_dims(field, value):
+    assert _fwd(_dims(**{field: value})) == binding.PA_ERR_INVALID_ARG
+
+
+def test_forward_rejects_null_pointers_and_dims():
+    assert _fwd(_dims(), q=None) == binding.PA_ERR_INVALID_ARG
+    lib = pa.library()
+    assert lib.pa_forward(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, None, None, FAKE, 1, None) \
+        == binding.PA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(head_dim_qk=96, head_dim_v=96), dict(head_dim_v=64),
+                                dict(page_size=12, max_pages_per_seq=30), dict(page_size=512, max_pages_per_seq=20),
+                                dict(dtype=binding.PA_F32, head_dim_qk=512, head_dim_v=512)])
+def test_forward_reports_unsupported(kw):
+    assert _fwd(_dims(**kw)) == binding.PA_ERR_UNSUPPORTED
+
+
+def test_forward_checks_workspace_before_launch():
+    d = _dims()
+    need = pa.pa_workspace_size(d)
+    assert _fwd(d, ws_bytes=need - 1) == binding.PA_ERR_WORKSPACE
+    lib = pa.library()
+    assert lib.pa_forward(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, None, ctypes.byref(d),
+                          None, need, None) == binding.PA_ERR_WORKSPACE
+
+
+def test_empty_batch_is_a_no_op():
+    assert _fwd(_dims(num_seqs=0, num_tokens=0)) == binding.PA_OK
+
+
+def test_decode_split_argument_checks():
+    lib = pa.library()
+    d = _dims()
+    call = lambda S, dd=d: lib.pa_decode_split(FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, S, FAKE, FAKE,
+                                               ctypes.byref(dd), None)
+    assert call(0) == binding.PA_ERR_INVALID_ARG
+    assert call(257) == binding.PA_ERR_INVALID_ARG
+    assert call(4, _dims(num_tokens=5)) == binding.PA_ERR_INVALID_ARG  # T != B
+    assert call(4, _dims(head_dim_qk=80, head_dim_v=80)) == binding.PA_ERR_UNSUPPORTED
+    assert call(4, _dims(num_seqs=0, num_tokens=0)) == binding.PA_OK
+
+
+def test_merge_argument_checks():
+    lib = pa.library()
+    m = lambda rows, S, Dv, dt: lib.pa_merge_lse(FAKE, FAKE, rows, S, Dv, FAKE, None, dt, None)
+    assert m(-1, 4, 128, 1) == binding.PA_ERR_INVALID_ARG
+    assert m(4, 0, 128, 1) == binding.PA_ERR_INVALID_ARG
+    assert m(4, 300, 128, 1) == binding.PA_ERR_INVALID_ARG
+    assert m(4, 4, 0, 1) == binding.PA_ERR_INVALID_ARG
+    assert m(4, 4, 128, 5) == binding.PA_ERR_INVALID_ARG
+    assert m(0, 4, 128, 1) == binding.PA_OK
+    assert lib.pa_merge_lse(None, FAKE, 4, 4, 128, FAKE, None, 1, None) == binding.PA_ERR_INVALID_ARG
+
+
+def test_mla_argument_checks():
+    lib = pa.library()
+    base = dict(num_seqs=4, num_tokens=4, num_q_heads=128, num_kv_heads=1, head_dim_qk=576,
+                head_dim_v=512, page_size=64, num_pages=100, max_pages_per_seq=20,
+                max_seq_len=1280, max_q_len=1)
+
+    def call(S=4, **kw):
+        b = dict(base)
+        b.update(kw)
+        d = _dims(**b)
+        return lib.mla_decode(FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, None, S, ctypes.byref(d), FAKE,
+                              1 << 40, None)
+
+    assert call(head_dim_qk=512) == binding.PA_ERR_UNSUPPORTED
+    assert call(num_kv_heads=2, num_q_heads=128) == binding.PA_ERR_UNSUPPORTED
+    assert call(num_q_heads=120) == binding.PA_ERR_UNSUPPORTED
+    assert call(num_q_heads=256) == binding.PA_ERR_UNSUPPORTED
+    assert call(dtype=binding.PA_F32) == binding.PA_ERR_UNSUPPORTED
+    assert call(num_tokens=5) == binding.PA_ERR_INVALID_ARG
+    assert call(S=65) == binding.PA_ERR_INVALID_ARG
+    assert call(num_seqs=0, num_tokens=0) == binding.PA_OK
+    d = _dims(**base)
+    assert pa.mla_workspace_size(d, 1) > 0
+    assert pa.mla_workspace_size(d, 8) > pa.mla_workspace_size(d, 2)
+    assert lib.mla_decode(FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, None, 8, ctypes.byref(d), FAKE,
+                          16, None) == binding.PA_ERR_WORKSPACE
+
+
+# ---- seeded input generator -------------------------------------------------
+
+def test_generator_is_deterministic_and_pages_are_exclusive():
+    a = workload.llama_decode(3, batch=6, hi=900)
+    b = workload.llama_decode(3, batch=6, hi=900)
+    assert torch.equal(a.block_table, b.block_table) and torch.equal(a.seq_lens, b.seq_lens)
+    assert torch.equal(a.q.view(torch.int16), b.q.view(torch.int16))
+    used = []
+    for i, L in enumerate(a.seq_lens_list):
+        n = (L + a.page_size - 1) // a.page_size
+        used += a.block_table[i, :n].tolist()
+    assert len(used) == len(set(used))  # no physical page serves two requests
+    spare = sorted(set(range(a.num_pages)) - set(used))
+    assert spare, "at least one poison page"
+    assert torch.isnan(a.k_cache[spare].float()).all() and torch.isnan(a.v_cache[spare].float()).all()
+    for i, L in enumerate(a.seq_lens_list):  # unused table entries point at poison
+        n = (L + a.page_size - 1) // a.page_size
+        assert set(a.block_table[i, n:].tolist()) <= set(spare)
+
+
+def test_generator_poisons_tail_slots_only():
+    b = workload.make_batch([1, 3], [20, 0], num_q_heads=4, num_kv_heads=2, head_dim_qk=64,
+                            page_size=16, seed=3)
+    for i, L in enumerate(b.seq_lens_list):
+        n = (L + 15) // 16
+        last = int(b.block_table[i, n - 1])
+        tail = L % 16
+        kc = b.k_cache[last].float()
+        vc = b.v_cache[last].float()
+        assert not torch.isnan(kc[:, :tail or 16]).any()
+        assert not torch.isnan(vc[:, :, :tail or 16]).any()
+        if tail:
+            assert torch.isnan(kc[:, tail:]).all() and torch.isnan(vc[:, :, tail:]).all()
+    assert not torch.isnan(b.q.float()).any()
+
+
+def test_workload_shapes():
+    c = workload.tiny_f32_decode(0)
+    assert c.q.dtype == torch.float32 and c.num_pages == 128 and c.num_seqs == 4
+    assert all(1 <= L <= 300 for L in c.seq_lens_list)
+    m = workload.qwen3_mixed(0, n_decode=3, n_extend=2, n_prefill=2, dec=(20, 40), ext_q=(3, 5),
+                             ext_c=(10, 20), pre_q=(5, 9))
+    assert m.q_lens[:3] == [1, 1, 1] and all(c == 0 for c in m.ctx_lens[-2:])
+    assert int(m.query_start_loc[-1]) == m.num_tokens == m.q.shape[0]
+    d = workload.deepseek_mla(0, batch=2, lo=70, hi=90)
+    assert d.k_cache is d.v_cache and d.k_cache.shape[1:] == (64, 576)

@@ -1,0 +1,333 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle on
+the same seeded inputs.
+
+Tolerances of the parity contract: bf16 max |err| <= 2e-2 and relative RMS
+<= 5e-3 over the output tensor; fp32 max |err| <= 1e-5; LSE within 1e-3
+(natural log).  Index handling must be exact: unused pages and the slots past
+each sequence end hold NaN, so any stray read shows up as a non-finite output.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_attention_kv_pa_amd as pa
+from paged_attention_kv_pa_amd import workload
+from pa_testutil import errors, finite_lse_err
+
+pytestmark = pytest.mark.gpu
+
+BF16_MAX, BF16_REL, F32_MAX, LSE_TOL = 2e-2, 5e-3, 1e-5, 1e-3
+DEV = torch.device("cuda:0")
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def check_out(got, ref, dtype, what):
+    got = np.asarray(got, dtype=np.float64)
+    assert np.isfinite(got).all(), "%s: non-finite output" % what
+    mx, rel = errors(got, ref)
+    say("%s: max_abs=%.3e rel_rms=%.3e" % (what, mx, rel))
+    if dtype == torch.float32:
+        assert mx <= F32_MAX, "%s: max_abs %.3e" % (what, mx)
+    else:
+        assert mx <= BF16_MAX and rel <= BF16_REL, "%s: max_abs %.3e rel %.3e" % (what, mx, rel)
+
+
+def check_lse(got, ref, what):
+    e = finite_lse_err(got, ref)
+    say("%s: lse max_abs=%.3e" % (what, e))
+    assert e <= LSE_TOL
+
+
+def run_forward(b, g=None, **kw):
+    g = g if g is not None else b.to(DEV)
+    lse = torch.full((b.num_tokens, b.num_q_heads), float("nan"), dtype=torch.float32, device=DEV)
+    out = pa.pa_forward(g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens, g.query_start_loc,
+                        b.scale, lse=lse, max_seq_len=max(b.seq_lens_list + [1]),
+                        max_q_len=max(b.q_lens + [1]), **kw)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def oracle_forward(b, rows=None):
+    lay = oracle.LAYOUT_MLA if b.layout == "mla" else oracle.LAYOUT_MHA
+    return oracle.attention(b.q, b.k_cache, b.v_cache, b.block_table, b.seq_lens,
+                            b.query_start_loc, b.scale, b.num_kv_heads,
+                            head_dim_v=b.head_dim_v, layout=lay, rows=rows)
+
+
+def forward_parity(b, what, rows=None):
+    say("case %s: B=%d T=%d keys=%d" % (what, b.num_seqs, b.num_tokens, sum(b.seq_lens_list)))
+    got, glse = run_forward(b)
+    ref, rlse = oracle_forward(b, rows)
+    if rows is not None:
+        sel = np.asarray(rows, dtype=bool)
+        got, ref, glse, rlse = got[sel], ref[sel], glse[sel], rlse[sel]
+    check_out(got, ref, b.dtype, what)
+    check_lse(glse, rlse, what)
+    return got
+
+
+# ---------------------------------------------------------------- fp32 (tiny)
+
+@pytest.mark.parametrize("case", [0, 1, 2])
+def test_tiny_f32_decode_forward(case):
+    b = workload.tiny_f32_decode(case)
+    forward_parity(b, "tiny_f32_decode/%d" % case)
+
+
+@pytest.mark.parametrize("S", [1, 3, 8, 40])
+def test_tiny_f32_decode_split_and_merge(S):
+    b = workload.tiny_f32_decode(0)
+    g = b.to(DEV)
+    say("case tiny_f32 split S=%d" % S)
+    po, pl = pa.pa_decode_split(g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens, b.scale, S)
+    out = pa.pa_merge_lse(po, pl, out_dtype=torch.float32)
+    lse = torch.empty(pl.shape[:2], dtype=torch.float32, device=DEV)
+    pa.pa_merge_lse(po, pl, lse=lse, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rpo, rpl = oracle.decode_split(b.q, b.k_cache, b.v_cache, b.block_table, b.seq_lens, b.scale,
+                                   S, b.num_kv_heads)
+    check_out(po.cpu().numpy(), rpo, torch.float32, "f32 partials S=%d" % S)
+    check_lse(pl.cpu().numpy(), rpl, "f32 partial lse S=%d" % S)
+    ref, rlse = oracle_forward(b)
+    check_out(out.cpu().numpy(), ref, torch.float32, "f32 merged S=%d" % S)
+    check_lse(lse.cpu().numpy(), rlse, "f32 merged lse S=%d" % S)
+
+
+# ------------------------------------------------------- Llama-3.1-8B decode
+
+@pytest.mark.parametrize("case", [0, 1, 2, 3])
+def test_llama_decode_forward_full_size(case):
+    b = workload.llama_decode(case)
+    forward_parity(b, "llama_decode/%d" % case)
+
+
+@pytest.mark.parametrize("S", [1, 2, 7, 64, 200])
+def test_llama_decode_split_matches_oracle_partials(S):
+    b = workload.llama_decode(3, batch=8)
+    g = b.to(DEV)
+    say("case llama split S=%d" % S)
+    po, pl = pa.pa_decode_split(g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens, b.scale, S)
+    out = pa.pa_merge_lse(po, pl)
+    torch.cuda.synchronize()
+    rpo, rpl = oracle.decode_split(b.q, b.k_cache, b.v_cache, b.block_table, b.seq_lens, b.scale,
+                                   S, b.num_kv_heads)
+    check_out(po.cpu().numpy(), rpo, torch.bfloat16, "bf16 partials S=%d" % S)
+    check_lse(pl.cpu().numpy(), rpl, "bf16 partial lse S=%d" % S)
+    ref, _ = oracle_forward(b)
+    check_out(out.float().cpu().numpy(), ref, torch.bfloat16, "bf16 merged S=%d" % S)
+
+
+# ------------------------------------------------- long-context split decode
+
+@pytest.mark.parametrize("batch,S,lengths", [(1, 64, None), (4, 32, None), (16, 16, None),
+                                             (1, 64, [32768]), (1, 64, [131072])])
+def test_long_context_split_full_size(batch, S, lengths):
+    b = workload.llama_long(batch=batch, lengths=lengths, device=DEV)
+    say("case llama_long B=%d S=%d keys=%d" % (b.num_seqs, S, sum(b.seq_lens_list)))
+    po, pl = pa.pa_decode_split(b.q, b.k_cache, b.v_cache, b.block_table, b.seq_lens, b.scale, S)
+    out = pa.pa_merge_lse(po, pl)
+    lse = torch.empty(pl.shape[:2], dtype=torch.float32, device=DEV)
+    pa.pa_merge_lse(po, pl, out=torch.empty_like(out), lse=lse)
+    torch.cuda.synchronize()
+    h = b.to("cpu")
+    ref, rlse = oracle_forward(h)
+    check_out(out.float().cpu().numpy(), ref, torch.bfloat16, "long B=%d S=%d" % (batch, S))
+    check_lse(lse.cpu().numpy(), rlse, "long B=%d S=%d" % (batch, S))
+    # the same batch through pa_forward (its planner splits internally)
+    got, glse = run_forward(h, g=b)
+    check_out(got, ref, torch.bfloat16, "long pa_forward B=%d" % batch)
+    check_lse(glse, rlse, "long pa_forward B=%d" % batch)
+
+
+# --------------------------------------------------- Qwen3 mixed batch (MHA)
+
+def test_qwen3_mixed_scaled_all_rows():
+    b = workload.qwen3_mixed(1, n_decode=12, n_extend=2, n_prefill=2, dec=(1024, 4096),
+                             ext_q=(256, 600), ext_c=(4096, 8192), pre_q=(512, 1500))
+    forward_parity(b, "qwen3_mixed scaled")
+
+
+def test_qwen3_mixed_full_size_sampled_rows():
+    b = workload.qwen3_mixed(0)
+    T, Hq = b.num_tokens, b.num_q_heads
+    rows = np.zeros((T, Hq), dtype=bool)
+    qsl = b.query_start_loc.numpy()
+    for i in range(b.num_seqs):  # every decode row, first/last row of each request, a stride
+        s, e = qsl[i], qsl[i + 1]
+        rows[s, :] = True
+        rows[e - 1, :] = True
+        rows[s:e:97, ::5] = True
+    forward_parity(b, "qwen3_mixed full (sampled rows)", rows=rows)
+
+
+# ------------------------------------------------------- DeepSeek-R1 MLA
+
+def mla_parity(b, what, S=0, heads=None):
+    say("case %s: B=%d keys=%d S=%d" % (what, b.num_seqs, sum(b.seq_lens_list), S))
+    g = b.to(DEV)
+    lse = torch.empty(b.num_seqs, b.num_q_heads, dtype=torch.float32, device=DEV)
+    out = pa.mla_decode(g.q, g.k_cache, g.block_table, g.seq_lens, b.scale, lse=lse, num_splits=S,
+                        max_seq_len=max(b.seq_lens_list))
+    torch.cuda.synchronize()
+    rows = None
+    if heads is not None:
+        rows = np.zeros((b.num_seqs, b.num_q_heads), dtype=bool)
+        rows[:, heads] = True
+    ref, rlse = oracle_forward(b, rows)
+    got, glse = out.float().cpu().numpy(), lse.cpu().numpy()
+    if rows is not None:
+        got, ref, glse, rlse = got[rows], ref[rows], glse[rows], rlse[rows]
+    check_out(got, ref, torch.bfloat16, what)
+    check_lse(glse, rlse, what)
+
+
+@pytest.mark.parametrize("S", [0, 1, 3, 16])
+def test_mla_scaled(S):
+    b = workload.deepseek_mla(1, batch=6, lo=1, hi=1500)
+    mla_parity(b, "mla scaled", S=S)
+
+
+def test_mla_full_size_sampled_heads():
+    b = workload.deepseek_mla(0)
+    mla_parity(b, "mla full (heads 0,1,37,64,127)", heads=[0, 1, 37, 64, 127])
+
+
+# --------------------------------------------------------------- edge cases
+
+def test_edge_empty_requests_single_keys_and_exact_pages():
+    b = workload.make_batch([1, 0, 1, 3, 0, 16, 1, 1], [0, 5, 15, 13, 0, 0, 31, 47],
+                            num_q_heads=32, num_kv_heads=8, head_dim_qk=128, page_size=16, seed=11)
+    forward_parity(b, "edge mix")
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,P", [(32, 8, 64, 16), (64, 2, 128, 16), (16, 16, 128, 32),
+                                        (8, 1, 128, 64), (12, 4, 64, 8)])
+def test_head_and_page_shapes(Hq, Hkv, D, P):
+    b = workload.make_batch([1, 5, 40, 1, 130], [700, 100, 0, 3, 60], num_q_heads=Hq,
+                            num_kv_heads=Hkv, head_dim_qk=D, page_size=P, seed=Hq * 7 + P)
+    forward_parity(b, "shapes Hq=%d Hkv=%d D=%d P=%d" % (Hq, Hkv, D, P))
+
+
+def test_page_permutation_invariance_bitwise():
+    a = workload.make_batch([1, 9, 70], [400, 33, 0], num_q_heads=32, num_kv_heads=8,
+                            head_dim_qk=128, page_size=16, seed=5)
+    out_a, lse_a = run_forward(a)
+    # move every page to a new physical slot and remap the table
+    perm = torch.randperm(a.num_pages, generator=torch.Generator().manual_seed(9))
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(a.num_pages)
+    b = workload.Batch(**{**a.__dict__})
+    b.k_cache = a.k_cache[inv]
+    b.v_cache = a.v_cache[inv]
+    b.block_table = perm[a.block_table.long()].to(torch.int32)
+    out_b, lse_b = run_forward(b)
+    assert np.array_equal(out_a, out_b) and np.array_equal(lse_a, lse_b)
+
+
+def test_determinism_bitwise():
+    b = workload.qwen3_mixed(2, n_decode=6, n_extend=1, n_prefill=1, dec=(500, 3000),
+                             ext_q=(100, 300), ext_c=(500, 900), pre_q=(200, 400))
+    g = b.to(DEV)
+    o1, l1 = run_forward(b, g)
+    o2, l2 = run_forward(b, g)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_split_count_larger_than_pages_gives_empty_partitions():
+    b = workload.make_batch([1, 1], [4, 40], num_q_heads=32, num_kv_heads=8, head_dim_qk=128,
+                            page_size=16, seed=13)
+    g = b.to(DEV)
+    po, pl = pa.pa_decode_split(g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens, b.scale, 9)
+    torch.cuda.synchronize()
+    pl = pl.cpu().numpy()
+    po = po.cpu().numpy()
+    assert np.isneginf(pl[0, :, 1:]).all() and (po[0, :, 1:] == 0).all()
+    assert np.isneginf(pl[1, :, 3:]).all() and np.isfinite(pl[1, :, :3]).all()
+
+
+# ------------------------------------------------------------ graph replay
+
+def test_graph_capture_replay_with_new_lengths():
+    """One captured pa_forward (planner + persistent kernel + merge) replayed
+    after rewriting seq_lens, query_start_loc and block_table in place."""
+    Hq, Hkv, D, P = 32, 8, 128, 16
+    specs = [([1, 1, 20, 1], [900, 40, 30, 2000]), ([1, 7, 1, 1], [60, 100, 2500, 5]),
+             ([3, 1, 1, 15], [10, 1200, 0, 700])]
+    batches = [workload.make_batch(q, c, num_q_heads=Hq, num_kv_heads=Hkv, head_dim_qk=D,
+                                   page_size=P, seed=100 + i, max_pages_per_seq=200,
+                                   pool_pages=700) for i, (q, c) in enumerate(specs)]
+    T = max(b.num_tokens for b in batches)
+    # fixed-capacity device buffers
+    q = torch.zeros(T, Hq, D, dtype=torch.bfloat16, device=DEV)
+    kc = batches[0].k_cache.to(DEV).clone()
+    vc = batches[0].v_cache.to(DEV).clone()
+    bt = torch.zeros(4, 200, dtype=torch.int32, device=DEV)
+    sl = torch.zeros(4, dtype=torch.int32, device=DEV)
+    qsl = torch.zeros(5, dtype=torch.int32, device=DEV)
+    out = torch.zeros(T, Hq, D, dtype=torch.bfloat16, device=DEV)
+    lse = torch.zeros(T, Hq, dtype=torch.float32, device=DEV)
+    dims_kw = dict(max_seq_len=200 * P, max_q_len=T)
+    ws = torch.empty(pa.pa_workspace_size(pa.make_dims(q, kc, vc, bt, sl, T, **dims_kw)),
+                     dtype=torch.uint8, device=DEV)
+
+    def load(b):
+        q.zero_()
+        q[:b.num_tokens].copy_(b.q)
+        kc.copy_(b.k_cache)
+        vc.copy_(b.v_cache)
+        bt.copy_(b.block_table)
+        sl.copy_(b.seq_lens)
+        qsl.copy_(torch.cat([b.query_start_loc,
+                             b.query_start_loc[-1:].expand(5 - b.query_start_loc.numel())]))
+
+    def call():
+        pa.pa_forward(q, kc, vc, bt, sl, qsl, batches[0].scale, out=out, lse=lse, workspace=ws,
+                      **dims_kw)
+
+    load(batches[0])
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        call()  # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for i, b in enumerate(batches):
+            say("graph replay %d batch %d" % (rep, i))
+            load(b)
+            out.fill_(float("nan"))
+            graph.replay()
+            torch.cuda.synchronize()
+            g_out = out[:b.num_tokens].float().cpu().numpy()
+            g_lse = lse[:b.num_tokens].cpu().numpy()
+            e_out, e_lse = run_forward(b)  # eager on a fresh copy
+            assert np.array_equal(g_out, e_out) and np.array_equal(g_lse, e_lse)
+            ref, rlse = oracle_forward(b)
+            check_out(g_out, ref, torch.bfloat16, "graph batch %d" % i)
+            check_lse(g_lse, rlse, "graph batch %d" % i)
+
+
+def test_validate_reports_bad_rows():
+    b = workload.make_batch([1, 2], [10, 30], num_q_heads=32, num_kv_heads=8, head_dim_qk=128,
+                            page_size=16, seed=17)
+    g = b.to(DEV)
+    dims = pa.make_dims(g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens, b.num_tokens,
+                        max_seq_len=32, max_q_len=2)
+    assert pa.pa_validate(g.block_table, g.seq_lens, g.query_start_loc, dims) == -1
+    bad = g.block_table.clone()
+    bad[1, 0] = b.num_pages + 5
+    assert pa.pa_validate(bad, g.seq_lens, g.query_start_loc, dims) == 1
+    sl = g.seq_lens.clone()
+    sl[0] = 0  # shorter than its one new token
+    assert pa.pa_validate(g.block_table, sl, g.query_start_loc, dims) == 0
