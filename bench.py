@@ -121,6 +121,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the split-KV and MLA measurements")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only time a plain 2 GiB device-to-device copy (HBM reference and the "
+                         "byte-counter calibration kernel)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -139,6 +144,23 @@ def main():
     lib.pa_set_kernel_events.restype = ctypes.c_int32
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        n = 2 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": round(ms, 4),
+                          "read_plus_write_GBs": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+        return
 
     # ---- decode: Llama-3.1-8B shapes, B = 64, L ~ U[500, 8192]
     b = workload.llama_decode(3, device=dev)
@@ -218,6 +240,58 @@ def main():
             "tflops": round(workload.algorithmic_flops(full) / (m_step_ms * 1e-3) / 1e12, 2),
             "hbm_gbs": round(workload.algorithmic_bytes(full) / (m_step_ms * 1e-3) / 1e9, 2)}
         del full, pre
+
+    if not args.no_extra:
+        xsteps = max(3, args.steps // 3)
+        # ---- long-context split-KV decode: 16 sequences, L ~ U[32K, 128K], 16 partitions
+        lb = workload.llama_long(batch=16, device=dev)
+        S = 16
+        po = torch.empty(16, lb.num_q_heads, S, lb.head_dim_v, dtype=torch.float32, device=dev)
+        pl = torch.empty(16, lb.num_q_heads, S, dtype=torch.float32, device=dev)
+        lo = torch.empty(16, lb.num_q_heads, lb.head_dim_v, dtype=lb.dtype, device=dev)
+
+        def sstep():
+            pa.pa_decode_split(lb.q, lb.k_cache, lb.v_cache, lb.block_table, lb.seq_lens,
+                               lb.scale, S, part_out=po, part_lse=pl,
+                               max_seq_len=max(lb.seq_lens_list))
+            pa.pa_merge_lse(po, pl, out=lo)
+
+        s_step_ms, s_kern_ms = time_steps(sstep, xsteps, 2, lib)
+        sbytes = workload.algorithmic_bytes(lb)
+        result["split_kv"] = {
+            "workload": "Llama-3.1-8B-shaped long-context decode, 16 sequences, L~U[32768,131072], "
+                        "pa_decode_split with 16 partitions + pa_merge_lse",
+            "hbm_gbs": round(sbytes / (s_step_ms * 1e-3) / 1e9, 2),
+            "split_kernel_gbs": round(sbytes / (s_kern_ms * 1e-3) / 1e9, 2),
+            "frac": round(sbytes / (s_kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "ms_per_step": round(s_step_ms, 4), "kernel_ms": round(s_kern_ms, 4),
+            "algorithmic_bytes": sbytes}
+        del lb, po, pl, lo
+        # ---- absorbed MLA decode: 64 sequences, 128 heads, latent 576 / 512, L ~ U[1K, 32K]
+        mb = workload.deepseek_mla(0, device=dev)
+        mout = torch.empty(mb.num_seqs, mb.num_q_heads, 512, dtype=mb.dtype, device=dev)
+        mdims = pa.make_dims(mb.q, mb.k_cache, mb.k_cache, mb.block_table, mb.seq_lens,
+                             mb.num_seqs, layout="mla", max_seq_len=max(mb.seq_lens_list),
+                             max_q_len=1)
+        mws = torch.empty(max(1, pa.mla_workspace_size(mdims, 0)), dtype=torch.uint8, device=dev)
+
+        def mstep():
+            pa.mla_decode(mb.q, mb.k_cache, mb.block_table, mb.seq_lens, mb.scale, out=mout,
+                          workspace=mws, max_seq_len=max(mb.seq_lens_list))
+
+        m_step_ms, m_kern_ms = time_steps(mstep, xsteps, 2, lib)
+        mbytes = workload.algorithmic_bytes(mb)
+        mflops = workload.algorithmic_flops(mb)
+        result["mla"] = {
+            "workload": "DeepSeek-R1-shaped absorbed MLA decode, 64 sequences, 128 heads, "
+                        "latent 576 (value 512), page 64, L~U[1024,32768]",
+            "hbm_gbs": round(mbytes / (m_step_ms * 1e-3) / 1e9, 2),
+            "kernel_gbs": round(mbytes / (m_kern_ms * 1e-3) / 1e9, 2),
+            "frac": round(mbytes / (m_kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "kernel_tflops": round(mflops / (m_kern_ms * 1e-3) / 1e12, 2),
+            "ms_per_step": round(m_step_ms, 4), "kernel_ms": round(m_kern_ms, 4),
+            "algorithmic_bytes": mbytes, "algorithmic_flops": mflops}
+        del mb, mout, mws
 
     if b_host_needed:
         result["cpu_baseline"] = cpu_baseline(b, nbytes)

@@ -197,21 +197,25 @@ pa_status pa_forward(const void* q, const void* k_cache, const void* v_cache,
 
   char* ws = (char*)workspace;
   pa::Control* ctrl = (pa::Control*)(ws + w.ctrl_off);
-  pa::WorkItem* items = (pa::WorkItem*)(ws + w.items_off);
-  pa::MergeItem* merges = (pa::MergeItem*)(ws + w.merges_off);
+  pa::ReqPlan* req = (pa::ReqPlan*)(ws + w.req_off);
+  int32_t* pre_off = (int32_t*)(ws + w.pre_off);
+  int32_t* dec_off = (int32_t*)(ws + w.dec_off);
+  int32_t* merge_off = (int32_t*)(ws + w.merge_off);
 
   pa::PlanArgs pl{};
   pl.seq_lens = seq_lens;
   pl.qsl = query_start_loc;
-  pl.items = items;
-  pl.merges = merges;
+  pl.req = req;
+  pl.pre_off = pre_off;
+  pl.dec_off = dec_off;
+  pl.merge_off = merge_off;
   pl.ctrl = ctrl;
   pl.B = d->num_seqs;
   pl.Hkv = d->num_kv_heads;
   pl.G = G;
   pl.P = d->page_size;
   pl.max_pages = d->max_pages_per_seq;
-  pl.target_items = std::max(1, 2 * grid);
+  pl.target_items = std::max(1, pa::kItemsPerWorkgroup * grid);
   hipError_t e = pa::launch_plan(pl, s);
   if (e != hipSuccess) return hip_fail(e);
 
@@ -226,8 +230,10 @@ pa_status pa_forward(const void* q, const void* k_cache, const void* v_cache,
   a.lse = lse;
   a.part_o = (float*)(ws + w.po_off);
   a.part_lse = (float*)(ws + w.plse_off);
-  a.items = items;
-  a.merges = merges;
+  a.req = req;
+  a.pre_off = pre_off;
+  a.dec_off = dec_off;
+  a.merge_off = merge_off;
   a.ctrl = ctrl;
   a.scale = scale;
   a.num_seqs = d->num_seqs;

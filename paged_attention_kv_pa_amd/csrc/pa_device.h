@@ -100,8 +100,8 @@ __device__ __forceinline__ u32x4 zero_tail8(u32x4 v, int key0, int limit) {
   return u32x4{w[0], w[1], w[2], w[3]};
 }
 
-// One unit of work of the persistent MHA kernel: rows = (new token x query
-// head of one KV head) of one request over the key range [kv_begin, kv_end).
+// One unit of work of the MHA kernels: rows = (new token x query head of one
+// KV head) of one request over the key range [kv_begin, kv_end).
 struct WorkItem {
   int32_t seq;       // request
   int32_t kvh;       // KV head
@@ -110,26 +110,30 @@ struct WorkItem {
   int32_t kv_begin;  // first key (multiple of 8)
   int32_t kv_end;    // one past the last key any row of the item may see
   int32_t part;      // < 0: write the final output; >= 0: partial slot
-  int32_t pad;
+  int32_t q0;        // row of the request's first new token in q / out
+  int32_t ctx;       // cached keys before the new tokens (seq_len - q_len)
+  int32_t pad[3];
 };
 
-// Merge of the partial slots of one split (request, KV head): the rows of
-// slots [slot0, slot0 + nsplit) are combined into the final output.
-struct MergeItem {
-  int32_t seq;
-  int32_t kvh;
-  int32_t slot0;
-  int32_t nsplit;
-  int32_t nrows;
-  int32_t pad[3];
+// Per-request plan written by the planner kernel of pa_forward.
+struct ReqPlan {
+  int32_t nq;      // new tokens (0: the request gets no work)
+  int32_t L;       // keys
+  int32_t q0;      // first query row
+  int32_t nblk;    // prefill-mode row blocks per KV head (0 for decode-mode requests)
+  int32_t nsplit;  // decode-mode key partitions per KV head (0 for prefill-mode requests)
+  int32_t per;     // keys per partition
+  int32_t slot0;   // first partial slot (requests with nsplit > 1)
+  int32_t pad;
 };
 
 // Control block at the start of the pa_forward workspace.
 struct Control {
-  int32_t n_items;
-  int32_t n_merge;
-  int32_t work_counter;
-  int32_t pad[61];
+  int32_t n_pre;         // prefill-mode items; item indices [0, n_pre)
+  int32_t n_items;       // all items; decode-mode items are [n_pre, n_items)
+  int32_t n_merge;       // (request, KV head) pairs whose decode rows were split
+  int32_t work_counter;  // next item index (reset by the planner)
+  int32_t pad[60];
 };
 
 }  // namespace pa

@@ -17,6 +17,7 @@ constexpr int kPrefillRowTiles = 2;    // 16-row tiles per wave in prefill mode
 constexpr int kPrefillRows = 4 * 16 * kPrefillRowTiles;  // rows of a prefill-mode item
 constexpr int kMaxFwdSplits = 64;      // key partitions per decode row in pa_forward
 constexpr int kMinChunk = 256;         // smallest key partition pa_forward makes
+constexpr int kItemsPerWorkgroup = 4;  // decode work is cut into ~this many items per workgroup
 constexpr int kMaxSplits = 256;        // pa_decode_split / pa_merge_lse / mla_decode limit
 
 struct MhaArgs {
@@ -30,8 +31,10 @@ struct MhaArgs {
   float* lse;                // may be NULL
   float* part_o;             // partial outputs (split items)
   float* part_lse;
-  const WorkItem* items;
-  const MergeItem* merges;
+  const ReqPlan* req;        // pa_forward planner output
+  const int32_t* pre_off;    // [B + 1] first prefill-mode item of each request
+  const int32_t* dec_off;    // [B + 1] first decode-mode item (relative to n_pre)
+  const int32_t* merge_off;  // [B + 1] first merge entry
   Control* ctrl;
   float scale;
   int32_t num_seqs;
@@ -42,8 +45,10 @@ struct MhaArgs {
 struct PlanArgs {
   const int32_t* seq_lens;
   const int32_t* qsl;
-  WorkItem* items;
-  MergeItem* merges;
+  ReqPlan* req;
+  int32_t* pre_off;
+  int32_t* dec_off;
+  int32_t* merge_off;
   Control* ctrl;
   int32_t B, Hkv, G;
   int32_t P, max_pages;
@@ -87,8 +92,8 @@ struct DeviceInfo {
 
 // Workspace layout of pa_forward.
 struct FwdWorkspace {
-  size_t ctrl_off, items_off, merges_off, plse_off, po_off, total;
-  int64_t cap_items, cap_merges, cap_slots;
+  size_t ctrl_off, req_off, pre_off, dec_off, merge_off, plse_off, po_off, total;
+  int64_t cap_slots;
 };
 FwdWorkspace fwd_workspace_layout(int B, int T, int Hkv, int G, int D);
 

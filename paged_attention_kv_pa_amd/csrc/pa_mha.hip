@@ -48,24 +48,6 @@ struct Dest {
   int64_t pl_base, pl_row;
 };
 
-struct RowMap {
-  int q0;    // first query row of the request in q / out
-  int ctx;   // cached keys before the new tokens
-};
-
-__device__ __forceinline__ RowMap row_map(const MhaArgs& a, int b) {
-  RowMap m;
-  const int L = a.seq_lens[b];
-  if (a.qsl) {
-    m.q0 = a.qsl[b];
-    m.ctx = L - (a.qsl[b + 1] - m.q0);
-  } else {
-    m.q0 = b;
-    m.ctx = L - 1;
-  }
-  return m;
-}
-
 template <int D>
 struct alignas(16) LdsDecode {
   static constexpr int kOStride = D + 4;  // floats per row of the merge buffer
@@ -123,7 +105,6 @@ __device__ void run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest
   constexpr int KS = D / 32, DT = D / 16;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
   const int b = it.seq, kvh = it.kvh, G = a.G, P = a.P;
-  const RowMap rm = row_map(a, b);
   const int kv_end = it.kv_end;
 
   // this lane's query row
@@ -131,11 +112,11 @@ __device__ void run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest
   const int ridx = it.row0 + r;
   const int tok = ridx / G;
   const int head = kvh * G + (ridx - tok * G);
-  const int lim = row_ok ? min(rm.ctx + tok + 1, kv_end) : it.kv_begin;
+  const int lim = row_ok ? min(it.ctx + tok + 1, kv_end) : it.kv_begin;
 
   bf16x8 qf[KS];
   {
-    const __bf16* qp = (const __bf16*)a.q + ((int64_t)(rm.q0 + tok) * a.Hq + head) * D + 8 * g;
+    const __bf16* qp = (const __bf16*)a.q + ((int64_t)(it.q0 + tok) * a.Hq + head) * D + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       qf[ks] = row_ok ? as_bf16x8(load16(qp + 32 * ks)) : as_bf16x8(u32x4{0, 0, 0, 0});
@@ -153,37 +134,40 @@ __device__ void run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest
   const __bf16* vbase = (const __bf16*)a.v_cache + (int64_t)kvh * D * P + (int64_t)r * P;
   const int last8 = (kv_end - 1) & ~7;
 
-  for (int t0 = it.kv_begin + 32 * wave; t0 < kv_end; t0 += 128) {
-    // K operand rows (clamped into the valid range; masked below)
+  // One 32-key step of this wave: load K / V^T operands, then update the
+  // online softmax and the accumulator.  Steps are software-pipelined: the
+  // next step's loads are in flight while the current one computes.
+  struct Step {
     bf16x8 kf[2][KS];
+    bf16x8 vf[DT];
+  };
+  auto load_step = [&](int t0, Step& st) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+    for (int mt = 0; mt < 2; ++mt) {  // K rows, clamped into the valid range (masked below)
       const int key = min(t0 + kperm(mt, r), kv_end - 1);
       const int page = bt[key / P];
       const __bf16* kp = kbase + (int64_t)page * page_elems + (key % P) * D;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kf[mt][ks] = as_bf16x8(load16(kp + 32 * ks));
+      for (int ks = 0; ks < KS; ++ks) st.kf[mt][ks] = as_bf16x8(load16(kp + 32 * ks));
     }
     // V^T operand: keys t0+8g .. t0+8g+7 of column 16dt + r
-    bf16x8 vf[DT];
-    {
-      const int key8 = min(t0 + 8 * g, last8);
-      const int page = bt[key8 / P];
-      const __bf16* vp = vbase + (int64_t)page * page_elems + (key8 % P);
-      const bool tail = t0 + 32 > kv_end;
+    const int key8 = min(t0 + 8 * g, last8);
+    const int page = bt[key8 / P];
+    const __bf16* vp = vbase + (int64_t)page * page_elems + (key8 % P);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        u32x4 raw = load16(vp + (int64_t)16 * dt * P);
-        if (tail) raw = zero_tail8(raw, t0 + 8 * g, kv_end);
-        vf[dt] = as_bf16x8(raw);
-      }
+    for (int dt = 0; dt < DT; ++dt) st.vf[dt] = as_bf16x8(load16(vp + (int64_t)16 * dt * P));
+  };
+  auto compute_step = [&](int t0, Step& st) {
+    if (t0 + 32 > kv_end) {  // keys past the end may be NaN poison: zero their values
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        st.vf[dt] = as_bf16x8(zero_tail8(as_u32x4(st.vf[dt]), t0 + 8 * g, kv_end));
     }
-    // S^T = K Q^T
     floatx4 s[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      s[0] = mfma_bf16(kf[0][ks], qf[ks], s[0]);
-      s[1] = mfma_bf16(kf[1][ks], qf[ks], s[1]);
+      s[0] = mfma_bf16(st.kf[0][ks], qf[ks], s[0]);
+      s[1] = mfma_bf16(st.kf[1][ks], qf[ks], s[1]);
     }
     // online softmax on keys t0 + 8g + j, j = 0..7
     float x[8];
@@ -215,7 +199,23 @@ __device__ void run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       acc[dt] *= alpha;
-      acc[dt] = mfma_bf16(vf[dt], pf, acc[dt]);
+      acc[dt] = mfma_bf16(st.vf[dt], pf, acc[dt]);
+    }
+  };
+
+  {
+    constexpr int kStride = 128;  // 4 waves x 32 keys
+    int t0 = it.kv_begin + 32 * wave;
+    Step sa, sb;
+    if (t0 < kv_end) load_step(t0, sa);
+    while (t0 < kv_end) {
+      if (t0 + kStride < kv_end) load_step(t0 + kStride, sb);
+      compute_step(t0, sa);
+      t0 += kStride;
+      if (t0 >= kv_end) break;
+      if (t0 + kStride < kv_end) load_step(t0 + kStride, sa);
+      compute_step(t0, sb);
+      t0 += kStride;
     }
   }
 
@@ -254,7 +254,7 @@ __device__ void run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest
       for (int e = 0; e < NC; ++e) o[e] *= inv;
       const int rid = it.row0 + row;
       const int t = rid / G;
-      const int64_t out_row = (int64_t)(rm.q0 + t) * a.Hq + kvh * G + (rid - t * G);
+      const int64_t out_row = (int64_t)(it.q0 + t) * a.Hq + kvh * G + (rid - t * G);
       store_row_chunk<D, NC>(a, dst, row, out_row, c0, o);
       if ((tid & 15) == 0)
         store_lse(a, dst, row, out_row, wsum > 0.f ? M * a.scale + __log2f(wsum) * kLn2 : kNegInf);
@@ -277,7 +277,6 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
   constexpr int VCH = D * kTK / 8 / kThreads;  // 16-byte V chunks per thread per tile
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
   const int b = it.seq, kvh = it.kvh, G = a.G, P = a.P;
-  const RowMap rm = row_map(a, b);
   const int kv_begin = it.kv_begin, kv_end = it.kv_end;
 
   // rows of this lane, one per row tile
@@ -292,8 +291,8 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
     const int rid = it.row0 + row;
     const int t = rid / G;
     const int head = kvh * G + (rid - t * G);
-    out_row[nt] = (int64_t)(rm.q0 + t) * a.Hq + head;
-    lim[nt] = row_ok[nt] ? min(rm.ctx + t + 1, kv_end) : kv_begin;
+    out_row[nt] = (int64_t)(it.q0 + t) * a.Hq + head;
+    lim[nt] = row_ok[nt] ? min(it.ctx + t + 1, kv_end) : kv_begin;
     const __bf16* qp = (const __bf16*)a.q + out_row[nt] * D + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -305,7 +304,7 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
     const int last_row = min(16 * NT * (wave + 1), it.nrows) - 1;
     if (last_row >= 16 * NT * wave) {
       const int t = (it.row0 + last_row) / G;
-      wave_lim = min(rm.ctx + t + 1, kv_end);
+      wave_lim = min(it.ctx + t + 1, kv_end);
     }
   }
 
@@ -479,20 +478,81 @@ __device__ __forceinline__ LdsDecode<D>& dec_lds(typename FwdLds<D, DECODE_ONLY>
   if constexpr (DECODE_ONLY) return s; else return s.dec;
 }
 
+// Largest b in [0, B) with off[b] <= idx (off is non-decreasing, off[0] = 0):
+// the request whose item range [off[b], off[b + 1]) holds idx.
+__device__ __forceinline__ int find_request(const int32_t* off, int B, int idx) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= idx) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Work item `idx` of pa_forward, decoded from the planner's per-request
+// offsets.  Prefill-mode items [0, n_pre) come first, the heaviest row block
+// of a request first; decode-mode items follow.
+__device__ WorkItem make_item(const MhaArgs& a, int idx, int n_pre) {
+  WorkItem it;
+  const int G = a.G;
+  if (idx < n_pre) {
+    const int b = find_request(a.pre_off, a.num_seqs, idx);
+    const ReqPlan rp = a.req[b];
+    const int local = idx - a.pre_off[b];
+    const int kvh = local / rp.nblk;
+    const int blk = rp.nblk - 1 - (local - kvh * rp.nblk);
+    const int rows = rp.nq * G;
+    it.seq = b;
+    it.kvh = kvh;
+    it.row0 = blk * kPrefillRows;
+    it.nrows = min(kPrefillRows, rows - it.row0);
+    it.ctx = rp.L - rp.nq;
+    it.kv_begin = 0;
+    it.kv_end = it.ctx + (it.row0 + it.nrows - 1) / G + 1;
+    it.part = -1;
+    it.q0 = rp.q0;
+  } else {
+    const int j = idx - n_pre;
+    const int b = find_request(a.dec_off, a.num_seqs, j);
+    const ReqPlan rp = a.req[b];
+    const int local = j - a.dec_off[b];
+    const int kvh = local / rp.nsplit;
+    const int sp = local - kvh * rp.nsplit;
+    it.seq = b;
+    it.kvh = kvh;
+    it.row0 = 0;
+    it.nrows = rp.nq * G;
+    it.ctx = rp.L - rp.nq;
+    it.kv_begin = sp * rp.per;
+    it.kv_end = min(rp.L, it.kv_begin + rp.per);
+    it.part = rp.nsplit > 1 ? rp.slot0 + kvh * rp.nsplit + sp : -1;
+    it.q0 = rp.q0;
+  }
+  it.pad[0] = it.pad[1] = it.pad[2] = 0;
+  return it;
+}
+
 // Persistent forward kernel: a fixed grid; each workgroup takes the next item
-// index from a device counter until the planner's list is exhausted.
+// index from a device counter until the planner's item count is reached.
 template <int D, bool DECODE_ONLY>
-__global__ __launch_bounds__(kThreads) void mha_forward_kernel(MhaArgs a) {
+__global__ __launch_bounds__(kThreads, DECODE_ONLY ? 2 : 1) void mha_forward_kernel(MhaArgs a) {
   __shared__ typename FwdLds<D, DECODE_ONLY>::type sm;
+  __shared__ WorkItem s_item;
   __shared__ int s_idx;
   const int n_items = a.ctrl->n_items;
+  const int n_pre = a.ctrl->n_pre;
   for (;;) {
-    if (threadIdx.x == 0) s_idx = atomicAdd(&a.ctrl->work_counter, 1);
+    if (threadIdx.x == 0) {
+      const int idx = atomicAdd(&a.ctrl->work_counter, 1);
+      s_idx = idx;
+      if (idx < n_items) s_item = make_item(a, idx, n_pre);
+    }
     __syncthreads();
     const int idx = s_idx;
+    const WorkItem it = s_item;
     __syncthreads();
     if (idx >= n_items) break;
-    const WorkItem it = a.items[idx];
     Dest dst;
     dst.partial = it.part >= 0;
     dst.po_base = (int64_t)it.part * kDecodeRows * D;
@@ -510,7 +570,7 @@ __global__ __launch_bounds__(kThreads) void mha_forward_kernel(MhaArgs a) {
 
 // pa_decode_split: one workgroup per (request, KV head, partition).
 template <int D, bool DEC>
-__global__ __launch_bounds__(kThreads) void mha_split_kernel(MhaArgs a) {
+__global__ __launch_bounds__(kThreads, DEC ? 2 : 1) void mha_split_kernel(MhaArgs a) {
   __shared__ typename std::conditional<DEC, LdsDecode<D>, LdsPrefill<D>>::type sm;
   const int S = a.num_splits;
   const int s = blockIdx.x % S;
@@ -542,36 +602,51 @@ __global__ __launch_bounds__(kThreads) void mha_split_kernel(MhaArgs a) {
   it.kv_begin = t0;
   it.kv_end = t1;
   it.part = 0;
-  it.pad = 0;
+  it.q0 = b;
+  it.ctx = L - 1;
+  it.pad[0] = it.pad[1] = it.pad[2] = 0;
   if constexpr (DEC) run_decode_item<D>(a, it, dst, sm);
   else run_prefill_item<D, kPrefillRowTiles>(a, it, dst, sm);
 }
 
 // Planner: one workgroup of 1024 threads turns (seq_lens, query_start_loc)
-// into the work list and the merge list.  Prefill-mode items come first
-// (heaviest rows of a request first), decode-mode items after them.
+// into per-request plans and item / merge offsets; the persistent kernel and
+// the merge kernel decode their units from these on the fly.
 constexpr int kPlanThreads = 1024;
 
-__device__ int4 block_exclusive_scan4(int4 v, int4* sh, int4* total) {
-  const int tid = threadIdx.x;
-  sh[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < kPlanThreads; off <<= 1) {
-    int4 u = tid >= off ? sh[tid - off] : int4{0, 0, 0, 0};
-    __syncthreads();
-    int4 w = sh[tid];
-    sh[tid] = int4{w.x + u.x, w.y + u.y, w.z + u.z, w.w + u.w};
-    __syncthreads();
+// Exclusive scan of one int4 per thread over the 1024-thread block: wave-level
+// scans with shuffles, then one wave scans the 16 wave totals.
+__device__ __forceinline__ int4 wave_inclusive_scan4(int4 v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int4 u = int4{__shfl_up(v.x, o), __shfl_up(v.y, o), __shfl_up(v.z, o), __shfl_up(v.w, o)};
+    if (lane >= o) v = int4{v.x + u.x, v.y + u.y, v.z + u.z, v.w + u.w};
   }
-  int4 incl = sh[tid];
-  *total = sh[kPlanThreads - 1];
+  return v;
+}
+
+__device__ int4 block_exclusive_scan4(int4 v, int4* wsum, int4* total) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int4 incl = wave_inclusive_scan4(v);
+  if (lane == 63) wsum[w] = incl;
   __syncthreads();
-  return int4{incl.x - v.x, incl.y - v.y, incl.z - v.z, incl.w - v.w};
+  if (w == 0) {
+    int4 t = lane < kPlanThreads / 64 ? wsum[lane] : int4{0, 0, 0, 0};
+    t = wave_inclusive_scan4(t);
+    if (lane < kPlanThreads / 64) wsum[lane] = t;  // inclusive prefix of wave totals
+  }
+  __syncthreads();
+  const int4 before = w > 0 ? wsum[w - 1] : int4{0, 0, 0, 0};
+  *total = wsum[kPlanThreads / 64 - 1];
+  __syncthreads();
+  return int4{before.x + incl.x - v.x, before.y + incl.y - v.y, before.z + incl.z - v.z,
+              before.w + incl.w - v.w};
 }
 
 // New-token count and key count of request b.  Requests whose lengths are
-// inconsistent (seq_len < q_len) get no work; seq_len is capped at the
-// block-table capacity so no item can index past a table row.
+// inconsistent (seq_len < q_len, or no key) get no work; seq_len is capped at
+// the block-table capacity so no item can index past a table row.
 __device__ __forceinline__ void request_shape(const PlanArgs& a, int b, int* nq, int* L) {
   int q = a.qsl[b + 1] - a.qsl[b];
   int l = a.seq_lens[b];
@@ -583,147 +658,136 @@ __device__ __forceinline__ void request_shape(const PlanArgs& a, int b, int* nq,
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
-  __shared__ int4 sh[kPlanThreads];
+  __shared__ int4 sh[kPlanThreads / 64];
   __shared__ unsigned long long s_dec_keys;
-  __shared__ int s_pre_items;
   const int tid = threadIdx.x;
   const int G = a.G, Hkv = a.Hkv;
-  if (tid == 0) {
-    s_dec_keys = 0;
-    s_pre_items = 0;
-  }
+  if (tid == 0) s_dec_keys = 0;
   __syncthreads();
-  // pass 1: totals
+  // pass 1: total decode-mode keys, which sets the partition size
   unsigned long long my_keys = 0;
-  int my_pre = 0;
   for (int b = tid; b < a.B; b += kPlanThreads) {
     int nq, L;
     request_shape(a, b, &nq, &L);
-    if (nq <= 0) continue;
-    const int rows = nq * G;
-    if (rows <= kDecodeRows) my_keys += (unsigned long long)L;
-    else my_pre += Hkv * ((rows + kPrefillRows - 1) / kPrefillRows);
+    if (nq > 0 && nq * G <= kDecodeRows) my_keys += (unsigned long long)L;
   }
-  atomicAdd(&s_dec_keys, my_keys);
-  atomicAdd(&s_pre_items, my_pre);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) my_keys += __shfl_xor(my_keys, o);
+  if ((tid & 63) == 0 && my_keys) atomicAdd(&s_dec_keys, my_keys);
   __syncthreads();
   const unsigned long long dec_work = s_dec_keys * (unsigned long long)Hkv;
   long long chunk = (long long)((dec_work + a.target_items - 1) / (unsigned long long)a.target_items);
   chunk = chunk < kMinChunk ? kMinChunk : chunk;
   chunk = (chunk + 63) & ~63LL;
-  const int pre_total = s_pre_items;
 
-  // pass 2: scan and write
-  int4 run = int4{0, pre_total, 0, 0};  // prefill offset, decode offset, slot offset, merge offset
+  // pass 2: per-request counts, exclusive scans, plans
+  int4 run = int4{0, 0, 0, 0};  // prefill items, decode items, partial slots, merge entries
   for (int base = 0; base < a.B; base += kPlanThreads) {
     const int b = base + tid;
-    int nq = 0, L = 0, rows = 0, nsplit = 0, per = 0, nblk = 0;
+    ReqPlan rp = {0, 0, 0, 0, 0, 0, 0, 0};
     int4 cnt = int4{0, 0, 0, 0};
     if (b < a.B) {
-      request_shape(a, b, &nq, &L);
-      rows = nq * G;
-      if (nq > 0 && rows <= kDecodeRows) {
-        long long s = (L + chunk - 1) / chunk;
-        s = s < 1 ? 1 : (s > kMaxFwdSplits ? kMaxFwdSplits : s);
-        per = 64 * (int)(((L + 63) / 64 + s - 1) / s);
-        nsplit = (L + per - 1) / per;
-        if (nsplit < 1) nsplit = 1;
-        cnt.y = Hkv * nsplit;
-        if (nsplit > 1) {
-          cnt.z = Hkv * nsplit;
+      request_shape(a, b, &rp.nq, &rp.L);
+      rp.q0 = a.qsl[b];
+      const int rows = rp.nq * G;
+      if (rp.nq > 0 && rows <= kDecodeRows) {
+        long long sp = (rp.L + chunk - 1) / chunk;
+        sp = sp < 1 ? 1 : (sp > kMaxFwdSplits ? kMaxFwdSplits : sp);
+        rp.per = 64 * (int)(((rp.L + 63) / 64 + sp - 1) / sp);
+        rp.nsplit = (rp.L + rp.per - 1) / rp.per;
+        cnt.y = Hkv * rp.nsplit;
+        if (rp.nsplit > 1) {
+          cnt.z = Hkv * rp.nsplit;
           cnt.w = Hkv;
         }
-      } else if (nq > 0) {
-        nblk = (rows + kPrefillRows - 1) / kPrefillRows;
-        cnt.x = Hkv * nblk;
+      } else if (rp.nq > 0) {
+        rp.nblk = (rows + kPrefillRows - 1) / kPrefillRows;
+        cnt.x = Hkv * rp.nblk;
       }
     }
     int4 tot;
     const int4 ex = block_exclusive_scan4(cnt, sh, &tot);
-    if (b < a.B && nq > 0) {
-      const int ctx = L - nq;
-      if (nblk > 0) {
-        for (int h = 0; h < Hkv; ++h)
-          for (int k = 0; k < nblk; ++k) {
-            const int blk = nblk - 1 - k;  // last (heaviest) row block first
-            WorkItem it;
-            it.seq = b;
-            it.kvh = h;
-            it.row0 = blk * kPrefillRows;
-            it.nrows = min(kPrefillRows, rows - it.row0);
-            it.kv_begin = 0;
-            it.kv_end = ctx + (it.row0 + it.nrows - 1) / G + 1;
-            it.part = -1;
-            it.pad = 0;
-            a.items[run.x + ex.x + h * nblk + k] = it;
-          }
-      } else {
-        const int slot0 = run.z + ex.z;
-        for (int h = 0; h < Hkv; ++h) {
-          for (int s = 0; s < nsplit; ++s) {
-            WorkItem it;
-            it.seq = b;
-            it.kvh = h;
-            it.row0 = 0;
-            it.nrows = rows;
-            it.kv_begin = s * per;
-            it.kv_end = min(L, (s + 1) * per);
-            it.part = nsplit > 1 ? slot0 + h * nsplit + s : -1;
-            it.pad = 0;
-            a.items[run.y + ex.y + h * nsplit + s] = it;
-          }
-          if (nsplit > 1) {
-            MergeItem mi;
-            mi.seq = b;
-            mi.kvh = h;
-            mi.slot0 = slot0 + h * nsplit;
-            mi.nsplit = nsplit;
-            mi.nrows = rows;
-            mi.pad[0] = mi.pad[1] = mi.pad[2] = 0;
-            a.merges[run.w + ex.w + h] = mi;
-          }
-        }
-      }
+    if (b < a.B) {
+      rp.slot0 = run.z + ex.z;
+      a.req[b] = rp;
+      a.pre_off[b] = run.x + ex.x;
+      a.dec_off[b] = run.y + ex.y;
+      a.merge_off[b] = run.w + ex.w;
     }
     run = int4{run.x + tot.x, run.y + tot.y, run.z + tot.z, run.w + tot.w};
   }
   if (tid == 0) {
-    a.ctrl->n_items = run.y;  // decode items are placed after all prefill items
+    a.pre_off[a.B] = run.x;
+    a.dec_off[a.B] = run.y;
+    a.merge_off[a.B] = run.w;
+    a.ctrl->n_pre = run.x;
+    a.ctrl->n_items = run.x + run.y;
     a.ctrl->n_merge = run.w;
     a.ctrl->work_counter = 0;
   }
 }
 
-// Merge of pa_forward's split decode rows: one wave per (merge item, row).
+// Merge of pa_forward's split decode rows.  One wave takes a (request, KV
+// head) pair whose rows were split and handles 4 rows at a time: 16 lanes per
+// row, each with D / 16 consecutive columns, folding the partitions in one
+// pass with a running log-sum-exp (max, rescaled weight sum, rescaled sum).
 template <int D>
 __global__ __launch_bounds__(kThreads) void mha_forward_merge_kernel(MhaArgs a) {
+  constexpr int NC = D / 16;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int n_units = a.ctrl->n_merge * kDecodeRows;
+  const int rsub = lane >> 4, c0 = (lane & 15) * NC;
+  const int n_merge = a.ctrl->n_merge;
   const int stride = gridDim.x * (kThreads / 64);
-  for (int u = blockIdx.x * (kThreads / 64) + wv; u < n_units; u += stride) {
-    const MergeItem mi = a.merges[u / kDecodeRows];
-    const int row = u % kDecodeRows;
-    if (row >= mi.nrows) continue;
-    const int S = mi.nsplit;  // <= 64: one lane per partition
-    const float ls = lane < S ? a.part_lse[(int64_t)(mi.slot0 + lane) * kDecodeRows + row] : kNegInf;
-    const float M = wave_max(ls);
-    const float w = (lane < S && ls != kNegInf) ? __expf(ls - M) : 0.f;
-    const float wsum = wave_sum(w);
-    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-    const int t = row / a.G;
-    const int64_t out_row = (int64_t)(a.qsl[mi.seq] + t) * a.Hq + mi.kvh * a.G + (row - t * a.G);
-    float o[D / 64];
+  for (int e = blockIdx.x * (kThreads / 64) + wv; e < n_merge; e += stride) {
+    const int b = find_request(a.merge_off, a.num_seqs, e);
+    const ReqPlan rp = a.req[b];
+    const int kvh = e - a.merge_off[b];
+    const int S = rp.nsplit;
+    const int slot0 = rp.slot0 + kvh * S;
+    const int nrows = rp.nq * a.G;
+    for (int r0 = 0; r0 < nrows; r0 += 4) {
+      const int row = r0 + rsub;
+      if (row >= nrows) continue;
+      // partition weights: lane j of the row's 16 lanes holds partitions j, j + 16, ...
+      float M = kNegInf;
+      for (int sp = lane & 15; sp < S; sp += 16)
+        M = fmaxf(M, a.part_lse[(int64_t)(slot0 + sp) * kDecodeRows + row]);
 #pragma unroll
-    for (int e = 0; e < D / 64; ++e) o[e] = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float ws = __shfl(w, s);
-      const float* po = a.part_o + ((int64_t)(mi.slot0 + s) * kDecodeRows + row) * D;
+      for (int o = 8; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+      float o[NC];
 #pragma unroll
-      for (int e = 0; e < D / 64; ++e) o[e] = fmaf(ws, po[lane + 64 * e], o[e]);
+      for (int c = 0; c < NC; ++c) o[c] = 0.f;
+      float wsum = 0.f;
+      if (M != kNegInf) {
+#pragma unroll 4
+        for (int sp = 0; sp < S; ++sp) {
+          const int64_t slot = slot0 + sp;
+          const float ls = a.part_lse[slot * kDecodeRows + row];
+          const floatx4* po = reinterpret_cast<const floatx4*>(a.part_o + (slot * kDecodeRows + row) * D + c0);
+          floatx4 v[NC / 4];
+#pragma unroll
+          for (int c = 0; c < NC / 4; ++c) v[c] = po[c];  // finite for every written partition
+          const float w = ls == kNegInf ? 0.f : __expf(ls - M);
+          wsum += w;
+#pragma unroll
+          for (int c = 0; c < NC / 4; ++c) {
+            o[4 * c] = fmaf(w, v[c][0], o[4 * c]);
+            o[4 * c + 1] = fmaf(w, v[c][1], o[4 * c + 1]);
+            o[4 * c + 2] = fmaf(w, v[c][2], o[4 * c + 2]);
+            o[4 * c + 3] = fmaf(w, v[c][3], o[4 * c + 3]);
+          }
+        }
+      }
+      const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+      const int t = row / a.G;
+      const int64_t out_row = (int64_t)(rp.q0 + t) * a.Hq + kvh * a.G + (row - t * a.G);
+      __bf16* op = (__bf16*)a.out + out_row * D + c0;
+#pragma unroll
+      for (int c = 0; c < NC; c += 4)
+        *reinterpret_cast<u32x2*>(op + c) =
+            u32x2{pack_bf16x2(o[c] * inv, o[c + 1] * inv), pack_bf16x2(o[c + 2] * inv, o[c + 3] * inv)};
+      if ((lane & 15) == 0 && a.lse) a.lse[out_row] = wsum > 0.f ? M + __logf(wsum) : kNegInf;
     }
-#pragma unroll
-    for (int e = 0; e < D / 64; ++e) ((__bf16*)a.out)[out_row * D + lane + 64 * e] = (__bf16)(o[e] * inv);
-    if (lane == 0 && a.lse) a.lse[out_row] = wsum > 0.f ? M + __logf(wsum) : kNegInf;
   }
 }
 
@@ -773,19 +837,22 @@ hipError_t launch_mha_split(const MhaArgs& a, int D, hipStream_t s) {
 }
 
 FwdWorkspace fwd_workspace_layout(int B, int T, int Hkv, int G, int D) {
+  (void)T;
+  (void)G;
   FwdWorkspace w;
   auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  w.cap_items = (int64_t)Hkv * ((int64_t)B * kMaxFwdSplits +
-                                ((int64_t)T * G + kPrefillRows - 1) / kPrefillRows + B);
-  w.cap_merges = (int64_t)Hkv * B;
   w.cap_slots = (int64_t)Hkv * B * kMaxFwdSplits;
   size_t off = 0;
   w.ctrl_off = off;
   off = align(off + sizeof(Control));
-  w.items_off = off;
-  off = align(off + (size_t)w.cap_items * sizeof(WorkItem));
-  w.merges_off = off;
-  off = align(off + (size_t)w.cap_merges * sizeof(MergeItem));
+  w.req_off = off;
+  off = align(off + (size_t)B * sizeof(ReqPlan));
+  w.pre_off = off;
+  off = align(off + (size_t)(B + 1) * sizeof(int32_t));
+  w.dec_off = off;
+  off = align(off + (size_t)(B + 1) * sizeof(int32_t));
+  w.merge_off = off;
+  off = align(off + (size_t)(B + 1) * sizeof(int32_t));
   w.plse_off = off;
   off = align(off + (size_t)w.cap_slots * kDecodeRows * sizeof(float));
   w.po_off = off;
