@@ -178,7 +178,7 @@ PA_API size_t mla_workspace_size(const pa_dims* dims, int32_t num_splits);
  * The keys of each request are split into num_splits page-aligned partitions
  * (as in pa_decode_split; 0 picks a count from B and the capacities) and
  * merged by log-sum-exp.  Requires bf16, Hkv == 1, Dqk == 576, Dv == 512,
- * Hq a multiple of 16 up to 128, P a multiple of 8 up to 256, seq_len >= 1.
+ * Hq a multiple of 16 up to 128, P a power of two in [8, 256], seq_len >= 1.
  */
 PA_API pa_status mla_decode(const void* q, const void* kv_cache, const int32_t* block_table,
                      const int32_t* seq_lens, float scale, void* out, float* lse,

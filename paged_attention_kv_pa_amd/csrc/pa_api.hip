@@ -107,7 +107,9 @@ pa_status check_mla(const pa_dims* d) {
       d->head_dim_v != 512)
     return PA_ERR_UNSUPPORTED;
   if (d->num_q_heads % 16 != 0 || d->num_q_heads > 128) return PA_ERR_UNSUPPORTED;
-  if (d->page_size % 8 != 0 || d->page_size > 256) return PA_ERR_UNSUPPORTED;
+  // page size: a power of two in [8, 256]
+  if (d->page_size < 8 || d->page_size > 256 || (d->page_size & (d->page_size - 1)) != 0)
+    return PA_ERR_UNSUPPORTED;
   if (d->num_tokens != d->num_seqs) return PA_ERR_INVALID_ARG;
   return PA_OK;
 }
@@ -374,6 +376,7 @@ pa_status mla_decode(const void* q, const void* kv_cache, const int32_t* block_t
   a.B = d->num_seqs;
   a.Hq = d->num_q_heads;
   a.P = d->page_size;
+  a.log2_page = __builtin_ctz((unsigned)d->page_size);
   a.max_pages = d->max_pages_per_seq;
   a.num_splits = S;
   hipStream_t s = (hipStream_t)stream;

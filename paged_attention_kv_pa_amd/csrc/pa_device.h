@@ -18,6 +18,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float floatx4;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+typedef __attribute__((ext_vector_type(16))) float floatx16;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -26,6 +27,35 @@ constexpr float kNegInf = -__builtin_huge_valf();
 __device__ __forceinline__ floatx4 mfma_bf16(const bf16x8& a, const bf16x8& b,
                                              const floatx4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// v_mfma_f32_32x32x16_bf16: A[m][k] (32 x 16): lane holds A[l % 32][8 (l / 32) ..];
+// B[k][n]: lane holds B[8 (l / 32) ..][l % 32]; D[m][n]: lane holds, in element
+// v, D[8 (v / 4) + 4 (l / 32) + v % 4][l % 32].
+__device__ __forceinline__ floatx16 mfma32_bf16(const bf16x8& a, const bf16x8& b,
+                                                const floatx16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Direct HBM -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane
+// L's bytes land at lds_wave_base + 16 L; lds_wave_base must be the same for
+// the whole wave.  Issued through inline assembly so that the compiler neither
+// waits for these copies at every barrier nor counts them: the caller waits
+// with wait_vmcnt<N>() and must not expect compiler-inserted waits for them.
+__device__ __forceinline__ void lds_dma16(const void* gsrc, const void* lds_wave_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)lds_wave_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(base), "v"(gsrc)
+               : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
 __device__ __forceinline__ u32x4 load16(const void* p) {

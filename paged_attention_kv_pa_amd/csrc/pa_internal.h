@@ -80,7 +80,7 @@ struct MlaArgs {
   float* part_o;             // [B, Hq, S, 512] (num_splits > 1)
   float* part_lse;           // [B, Hq, S]
   float scale;
-  int32_t B, Hq, P, max_pages, num_splits;
+  int32_t B, Hq, P, log2_page, max_pages, num_splits;
 };
 
 // Device properties cached per device by the ABI layer.

@@ -4,20 +4,31 @@
 // the row (576 columns) is the key and its first 512 columns are the value
 // ("vLLM AMD ROCm Attention Backend Optimization", sections "AITER MLA
 // backend" and "Hybrid processing strategy").  With 128 heads on one latent
-// head the work per cached byte is high, so a workgroup of 8 waves takes all
-// heads of one request (wave w owns the kMNT 16-row MFMA tiles of heads
-// 16 kMNT w ..) and each latent tile is read from HBM once.
+// head the work per cached byte is high (about 240 flop per byte), so one
+// workgroup of 4 waves takes all heads of one request — wave w owns heads
+// 32w .. 32w+31 as one 32-row MFMA tile — and every latent tile is read from
+// HBM exactly once.
 //
 // Per 32-key tile:
-//   * the tile is copied to LDS row-major (the key operand), then transposed
-//     inside LDS into [column][key] (the value operand), so that each of the
-//     waves reads 16-byte MFMA operands for both products;
-//   * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16 with the same
-//     lane-local row statistics as the MHA kernel (key rows of the K operand
-//     permuted so lane group g holds keys 8g .. 8g+7);
-//   * online softmax in base 2, probabilities rounded to bf16.
-// The keys of a request are split into page-aligned partitions, one
-// workgroup each, and merged by log-sum-exp in a second launch.
+//   * HBM -> LDS by direct-to-LDS copies (16 bytes per lane, no registers)
+//     into a 3-stage ring with one barrier per tile.  The tile is stored
+//     "chunk-group major": [9 groups of 8 sixteen-byte chunks][32 keys][8],
+//     with the chunk index inside a group XOR-swizzled by the key, so that a
+//     thread's 9 copies of a tile are 128 bytes apart in HBM (one address
+//     register) and the operand reads of different keys hit different banks;
+//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (32 keys x 32 heads x 16
+//     columns per instruction).  The 32 M-rows of the K operand are permuted
+//     so that lanes l and l + 32 end up holding keys 8h .. 8h+7 and
+//     16 + 8h .. 16 + 8h+7 (h = l / 32) of head l % 32 — exactly the slots
+//     they must supply as the B operand (P^T) of the value product;
+//   * O^T = V^T P^T on the same instruction (32 columns x 32 heads x 16 keys):
+//     the V^T operand (8 consecutive keys of one column per lane) is read from
+//     the row-major tile with the LDS transpose read ds_read_b64_tr_b16;
+//   * online softmax in base 2 with lazy rescaling: the running max of a head
+//     only moves when a tile would push probabilities above 2^8, so the
+//     accumulator (256 registers per lane) is rarely touched by vector ALUs.
+// The keys of a request are cut into page-aligned partitions, one workgroup
+// each, combined by the log-sum-exp merge in a second launch.
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -25,197 +36,259 @@ namespace pa {
 
 namespace {
 
-constexpr int kMlaThreads = 512;
-constexpr int kMNT = 1;                  // 16-row tiles per wave
+constexpr int kMlaThreads = 256;
 constexpr int kDqk = 576, kDv = 512;
-constexpr int kMTK = 32;                 // keys per tile
-constexpr int kMKRow = kDqk + 8;         // bf16 per K row in LDS
-constexpr int kMVRow = kMTK + 8;         // bf16 per V^T row in LDS
-constexpr int kMChunks = kMTK * kDqk / 8;  // 16-byte chunks per tile (2304)
-constexpr int kMLoads = (kMChunks + kMlaThreads - 1) / kMlaThreads;  // 5
+constexpr int kMTK = 32;                   // keys per tile
+constexpr int kRowChunks = kDqk / 8;       // 16-byte chunks per latent row (72)
+constexpr int kGroups = kRowChunks / 8;    // chunk groups per row (9)
+constexpr int kStages = 3;
+constexpr int kStageBytes = kMTK * kDqk * 2;  // 36 KiB
+constexpr float kLazyLog2 = 8.f;           // rescale when probabilities would exceed 2^8
+// The query's trailing kQLdsSteps K-steps (16 columns each) are kept in LDS
+// instead of registers: the 256 accumulator registers plus the whole query
+// would not fit in one wave's register budget.
+constexpr int kQRegSteps = 25;
+constexpr int kQLdsSteps = kDqk / 16 - kQRegSteps;  // 11
+constexpr int kQLdsCols = 16 * kQLdsSteps;          // 176
+constexpr int kQLdsStride = kQLdsCols * 2 + 16;     // bytes per head row (padded: 368)
+constexpr int kQLdsBytes = 128 * kQLdsStride;
 
-struct alignas(16) MlaLds {
-  __bf16 k[2][kMTK * kMKRow];
-  __bf16 v[2][kDv * kMVRow];
-};
+typedef __attribute__((ext_vector_type(4))) short short4v;
+typedef __attribute__((address_space(3))) short4v lds_short4;
 
-__device__ __forceinline__ int kperm(int mt, int m) { return 8 * (m >> 2) + 4 * mt + (m & 3); }
+// Swizzle of the chunk index inside its group of 8, by key.
+__device__ __forceinline__ int swz(int k) { return (k >> 1) & 7; }
+
+// Byte offset of 16-byte chunk c (0..71) of key k (0..31) inside a stage.
+__device__ __forceinline__ int chunk_off(int k, int c) {
+  return (((c >> 3) * kMTK + k) * 8 + ((c & 7) ^ swz(k))) * 16;
+}
+
+// x *= alpha for a value the caller keeps in an accumulation register (AGPR).
+__device__ __forceinline__ void agpr_scale(float& x, float alpha) {
+  float t;
+  asm volatile(
+      "v_accvgpr_read_b32 %1, %0\n\ts_nop 1\n\tv_mul_f32 %1, %1, %2\n\ts_nop 1\n\t"
+      "v_accvgpr_write_b32 %0, %1"
+      : "+a"(x), "=&v"(t)
+      : "v"(alpha));
+}
+
+// Key held by M-row m of the K operand (see the file comment).
+__device__ __forceinline__ int kperm32(int m) {
+  const int q = m >> 3, h = (m >> 2) & 1, w = m & 3;
+  return 16 * (q >> 1) + 8 * h + 4 * (q & 1) + w;
+}
 
 __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
   extern __shared__ __align__(16) char mla_smem[];
-  MlaLds& sm = *reinterpret_cast<MlaLds*>(mla_smem);
-  constexpr int KS = kDqk / 32, DT = kDv / 16;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
+  constexpr int KS = kDqk / 16;  // 36 K-steps of S^T
+  constexpr int DT = kDv / 32;   // 16 column tiles of O^T
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n = lane & 31, h = lane >> 5;
   const int S = a.num_splits;
   const int s = blockIdx.x % S, b = blockIdx.x / S;
-  const int L = a.seq_lens[b], P = a.P;
-  const int pages = (L + P - 1) / P;
+  const int L = a.seq_lens[b], P = a.P, lp = a.log2_page;
+  const int pages = (L + P - 1) >> lp;
   const long long per = (long long)P * ((pages + S - 1) / S);
   const long long a0 = per * s, a1 = a0 + per;
   const int t0k = a0 < L ? (int)a0 : L, t1k = a1 < L ? (int)a1 : L;
-
-  int head[kMNT];
-  bool row_ok[kMNT];
-  bf16x8 qf[kMNT][KS];
-#pragma unroll
-  for (int nt = 0; nt < kMNT; ++nt) {
-    head[nt] = 16 * (kMNT * wave + nt) + r;
-    row_ok[nt] = head[nt] < a.Hq;
-    const __bf16* qp = (const __bf16*)a.q + ((int64_t)b * a.Hq + head[nt]) * kDqk + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[nt][ks] = row_ok[nt] ? as_bf16x8(load16(qp + 32 * ks)) : as_bf16x8(u32x4{0, 0, 0, 0});
-  }
-  const float sc = a.scale * kLog2e;
-  float m[kMNT], l[kMNT];
-  floatx4 acc[kMNT][DT];
-#pragma unroll
-  for (int nt = 0; nt < kMNT; ++nt) {
-    m[nt] = kNegInf;
-    l[nt] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc[nt][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  }
+  const int ntiles = (t1k - t0k + kMTK - 1) / kMTK;
 
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
-  const __bf16* kv = (const __bf16*)a.kv;
-  u32x4 reg[kMLoads];
-  auto gload = [&](int t0) {
-#pragma unroll
-    for (int j = 0; j < kMLoads; ++j) {
-      const int c = j * kMlaThreads + tid;
-      if (c < kMChunks) {
-        const int key = min(t0 + c / (kDqk / 8), t1k - 1);  // clamped: real data
-        const int page = bt[key / P];
-        reg[j] = load16(kv + ((int64_t)page * P + (key % P)) * kDqk + (c % (kDqk / 8)) * 8);
-      }
-    }
-  };
-  auto kstore = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < kMLoads; ++j) {
-      const int c = j * kMlaThreads + tid;
-      if (c < kMChunks) store16(&sm.k[buf][(c / (kDqk / 8)) * kMKRow + (c % (kDqk / 8)) * 8], reg[j]);
-    }
-  };
-  // V^T[col][key] for col < 512 from the row-major tile: thread task u covers
-  // column u % 512 and keys 8 (u / 512) .. +7.
-  auto transpose = [&](int buf) {
-    const unsigned short* kt = reinterpret_cast<const unsigned short*>(sm.k[buf]);
-#pragma unroll
-    for (int j = 0; j < kDv * (kMTK / 8) / kMlaThreads; ++j) {
-      const int u = j * kMlaThreads + tid;
-      const int col = u % kDv, kg = u / kDv;
-      uint32_t w[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = kt[(8 * kg + 2 * e) * kMKRow + col];
-        const uint32_t hi = kt[(8 * kg + 2 * e + 1) * kMKRow + col];
-        w[e] = lo | (hi << 16);
-      }
-      store16(&sm.v[buf][col * kMVRow + 8 * kg], u32x4{w[0], w[1], w[2], w[3]});
-    }
-  };
+  const char* kv = (const char*)a.kv;
 
-  const int ntiles = (t1k - t0k + kMTK - 1) / kMTK;
-  if (ntiles > 0) {
-    gload(t0k);
-    kstore(0);
-  }
-  __syncthreads();
-  if (ntiles > 0) transpose(0);
-  __syncthreads();
-  for (int ti = 0; ti < ntiles; ++ti) {
+  // DMA of tile ti into stage st: thread tid copies key tid / 8, chunk slot
+  // tid % 8 of each of the 9 groups; one wave instruction fills 64
+  // consecutive chunk positions of a group.
+  const int dkey = tid >> 3;
+  const int dchunk = (tid & 7) ^ swz(dkey);
+  auto issue_tile = [&](int ti, int st) {
     const int t0 = t0k + ti * kMTK;
-    const int buf = ti & 1;
-    {
-      const __bf16* kt = sm.k[buf];
-      const __bf16* vt = sm.v[buf];
-      floatx4 sacc[kMNT][2];
+    const int key = min(t0 + dkey, t1k - 1);  // clamped: real data, masked later
+    // pages of this tile, read through scalar loads (uniform indices)
+    const int last_pg = (t1k - 1) >> lp;
+    const int pg0 = __builtin_amdgcn_readfirstlane(t0 >> lp);
+    int page;
+    if (P >= kMTK) {
+      page = bt[pg0];
+    } else {
+      const int j = (key >> lp) - pg0;  // 0 .. 32 / P - 1
+      const int p0 = bt[pg0];
+      const int p1 = bt[min(pg0 + 1, last_pg)];
+      const int p2 = bt[min(pg0 + 2, last_pg)];
+      const int p3 = bt[min(pg0 + 3, last_pg)];
+      page = j == 0 ? p0 : (j == 1 ? p1 : (j == 2 ? p2 : p3));
+    }
+    const char* src = kv + (((int64_t)page << lp) + (key & (P - 1))) * (kDqk * 2) + dchunk * 16;
+    const char* dst = mla_smem + st * kStageBytes + wave * 64 * 16;
 #pragma unroll
-      for (int nt = 0; nt < kMNT; ++nt) sacc[nt][0] = sacc[nt][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < kGroups; ++j) lds_dma16(src + 128 * j, dst + j * kMTK * 8 * 16);
+  };
+
+  // query fragments first (plain loads, waited for before the copies start):
+  // K-steps [0, kQRegSteps) in registers, the rest in LDS after the KV ring
+  const int head = 32 * wave + n;
+  const bool row_ok = head < a.Hq;
+  char* qlds = mla_smem + kStages * kStageBytes;
+  bf16x8 qf[kQRegSteps];  // B operand of S^T: Q[head][16 ks + 8h .. +7]
+  {
+    const __bf16* qp = (const __bf16*)a.q + ((int64_t)b * a.Hq + head) * kDqk + 8 * h;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 k0 = as_bf16x8(load16(kt + kperm(0, r) * kMKRow + 32 * ks + 8 * g));
-        const bf16x8 k1 = as_bf16x8(load16(kt + kperm(1, r) * kMKRow + 32 * ks + 8 * g));
+    for (int ks = 0; ks < kQRegSteps; ++ks)
+      qf[ks] = row_ok ? as_bf16x8(load16(qp + 16 * ks)) : as_bf16x8(u32x4{0, 0, 0, 0});
 #pragma unroll
-        for (int nt = 0; nt < kMNT; ++nt) {
-          sacc[nt][0] = mfma_bf16(k0, qf[nt][ks], sacc[nt][0]);
-          sacc[nt][1] = mfma_bf16(k1, qf[nt][ks], sacc[nt][1]);
-        }
+    for (int ks = kQRegSteps; ks < KS; ++ks) {
+      const u32x4 v = row_ok ? load16(qp + 16 * ks) : u32x4{0, 0, 0, 0};
+      store16(qlds + head * kQLdsStride + (16 * (ks - kQRegSteps) + 8 * h) * 2, v);
+    }
+  }
+  wait_vmcnt<0>();
+  if (ntiles > 0) issue_tile(0, 0);
+  if (ntiles > 1) issue_tile(1, 1);
+
+  const float sc = a.scale * kLog2e;
+  float m = kNegInf, l = 0.f;
+  floatx16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[dt][v] = 0.f;
+
+  // K operand: M-row n reads key kperm32(n), columns 16 ks + 8h (chunk 2 ks + h)
+  const int krow = kperm32(n);
+  int koff[4];  // offset of chunk 2 u + h (u = ks % 4); chunk group ks / 4 adds 4 KiB each
+#pragma unroll
+  for (int u = 0; u < 4; ++u) koff[u] = chunk_off(krow, 2 * u + h);
+  // V^T operand via transpose reads.  16-lane group G = lane / 16 of the wave
+  // serves columns 32 dt + 16 (G & 1) + .. and keys 16 kk + 8 (G >> 1) + ..;
+  // its source lane k' reads key 16 kk + 8 (G >> 1) + 4 hh + (k' >> 2),
+  // columns 32 dt + 16 (G & 1) + 4 (k' & 3) .. +3 (chunk 4 dt + 2 (G & 1) +
+  // ((k' & 3) >> 1), half (k' & 1)).
+  const int G = lane >> 4, kq = lane & 15;
+  int voff[2][2][2];  // [kk][hh][dt & 1]; the group index dt >> 1 adds a constant
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int d2 = 0; d2 < 2; ++d2) {
+        const int key = 16 * kk + 8 * (G >> 1) + 4 * hh + (kq >> 2);
+        const int c = 4 * d2 + 2 * (G & 1) + ((kq & 3) >> 1);
+        voff[kk][hh][d2] = chunk_off(key, c) + 8 * (kq & 1);
       }
-      bf16x8 pf[kMNT];
-      float alpha[kMNT];
+
+  for (int ti = 0; ti < ntiles; ++ti) {
+    if (ti + 1 < ntiles) wait_vmcnt<kGroups>();
+    else wait_vmcnt<0>();
+    __syncthreads();  // tile ti is in LDS; stage (ti + 2) % 3 is no longer read
+    if (ti + 2 < ntiles) issue_tile(ti + 2, (ti + 2) % kStages);
+    const int t0 = t0k + ti * kMTK;
+    const char* stage = mla_smem + (ti % kStages) * kStageBytes;
+
+    // S^T (two accumulation chains: even / odd K-steps)
+    floatx16 sa, sb;
 #pragma unroll
-      for (int nt = 0; nt < kMNT; ++nt) {
-        float x[8];
+    for (int v = 0; v < 16; ++v) sa[v] = sb[v] = 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float v = j < 4 ? sacc[nt][0][j] : sacc[nt][1][j - 4];
-          x[j] = (t0 + 8 * g + j) < t1k ? v : kNegInf;
+    for (int ks = 0; ks < KS; ++ks) {
+      // chunk 2 ks + h lives in group (2 ks + h) >> 3 = ks >> 2
+      const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(
+          stage + koff[ks & 3] + (ks >> 2) * (kMTK * 8 * 16)));
+      const bf16x8 qv = ks < kQRegSteps
+                            ? qf[ks < kQRegSteps ? ks : 0]
+                            : as_bf16x8(*reinterpret_cast<const u32x4*>(
+                                  qlds + head * kQLdsStride + (16 * (ks - kQRegSteps) + 8 * h) * 2));
+      if (ks & 1) sb = mfma32_bf16(kf, qv, sb);
+      else sa = mfma32_bf16(kf, qv, sa);
+    }
+    // lane holds S[head][key] for keys 8h + v (v < 8) and 16 + 8h + (v - 8)
+    float x[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int key = t0 + (v < 8 ? 8 * h + v : 16 + 8 * h + (v - 8));
+      x[v] = key < t1k ? sa[v] + sb[v] : kNegInf;
+    }
+    float tmax = x[0];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) tmax = fmaxf(tmax, x[v]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const bool grow = (tmax - m) * sc > kLazyLog2;  // always true on the first tile
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float mnew = grow ? tmax : m;
+      const float alpha = grow ? fast_exp2((m - mnew) * sc) : 1.f;  // 0 while m = -inf
+      l *= alpha;
+      // acc lives in AGPRs; scale it there (read, multiply, write back) so
+      // that the allocator never has to hold it in vector registers.
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float x = acc[dt][v];
+          agpr_scale(x, alpha);
+          acc[dt][v] = x;
         }
-        float tmax = x[0];
+      asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");  // settle before the next MFMA reads acc
+      m = mnew;
+    }
+    const float msc = (m == kNegInf ? 0.f : m) * sc;
+    float p[16];
 #pragma unroll
-        for (int j = 1; j < 8; ++j) tmax = fmaxf(tmax, x[j]);
-        tmax = group_max4(tmax);
-        const float mnew = fmaxf(m[nt], tmax);
-        const float muse = mnew == kNegInf ? 0.f : mnew;
-        alpha[nt] = fast_exp2((m[nt] - muse) * sc);
-        const float msc = muse * sc;
-        float p[8], psum = 0.f;
+    for (int v = 0; v < 16; ++v) {
+      p[v] = fast_exp2(fmaf(x[v], sc, -msc));
+      l += p[v];
+    }
+    bf16x8 pf[2];  // B operand of O^T per 16-key step kk: keys 16 kk + 8h + i
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          p[j] = fast_exp2(fmaf(x[j], sc, -msc));
-          psum += p[j];
-        }
-        l[nt] = fmaf(l[nt], alpha[nt], psum);
-        m[nt] = mnew;
-        pf[nt] = __builtin_bit_cast(
-            bf16x8, u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                          pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])});
-      }
+    for (int kk = 0; kk < 2; ++kk)
+      pf[kk] = __builtin_bit_cast(
+          bf16x8, u32x4{pack_bf16x2(p[8 * kk + 0], p[8 * kk + 1]),
+                        pack_bf16x2(p[8 * kk + 2], p[8 * kk + 3]),
+                        pack_bf16x2(p[8 * kk + 4], p[8 * kk + 5]),
+                        pack_bf16x2(p[8 * kk + 6], p[8 * kk + 7])});
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const bf16x8 vf = as_bf16x8(load16(vt + (16 * dt + r) * kMVRow + 8 * g));
+    for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
-        for (int nt = 0; nt < kMNT; ++nt) {
-          acc[nt][dt] *= alpha[nt];
-          acc[nt][dt] = mfma_bf16(vf, pf[nt], acc[nt][dt]);
-        }
+      for (int kk = 0; kk < 2; ++kk) {
+        const int goff = (dt >> 1) * (kMTK * 8 * 16);  // chunk group of columns 32 dt ..
+        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_short4*)(stage + voff[kk][0][dt & 1] + goff));
+        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_short4*)(stage + voff[kk][1][dt & 1] + goff));
+        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
+        acc[dt] = mfma32_bf16(vf, pf[kk], acc[dt]);
       }
     }
-    if (ti + 1 < ntiles) {
-      gload(t0 + kMTK);
-      kstore(buf ^ 1);
-    }
-    __syncthreads();
-    if (ti + 1 < ntiles) transpose(buf ^ 1);
-    __syncthreads();
   }
 
-  // epilogue: lane holds O[head][16 dt + 4g + i]
+  // epilogue: lane holds O[head][32 dt + 8 (v / 4) + 4h + v % 4]
+  const float lrow = l + __shfl_xor(l, 32);
+  if (!row_ok) return;
+  const float inv = lrow > 0.f ? 1.f / lrow : 0.f;
+  const float lse = lrow > 0.f ? m * a.scale + __log2f(lrow) * kLn2 : kNegInf;
+  const int64_t bh = (int64_t)b * a.Hq + head;
+  if (S == 1) {
+    __bf16* op = (__bf16*)a.out + bh * kDv + 4 * h;
 #pragma unroll
-  for (int nt = 0; nt < kMNT; ++nt) {
-    const float lrow = group_sum4(l[nt]);
-    if (!row_ok[nt]) continue;
-    const float inv = lrow > 0.f ? 1.f / lrow : 0.f;
-    const float lse = lrow > 0.f ? m[nt] * a.scale + __log2f(lrow) * kLn2 : kNegInf;
-    const int64_t bh = (int64_t)b * a.Hq + head[nt];
-    if (S == 1) {
-      __bf16* op = (__bf16*)a.out + bh * kDv + 4 * g;
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<u32x2*>(op + 16 * dt) =
-            u32x2{pack_bf16x2(acc[nt][dt][0] * inv, acc[nt][dt][1] * inv),
-                  pack_bf16x2(acc[nt][dt][2] * inv, acc[nt][dt][3] * inv)};
-      if (g == 0 && a.lse) a.lse[bh] = lse;
-    } else {
-      float* op = a.part_o + (bh * S + s) * kDv + 4 * g;
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * q) =
+            u32x2{pack_bf16x2(acc[dt][4 * q] * inv, acc[dt][4 * q + 1] * inv),
+                  pack_bf16x2(acc[dt][4 * q + 2] * inv, acc[dt][4 * q + 3] * inv)};
+    if (h == 0 && a.lse) a.lse[bh] = lse;
+  } else {
+    float* op = a.part_o + (bh * S + s) * kDv + 4 * h;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        store16(op + 16 * dt, __builtin_bit_cast(u32x4, acc[nt][dt] * inv));
-      if (g == 0) a.part_lse[bh * S + s] = lse;
-    }
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        store16(op + 32 * dt + 8 * q,
+                __builtin_bit_cast(u32x4, floatx4{acc[dt][4 * q] * inv, acc[dt][4 * q + 1] * inv,
+                                                  acc[dt][4 * q + 2] * inv,
+                                                  acc[dt][4 * q + 3] * inv}));
+    if (h == 0) a.part_lse[bh * S + s] = lse;
   }
 }
 
@@ -224,7 +297,7 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
 hipError_t launch_mla_split(const MlaArgs& a, hipStream_t s) {
   const int64_t blocks = (int64_t)a.B * a.num_splits;
   if (blocks <= 0) return hipSuccess;
-  const size_t lds = sizeof(MlaLds);
+  const size_t lds = (size_t)kStages * kStageBytes + kQLdsBytes;
   hipError_t e = hipFuncSetAttribute((const void*)mla_split_kernel,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
