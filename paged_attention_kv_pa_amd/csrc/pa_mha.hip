@@ -56,14 +56,6 @@ struct alignas(16) LdsDecode {
   float o[4][16][kOStride];
 };
 
-template <int D>
-struct alignas(16) LdsPrefill {
-  static constexpr int kKRow = D + 8;    // bf16 per K row (16 B pad)
-  static constexpr int kVRow = kTK + 8;  // bf16 per V^T row (16 B pad)
-  __bf16 k[2][kTK * kKRow];
-  __bf16 v[2][D * kVRow];
-};
-
 // Write one finished row: o[] are this thread's `n` consecutive columns
 // starting at column c0, already divided by the row sum.
 template <int D, int N>
@@ -264,204 +256,256 @@ __device__ void run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest
 }
 
 // ---------------------------------------------------------------------------
-// Prefill mode: an item of up to 64 * NT rows; wave w owns rows
-// [16 NT w, 16 NT (w + 1)).  64-key tiles of K ([key][dim]) and V^T ([dim][key])
-// are staged in LDS, double buffered, and shared by the 4 waves.
+// Prefill mode: an item of up to 128 rows; wave w owns rows [32 w, 32 w + 32).
+// Both products run on v_mfma_f32_32x32x16_bf16, again transposed:
+//   * S^T = K Q^T per 32-key block: lane l (n = l % 32, h = l / 32) supplies
+//     K row kperm32(n) of the block, columns 16 ks + 8 h .. +7 (A operand) and
+//     Q row n, the same columns (B operand, kept in registers); element v of
+//     the result is the score of row n and key 16 (v / 8) + 8 h + v % 8;
+//   * O^T = V^T P^T per 16-key step: the lane's probabilities for keys
+//     16 kc + 8 h .. +7 are exactly its B operand, and V^T[32 dt + n][16 kc +
+//     8 h ..] its A operand, so P never leaves the lane.
+// 64-key tiles are copied HBM -> LDS by global_load_lds_dwordx4 into a
+// two-stage ring shared by the 4 waves.  LDS layouts (16-byte chunks):
+//   K   [key][chunk ^ swizzle(key)]  — one copy instruction moves whole keys,
+//       so its page is wave-uniform; the swizzle makes the 16 lanes of a
+//       read phase hit 16 distinct bank groups;
+//   V^T [key chunk][column]          — one copy instruction moves 64 columns
+//       of one 8-key chunk (one page); operand reads are consecutive.
+// The online softmax rescales the accumulator only when a row maximum grows by
+// more than 2^8 (exact either way: numerator and denominator share the stale
+// maximum).
 // ---------------------------------------------------------------------------
-template <int D, int NT>
+
+// Key held by M-row m (0..31) of the K operand of a 32-key block.
+__device__ __forceinline__ int kperm32(int m) {
+  const int q = m >> 3, h = (m >> 2) & 1, w = m & 3;
+  return 16 * (q >> 1) + 8 * h + 4 * (q & 1) + w;
+}
+
+template <int D>
+struct PrefillLayout {
+  static constexpr int kChunks = D / 8;                  // 16-byte chunks per key row
+  static constexpr int kKBytes = kTK * D * 2;            // K tile
+  static constexpr int kVBytes = kTK * D * 2;            // V^T tile
+  static constexpr int kStageBytes = kKBytes + kVBytes;
+  static constexpr int kKeysPerCopy = 1024 / (2 * D);    // keys per K copy instruction
+  static constexpr int kKCopies = 16 / kKeysPerCopy;     // per wave per tile (16 keys)
+  static constexpr int kVCopiesPerChunk = D / 64;        // per 8-key chunk
+  __device__ static __forceinline__ int kswz(int key) {
+    return kChunks == 16 ? (key & 15) : ((key >> 1) & 7);
+  }
+  // byte offset of logical chunk c of tile key k in the K tile
+  __device__ static __forceinline__ int koff(int k, int c) {
+    return (k * kChunks + (c ^ kswz(k))) * 16;
+  }
+  // byte offset of key chunk c (keys 8c .. 8c + 7), column d in the V^T tile
+  __device__ static __forceinline__ int voff(int c, int d) { return kKBytes + (c * D + d) * 16; }
+};
+
+template <int D>
+struct alignas(16) LdsPrefill {
+  char stage[2][PrefillLayout<D>::kStageBytes];
+};
+
+template <int D>
 __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Dest& dst,
                                  LdsPrefill<D>& sm) {
-  constexpr int KS = D / 32, DT = D / 16;
-  constexpr int KROW = LdsPrefill<D>::kKRow, VROW = LdsPrefill<D>::kVRow;
-  constexpr int KCH = kTK * D / 8 / kThreads;  // 16-byte K chunks per thread per tile
-  constexpr int VCH = D * kTK / 8 / kThreads;  // 16-byte V chunks per thread per tile
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
+  using LY = PrefillLayout<D>;
+  constexpr int KS = D / 16, DT = D / 32;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 31, h = lane >> 5;
   const int b = it.seq, kvh = it.kvh, G = a.G, P = a.P;
   const int kv_begin = it.kv_begin, kv_end = it.kv_end;
 
-  // rows of this lane, one per row tile
-  int lim[NT];
-  int64_t out_row[NT];
-  bool row_ok[NT];
-  bf16x8 qf[NT][KS];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int row = 16 * (NT * wave + nt) + r;
-    row_ok[nt] = row < it.nrows;
+  // this lane's row
+  const int row = 32 * wave + n;
+  const bool row_ok = row < it.nrows;
+  int64_t out_row;
+  int lim;
+  bf16x8 qf[KS];  // B operand of S^T: Q[row][16 ks + 8 h .. +7]
+  {
     const int rid = it.row0 + row;
     const int t = rid / G;
     const int head = kvh * G + (rid - t * G);
-    out_row[nt] = (int64_t)(it.q0 + t) * a.Hq + head;
-    lim[nt] = row_ok[nt] ? min(it.ctx + t + 1, kv_end) : kv_begin;
-    const __bf16* qp = (const __bf16*)a.q + out_row[nt] * D + 8 * g;
+    out_row = (int64_t)(it.q0 + t) * a.Hq + head;
+    lim = row_ok ? min(it.ctx + t + 1, kv_end) : kv_begin;
+    const __bf16* qp = (const __bf16*)a.q + out_row * D + 8 * h;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      qf[nt][ks] = row_ok[nt] ? as_bf16x8(load16(qp + 32 * ks)) : as_bf16x8(u32x4{0, 0, 0, 0});
+      qf[ks] = row_ok ? as_bf16x8(load16(qp + 16 * ks)) : as_bf16x8(u32x4{0, 0, 0, 0});
   }
-  // largest key limit of the wave's rows (wave-uniform)
-  int wave_lim = kv_begin;
+  // key limits of the wave's valid rows (rows ascend with the token, so the
+  // first row has the smallest limit and the last the largest)
+  int wave_lim = kv_begin, wave_min = kv_begin;
   {
-    const int last_row = min(16 * NT * (wave + 1), it.nrows) - 1;
-    if (last_row >= 16 * NT * wave) {
-      const int t = (it.row0 + last_row) / G;
-      wave_lim = min(it.ctx + t + 1, kv_end);
+    const int first = 32 * wave, last = min(32 * wave + 32, it.nrows) - 1;
+    if (last >= first) {
+      wave_min = min(it.ctx + (it.row0 + first) / G + 1, kv_end);
+      wave_lim = min(it.ctx + (it.row0 + last) / G + 1, kv_end);
     }
   }
-
-  const float sc = a.scale * kLog2e;
-  float m[NT], l[NT];
-  floatx4 acc[NT][DT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    m[nt] = kNegInf;
-    l[nt] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc[nt][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  }
+  wait_vmcnt<0>();  // q is in registers before the copies start counting
 
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
   const int64_t page_elems = (int64_t)a.Hkv * P * D;
-  const __bf16* kbase = (const __bf16*)a.k_cache + (int64_t)kvh * P * D;
-  const __bf16* vbase = (const __bf16*)a.v_cache + (int64_t)kvh * D * P;
-  const int last8 = (kv_end - 1) & ~7;
+  const char* kbase = (const char*)((const __bf16*)a.k_cache + (int64_t)kvh * P * D);
+  const char* vbase = (const char*)((const __bf16*)a.v_cache + (int64_t)kvh * D * P);
 
-  u32x4 kreg[KCH], vreg[VCH];
-  auto gload = [&](int t0) {
+  // Copy of tile t0 into stage st.  Wave w moves keys [16 w, 16 w + 16) of the
+  // tile: its two 8-key groups (one page each) for both K and V^T.  Keys at or
+  // past kv_end are clamped to kv_end - 1 (real data; masked or zeroed later).
+  auto issue_tile = [&](int t0, int st) {
+    char* stage = sm.stage[st];
+    int pg[2], g0c[2];
 #pragma unroll
-    for (int j = 0; j < KCH; ++j) {
-      const int c = j * kThreads + tid;
-      const int key = min(t0 + c / (D / 8), kv_end - 1);
-      const int page = bt[key / P];
-      kreg[j] = load16(kbase + (int64_t)page * page_elems + (key % P) * D + (c % (D / 8)) * 8);
+    for (int u = 0; u < 2; ++u) {
+      const int gs = __builtin_amdgcn_readfirstlane(min(t0 + 16 * wave + 8 * u, kv_end - 1));
+      const int pidx = gs / P;
+      pg[u] = bt[pidx];
+      g0c[u] = pidx * P;  // first key of that page
     }
+    // K: copy j moves keys 16 w + kKeysPerCopy j + lane / kChunks
 #pragma unroll
-    for (int j = 0; j < VCH; ++j) {
-      const int c = j * kThreads + tid;
-      const int dim = c / (kTK / 8);
-      const int key8 = t0 + 8 * (c % (kTK / 8));
-      const int kk = min(key8, last8);
-      const int page = bt[kk / P];
-      u32x4 raw = load16(vbase + (int64_t)page * page_elems + (int64_t)dim * P + (kk % P));
-      vreg[j] = zero_tail8(raw, key8, kv_end);
+    for (int j = 0; j < LY::kKCopies; ++j) {
+      const int u = (j * LY::kKeysPerCopy) >> 3;
+      const int kl = 16 * wave + LY::kKeysPerCopy * j + lane / LY::kChunks;
+      const int c = (lane % LY::kChunks) ^ LY::kswz(kl);
+      const int key = min(t0 + kl, kv_end - 1);
+      const char* src = kbase + ((int64_t)pg[u] * page_elems + (int64_t)(key - g0c[u]) * D + 8 * c) * 2;
+      lds_dma16(src, stage + (16 * wave + LY::kKeysPerCopy * j) * D * 2);
+    }
+    // V^T: chunk 2 w + u, columns 64 i + lane
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int cs = min(t0 + 16 * wave + 8 * u, (kv_end - 1) & ~7);
+      const int slot = cs - g0c[u];
+#pragma unroll
+      for (int i = 0; i < LY::kVCopiesPerChunk; ++i) {
+        const int d = 64 * i + lane;
+        const char* src = vbase + ((int64_t)pg[u] * page_elems + (int64_t)d * P + slot) * 2;
+        lds_dma16(src, stage + LY::voff(2 * wave + u, 64 * i));
+      }
     }
   };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < KCH; ++j) {
-      const int c = j * kThreads + tid;
-      store16(&sm.k[buf][(c / (D / 8)) * KROW + (c % (D / 8)) * 8], kreg[j]);
-    }
-#pragma unroll
-    for (int j = 0; j < VCH; ++j) {
-      const int c = j * kThreads + tid;
-      store16(&sm.v[buf][(c / (kTK / 8)) * VROW + (c % (kTK / 8)) * 8], vreg[j]);
-    }
-  };
 
+  const float sc = a.scale * kLog2e;
+  float m = kNegInf, l = 0.f;  // m in scaled base-2 units
+  floatx16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[dt][v] = 0.f;
+
+  const int krow = kperm32(n);
   const int ntiles = (kv_end - kv_begin + kTK - 1) / kTK;
-  if (ntiles > 0) {
-    gload(kv_begin);
-    lstore(0);
-  }
-  __syncthreads();
+  if (ntiles > 0) issue_tile(kv_begin, 0);
   for (int ti = 0; ti < ntiles; ++ti) {
     const int t0 = kv_begin + ti * kTK;
-    const int buf = ti & 1;
-    if (ti + 1 < ntiles) gload(t0 + kTK);
-    if (t0 < wave_lim) {
-      const __bf16* kt = sm.k[buf];
-      const __bf16* vt = sm.v[buf];
-      floatx4 s[NT][2][2];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt) s[nt][kh][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 kf =
-                as_bf16x8(load16(kt + (32 * kh + kperm(mt, r)) * KROW + 32 * ks + 8 * g));
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) s[nt][kh][mt] = mfma_bf16(kf, qf[nt][ks], s[nt][kh][mt]);
-          }
-      bf16x8 pf[NT][2];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        float x[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int kh = j >> 3, jj = j & 7;
-          const int key = t0 + 32 * kh + 8 * g + jj;
-          const float v = s[nt][kh][jj >> 2][jj & 3];
-          x[j] = key < lim[nt] ? v : kNegInf;
+    char* stage = sm.stage[ti & 1];
+    wait_vmcnt<0>();
+    __syncthreads();  // tile ti is in LDS; the other stage is no longer read
+    if (t0 + kTK > kv_end) {
+      // last tile: zero the values of keys >= kv_end (their slots may hold
+      // anything, and 0 * NaN would reach the output)
+      for (int e = tid; e < 8 * D; e += kThreads) {
+        const int c = e / D, d = e - c * D;
+        const int k0 = t0 + 8 * c;
+        if (k0 + 8 > kv_end) {
+          u32x4* p = reinterpret_cast<u32x4*>(stage + LY::voff(c, d));
+          *p = zero_tail8(*p, k0, kv_end);
         }
-        float tmax = x[0];
-#pragma unroll
-        for (int j = 1; j < 16; ++j) tmax = fmaxf(tmax, x[j]);
-        tmax = group_max4(tmax);
-        const float mnew = fmaxf(m[nt], tmax);
-        const float muse = mnew == kNegInf ? 0.f : mnew;
-        const float alpha = fast_exp2((m[nt] - muse) * sc);
-        const float msc = muse * sc;
-        float p[16], psum = 0.f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          p[j] = fast_exp2(fmaf(x[j], sc, -msc));
-          psum += p[j];
-        }
-        l[nt] = fmaf(l[nt], alpha, psum);
-        m[nt] = mnew;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) acc[nt][dt] *= alpha;
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
-          pf[nt][kh] = __builtin_bit_cast(
-              bf16x8, u32x4{pack_bf16x2(p[8 * kh + 0], p[8 * kh + 1]),
-                            pack_bf16x2(p[8 * kh + 2], p[8 * kh + 3]),
-                            pack_bf16x2(p[8 * kh + 4], p[8 * kh + 5]),
-                            pack_bf16x2(p[8 * kh + 6], p[8 * kh + 7])});
       }
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const bf16x8 vf = as_bf16x8(load16(vt + (16 * dt + r) * VROW + 32 * kh + 8 * g));
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) acc[nt][dt] = mfma_bf16(vf, pf[nt][kh], acc[nt][dt]);
-        }
+      __syncthreads();
     }
-    if (ti + 1 < ntiles) lstore(buf ^ 1);
-    __syncthreads();
-  }
+    if (ti + 1 < ntiles) issue_tile(t0 + kTK, (ti + 1) & 1);
+    if (t0 >= wave_lim) continue;
 
-  // epilogue: lane holds O[row][16 dt + 4g + i]
+    // S^T for the two 32-key blocks (two accumulation chains)
+    floatx16 s[2];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const float lrow = group_sum4(l[nt]);
-    if (!row_ok[nt]) continue;
-    const float inv = lrow > 0.f ? 1.f / lrow : 0.f;
-    const int row = 16 * (NT * wave + nt) + r;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const float o[4] = {acc[nt][dt][0] * inv, acc[nt][dt][1] * inv, acc[nt][dt][2] * inv,
-                          acc[nt][dt][3] * inv};
-      if (dst.partial) {
-        float* p = a.part_o + dst.po_base + (int64_t)row * dst.po_row + 16 * dt + 4 * g;
-        store16(p, __builtin_bit_cast(u32x4, floatx4{o[0], o[1], o[2], o[3]}));
-      } else {
-        __bf16* p = (__bf16*)a.out + out_row[nt] * D + 16 * dt + 4 * g;
-        *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+      for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(
+            stage + LY::koff(32 * kb + krow, 2 * ks + h)));
+        s[kb] = mfma32_bf16(kf, qf[ks], s[kb]);
+      }
+
+    // masks (only tiles that reach past the wave's smallest limit need them)
+    float x[32];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) x[16 * kb + v] = s[kb][v] * sc;
+    if (t0 + kTK > wave_min) {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const int key = t0 + 32 * (j >> 4) + 16 * ((j >> 3) & 1) + 8 * h + (j & 7);
+        if (key >= lim) x[j] = kNegInf;
       }
     }
-    if (g == 0)
-      store_lse(a, dst, row, out_row[nt],
-                lrow > 0.f ? m[nt] * a.scale + __log2f(lrow) * kLn2 : kNegInf);
+    float tmax = x[0];
+#pragma unroll
+    for (int j = 1; j < 32; ++j) tmax = fmaxf(tmax, x[j]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    // lazy rescale: move the reference maximum only when it grew by > 2^8
+    const bool grow = tmax > m + 8.f;
+    if (__any(grow)) {
+      const float mnew = grow ? tmax : m;
+      const float alpha = grow ? fast_exp2(m - mnew) : 1.f;  // m = -inf gives 0
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[dt][v] *= alpha;
+      m = mnew;
+    }
+    const float muse = m == kNegInf ? 0.f : m;
+    float p[32];
+    float psum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      p[j] = fast_exp2(x[j] - muse);
+      psum += p[j];
+    }
+    l += psum;
+
+    // O^T += V^T P^T, four 16-key steps
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const bf16x8 pf = __builtin_bit_cast(
+          bf16x8, u32x4{pack_bf16x2(p[8 * kc + 0], p[8 * kc + 1]),
+                        pack_bf16x2(p[8 * kc + 2], p[8 * kc + 3]),
+                        pack_bf16x2(p[8 * kc + 4], p[8 * kc + 5]),
+                        pack_bf16x2(p[8 * kc + 6], p[8 * kc + 7])});
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8 vf = as_bf16x8(
+            *reinterpret_cast<const u32x4*>(stage + LY::voff(2 * kc + h, 32 * dt + n)));
+        acc[dt] = mfma32_bf16(vf, pf, acc[dt]);
+      }
+    }
   }
+  __syncthreads();  // every wave is done with the ring before the next item
+
+  // epilogue: element v of acc[dt] is O[row][32 dt + 8 (v / 4) + 4 h + v % 4]
+  const float lrow = l + __shfl_xor(l, 32);
+  if (!row_ok) return;
+  const float inv = lrow > 0.f ? 1.f / lrow : 0.f;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float o[4] = {acc[dt][4 * q] * inv, acc[dt][4 * q + 1] * inv,
+                          acc[dt][4 * q + 2] * inv, acc[dt][4 * q + 3] * inv};
+      store_row_chunk<D, 4>(a, dst, row, out_row, 32 * dt + 8 * q + 4 * h, o);
+    }
+  if (h == 0)
+    store_lse(a, dst, row, out_row, lrow > 0.f ? (m + __log2f(lrow)) * kLn2 : kNegInf);
 }
 
 template <int D, bool DECODE_ONLY>
@@ -535,42 +579,48 @@ __device__ WorkItem make_item(const MhaArgs& a, int idx, int n_pre) {
 
 // Persistent forward kernel: a fixed grid; each workgroup takes the next item
 // index from a device counter until the planner's item count is reached.
+// Prefill-mode items (indices below n_pre) are handed out first, so a
+// workgroup runs one loop over them and then one over decode-mode items; the
+// two loops keep the register allocation of the two item kinds apart.
 template <int D, bool DECODE_ONLY>
-__global__ __launch_bounds__(kThreads, DECODE_ONLY ? 2 : 1) void mha_forward_kernel(MhaArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void mha_forward_kernel(MhaArgs a) {
   __shared__ typename FwdLds<D, DECODE_ONLY>::type sm;
   __shared__ WorkItem s_item;
   __shared__ int s_idx;
   const int n_items = a.ctrl->n_items;
   const int n_pre = a.ctrl->n_pre;
-  for (;;) {
+  int idx;
+  WorkItem it;
+  auto next = [&]() {
     if (threadIdx.x == 0) {
-      const int idx = atomicAdd(&a.ctrl->work_counter, 1);
-      s_idx = idx;
-      if (idx < n_items) s_item = make_item(a, idx, n_pre);
+      const int i = atomicAdd(&a.ctrl->work_counter, 1);
+      s_idx = i;
+      if (i < n_items) s_item = make_item(a, i, n_pre);
     }
     __syncthreads();
-    const int idx = s_idx;
-    const WorkItem it = s_item;
+    idx = s_idx;
+    it = s_item;
     __syncthreads();
-    if (idx >= n_items) break;
+  };
+  auto dest = [&]() {
     Dest dst;
     dst.partial = it.part >= 0;
     dst.po_base = (int64_t)it.part * kDecodeRows * D;
     dst.po_row = D;
     dst.pl_base = (int64_t)it.part * kDecodeRows;
     dst.pl_row = 1;
-    if constexpr (DECODE_ONLY) {
-      run_decode_item<D>(a, it, dst, sm);
-    } else {
-      if (it.nrows <= kDecodeRows) run_decode_item<D>(a, it, dst, sm.dec);
-      else run_prefill_item<D, kPrefillRowTiles>(a, it, dst, sm.pre);
-    }
+    return dst;
+  };
+  next();
+  if constexpr (!DECODE_ONLY) {
+    for (; idx < n_pre && idx < n_items; next()) run_prefill_item<D>(a, it, dest(), sm.pre);
   }
+  for (; idx < n_items; next()) run_decode_item<D>(a, it, dest(), dec_lds<D, DECODE_ONLY>(sm));
 }
 
 // pa_decode_split: one workgroup per (request, KV head, partition).
 template <int D, bool DEC>
-__global__ __launch_bounds__(kThreads, DEC ? 2 : 1) void mha_split_kernel(MhaArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void mha_split_kernel(MhaArgs a) {
   __shared__ typename std::conditional<DEC, LdsDecode<D>, LdsPrefill<D>>::type sm;
   const int S = a.num_splits;
   const int s = blockIdx.x % S;
@@ -606,7 +656,7 @@ __global__ __launch_bounds__(kThreads, DEC ? 2 : 1) void mha_split_kernel(MhaArg
   it.ctx = L - 1;
   it.pad[0] = it.pad[1] = it.pad[2] = 0;
   if constexpr (DEC) run_decode_item<D>(a, it, dst, sm);
-  else run_prefill_item<D, kPrefillRowTiles>(a, it, dst, sm);
+  else run_prefill_item<D>(a, it, dst, sm);
 }
 
 // Planner: one workgroup of 1024 threads turns (seq_lens, query_start_loc)
