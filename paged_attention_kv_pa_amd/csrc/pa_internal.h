@@ -11,10 +11,11 @@
 namespace pa {
 
 // Tunables shared by the planner, the workspace sizing and the kernels.
-constexpr int kThreads = 256;          // threads of an MHA workgroup (4 waves)
+constexpr int kThreads = 256;          // threads of a decode-only MHA workgroup (4 waves)
+constexpr int kPrefillWaves = 8;       // waves of a workgroup that runs prefill-mode items
+constexpr int kPrefillThreads = 64 * kPrefillWaves;
 constexpr int kDecodeRows = 16;        // rows of one decode-mode item (one MFMA tile)
-constexpr int kPrefillRowTiles = 2;    // 16-row tiles per wave in prefill mode
-constexpr int kPrefillRows = 4 * 16 * kPrefillRowTiles;  // rows of a prefill-mode item
+constexpr int kPrefillRows = 32 * kPrefillWaves;  // rows of a prefill-mode item (32 per wave)
 constexpr int kMaxFwdSplits = 64;      // key partitions per decode row in pa_forward
 constexpr int kMinChunk = 256;         // smallest key partition pa_forward makes
 constexpr int kItemsPerWorkgroup = 4;  // decode work is cut into ~this many items per workgroup

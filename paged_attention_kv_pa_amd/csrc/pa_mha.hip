@@ -48,12 +48,12 @@ struct Dest {
   int64_t pl_base, pl_row;
 };
 
-template <int D>
+template <int D, int NW>
 struct alignas(16) LdsDecode {
   static constexpr int kOStride = D + 4;  // floats per row of the merge buffer
-  float m[4][16];
-  float l[4][16];
-  float o[4][16][kOStride];
+  float m[NW][16];
+  float l[NW][16];
+  float o[NW][16][kOStride];
 };
 
 // Write one finished row: o[] are this thread's `n` consecutive columns
@@ -61,17 +61,25 @@ struct alignas(16) LdsDecode {
 template <int D, int N>
 __device__ __forceinline__ void store_row_chunk(const MhaArgs& a, const Dest& dst, int row,
                                                 int64_t out_row, int c0, const float* o) {
+  static_assert(N == 2 || N == 4 || N == 8, "columns per store");
   if (dst.partial) {
     float* p = a.part_o + dst.po_base + (int64_t)row * dst.po_row + c0;
+    if constexpr (N == 2) {
+      *reinterpret_cast<u32x2*>(p) = u32x2{__float_as_uint(o[0]), __float_as_uint(o[1])};
+    } else {
 #pragma unroll
-    for (int e = 0; e < N; e += 4) store16(p + e, __builtin_bit_cast(u32x4, floatx4{o[e], o[e + 1], o[e + 2], o[e + 3]}));
+      for (int e = 0; e < N; e += 4)
+        store16(p + e, __builtin_bit_cast(u32x4, floatx4{o[e], o[e + 1], o[e + 2], o[e + 3]}));
+    }
   } else {
     __bf16* p = (__bf16*)a.out + out_row * D + c0;
     if constexpr (N == 8) {
       store16(p, u32x4{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
                        pack_bf16x2(o[6], o[7])});
-    } else {
+    } else if constexpr (N == 4) {
       *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    } else {
+      *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(o[0], o[1]);
     }
   }
 }
@@ -91,9 +99,9 @@ __device__ __forceinline__ void store_lse(const MhaArgs& a, const Dest& dst, int
 // operands (no LDS staging: nothing is shared between waves), then merge their
 // partial softmax states through LDS.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int NW>
 __device__ void run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest& dst,
-                                LdsDecode<D>& sm) {
+                                LdsDecode<D, NW>& sm) {
   constexpr int KS = D / 32, DT = D / 16;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
   const int b = it.seq, kvh = it.kvh, G = a.G, P = a.P;
@@ -196,7 +204,7 @@ __device__ void run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest
   };
 
   {
-    constexpr int kStride = 128;  // 4 waves x 32 keys
+    constexpr int kStride = 32 * NW;  // NW waves x 32 keys
     int t0 = it.kv_begin + 32 * wave;
     Step sa, sb;
     if (t0 < kv_end) load_step(t0, sa);
@@ -211,7 +219,7 @@ __device__ void run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest
     }
   }
 
-  // merge the 4 waves' states
+  // merge the NW waves' states
   const float lrow = group_sum4(l);
   if (g == 0) {
     sm.m[wave][r] = m;
@@ -222,18 +230,19 @@ __device__ void run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest
     store16(&sm.o[wave][r][16 * dt + 4 * g], __builtin_bit_cast(u32x4, acc[dt]));
   __syncthreads();
   {
-    constexpr int NC = D / 16;  // columns per thread
-    const int row = tid >> 4, c0 = (tid & 15) * NC;
+    constexpr int TPR = 4 * NW;   // threads per row
+    constexpr int NC = D / TPR;   // columns per thread
+    const int row = tid / TPR, c0 = (tid % TPR) * NC;
     float M = kNegInf;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm.m[w][row]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.m[w][row]);
     float o[NC];
 #pragma unroll
     for (int e = 0; e < NC; ++e) o[e] = 0.f;
     float wsum = 0.f;
     if (M != kNegInf) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      for (int w = 0; w < NW; ++w) {
         const float f = fast_exp2((sm.m[w][row] - M) * sc);
         wsum = fmaf(f, sm.l[w][row], wsum);
 #pragma unroll
@@ -248,7 +257,7 @@ __device__ void run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest
       const int t = rid / G;
       const int64_t out_row = (int64_t)(it.q0 + t) * a.Hq + kvh * G + (rid - t * G);
       store_row_chunk<D, NC>(a, dst, row, out_row, c0, o);
-      if ((tid & 15) == 0)
+      if (tid % TPR == 0)
         store_lse(a, dst, row, out_row, wsum > 0.f ? M * a.scale + __log2f(wsum) * kLn2 : kNegInf);
     }
   }
@@ -256,7 +265,8 @@ __device__ void run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest
 }
 
 // ---------------------------------------------------------------------------
-// Prefill mode: an item of up to 128 rows; wave w owns rows [32 w, 32 w + 32).
+// Prefill mode: an item of up to 256 rows; wave w (of 8) owns rows
+// [32 w, 32 w + 32), two waves per SIMD.
 // Both products run on v_mfma_f32_32x32x16_bf16, again transposed:
 //   * S^T = K Q^T per 32-key block: lane l (n = l % 32, h = l / 32) supplies
 //     K row kperm32(n) of the block, columns 16 ks + 8 h .. +7 (A operand) and
@@ -266,10 +276,11 @@ __device__ void run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest
 //     16 kc + 8 h .. +7 are exactly its B operand, and V^T[32 dt + n][16 kc +
 //     8 h ..] its A operand, so P never leaves the lane.
 // 64-key tiles are copied HBM -> LDS by global_load_lds_dwordx4 into a
-// two-stage ring shared by the 4 waves.  LDS layouts (16-byte chunks):
-//   K   [key][chunk ^ swizzle(key)]  — one copy instruction moves whole keys,
-//       so its page is wave-uniform; the swizzle makes the 16 lanes of a
-//       read phase hit 16 distinct bank groups;
+// three-stage ring shared by the 8 waves: one 64-key tile feeds 256 rows, so
+// the L2 -> LDS traffic is 32 KiB per 8.4 MFLOP.  LDS layouts (16-byte chunks):
+//   K   [16-key group][column chunk][key % 16] — one copy instruction moves
+//       4 column chunks of 16 keys; the 16 lanes of a read phase read 16
+//       consecutive chunks, and a lane's K-steps sit at fixed offsets;
 //   V^T [key chunk][column]          — one copy instruction moves 64 columns
 //       of one 8-key chunk (one page); operand reads are consecutive.
 // The online softmax rescales the accumulator only when a row maximum grows by
@@ -283,21 +294,34 @@ __device__ __forceinline__ int kperm32(int m) {
   return 16 * (q >> 1) + 8 * h + 4 * (q & 1) + w;
 }
 
+// Scheduling hint for a block of N LDS operand reads each feeding one MFMA:
+// keep 4 reads in flight ahead of the matrix instructions instead of waiting
+// for each operand right before its use.
+template <int N>
+__device__ __forceinline__ void pipeline_reads_and_mfma() {
+  constexpr int kAhead = N < 4 ? N : 4;
+  __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);  // LDS reads
+#pragma unroll
+  for (int i = 0; i < N - kAhead; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
+}
+
 template <int D>
 struct PrefillLayout {
+  static constexpr int kStages = 3;
   static constexpr int kChunks = D / 8;                  // 16-byte chunks per key row
   static constexpr int kKBytes = kTK * D * 2;            // K tile
   static constexpr int kVBytes = kTK * D * 2;            // V^T tile
   static constexpr int kStageBytes = kKBytes + kVBytes;
-  static constexpr int kKeysPerCopy = 1024 / (2 * D);    // keys per K copy instruction
-  static constexpr int kKCopies = 16 / kKeysPerCopy;     // per wave per tile (16 keys)
-  static constexpr int kVCopiesPerChunk = D / 64;        // per 8-key chunk
-  __device__ static __forceinline__ int kswz(int key) {
-    return kChunks == 16 ? (key & 15) : ((key >> 1) & 7);
-  }
-  // byte offset of logical chunk c of tile key k in the K tile
+  static constexpr int kKCopies = kChunks / 8;           // K copies per wave per tile
+  static constexpr int kVCopies = D / 64;                // V copies per wave per tile
+  static constexpr int kCopies = kKCopies + kVCopies;    // copy instructions per thread per tile
+  // byte offset of column chunk c of tile key k in the K tile
   __device__ static __forceinline__ int koff(int k, int c) {
-    return (k * kChunks + (c ^ kswz(k))) * 16;
+    return (((k >> 4) * kChunks + c) * 16 + (k & 15)) * 16;
   }
   // byte offset of key chunk c (keys 8c .. 8c + 7), column d in the V^T tile
   __device__ static __forceinline__ int voff(int c, int d) { return kKBytes + (c * D + d) * 16; }
@@ -305,30 +329,39 @@ struct PrefillLayout {
 
 template <int D>
 struct alignas(16) LdsPrefill {
-  char stage[2][PrefillLayout<D>::kStageBytes];
+  char stage[PrefillLayout<D>::kStages][PrefillLayout<D>::kStageBytes];
 };
 
 template <int D>
 __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Dest& dst,
                                  LdsPrefill<D>& sm) {
   using LY = PrefillLayout<D>;
-  constexpr int KS = D / 16, DT = D / 32;
+  constexpr int KS = D / 16, DT = D / 32, NST = LY::kStages;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 31, h = lane >> 5;
-  const int b = it.seq, kvh = it.kvh, G = a.G, P = a.P;
-  const int kv_begin = it.kv_begin, kv_end = it.kv_end;
+  const int G = a.G, P = a.P;
+  // item fields are workgroup-uniform: keep them in scalar registers so that
+  // block-table reads become scalar loads
+  const int b = __builtin_amdgcn_readfirstlane(it.seq);
+  const int kvh = __builtin_amdgcn_readfirstlane(it.kvh);
+  const int kv_begin = __builtin_amdgcn_readfirstlane(it.kv_begin);
+  const int kv_end = __builtin_amdgcn_readfirstlane(it.kv_end);
+  const int nrows = __builtin_amdgcn_readfirstlane(it.nrows);
+  const int row0 = __builtin_amdgcn_readfirstlane(it.row0);
+  const int ctx = __builtin_amdgcn_readfirstlane(it.ctx);
+  const int q0 = __builtin_amdgcn_readfirstlane(it.q0);
 
   // this lane's row
   const int row = 32 * wave + n;
-  const bool row_ok = row < it.nrows;
+  const bool row_ok = row < nrows;
   int64_t out_row;
   int lim;
   bf16x8 qf[KS];  // B operand of S^T: Q[row][16 ks + 8 h .. +7]
   {
-    const int rid = it.row0 + row;
+    const int rid = row0 + row;
     const int t = rid / G;
     const int head = kvh * G + (rid - t * G);
-    out_row = (int64_t)(it.q0 + t) * a.Hq + head;
-    lim = row_ok ? min(it.ctx + t + 1, kv_end) : kv_begin;
+    out_row = (int64_t)(q0 + t) * a.Hq + head;
+    lim = row_ok ? min(ctx + t + 1, kv_end) : kv_begin;
     const __bf16* qp = (const __bf16*)a.q + out_row * D + 8 * h;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -338,52 +371,73 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
   // first row has the smallest limit and the last the largest)
   int wave_lim = kv_begin, wave_min = kv_begin;
   {
-    const int first = 32 * wave, last = min(32 * wave + 32, it.nrows) - 1;
+    const int first = 32 * wave, last = min(32 * wave + 32, nrows) - 1;
     if (last >= first) {
-      wave_min = min(it.ctx + (it.row0 + first) / G + 1, kv_end);
-      wave_lim = min(it.ctx + (it.row0 + last) / G + 1, kv_end);
+      wave_min = min(ctx + (row0 + first) / G + 1, kv_end);
+      wave_lim = min(ctx + (row0 + last) / G + 1, kv_end);
     }
   }
-  wait_vmcnt<0>();  // q is in registers before the copies start counting
+  // q must be in registers before the copies start counting; tying the
+  // fragments to an empty asm makes the compiler wait for them here and not
+  // at their first use inside the key loop (where the wait would also drain
+  // the copies in flight)
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qf[ks]));
+  wait_vmcnt<0>();
 
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
   const int64_t page_elems = (int64_t)a.Hkv * P * D;
   const char* kbase = (const char*)((const __bf16*)a.k_cache + (int64_t)kvh * P * D);
   const char* vbase = (const char*)((const __bf16*)a.v_cache + (int64_t)kvh * D * P);
 
-  // Copy of tile t0 into stage st.  Wave w moves keys [16 w, 16 w + 16) of the
-  // tile: its two 8-key groups (one page each) for both K and V^T.  Keys at or
-  // past kv_end are clamped to kv_end - 1 (real data; masked or zeroed later).
-  auto issue_tile = [&](int t0, int st) {
+  // Wave w copies, of each 64-key tile, half of the column chunks of K (the
+  // half w & 1) for the 16 keys of group w / 2, and V^T of the 8-key chunk w.  Its
+  // keys lie in the two 8-key groups of key group w / 2, one page each; keys
+  // at or past kv_end are clamped to kv_end - 1 (real data, masked or zeroed
+  // later).  The block table is read-only for the whole call: reading it
+  // through the constant address space lets these uniform reads become
+  // scalar loads.
+  typedef const __attribute__((address_space(4))) int32_t* ConstI32Ptr;
+  const ConstI32Ptr cbt = (ConstI32Ptr)bt;
+  const int kgroup = wave >> 1;
+  struct TilePages {
+    int pg[2], first[2];  // physical page, first key of that page
+  };
+  auto load_pages = [&](int t0) {
+    TilePages tp;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int gs = min(t0 + 16 * kgroup + 8 * u, kv_end - 1);
+      const int pidx = __builtin_amdgcn_readfirstlane(gs / P);
+      tp.pg[u] = cbt[pidx];
+      tp.first[u] = pidx * P;
+    }
+    return tp;
+  };
+  auto issue_tile = [&](int t0, int st, const TilePages& tp) {
     char* stage = sm.stage[st];
-    int pg[2], g0c[2];
+    {
+      const int k16 = lane & 15;
+      const int u = k16 >> 3;
+      const int key = min(t0 + 16 * kgroup + k16, kv_end - 1);
+      const int pg = u ? tp.pg[1] : tp.pg[0];
+      const int first = u ? tp.first[1] : tp.first[0];
+      const int c0 = (wave & 1) * (LY::kChunks / 2);  // first column chunk of this wave
+      const char* src = kbase + ((int64_t)pg * page_elems + (int64_t)(key - first) * D +
+                                 8 * (c0 + (lane >> 4))) * 2;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int gs = __builtin_amdgcn_readfirstlane(min(t0 + 16 * wave + 8 * u, kv_end - 1));
-      const int pidx = gs / P;
-      pg[u] = bt[pidx];
-      g0c[u] = pidx * P;  // first key of that page
+      for (int j = 0; j < LY::kKCopies; ++j)
+        lds_dma16(src + 64 * j, stage + LY::koff(16 * kgroup, c0 + 4 * j));
     }
-    // K: copy j moves keys 16 w + kKeysPerCopy j + lane / kChunks
+    {
+      const int u = wave & 1;
+      const int cs = min(t0 + 8 * wave, (kv_end - 1) & ~7);
+      const int slot = cs - tp.first[u];
 #pragma unroll
-    for (int j = 0; j < LY::kKCopies; ++j) {
-      const int u = (j * LY::kKeysPerCopy) >> 3;
-      const int kl = 16 * wave + LY::kKeysPerCopy * j + lane / LY::kChunks;
-      const int c = (lane % LY::kChunks) ^ LY::kswz(kl);
-      const int key = min(t0 + kl, kv_end - 1);
-      const char* src = kbase + ((int64_t)pg[u] * page_elems + (int64_t)(key - g0c[u]) * D + 8 * c) * 2;
-      lds_dma16(src, stage + (16 * wave + LY::kKeysPerCopy * j) * D * 2);
-    }
-    // V^T: chunk 2 w + u, columns 64 i + lane
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int cs = min(t0 + 16 * wave + 8 * u, (kv_end - 1) & ~7);
-      const int slot = cs - g0c[u];
-#pragma unroll
-      for (int i = 0; i < LY::kVCopiesPerChunk; ++i) {
+      for (int i = 0; i < LY::kVCopies; ++i) {
         const int d = 64 * i + lane;
-        const char* src = vbase + ((int64_t)pg[u] * page_elems + (int64_t)d * P + slot) * 2;
-        lds_dma16(src, stage + LY::voff(2 * wave + u, 64 * i));
+        const char* src = vbase + ((int64_t)tp.pg[u] * page_elems + (int64_t)d * P + slot) * 2;
+        lds_dma16(src, stage + LY::voff(wave, 64 * i));
       }
     }
   };
@@ -398,16 +452,20 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
 
   const int krow = kperm32(n);
   const int ntiles = (kv_end - kv_begin + kTK - 1) / kTK;
-  if (ntiles > 0) issue_tile(kv_begin, 0);
+  if (ntiles > 0) issue_tile(kv_begin, 0, load_pages(kv_begin));
+  if (ntiles > 1) issue_tile(kv_begin + kTK, 1, load_pages(kv_begin + kTK));
   for (int ti = 0; ti < ntiles; ++ti) {
     const int t0 = kv_begin + ti * kTK;
-    char* stage = sm.stage[ti & 1];
-    wait_vmcnt<0>();
-    __syncthreads();  // tile ti is in LDS; the other stage is no longer read
+    char* stage = sm.stage[ti % NST];
+    TilePages next_pages;
+    if (ti + 2 < ntiles) next_pages = load_pages(t0 + 2 * kTK);
+    if (ti + 1 < ntiles) wait_vmcnt<LY::kCopies>();  // tile ti + 1 may stay in flight
+    else wait_vmcnt<0>();
+    __syncthreads();  // tile ti is in LDS; stage (ti + 2) % 3 is no longer read
     if (t0 + kTK > kv_end) {
       // last tile: zero the values of keys >= kv_end (their slots may hold
       // anything, and 0 * NaN would reach the output)
-      for (int e = tid; e < 8 * D; e += kThreads) {
+      for (int e = tid; e < 8 * D; e += kPrefillThreads) {
         const int c = e / D, d = e - c * D;
         const int k0 = t0 + 8 * c;
         if (k0 + 8 > kv_end) {
@@ -417,7 +475,7 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
       }
       __syncthreads();
     }
-    if (ti + 1 < ntiles) issue_tile(t0 + kTK, (ti + 1) & 1);
+    if (ti + 2 < ntiles) issue_tile(t0 + 2 * kTK, (ti + 2) % NST, next_pages);
     if (t0 >= wave_lim) continue;
 
     // S^T for the two 32-key blocks (two accumulation chains)
@@ -434,13 +492,14 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
             stage + LY::koff(32 * kb + krow, 2 * ks + h)));
         s[kb] = mfma32_bf16(kf, qf[ks], s[kb]);
       }
+    pipeline_reads_and_mfma<2 * KS>();
 
     // masks (only tiles that reach past the wave's smallest limit need them)
     float x[32];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) x[16 * kb + v] = s[kb][v] * sc;
+      for (int v = 0; v < 16; ++v) x[16 * kb + v] = s[kb][v];
     if (t0 + kTK > wave_min) {
 #pragma unroll
       for (int j = 0; j < 32; ++j) {
@@ -451,7 +510,7 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
     float tmax = x[0];
 #pragma unroll
     for (int j = 1; j < 32; ++j) tmax = fmaxf(tmax, x[j]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * sc;  // scale > 0
     // lazy rescale: move the reference maximum only when it grew by > 2^8
     const bool grow = tmax > m + 8.f;
     if (__any(grow)) {
@@ -469,7 +528,7 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
     float psum = 0.f;
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
-      p[j] = fast_exp2(x[j] - muse);
+      p[j] = fast_exp2(fmaf(x[j], sc, -muse));
       psum += p[j];
     }
     l += psum;
@@ -489,6 +548,7 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
         acc[dt] = mfma32_bf16(vf, pf, acc[dt]);
       }
     }
+    pipeline_reads_and_mfma<4 * DT>();
   }
   __syncthreads();  // every wave is done with the ring before the next item
 
@@ -511,16 +571,11 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
 template <int D, bool DECODE_ONLY>
 struct FwdLds {
   union U {
-    LdsDecode<D> dec;
+    LdsDecode<D, kPrefillWaves> dec;
     LdsPrefill<D> pre;
   };
-  typedef typename std::conditional<DECODE_ONLY, LdsDecode<D>, U>::type type;
+  typedef typename std::conditional<DECODE_ONLY, LdsDecode<D, 4>, U>::type type;
 };
-
-template <int D, bool DECODE_ONLY>
-__device__ __forceinline__ LdsDecode<D>& dec_lds(typename FwdLds<D, DECODE_ONLY>::type& s) {
-  if constexpr (DECODE_ONLY) return s; else return s.dec;
-}
 
 // Largest b in [0, B) with off[b] <= idx (off is non-decreasing, off[0] = 0):
 // the request whose item range [off[b], off[b + 1]) holds idx.
@@ -577,13 +632,24 @@ __device__ WorkItem make_item(const MhaArgs& a, int idx, int n_pre) {
   return it;
 }
 
+// The prefill item as a real call: in the kernel that also runs decode items,
+// this keeps the two item kinds' register allocations apart, so the prefill
+// loop keeps its operand reads in flight (a call costs little next to an
+// item of up to 256 rows over all its keys).
+template <int D>
+__device__ __noinline__ void run_prefill_item_outlined(const MhaArgs& a, const WorkItem& it,
+                                                       const Dest& dst, LdsPrefill<D>& sm) {
+  run_prefill_item<D>(a, it, dst, sm);
+}
+
 // Persistent forward kernel: a fixed grid; each workgroup takes the next item
 // index from a device counter until the planner's item count is reached.
 // Prefill-mode items (indices below n_pre) are handed out first, so a
 // workgroup runs one loop over them and then one over decode-mode items; the
 // two loops keep the register allocation of the two item kinds apart.
 template <int D, bool DECODE_ONLY>
-__global__ __launch_bounds__(kThreads, 2) void mha_forward_kernel(MhaArgs a) {
+__global__ __launch_bounds__(DECODE_ONLY ? kThreads : kPrefillThreads, DECODE_ONLY ? 2 : 1)
+void mha_forward_kernel(MhaArgs a) {
   __shared__ typename FwdLds<D, DECODE_ONLY>::type sm;
   __shared__ WorkItem s_item;
   __shared__ int s_idx;
@@ -613,15 +679,19 @@ __global__ __launch_bounds__(kThreads, 2) void mha_forward_kernel(MhaArgs a) {
   };
   next();
   if constexpr (!DECODE_ONLY) {
-    for (; idx < n_pre && idx < n_items; next()) run_prefill_item<D>(a, it, dest(), sm.pre);
+    for (; idx < n_pre && idx < n_items; next()) run_prefill_item_outlined<D>(a, it, dest(), sm.pre);
   }
-  for (; idx < n_items; next()) run_decode_item<D>(a, it, dest(), dec_lds<D, DECODE_ONLY>(sm));
+  for (; idx < n_items; next()) {
+    if constexpr (DECODE_ONLY) run_decode_item<D, 4>(a, it, dest(), sm);
+    else run_decode_item<D, kPrefillWaves>(a, it, dest(), sm.dec);
+  }
 }
 
 // pa_decode_split: one workgroup per (request, KV head, partition).
 template <int D, bool DEC>
-__global__ __launch_bounds__(kThreads, 2) void mha_split_kernel(MhaArgs a) {
-  __shared__ typename std::conditional<DEC, LdsDecode<D>, LdsPrefill<D>>::type sm;
+__global__ __launch_bounds__(DEC ? kThreads : kPrefillThreads, DEC ? 2 : 1)
+void mha_split_kernel(MhaArgs a) {
+  __shared__ typename std::conditional<DEC, LdsDecode<D, 4>, LdsPrefill<D>>::type sm;
   const int S = a.num_splits;
   const int s = blockIdx.x % S;
   const int bk = blockIdx.x / S;
@@ -638,9 +708,9 @@ __global__ __launch_bounds__(kThreads, 2) void mha_split_kernel(MhaArgs a) {
   dst.pl_base = (int64_t)(b * a.Hq + kvh * a.G) * S + s;
   dst.pl_row = S;
   if (t1 <= t0) {  // empty partition: zeros and -inf
-    for (int i = threadIdx.x; i < a.G * D; i += kThreads)
+    for (int i = threadIdx.x; i < a.G * D; i += blockDim.x)
       a.part_o[dst.po_base + (int64_t)(i / D) * dst.po_row + (i % D)] = 0.f;
-    for (int i = threadIdx.x; i < a.G; i += kThreads)
+    for (int i = threadIdx.x; i < a.G; i += blockDim.x)
       a.part_lse[dst.pl_base + (int64_t)i * dst.pl_row] = kNegInf;
     return;
   }
@@ -655,7 +725,7 @@ __global__ __launch_bounds__(kThreads, 2) void mha_split_kernel(MhaArgs a) {
   it.q0 = b;
   it.ctx = L - 1;
   it.pad[0] = it.pad[1] = it.pad[2] = 0;
-  if constexpr (DEC) run_decode_item<D>(a, it, dst, sm);
+  if constexpr (DEC) run_decode_item<D, 4>(a, it, dst, sm);
   else run_prefill_item<D>(a, it, dst, sm);
 }
 
@@ -852,16 +922,17 @@ hipError_t mha_occupancy(int D, bool decode_only, int* blocks_per_cu) {
   const void* f;
   if (D == 128) f = decode_only ? (const void*)mha_forward_kernel<128, true> : (const void*)mha_forward_kernel<128, false>;
   else f = decode_only ? (const void*)mha_forward_kernel<64, true> : (const void*)mha_forward_kernel<64, false>;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, f, kThreads, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, f,
+                                                      decode_only ? kThreads : kPrefillThreads, 0);
 }
 
 hipError_t launch_mha_forward(const MhaArgs& a, int D, bool decode_only, int grid, hipStream_t s) {
   if (D == 128) {
     if (decode_only) hipLaunchKernelGGL((mha_forward_kernel<128, true>), dim3(grid), dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((mha_forward_kernel<128, false>), dim3(grid), dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((mha_forward_kernel<128, false>), dim3(grid), dim3(kPrefillThreads), 0, s, a);
   } else {
     if (decode_only) hipLaunchKernelGGL((mha_forward_kernel<64, true>), dim3(grid), dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((mha_forward_kernel<64, false>), dim3(grid), dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((mha_forward_kernel<64, false>), dim3(grid), dim3(kPrefillThreads), 0, s, a);
   }
   return hipGetLastError();
 }
@@ -878,10 +949,10 @@ hipError_t launch_mha_split(const MhaArgs& a, int D, hipStream_t s) {
   const bool dec = a.G <= kDecodeRows;
   if (D == 128) {
     if (dec) hipLaunchKernelGGL((mha_split_kernel<128, true>), dim3(blocks), dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((mha_split_kernel<128, false>), dim3(blocks), dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((mha_split_kernel<128, false>), dim3(blocks), dim3(kPrefillThreads), 0, s, a);
   } else {
     if (dec) hipLaunchKernelGGL((mha_split_kernel<64, true>), dim3(blocks), dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((mha_split_kernel<64, false>), dim3(blocks), dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((mha_split_kernel<64, false>), dim3(blocks), dim3(kPrefillThreads), 0, s, a);
   }
   return hipGetLastError();
 }
