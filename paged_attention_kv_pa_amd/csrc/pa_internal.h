@@ -16,6 +16,7 @@ constexpr int kPrefillWaves = 8;       // waves of a workgroup that runs prefill
 constexpr int kPrefillThreads = 64 * kPrefillWaves;
 constexpr int kDecodeRows = 16;        // rows of one decode-mode item (one MFMA tile)
 constexpr int kPrefillRows = 32 * kPrefillWaves;  // rows of a prefill-mode item (32 per wave)
+constexpr int kXcdRun = 32;           // consecutive prefill-mode items per queue run (CUs per XCD)
 constexpr int kMaxFwdSplits = 64;      // key partitions per decode row in pa_forward
 constexpr int kMinChunk = 256;         // smallest key partition pa_forward makes
 constexpr int kItemsPerWorkgroup = 4;  // decode work is cut into ~this many items per workgroup

@@ -276,11 +276,14 @@ __device__ void run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest
 //     16 kc + 8 h .. +7 are exactly its B operand, and V^T[32 dt + n][16 kc +
 //     8 h ..] its A operand, so P never leaves the lane.
 // 64-key tiles are copied HBM -> LDS by global_load_lds_dwordx4 into a
-// three-stage ring shared by the 8 waves: one 64-key tile feeds 256 rows, so
-// the L2 -> LDS traffic is 32 KiB per 8.4 MFLOP.  LDS layouts (16-byte chunks):
-//   K   [16-key group][column chunk][key % 16] — one copy instruction moves
-//       4 column chunks of 16 keys; the 16 lanes of a read phase read 16
-//       consecutive chunks, and a lane's K-steps sit at fixed offsets;
+// four-stage ring shared by the 8 waves: one 64-key tile feeds 256 rows, so
+// the L2 -> LDS traffic is 32 KiB per 8.4 MFLOP.  The two waves of a SIMD
+// work in ping-pong: while one runs its matrix products, the other runs its
+// softmax (see the schedule in run_prefill_item).  LDS layouts (16-byte chunks):
+//   K   [16-key group][4-chunk column group][key % 16][chunk % 4 ^ swizzle]
+//       — one copy instruction moves 4 column chunks of 16 keys, four
+//       consecutive lanes reading 64 contiguous bytes of a key row; the
+//       swizzle puts the 16 lanes of a read phase on 16 distinct bank groups;
 //   V^T [key chunk][column]          — one copy instruction moves 64 columns
 //       of one 8-key chunk (one page); operand reads are consecutive.
 // The online softmax rescales the accumulator only when a row maximum grows by
@@ -311,7 +314,7 @@ __device__ __forceinline__ void pipeline_reads_and_mfma() {
 
 template <int D>
 struct PrefillLayout {
-  static constexpr int kStages = 3;
+  static constexpr int kStages = 4;
   static constexpr int kChunks = D / 8;                  // 16-byte chunks per key row
   static constexpr int kKBytes = kTK * D * 2;            // K tile
   static constexpr int kVBytes = kTK * D * 2;            // V^T tile
@@ -319,9 +322,12 @@ struct PrefillLayout {
   static constexpr int kKCopies = kChunks / 8;           // K copies per wave per tile
   static constexpr int kVCopies = D / 64;                // V copies per wave per tile
   static constexpr int kCopies = kKCopies + kVCopies;    // copy instructions per thread per tile
-  // byte offset of column chunk c of tile key k in the K tile
+  // byte offset of column chunk c of tile key k in the K tile: blocks of
+  // 16 keys x 4 chunks (1 KiB, one copy instruction), key-major inside, the
+  // chunk position XOR-swizzled by key bits 2..3
   __device__ static __forceinline__ int koff(int k, int c) {
-    return (((k >> 4) * kChunks + c) * 16 + (k & 15)) * 16;
+    return (((((k >> 4) * (kChunks / 4) + (c >> 2)) * 16 + (k & 15)) * 4) +
+            ((c & 3) ^ ((k >> 2) & 3))) * 16;
   }
   // byte offset of key chunk c (keys 8c .. 8c + 7), column d in the V^T tile
   __device__ static __forceinline__ int voff(int c, int d) { return kKBytes + (c * D + d) * 16; }
@@ -401,42 +407,46 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
   const ConstI32Ptr cbt = (ConstI32Ptr)bt;
   const int kgroup = wave >> 1;
   struct TilePages {
-    int pg[2], first[2];  // physical page, first key of that page
+    int pg0, first0;  // physical page and its first key, keys 16 (w / 2) + 0 .. 7
+    int pg1, first1;  // the same for keys 16 (w / 2) + 8 .. 15
   };
   auto load_pages = [&](int t0) {
     TilePages tp;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int gs = min(t0 + 16 * kgroup + 8 * u, kv_end - 1);
-      const int pidx = __builtin_amdgcn_readfirstlane(gs / P);
-      tp.pg[u] = cbt[pidx];
-      tp.first[u] = pidx * P;
-    }
+    const int i0 = __builtin_amdgcn_readfirstlane(min(t0 + 16 * kgroup, kv_end - 1) / P);
+    const int i1 = __builtin_amdgcn_readfirstlane(min(t0 + 16 * kgroup + 8, kv_end - 1) / P);
+    tp.pg0 = cbt[i0];
+    tp.pg1 = cbt[i1];
+    tp.first0 = i0 * P;
+    tp.first1 = i1 * P;
     return tp;
   };
   auto issue_tile = [&](int t0, int st, const TilePages& tp) {
     char* stage = sm.stage[st];
     {
-      const int k16 = lane & 15;
-      const int u = k16 >> 3;
+      // four consecutive lanes copy 64 contiguous bytes of one key row (in
+      // swizzled order), so a copy instruction reads 16 whole 64-byte pieces
+      const int k16 = lane >> 2;
+      const int cl = (lane & 3) ^ ((k16 >> 2) & 3);
+      const bool hi = k16 >= 8;
       const int key = min(t0 + 16 * kgroup + k16, kv_end - 1);
-      const int pg = u ? tp.pg[1] : tp.pg[0];
-      const int first = u ? tp.first[1] : tp.first[0];
+      const int pg = hi ? tp.pg1 : tp.pg0;
+      const int first = hi ? tp.first1 : tp.first0;
       const int c0 = (wave & 1) * (LY::kChunks / 2);  // first column chunk of this wave
       const char* src = kbase + ((int64_t)pg * page_elems + (int64_t)(key - first) * D +
-                                 8 * (c0 + (lane >> 4))) * 2;
+                                 8 * (c0 + cl)) * 2;
 #pragma unroll
       for (int j = 0; j < LY::kKCopies; ++j)
         lds_dma16(src + 64 * j, stage + LY::koff(16 * kgroup, c0 + 4 * j));
     }
     {
-      const int u = wave & 1;
+      const bool hi = wave & 1;
       const int cs = min(t0 + 8 * wave, (kv_end - 1) & ~7);
-      const int slot = cs - tp.first[u];
+      const int pg = hi ? tp.pg1 : tp.pg0;
+      const int slot = cs - (hi ? tp.first1 : tp.first0);
 #pragma unroll
       for (int i = 0; i < LY::kVCopies; ++i) {
         const int d = 64 * i + lane;
-        const char* src = vbase + ((int64_t)tp.pg[u] * page_elems + (int64_t)d * P + slot) * 2;
+        const char* src = vbase + ((int64_t)pg * page_elems + (int64_t)d * P + slot) * 2;
         lds_dma16(src, stage + LY::voff(wave, 64 * i));
       }
     }
@@ -452,64 +462,64 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
 
   const int krow = kperm32(n);
   const int ntiles = (kv_end - kv_begin + kTK - 1) / kTK;
-  if (ntiles > 0) issue_tile(kv_begin, 0, load_pages(kv_begin));
-  if (ntiles > 1) issue_tile(kv_begin + kTK, 1, load_pages(kv_begin + kTK));
-  for (int ti = 0; ti < ntiles; ++ti) {
-    const int t0 = kv_begin + ti * kTK;
-    char* stage = sm.stage[ti % NST];
-    TilePages next_pages;
-    if (ti + 2 < ntiles) next_pages = load_pages(t0 + 2 * kTK);
-    if (ti + 1 < ntiles) wait_vmcnt<LY::kCopies>();  // tile ti + 1 may stay in flight
-    else wait_vmcnt<0>();
-    __syncthreads();  // tile ti is in LDS; stage (ti + 2) % 3 is no longer read
-    if (t0 + kTK > kv_end) {
-      // last tile: zero the values of keys >= kv_end (their slots may hold
-      // anything, and 0 * NaN would reach the output)
-      for (int e = tid; e < 8 * D; e += kPrefillThreads) {
-        const int c = e / D, d = e - c * D;
-        const int k0 = t0 + 8 * c;
-        if (k0 + 8 > kv_end) {
-          u32x4* p = reinterpret_cast<u32x4*>(stage + LY::voff(c, d));
-          *p = zero_tail8(*p, k0, kv_end);
+  // tiles this wave computes on: those starting below its largest key limit
+  const int wave_tiles = min(ntiles, (wave_lim - kv_begin + kTK - 1) / kTK);
+
+  floatx16 s[2];  // S^T of the tile between its GEMM phase and its softmax phase
+  bf16x8 pf[4];   // P^T of the tile between its softmax phase and the next GEMM phase
+
+  // GEMM phase of step t: S^T of tile t, then O^T += V^T P^T of tile t - 1
+  auto gemm_phase = [&](int t) {
+    if (t < wave_tiles) {
+      const char* stage = sm.stage[t % NST];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(
+              stage + LY::koff(32 * kb + krow, 2 * ks + h)));
+          s[kb] = mfma32_bf16(kf, qf[ks], s[kb]);
         }
-      }
-      __syncthreads();
+      pipeline_reads_and_mfma<2 * KS>();
     }
-    if (ti + 2 < ntiles) issue_tile(t0 + 2 * kTK, (ti + 2) % NST, next_pages);
-    if (t0 >= wave_lim) continue;
+    if (t >= 1 && t - 1 < wave_tiles) {
+      const char* stage = sm.stage[(t - 1) % NST];
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const bf16x8 vf = as_bf16x8(
+              *reinterpret_cast<const u32x4*>(stage + LY::voff(2 * kc + h, 32 * dt + n)));
+          acc[dt] = mfma32_bf16(vf, pf[kc], acc[dt]);
+        }
+      pipeline_reads_and_mfma<4 * DT>();
+    }
+  };
 
-    // S^T for the two 32-key blocks (two accumulation chains)
-    floatx16 s[2];
+  // softmax phase of tile t: masks, running maximum, lazy rescale of the
+  // accumulator (which already holds tiles < t), probabilities.  Works in
+  // place on the scores; element (kb, v) is key t0 + 32 kb + 16 (v / 8) + 8 h
+  // + v % 8.
+  auto softmax_phase = [&](int t) {
+    if (t < 0 || t >= wave_tiles) return;
+    const int t0 = kv_begin + t * kTK;
+    if (t0 + kTK > wave_min) {  // only tiles that reach past the smallest limit need masks
+      const int rel = lim - t0 - 8 * h;  // visible iff the key's offset from t0 + 8 h is < rel
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (32 * kb + 16 * (v >> 3) + (v & 7) >= rel) s[kb][v] = kNegInf;
+    }
+    float tmax = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(
-            stage + LY::koff(32 * kb + krow, 2 * ks + h)));
-        s[kb] = mfma32_bf16(kf, qf[ks], s[kb]);
-      }
-    pipeline_reads_and_mfma<2 * KS>();
-
-    // masks (only tiles that reach past the wave's smallest limit need them)
-    float x[32];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) x[16 * kb + v] = s[kb][v];
-    if (t0 + kTK > wave_min) {
-#pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        const int key = t0 + 32 * (j >> 4) + 16 * ((j >> 3) & 1) + 8 * h + (j & 7);
-        if (key >= lim) x[j] = kNegInf;
-      }
-    }
-    float tmax = x[0];
-#pragma unroll
-    for (int j = 1; j < 32; ++j) tmax = fmaxf(tmax, x[j]);
+      for (int v = (kb == 0 ? 2 : 0); v < 16; ++v) tmax = fmaxf(tmax, s[kb][v]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * sc;  // scale > 0
     // lazy rescale: move the reference maximum only when it grew by > 2^8
     const bool grow = tmax > m + 8.f;
@@ -523,32 +533,73 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
         for (int v = 0; v < 16; ++v) acc[dt][v] *= alpha;
       m = mnew;
     }
-    const float muse = m == kNegInf ? 0.f : m;
-    float p[32];
+    const float nmuse = m == kNegInf ? 0.f : -m;
     float psum = 0.f;
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      p[j] = fast_exp2(fmaf(x[j], sc, -muse));
-      psum += p[j];
-    }
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        s[kb][v] = fast_exp2(fmaf(s[kb][v], sc, nmuse));
+        psum += s[kb][v];
+      }
     l += psum;
-
-    // O^T += V^T P^T, four 16-key steps
+    // bf16 probabilities: the B operand of O^T
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
-      const bf16x8 pf = __builtin_bit_cast(
-          bf16x8, u32x4{pack_bf16x2(p[8 * kc + 0], p[8 * kc + 1]),
-                        pack_bf16x2(p[8 * kc + 2], p[8 * kc + 3]),
-                        pack_bf16x2(p[8 * kc + 4], p[8 * kc + 5]),
-                        pack_bf16x2(p[8 * kc + 6], p[8 * kc + 7])});
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const bf16x8 vf = as_bf16x8(
-            *reinterpret_cast<const u32x4*>(stage + LY::voff(2 * kc + h, 32 * dt + n)));
-        acc[dt] = mfma32_bf16(vf, pf, acc[dt]);
+      const int kb = kc >> 1, v0 = 8 * (kc & 1);
+      pf[kc] = __builtin_bit_cast(
+          bf16x8, u32x4{pack_bf16x2(s[kb][v0 + 0], s[kb][v0 + 1]), pack_bf16x2(s[kb][v0 + 2], s[kb][v0 + 3]),
+                        pack_bf16x2(s[kb][v0 + 4], s[kb][v0 + 5]), pack_bf16x2(s[kb][v0 + 6], s[kb][v0 + 7])});
+    }
+  };
+
+  // Ping-pong schedule.  Waves 0-3 (group A, one per SIMD) and 4-7 (group B)
+  // alternate between a GEMM phase and a softmax phase, B one phase behind A,
+  // so each SIMD always has one wave on the matrix core and one on the
+  // vector ALU.  Every phase ends with a workgroup barrier.  Step t:
+  //   even phase: A gemm(t)       B softmax(t - 1)   (copy of tile t + 2 starts)
+  //   odd phase:  A softmax(t)    B gemm(t)          (copy of tile t + 1 waited)
+  // Tile t is read in steps t and t + 1; tile t + 2 lands in stage
+  // (t + 2) % 4, last read in step t - 1.
+  static_assert(NST == 4, "two tiles in flight ahead of the two being read");
+  const bool group_b = wave >= kPrefillWaves / 2;
+  if (ntiles > 0) issue_tile(kv_begin, 0, load_pages(kv_begin));
+  if (ntiles > 1) {
+    issue_tile(kv_begin + kTK, 1, load_pages(kv_begin + kTK));
+    wait_vmcnt<LY::kCopies>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  __syncthreads();
+  TilePages next_pages;
+  if (ntiles > 2) next_pages = load_pages(kv_begin + 2 * kTK);
+  for (int t = 0; t <= ntiles; ++t) {
+    if (t + 2 < ntiles) issue_tile(kv_begin + (t + 2) * kTK, (t + 2) % NST, next_pages);
+    if (group_b) softmax_phase(t - 1);
+    else gemm_phase(t);
+    __syncthreads();
+    if (t + 3 < ntiles) next_pages = load_pages(kv_begin + (t + 3) * kTK);
+    if (t == ntiles - 1 && kv_begin + (t + 1) * kTK > kv_end) {
+      // last tile: zero the values of keys >= kv_end before their first use
+      // in the next step (their slots may hold anything, and 0 * NaN would
+      // reach the output)
+      char* stage = sm.stage[t % NST];
+      const int t0 = kv_begin + t * kTK;
+      for (int e = tid; e < 8 * D; e += kPrefillThreads) {
+        const int c = e / D, d = e - c * D;
+        const int k0 = t0 + 8 * c;
+        if (k0 + 8 > kv_end) {
+          u32x4* pz = reinterpret_cast<u32x4*>(stage + LY::voff(c, d));
+          *pz = zero_tail8(*pz, k0, kv_end);
+        }
       }
     }
-    pipeline_reads_and_mfma<4 * DT>();
+    if (group_b) gemm_phase(t);
+    else softmax_phase(t);
+    // this thread's part of tile t + 1 is in LDS (tile t + 2 may stay in flight)
+    if (t + 2 < ntiles) wait_vmcnt<LY::kCopies>();
+    else wait_vmcnt<0>();
+    __syncthreads();
   }
   __syncthreads();  // every wave is done with the ring before the next item
 
@@ -642,11 +693,22 @@ __device__ __noinline__ void run_prefill_item_outlined(const MhaArgs& a, const W
   run_prefill_item<D>(a, it, dst, sm);
 }
 
-// Persistent forward kernel: a fixed grid; each workgroup takes the next item
-// index from a device counter until the planner's item count is reached.
-// Prefill-mode items (indices below n_pre) are handed out first, so a
-// workgroup runs one loop over them and then one over decode-mode items; the
-// two loops keep the register allocation of the two item kinds apart.
+// Persistent forward kernel: a fixed grid; each workgroup takes items from
+// device counters until the planner's item count is reached.
+//
+// Prefill-mode items (indices below n_pre) are dealt to 8 queues in runs of
+// kXcdRun consecutive indices (run r goes to queue r % 8).  Consecutive
+// indices are row blocks of one (request, KV head), which read the same keys;
+// workgroup w serves queue w % 8 first, and workgroups are placed on the 8
+// chiplets (XCDs, each with its own L2) round-robin by index, so the row
+// blocks that share keys run side by side on one chiplet and share its L2.
+// A workgroup whose queue is empty takes from the next queues, then from the
+// decode-mode items.  The item order only affects speed: every index is
+// handed out exactly once.
+//
+// A workgroup runs one loop over prefill-mode items and then one over
+// decode-mode items; the two loops keep the register allocation of the two
+// item kinds apart.
 template <int D, bool DECODE_ONLY>
 __global__ __launch_bounds__(DECODE_ONLY ? kThreads : kPrefillThreads, DECODE_ONLY ? 2 : 1)
 void mha_forward_kernel(MhaArgs a) {
@@ -657,9 +719,22 @@ void mha_forward_kernel(MhaArgs a) {
   const int n_pre = a.ctrl->n_pre;
   int idx;
   WorkItem it;
+  const int home = blockIdx.x & 7;
+  int drained = 0;  // queues found empty (thread 0)
   auto next = [&]() {
     if (threadIdx.x == 0) {
-      const int i = atomicAdd(&a.ctrl->work_counter, 1);
+      int i = -1;
+      if constexpr (!DECODE_ONLY) {
+        for (int q = 0; q < 8 && i < 0; ++q) {
+          const int qx = (home + q) & 7;
+          if ((drained >> qx) & 1) continue;
+          const int j = atomicAdd(&a.ctrl->xcd_counter[qx], 1);
+          const int cand = (8 * (j / kXcdRun) + qx) * kXcdRun + j % kXcdRun;
+          if (cand < n_pre) i = cand;
+          else drained |= 1 << qx;
+        }
+      }
+      if (i < 0) i = n_pre + atomicAdd(&a.ctrl->work_counter, 1);
       s_idx = i;
       if (i < n_items) s_item = make_item(a, i, n_pre);
     }
@@ -844,6 +919,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     a.ctrl->n_items = run.x + run.y;
     a.ctrl->n_merge = run.w;
     a.ctrl->work_counter = 0;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) a.ctrl->xcd_counter[x] = 0;
   }
 }
 
