@@ -469,34 +469,46 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
   bf16x8 pf[4];   // P^T of the tile between its softmax phase and the next GEMM phase
 
   // GEMM phase of step t: S^T of tile t, then O^T += V^T P^T of tile t - 1
+  // The operand reads are software-pipelined by hand, kAhead reads ahead of
+  // the matrix instruction that consumes them; scheduling barriers keep that
+  // order (left to itself the scheduler sinks each read next to its use).
+  constexpr int kAhead = 4;
   auto gemm_phase = [&](int t) {
     if (t < wave_tiles) {
       const char* stage = sm.stage[t % NST];
+      auto kread = [&](int i) {  // operand i = (ks, kb) = (i / 2, i % 2)
+        return as_bf16x8(*reinterpret_cast<const u32x4*>(
+            stage + LY::koff(32 * (i & 1) + krow, 2 * (i >> 1) + h)));
+      };
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
+      bf16x8 buf[kAhead];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+      for (int i = 0; i < kAhead; ++i) buf[i] = kread(i);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(
-              stage + LY::koff(32 * kb + krow, 2 * ks + h)));
-          s[kb] = mfma32_bf16(kf, qf[ks], s[kb]);
-        }
-      pipeline_reads_and_mfma<2 * KS>();
+      for (int i = 0; i < 2 * KS; ++i) {
+        s[i & 1] = mfma32_bf16(buf[i % kAhead], qf[i >> 1], s[i & 1]);
+        if (i + kAhead < 2 * KS) buf[i % kAhead] = kread(i + kAhead);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     if (t >= 1 && t - 1 < wave_tiles) {
       const char* stage = sm.stage[(t - 1) % NST];
+      auto vread = [&](int i) {  // operand i = (kc, dt) = (i / DT, i % DT)
+        return as_bf16x8(*reinterpret_cast<const u32x4*>(
+            stage + LY::voff(2 * (i / DT) + h, 32 * (i % DT) + n)));
+      };
+      bf16x8 buf[kAhead];
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc)
+      for (int i = 0; i < kAhead; ++i) buf[i] = vread(i);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const bf16x8 vf = as_bf16x8(
-              *reinterpret_cast<const u32x4*>(stage + LY::voff(2 * kc + h, 32 * dt + n)));
-          acc[dt] = mfma32_bf16(vf, pf[kc], acc[dt]);
-        }
-      pipeline_reads_and_mfma<4 * DT>();
+      for (int i = 0; i < 4 * DT; ++i) {
+        acc[i % DT] = mfma32_bf16(buf[i % kAhead], pf[i / DT], acc[i % DT]);
+        if (i + kAhead < 4 * DT) buf[i % kAhead] = vread(i + kAhead);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
 
@@ -683,14 +695,14 @@ __device__ WorkItem make_item(const MhaArgs& a, int idx, int n_pre) {
   return it;
 }
 
-// The prefill item as a real call: in the kernel that also runs decode items,
-// this keeps the two item kinds' register allocations apart, so the prefill
-// loop keeps its operand reads in flight (a call costs little next to an
-// item of up to 256 rows over all its keys).
+// The decode item as a real call, for the kernel that also runs prefill
+// items: this keeps the decode code's register allocation out of the prefill
+// loop (a call costs little next to a decode item's key loads).
 template <int D>
-__device__ __noinline__ void run_prefill_item_outlined(const MhaArgs& a, const WorkItem& it,
-                                                       const Dest& dst, LdsPrefill<D>& sm) {
-  run_prefill_item<D>(a, it, dst, sm);
+__device__ __noinline__ void run_decode_item_outlined(const MhaArgs& a, const WorkItem& it,
+                                                      const Dest& dst,
+                                                      LdsDecode<D, kPrefillWaves>& sm) {
+  run_decode_item<D, kPrefillWaves>(a, it, dst, sm);
 }
 
 // Persistent forward kernel: a fixed grid; each workgroup takes items from
@@ -754,11 +766,11 @@ void mha_forward_kernel(MhaArgs a) {
   };
   next();
   if constexpr (!DECODE_ONLY) {
-    for (; idx < n_pre && idx < n_items; next()) run_prefill_item_outlined<D>(a, it, dest(), sm.pre);
+    for (; idx < n_pre && idx < n_items; next()) run_prefill_item<D>(a, it, dest(), sm.pre);
   }
   for (; idx < n_items; next()) {
     if constexpr (DECODE_ONLY) run_decode_item<D, 4>(a, it, dest(), sm);
-    else run_decode_item<D, kPrefillWaves>(a, it, dest(), sm.dec);
+    else run_decode_item_outlined<D>(a, it, dest(), sm.dec);
   }
 }
 
