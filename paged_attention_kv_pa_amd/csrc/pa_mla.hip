@@ -74,6 +74,15 @@ __device__ __forceinline__ void agpr_scale(float& x, float alpha) {
       : "v"(alpha));
 }
 
+// acc += A B on v_mfma_f32_32x32x16_bf16 with acc pinned in AGPRs (inline
+// assembly: the accumulators of all 16 column tiles fill the AGPR file, and
+// pinning them keeps the allocator from parking other values there).  The
+// caller pads hazards: vector writes of a or b need 2 wait states before this
+// instruction, and reads of acc need the instruction to have retired.
+__device__ __forceinline__ void mfma32_acc_agpr(floatx16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
 // Key held by M-row m of the K operand (see the file comment).
 __device__ __forceinline__ int kperm32(int m) {
   const int q = m >> 3, h = (m >> 2) & 1, w = m & 3;
@@ -95,7 +104,11 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
   const int t0k = a0 < L ? (int)a0 : L, t1k = a1 < L ? (int)a1 : L;
   const int ntiles = (t1k - t0k + kMTK - 1) / kMTK;
 
-  const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
+  // The block table is read-only for the whole call: reading it through the
+  // constant address space lets the uniform reads become scalar loads (a
+  // vector load would make the compiler wait for every copy in flight).
+  typedef const __attribute__((address_space(4))) int32_t* ConstI32Ptr;
+  const ConstI32Ptr bt = (ConstI32Ptr)(a.block_table + (int64_t)b * a.max_pages);
   const char* kv = (const char*)a.kv;
 
   // DMA of tile ti into stage st: thread tid copies key tid / 8, chunk slot
@@ -190,17 +203,33 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
     floatx16 sa, sb;
 #pragma unroll
     for (int v = 0; v < 16; ++v) sa[v] = sb[v] = 0.f;
+    // operand reads run kAhead K-steps ahead of the matrix instructions (by
+    // hand: left alone, the scheduler sinks each read next to its use)
+    constexpr int kAhead = 2;
+    auto kread = [&](int ks) {  // chunk 2 ks + h lives in group (2 ks + h) >> 3 = ks >> 2
+      return as_bf16x8(*reinterpret_cast<const u32x4*>(stage + koff[ks & 3] + (ks >> 2) * (kMTK * 8 * 16)));
+    };
+    auto qread = [&](int ks) {
+      return as_bf16x8(*reinterpret_cast<const u32x4*>(
+          qlds + head * kQLdsStride + (16 * (ks - kQRegSteps) + 8 * h) * 2));
+    };
+    bf16x8 kbuf[kAhead], qbuf[kAhead];
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) {
+      kbuf[i] = kread(i);
+      if (i >= kQRegSteps) qbuf[i] = qread(i);
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      // chunk 2 ks + h lives in group (2 ks + h) >> 3 = ks >> 2
-      const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(
-          stage + koff[ks & 3] + (ks >> 2) * (kMTK * 8 * 16)));
-      const bf16x8 qv = ks < kQRegSteps
-                            ? qf[ks < kQRegSteps ? ks : 0]
-                            : as_bf16x8(*reinterpret_cast<const u32x4*>(
-                                  qlds + head * kQLdsStride + (16 * (ks - kQRegSteps) + 8 * h) * 2));
+      const bf16x8 kf = kbuf[ks % kAhead];
+      const bf16x8 qv = ks < kQRegSteps ? qf[ks < kQRegSteps ? ks : 0] : qbuf[ks % kAhead];
       if (ks & 1) sb = mfma32_bf16(kf, qv, sb);
       else sa = mfma32_bf16(kf, qv, sa);
+      if (ks + kAhead < KS) {
+        kbuf[ks % kAhead] = kread(ks + kAhead);
+        if (ks + kAhead >= kQRegSteps) qbuf[ks % kAhead] = qread(ks + kAhead);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     // lane holds S[head][key] for keys 8h + v (v < 8) and 16 + 8h + (v - 8)
     float x[16];
@@ -219,7 +248,9 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
       const float alpha = grow ? fast_exp2((m - mnew) * sc) : 1.f;  // 0 while m = -inf
       l *= alpha;
       // acc lives in AGPRs; scale it there (read, multiply, write back) so
-      // that the allocator never has to hold it in vector registers.
+      // that the allocator never has to hold it in vector registers.  The
+      // last matrix instruction that wrote it must have retired first.
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -246,23 +277,35 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
                         pack_bf16x2(p[8 * kk + 2], p[8 * kk + 3]),
                         pack_bf16x2(p[8 * kk + 4], p[8 * kk + 5]),
                         pack_bf16x2(p[8 * kk + 6], p[8 * kk + 7])});
+    // the matrix instructions below are inline assembly, which the compiler
+    // does not pad against hazards: let the vector writes of pf settle
+    asm volatile("s_nop 4" ::: "memory");
+    // V^T operands: two transposing reads each, kAheadV instructions ahead
+    constexpr int kAheadV = 2;
+    auto vread = [&](int i) {  // i = 2 dt + kk
+      const int dt = i >> 1, kk = i & 1;
+      const int goff = (dt >> 1) * (kMTK * 8 * 16);  // chunk group of columns 32 dt ..
+      const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_short4*)(stage + voff[kk][0][dt & 1] + goff));
+      const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_short4*)(stage + voff[kk][1][dt & 1] + goff));
+      const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+      return __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
+    };
+    bf16x8 vbuf[kAheadV];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
+    for (int i = 0; i < kAheadV; ++i) vbuf[i] = vread(i);
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int goff = (dt >> 1) * (kMTK * 8 * 16);  // chunk group of columns 32 dt ..
-        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_short4*)(stage + voff[kk][0][dt & 1] + goff));
-        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_short4*)(stage + voff[kk][1][dt & 1] + goff));
-        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
-        acc[dt] = mfma32_bf16(vf, pf[kk], acc[dt]);
-      }
+    for (int i = 0; i < 2 * DT; ++i) {
+      mfma32_acc_agpr(acc[i >> 1], vbuf[i % kAheadV], pf[i & 1]);
+      if (i + kAheadV < 2 * DT) vbuf[i % kAheadV] = vread(i + kAheadV);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  // epilogue: lane holds O[head][32 dt + 8 (v / 4) + 4h + v % 4]
+  // epilogue: lane holds O[head][32 dt + 8 (v / 4) + 4h + v % 4]; the last
+  // matrix instruction (inline assembly) must have retired before acc is read
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
   const float lrow = l + __shfl_xor(l, 32);
   if (!row_ok) return;
   const float inv = lrow > 0.f ? 1.f / lrow : 0.f;
