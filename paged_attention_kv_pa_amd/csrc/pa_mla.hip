@@ -278,8 +278,9 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
                         pack_bf16x2(p[8 * kk + 4], p[8 * kk + 5]),
                         pack_bf16x2(p[8 * kk + 6], p[8 * kk + 7])});
     // the matrix instructions below are inline assembly, which the compiler
-    // does not pad against hazards: let the vector writes of pf settle
-    asm volatile("s_nop 4" ::: "memory");
+    // does not pad against hazards: let the vector writes of pf settle (the
+    // operands keep those writes before this point)
+    asm volatile("s_nop 4" : "+v"(pf[0]), "+v"(pf[1]));
     // V^T operands: two transposing reads each, kAheadV instructions ahead
     constexpr int kAheadV = 2;
     auto vread = [&](int i) {  // i = 2 dt + kk
@@ -303,9 +304,11 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
     }
   }
 
-  // epilogue: lane holds O[head][32 dt + 8 (v / 4) + 4h + v % 4]; the last
-  // matrix instruction (inline assembly) must have retired before acc is read
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  // epilogue: lane holds O[head][32 dt + 8 (v / 4) + 4h + v % 4].  The last
+  // matrix instructions (inline assembly, issued in column-tile order) must
+  // have retired before acc is read: the wait is tied to the last two tiles
+  // (earlier tiles were written at least four instructions before the end).
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[DT - 1]), "+a"(acc[DT - 2]));
   const float lrow = l + __shfl_xor(l, 32);
   if (!row_ok) return;
   const float inv = lrow > 0.f ? 1.f / lrow : 0.f;
