@@ -641,13 +641,20 @@ struct FwdLds {
 };
 
 // Largest b in [0, B) with off[b] <= idx (off is non-decreasing, off[0] = 0):
-// the request whose item range [off[b], off[b + 1]) holds idx.
+// the request whose item range [off[b], off[b + 1]) holds idx.  Called by a
+// whole wave with a wave-uniform idx: the 64 lanes probe 64 evenly spaced
+// entries at once, so B <= 64 takes one round of loads and B <= 4096 two
+// (a one-lane binary search would take log2 B dependent loads).
 __device__ __forceinline__ int find_request(const int32_t* off, int B, int idx) {
-  int lo = 0, hi = B - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (off[mid] <= idx) lo = mid;
-    else hi = mid - 1;
+  const int lane = threadIdx.x & 63;
+  int lo = 0, n = B;  // the answer lies in [lo, lo + n)
+  while (n > 1) {
+    const int step = (n + 63) / 64;
+    const int k = lane * step;
+    const bool ok = k < n && off[lo + k] <= idx;
+    const int c = __popcll(__ballot(ok));  // >= 1: off[lo] <= idx
+    lo += (c - 1) * step;
+    n = min(step, n - (c - 1) * step);
   }
   return lo;
 }
@@ -733,22 +740,33 @@ void mha_forward_kernel(MhaArgs a) {
   WorkItem it;
   const int home = blockIdx.x & 7;
   int drained = 0;  // queues found empty (thread 0)
+  // wave 0 takes the next index (lane 0's atomics, broadcast to the wave)
+  // and decodes the item with wave-wide searches
   auto next = [&]() {
-    if (threadIdx.x == 0) {
+    if (threadIdx.x < 64) {
       int i = -1;
       if constexpr (!DECODE_ONLY) {
         for (int q = 0; q < 8 && i < 0; ++q) {
           const int qx = (home + q) & 7;
           if ((drained >> qx) & 1) continue;
-          const int j = atomicAdd(&a.ctrl->xcd_counter[qx], 1);
+          int j = 0;
+          if (threadIdx.x == 0) j = atomicAdd(&a.ctrl->xcd_counter[qx], 1);
+          j = __shfl(j, 0);
           const int cand = (8 * (j / kXcdRun) + qx) * kXcdRun + j % kXcdRun;
           if (cand < n_pre) i = cand;
           else drained |= 1 << qx;
         }
       }
-      if (i < 0) i = n_pre + atomicAdd(&a.ctrl->work_counter, 1);
-      s_idx = i;
-      if (i < n_items) s_item = make_item(a, i, n_pre);
+      if (i < 0) {
+        int j = 0;
+        if (threadIdx.x == 0) j = atomicAdd(&a.ctrl->work_counter, 1);
+        i = n_pre + __shfl(j, 0);
+      }
+      const WorkItem w = i < n_items ? make_item(a, i, n_pre) : WorkItem{};
+      if (threadIdx.x == 0) {
+        s_idx = i;
+        s_item = w;
+      }
     }
     __syncthreads();
     idx = s_idx;
