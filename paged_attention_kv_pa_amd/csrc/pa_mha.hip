@@ -916,7 +916,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       rp.q0 = a.qsl[b];
       const int rows = rp.nq * G;
       if (rp.nq > 0 && rows <= kDecodeRows) {
-        long long sp = (rp.L + chunk - 1) / chunk;
+        // Items are handed out in request order, so the last requests' items
+        // run last: cutting those finer shortens the tail where workgroups
+        // finish at different times (the extra partial rows stay few).
+        long long ck = chunk;
+        if (b >= a.B - a.B / kTailFraction) {
+          ck = (chunk / kTailDivisor + 63) & ~63LL;
+          ck = ck < kMinChunk ? kMinChunk : ck;
+        }
+        long long sp = (rp.L + ck - 1) / ck;
         sp = sp < 1 ? 1 : (sp > kMaxFwdSplits ? kMaxFwdSplits : sp);
         rp.per = 64 * (int)(((rp.L + 63) / 64 + sp - 1) / sp);
         rp.nsplit = (rp.L + rp.per - 1) / rp.per;
