@@ -124,6 +124,34 @@ def test_llama_decode_split_matches_oracle_partials(S):
     check_out(out.float().cpu().numpy(), ref, torch.bfloat16, "bf16 merged S=%d" % S)
 
 
+@pytest.mark.parametrize("Hq,Hkv,D,S", [(64, 2, 128, 1), (64, 2, 128, 5), (64, 1, 64, 3)])
+def test_decode_split_wide_groups(Hq, Hkv, D, S):
+    # more query heads per KV head than one decode tile holds: the split
+    # kernel runs these rows through the prefill-mode item
+    b = workload.make_batch([1, 1, 1], [2900, 77, 1500], num_q_heads=Hq, num_kv_heads=Hkv,
+                            head_dim_qk=D, page_size=16, seed=Hq + D + S)
+    g = b.to(DEV)
+    say("case wide split Hq=%d Hkv=%d D=%d S=%d" % (Hq, Hkv, D, S))
+    po, pl = pa.pa_decode_split(g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens, b.scale, S)
+    out = pa.pa_merge_lse(po, pl)
+    torch.cuda.synchronize()
+    rpo, rpl = oracle.decode_split(b.q, b.k_cache, b.v_cache, b.block_table, b.seq_lens, b.scale,
+                                   S, b.num_kv_heads)
+    check_out(po.cpu().numpy(), rpo, torch.bfloat16, "wide partials S=%d" % S)
+    check_lse(pl.cpu().numpy(), rpl, "wide partial lse S=%d" % S)
+    ref, _ = oracle_forward(b)
+    check_out(out.float().cpu().numpy(), ref, torch.bfloat16, "wide merged S=%d" % S)
+
+
+@pytest.mark.parametrize("D,P", [(64, 16), (128, 8), (128, 32)])
+def test_prefill_multi_item_shapes(D, P):
+    # several 256-row items per (request, KV head), key ranges over many
+    # copy tiles with a ragged last tile, for the other head dim and pages
+    b = workload.make_batch([300, 37, 1], [700, 0, 900], num_q_heads=32, num_kv_heads=4,
+                            head_dim_qk=D, page_size=P, seed=D + P)
+    forward_parity(b, "prefill items D=%d P=%d" % (D, P))
+
+
 # ------------------------------------------------- long-context split decode
 
 @pytest.mark.parametrize("batch,S,lengths", [(1, 64, None), (4, 32, None), (16, 16, None),
