@@ -59,23 +59,33 @@ class HipEvents:
 
 
 def time_steps(call, steps, warmup, lib):
-    """Run `call` warmup + steps times; returns (ms per step, mean attention-kernel ms)."""
+    """Run `call` warmup + steps times, then `steps` more times.
+
+    Returns (ms per step, mean attention-kernel ms).  The step time comes from
+    the first timed run, made exactly as a caller would make the calls.  The
+    kernel time comes from the second, in which the library records a HIP event
+    pair on its stream right around every attention-kernel launch; those
+    markers widen the gaps between the launches of a step, so they stay out of
+    the step timing.
+    """
     import torch
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
-    ev = HipEvents(steps)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0.record()
+    for _ in range(steps):
+        call()
+    t1.record()
+    torch.cuda.synchronize()
+    step_ms = t0.elapsed_time(t1) / steps
+    ev = HipEvents(steps)
     for i in range(steps):
         lib.pa_set_kernel_events(ev.pairs[i][0], ev.pairs[i][1])
         call()
     lib.pa_set_kernel_events(None, None)
-    t1.record()
     torch.cuda.synchronize()
-    step_ms = t0.elapsed_time(t1) / steps
     kern_ms = sum(ev.elapsed_ms(i) for i in range(steps)) / steps
     ev.close()
     return step_ms, kern_ms

@@ -201,7 +201,7 @@ pa_status pa_forward(const void* q, const void* k_cache, const void* v_cache,
   pa::Control* ctrl = (pa::Control*)(ws + w.ctrl_off);
   pa::ReqPlan* req = (pa::ReqPlan*)(ws + w.req_off);
   int32_t* pre_off = (int32_t*)(ws + w.pre_off);
-  int32_t* dec_off = (int32_t*)(ws + w.dec_off);
+  int32_t* dec_items = (int32_t*)(ws + w.items_off);
   int32_t* merge_off = (int32_t*)(ws + w.merge_off);
 
   pa::PlanArgs pl{};
@@ -209,7 +209,7 @@ pa_status pa_forward(const void* q, const void* k_cache, const void* v_cache,
   pl.qsl = query_start_loc;
   pl.req = req;
   pl.pre_off = pre_off;
-  pl.dec_off = dec_off;
+  pl.dec_items = dec_items;
   pl.merge_off = merge_off;
   pl.ctrl = ctrl;
   pl.B = d->num_seqs;
@@ -234,7 +234,7 @@ pa_status pa_forward(const void* q, const void* k_cache, const void* v_cache,
   a.part_lse = (float*)(ws + w.plse_off);
   a.req = req;
   a.pre_off = pre_off;
-  a.dec_off = dec_off;
+  a.dec_items = dec_items;
   a.merge_off = merge_off;
   a.ctrl = ctrl;
   a.scale = scale;

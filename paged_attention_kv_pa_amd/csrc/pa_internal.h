@@ -23,6 +23,7 @@ constexpr int kTailFraction = 8;       // the last 1 / kTailFraction of the requ
 constexpr int kTailDivisor = 2;        // ... get decode partitions kTailDivisor times smaller
 constexpr int kItemsPerWorkgroup = 4;  // decode work is cut into ~this many items per workgroup
 constexpr int kMaxSplits = 256;        // pa_decode_split / pa_merge_lse / mla_decode limit
+constexpr int kItemInts = 12;          // int32 words of one pa_forward work item
 
 struct MhaArgs {
   const void* q;
@@ -37,7 +38,7 @@ struct MhaArgs {
   float* part_lse;
   const ReqPlan* req;        // pa_forward planner output
   const int32_t* pre_off;    // [B + 1] first prefill-mode item of each request
-  const int32_t* dec_off;    // [B + 1] first decode-mode item (relative to n_pre)
+  const int32_t* dec_items;  // decode-mode items (relative to n_pre), kItemInts int32 each
   const int32_t* merge_off;  // [B + 1] first merge entry
   Control* ctrl;
   float scale;
@@ -51,7 +52,7 @@ struct PlanArgs {
   const int32_t* qsl;
   ReqPlan* req;
   int32_t* pre_off;
-  int32_t* dec_off;
+  int32_t* dec_items;
   int32_t* merge_off;
   Control* ctrl;
   int32_t B, Hkv, G;
@@ -96,7 +97,7 @@ struct DeviceInfo {
 
 // Workspace layout of pa_forward.
 struct FwdWorkspace {
-  size_t ctrl_off, req_off, pre_off, dec_off, merge_off, plse_off, po_off, total;
+  size_t ctrl_off, req_off, pre_off, items_off, merge_off, plse_off, po_off, total;
   int64_t cap_slots;
 };
 FwdWorkspace fwd_workspace_layout(int B, int T, int Hkv, int G, int D);

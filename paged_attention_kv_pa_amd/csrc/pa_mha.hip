@@ -99,9 +99,12 @@ __device__ __forceinline__ void store_lse(const MhaArgs& a, const Dest& dst, int
 // operands (no LDS staging: nothing is shared between waves), then merge their
 // partial softmax states through LDS.
 // ---------------------------------------------------------------------------
+// `counter` (may be NULL): thread 0 takes the workgroup's next item index from
+// it once the keys are done, so the round trip overlaps the epilogue; the
+// index is returned in thread 0.
 template <int D, int NW>
-__device__ void run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest& dst,
-                                LdsDecode<D, NW>& sm) {
+__device__ int run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest& dst,
+                               LdsDecode<D, NW>& sm, int32_t* counter) {
   constexpr int KS = D / 32, DT = D / 16;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
   const int b = it.seq, kvh = it.kvh, G = a.G, P = a.P;
@@ -219,6 +222,9 @@ __device__ void run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest
     }
   }
 
+  int claim = 0;
+  if (counter && tid == 0) claim = atomicAdd(counter, 1);
+
   // merge the NW waves' states
   const float lrow = group_sum4(l);
   if (g == 0) {
@@ -262,6 +268,7 @@ __device__ void run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest
     }
   }
   __syncthreads();
+  return claim;
 }
 
 // ---------------------------------------------------------------------------
@@ -659,45 +666,28 @@ __device__ __forceinline__ int find_request(const int32_t* off, int B, int idx) 
   return lo;
 }
 
-// Work item `idx` of pa_forward, decoded from the planner's per-request
-// offsets.  Prefill-mode items [0, n_pre) come first, the heaviest row block
-// of a request first; decode-mode items follow.
-__device__ WorkItem make_item(const MhaArgs& a, int idx, int n_pre) {
+static_assert(sizeof(WorkItem) == kItemInts * sizeof(int32_t), "work item size");
+
+// Prefill-mode work item `idx` of pa_forward, decoded from the planner's
+// per-request offsets; the heaviest row block of a request comes first.
+__device__ WorkItem make_prefill_item(const MhaArgs& a, int idx) {
   WorkItem it;
   const int G = a.G;
-  if (idx < n_pre) {
-    const int b = find_request(a.pre_off, a.num_seqs, idx);
-    const ReqPlan rp = a.req[b];
-    const int local = idx - a.pre_off[b];
-    const int kvh = local / rp.nblk;
-    const int blk = rp.nblk - 1 - (local - kvh * rp.nblk);
-    const int rows = rp.nq * G;
-    it.seq = b;
-    it.kvh = kvh;
-    it.row0 = blk * kPrefillRows;
-    it.nrows = min(kPrefillRows, rows - it.row0);
-    it.ctx = rp.L - rp.nq;
-    it.kv_begin = 0;
-    it.kv_end = it.ctx + (it.row0 + it.nrows - 1) / G + 1;
-    it.part = -1;
-    it.q0 = rp.q0;
-  } else {
-    const int j = idx - n_pre;
-    const int b = find_request(a.dec_off, a.num_seqs, j);
-    const ReqPlan rp = a.req[b];
-    const int local = j - a.dec_off[b];
-    const int kvh = local / rp.nsplit;
-    const int sp = local - kvh * rp.nsplit;
-    it.seq = b;
-    it.kvh = kvh;
-    it.row0 = 0;
-    it.nrows = rp.nq * G;
-    it.ctx = rp.L - rp.nq;
-    it.kv_begin = sp * rp.per;
-    it.kv_end = min(rp.L, it.kv_begin + rp.per);
-    it.part = rp.nsplit > 1 ? rp.slot0 + kvh * rp.nsplit + sp : -1;
-    it.q0 = rp.q0;
-  }
+  const int b = find_request(a.pre_off, a.num_seqs, idx);
+  const ReqPlan rp = a.req[b];
+  const int local = idx - a.pre_off[b];
+  const int kvh = local / rp.nblk;
+  const int blk = rp.nblk - 1 - (local - kvh * rp.nblk);
+  const int rows = rp.nq * G;
+  it.seq = b;
+  it.kvh = kvh;
+  it.row0 = blk * kPrefillRows;
+  it.nrows = min(kPrefillRows, rows - it.row0);
+  it.ctx = rp.L - rp.nq;
+  it.kv_begin = 0;
+  it.kv_end = it.ctx + (it.row0 + it.nrows - 1) / G + 1;
+  it.part = -1;
+  it.q0 = rp.q0;
   it.pad[0] = it.pad[1] = it.pad[2] = 0;
   return it;
 }
@@ -706,10 +696,11 @@ __device__ WorkItem make_item(const MhaArgs& a, int idx, int n_pre) {
 // items: this keeps the decode code's register allocation out of the prefill
 // loop (a call costs little next to a decode item's key loads).
 template <int D>
-__device__ __noinline__ void run_decode_item_outlined(const MhaArgs& a, const WorkItem& it,
-                                                      const Dest& dst,
-                                                      LdsDecode<D, kPrefillWaves>& sm) {
-  run_decode_item<D, kPrefillWaves>(a, it, dst, sm);
+__device__ __noinline__ int run_decode_item_outlined(const MhaArgs& a, const WorkItem& it,
+                                                     const Dest& dst,
+                                                     LdsDecode<D, kPrefillWaves>& sm,
+                                                     int32_t* counter) {
+  return run_decode_item<D, kPrefillWaves>(a, it, dst, sm, counter);
 }
 
 // Persistent forward kernel: a fixed grid; each workgroup takes items from
@@ -736,12 +727,30 @@ void mha_forward_kernel(MhaArgs a) {
   __shared__ int s_idx;
   const int n_items = a.ctrl->n_items;
   const int n_pre = a.ctrl->n_pre;
+  const int n_dec = n_items - n_pre;
+  // A decode-only grid starts workgroup w on decode-mode item w, so the queue
+  // hands out the items after the first gridDim.x.
+  const int dec_base = DECODE_ONLY ? (int)gridDim.x : 0;
+  int32_t* const counter = &a.ctrl->work_counter;
   int idx;
   WorkItem it;
   const int home = blockIdx.x & 7;
   int drained = 0;  // queues found empty (thread 0)
-  // wave 0 takes the next index (lane 0's atomics, broadcast to the wave)
-  // and decodes the item with wave-wide searches
+  // wave 0: decode-mode item j into s_item, lane k copying word k
+  auto fetch_decode = [&](int j) {
+    const int lane = threadIdx.x;
+    if (j < n_dec && lane < kItemInts)
+      reinterpret_cast<int32_t*>(&s_item)[lane] = a.dec_items[(int64_t)j * kItemInts + lane];
+    if (lane == 0) s_idx = n_pre + j;
+  };
+  auto publish = [&]() {
+    __syncthreads();
+    idx = s_idx;
+    it = s_item;
+    __syncthreads();
+  };
+  // wave 0 takes the next index (lane 0's atomics, broadcast to the wave):
+  // the prefill-mode queues first, then the decode-mode queue
   auto next = [&]() {
     if (threadIdx.x < 64) {
       int i = -1;
@@ -757,21 +766,19 @@ void mha_forward_kernel(MhaArgs a) {
           else drained |= 1 << qx;
         }
       }
-      if (i < 0) {
+      if (i >= 0) {
+        const WorkItem w = make_prefill_item(a, i);
+        if (threadIdx.x == 0) {
+          s_idx = i;
+          s_item = w;
+        }
+      } else {
         int j = 0;
-        if (threadIdx.x == 0) j = atomicAdd(&a.ctrl->work_counter, 1);
-        i = n_pre + __shfl(j, 0);
-      }
-      const WorkItem w = i < n_items ? make_item(a, i, n_pre) : WorkItem{};
-      if (threadIdx.x == 0) {
-        s_idx = i;
-        s_item = w;
+        if (threadIdx.x == 0) j = atomicAdd(counter, 1);
+        fetch_decode(__shfl(j, 0) + dec_base);
       }
     }
-    __syncthreads();
-    idx = s_idx;
-    it = s_item;
-    __syncthreads();
+    publish();
   };
   auto dest = [&]() {
     Dest dst;
@@ -782,13 +789,20 @@ void mha_forward_kernel(MhaArgs a) {
     dst.pl_row = 1;
     return dst;
   };
-  next();
-  if constexpr (!DECODE_ONLY) {
+  if constexpr (DECODE_ONLY) {
+    if (threadIdx.x < 64) fetch_decode(blockIdx.x);
+    publish();
+  } else {
+    next();
     for (; idx < n_pre && idx < n_items; next()) run_prefill_item<D>(a, it, dest(), sm.pre);
   }
-  for (; idx < n_items; next()) {
-    if constexpr (DECODE_ONLY) run_decode_item<D, 4>(a, it, dest(), sm);
-    else run_decode_item_outlined<D>(a, it, dest(), sm.dec);
+  // decode-mode items: each one claims its successor while its epilogue runs
+  while (idx < n_items) {
+    int j;
+    if constexpr (DECODE_ONLY) j = run_decode_item<D, 4>(a, it, dest(), sm, counter);
+    else j = run_decode_item_outlined<D>(a, it, dest(), sm.dec, counter);
+    if (threadIdx.x < 64) fetch_decode(__shfl(j, 0) + dec_base);
+    publish();
   }
 }
 
@@ -830,7 +844,7 @@ void mha_split_kernel(MhaArgs a) {
   it.q0 = b;
   it.ctx = L - 1;
   it.pad[0] = it.pad[1] = it.pad[2] = 0;
-  if constexpr (DEC) run_decode_item<D, 4>(a, it, dst, sm);
+  if constexpr (DEC) run_decode_item<D, 4>(a, it, dst, sm, nullptr);
   else run_prefill_item<D>(a, it, dst, sm);
 }
 
@@ -885,6 +899,8 @@ __device__ __forceinline__ void request_shape(const PlanArgs& a, int b, int* nq,
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ int4 sh[kPlanThreads / 64];
   __shared__ unsigned long long s_dec_keys;
+  __shared__ int s_doff[kPlanThreads + 1];
+  __shared__ ReqPlan s_plan[kPlanThreads];
   const int tid = threadIdx.x;
   const int G = a.G, Hkv = a.Hkv;
   if (tid == 0) s_dec_keys = 0;
@@ -944,14 +960,34 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       rp.slot0 = run.z + ex.z;
       a.req[b] = rp;
       a.pre_off[b] = run.x + ex.x;
-      a.dec_off[b] = run.y + ex.y;
       a.merge_off[b] = run.w + ex.w;
     }
+    // Decode-mode items of this chunk of requests, written by all threads:
+    // item i of the chunk belongs to the last request whose first item is at
+    // or before i; a request's items are KV head major, then partition.
+    s_doff[tid] = ex.y;
+    s_plan[tid] = rp;
+    if (tid == kPlanThreads - 1) s_doff[kPlanThreads] = tot.y;
+    __syncthreads();
+    for (int i = tid; i < tot.y; i += kPlanThreads) {
+      int lo = 0;  // largest k with s_doff[k] <= i; empty requests share offsets
+      for (int step = kPlanThreads / 2; step >= 1; step >>= 1)
+        if (s_doff[lo + step] <= i) lo += step;
+      const ReqPlan q = s_plan[lo];
+      const int local = i - s_doff[lo];
+      const int kvh = local / q.nsplit, sp = local - kvh * q.nsplit;
+      const int kb = sp * q.per;
+      int4* d4 = reinterpret_cast<int4*>(a.dec_items + (int64_t)(run.y + i) * kItemInts);
+      // seq, kvh, row0, nrows | kv_begin, kv_end, part, q0 | ctx, pad
+      d4[0] = int4{base + lo, kvh, 0, q.nq * G};
+      d4[1] = int4{kb, min(q.L, kb + q.per), q.nsplit > 1 ? q.slot0 + kvh * q.nsplit + sp : -1, q.q0};
+      d4[2] = int4{q.L - q.nq, 0, 0, 0};
+    }
+    __syncthreads();
     run = int4{run.x + tot.x, run.y + tot.y, run.z + tot.z, run.w + tot.w};
   }
   if (tid == 0) {
     a.pre_off[a.B] = run.x;
-    a.dec_off[a.B] = run.y;
     a.merge_off[a.B] = run.w;
     a.ctrl->n_pre = run.x;
     a.ctrl->n_items = run.x + run.y;
@@ -1085,8 +1121,8 @@ FwdWorkspace fwd_workspace_layout(int B, int T, int Hkv, int G, int D) {
   off = align(off + (size_t)B * sizeof(ReqPlan));
   w.pre_off = off;
   off = align(off + (size_t)(B + 1) * sizeof(int32_t));
-  w.dec_off = off;
-  off = align(off + (size_t)(B + 1) * sizeof(int32_t));
+  w.items_off = off;
+  off = align(off + (size_t)w.cap_slots * kItemInts * sizeof(int32_t));
   w.merge_off = off;
   off = align(off + (size_t)(B + 1) * sizeof(int32_t));
   w.plse_off = off;
