@@ -202,7 +202,7 @@ pa_status pa_forward(const void* q, const void* k_cache, const void* v_cache,
   pa::ReqPlan* req = (pa::ReqPlan*)(ws + w.req_off);
   int32_t* pre_off = (int32_t*)(ws + w.pre_off);
   int32_t* dec_items = (int32_t*)(ws + w.items_off);
-  int32_t* merge_off = (int32_t*)(ws + w.merge_off);
+  int32_t* merges = (int32_t*)(ws + w.merges_off);
 
   pa::PlanArgs pl{};
   pl.seq_lens = seq_lens;
@@ -210,7 +210,7 @@ pa_status pa_forward(const void* q, const void* k_cache, const void* v_cache,
   pl.req = req;
   pl.pre_off = pre_off;
   pl.dec_items = dec_items;
-  pl.merge_off = merge_off;
+  pl.merges = merges;
   pl.ctrl = ctrl;
   pl.B = d->num_seqs;
   pl.Hkv = d->num_kv_heads;
@@ -235,7 +235,7 @@ pa_status pa_forward(const void* q, const void* k_cache, const void* v_cache,
   a.req = req;
   a.pre_off = pre_off;
   a.dec_items = dec_items;
-  a.merge_off = merge_off;
+  a.merges = merges;
   a.ctrl = ctrl;
   a.scale = scale;
   a.num_seqs = d->num_seqs;

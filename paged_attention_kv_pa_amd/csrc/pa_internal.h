@@ -39,7 +39,7 @@ struct MhaArgs {
   const ReqPlan* req;        // pa_forward planner output
   const int32_t* pre_off;    // [B + 1] first prefill-mode item of each request
   const int32_t* dec_items;  // decode-mode items (relative to n_pre), kItemInts int32 each
-  const int32_t* merge_off;  // [B + 1] first merge entry
+  const int32_t* merges;     // merge entries, 4 int32 each: first slot, S | nrows << 16, q0, kvh
   Control* ctrl;
   float scale;
   int32_t num_seqs;
@@ -53,7 +53,7 @@ struct PlanArgs {
   ReqPlan* req;
   int32_t* pre_off;
   int32_t* dec_items;
-  int32_t* merge_off;
+  int32_t* merges;
   Control* ctrl;
   int32_t B, Hkv, G;
   int32_t P, max_pages;
@@ -97,7 +97,7 @@ struct DeviceInfo {
 
 // Workspace layout of pa_forward.
 struct FwdWorkspace {
-  size_t ctrl_off, req_off, pre_off, items_off, merge_off, plse_off, po_off, total;
+  size_t ctrl_off, req_off, pre_off, items_off, merges_off, plse_off, po_off, total;
   int64_t cap_slots;
 };
 FwdWorkspace fwd_workspace_layout(int B, int T, int Hkv, int G, int D);

@@ -886,8 +886,9 @@ __device__ int4 block_exclusive_scan4(int4 v, int4* wsum, int4* total) {
 // New-token count and key count of request b.  Requests whose lengths are
 // inconsistent (seq_len < q_len, or no key) get no work; seq_len is capped at
 // the block-table capacity so no item can index past a table row.
-__device__ __forceinline__ void request_shape(const PlanArgs& a, int b, int* nq, int* L) {
-  int q = a.qsl[b + 1] - a.qsl[b];
+__device__ __forceinline__ void request_shape(const PlanArgs& a, int b, int* nq, int* L, int* q0) {
+  *q0 = a.qsl[b];
+  int q = a.qsl[b + 1] - *q0;
   int l = a.seq_lens[b];
   const long long cap = (long long)a.max_pages * a.P;
   if (l > cap) l = (int)cap;
@@ -907,9 +908,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __syncthreads();
   // pass 1: total decode-mode keys, which sets the partition size
   unsigned long long my_keys = 0;
+  int nq_first = 0, L_first = 0, q0_first = 0;  // request tid, reused by pass 2
   for (int b = tid; b < a.B; b += kPlanThreads) {
-    int nq, L;
-    request_shape(a, b, &nq, &L);
+    int nq, L, q0;
+    request_shape(a, b, &nq, &L, &q0);
+    if (b == tid) {
+      nq_first = nq;
+      L_first = L;
+      q0_first = q0;
+    }
     if (nq > 0 && nq * G <= kDecodeRows) my_keys += (unsigned long long)L;
   }
 #pragma unroll
@@ -928,8 +935,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     ReqPlan rp = {0, 0, 0, 0, 0, 0, 0, 0};
     int4 cnt = int4{0, 0, 0, 0};
     if (b < a.B) {
-      request_shape(a, b, &rp.nq, &rp.L);
-      rp.q0 = a.qsl[b];
+      if (base == 0) {
+        rp.nq = nq_first;
+        rp.L = L_first;
+        rp.q0 = q0_first;
+      } else {
+        request_shape(a, b, &rp.nq, &rp.L, &rp.q0);
+      }
       const int rows = rp.nq * G;
       if (rp.nq > 0 && rows <= kDecodeRows) {
         // Items are handed out in request order, so the last requests' items
@@ -960,7 +972,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       rp.slot0 = run.z + ex.z;
       a.req[b] = rp;
       a.pre_off[b] = run.x + ex.x;
-      a.merge_off[b] = run.w + ex.w;
+      // merge entries of the request's split (request, KV head) pairs
+      if (rp.nsplit > 1) {
+        int4* me = reinterpret_cast<int4*>(a.merges) + run.w + ex.w;
+        for (int kvh = 0; kvh < Hkv; ++kvh)
+          me[kvh] = int4{rp.slot0 + kvh * rp.nsplit, rp.nsplit | (rp.nq * G) << 16, rp.q0, kvh};
+      }
     }
     // Decode-mode items of this chunk of requests, written by all threads:
     // item i of the chunk belongs to the last request whose first item is at
@@ -988,7 +1005,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   }
   if (tid == 0) {
     a.pre_off[a.B] = run.x;
-    a.merge_off[a.B] = run.w;
     a.ctrl->n_pre = run.x;
     a.ctrl->n_items = run.x + run.y;
     a.ctrl->n_merge = run.w;
@@ -1001,7 +1017,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 // Merge of pa_forward's split decode rows.  One wave takes a (request, KV
 // head) pair whose rows were split and handles 4 rows at a time: 16 lanes per
 // row, each with D / 16 consecutive columns, folding the partitions in one
-// pass with a running log-sum-exp (max, rescaled weight sum, rescaled sum).
+// pass with a running log-sum-exp (max, rescaled weight sum, rescaled sum);
+// the loads of several partitions are in flight together.
 template <int D>
 __global__ __launch_bounds__(kThreads) void mha_forward_merge_kernel(MhaArgs a) {
   constexpr int NC = D / 16;
@@ -1010,54 +1027,45 @@ __global__ __launch_bounds__(kThreads) void mha_forward_merge_kernel(MhaArgs a) 
   const int n_merge = a.ctrl->n_merge;
   const int stride = gridDim.x * (kThreads / 64);
   for (int e = blockIdx.x * (kThreads / 64) + wv; e < n_merge; e += stride) {
-    const int b = find_request(a.merge_off, a.num_seqs, e);
-    const ReqPlan rp = a.req[b];
-    const int kvh = e - a.merge_off[b];
-    const int S = rp.nsplit;
-    const int slot0 = rp.slot0 + kvh * S;
-    const int nrows = rp.nq * a.G;
+    const int4 me = reinterpret_cast<const int4*>(a.merges)[e];
+    const int slot0 = me.x, S = me.y & 0xffff, nrows = me.y >> 16, q0 = me.z, kvh = me.w;
     for (int r0 = 0; r0 < nrows; r0 += 4) {
       const int row = r0 + rsub;
       if (row >= nrows) continue;
-      // partition weights: lane j of the row's 16 lanes holds partitions j, j + 16, ...
-      float M = kNegInf;
-      for (int sp = lane & 15; sp < S; sp += 16)
-        M = fmaxf(M, a.part_lse[(int64_t)(slot0 + sp) * kDecodeRows + row]);
-#pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+      float m = kNegInf, wsum = 0.f;
       float o[NC];
 #pragma unroll
       for (int c = 0; c < NC; ++c) o[c] = 0.f;
-      float wsum = 0.f;
-      if (M != kNegInf) {
-#pragma unroll 4
-        for (int sp = 0; sp < S; ++sp) {
-          const int64_t slot = slot0 + sp;
-          const float ls = a.part_lse[slot * kDecodeRows + row];
-          const floatx4* po = reinterpret_cast<const floatx4*>(a.part_o + (slot * kDecodeRows + row) * D + c0);
-          floatx4 v[NC / 4];
+#pragma unroll 8
+      for (int sp = 0; sp < S; ++sp) {
+        const int64_t slot = slot0 + sp;
+        const float ls = a.part_lse[slot * kDecodeRows + row];
+        const floatx4* po = reinterpret_cast<const floatx4*>(a.part_o + (slot * kDecodeRows + row) * D + c0);
+        floatx4 v[NC / 4];
 #pragma unroll
-          for (int c = 0; c < NC / 4; ++c) v[c] = po[c];  // finite for every written partition
-          const float w = ls == kNegInf ? 0.f : __expf(ls - M);
-          wsum += w;
+        for (int c = 0; c < NC / 4; ++c) v[c] = po[c];  // finite for every written partition
+        const float mn = fmaxf(m, ls);
+        const float f = mn == kNegInf ? 1.f : __expf(m - mn);   // rescale of the running sums
+        const float w = ls == kNegInf ? 0.f : __expf(ls - mn);  // weight of this partition
+        m = mn;
+        wsum = fmaf(wsum, f, w);
 #pragma unroll
-          for (int c = 0; c < NC / 4; ++c) {
-            o[4 * c] = fmaf(w, v[c][0], o[4 * c]);
-            o[4 * c + 1] = fmaf(w, v[c][1], o[4 * c + 1]);
-            o[4 * c + 2] = fmaf(w, v[c][2], o[4 * c + 2]);
-            o[4 * c + 3] = fmaf(w, v[c][3], o[4 * c + 3]);
-          }
+        for (int c = 0; c < NC / 4; ++c) {
+          o[4 * c] = fmaf(w, v[c][0], o[4 * c] * f);
+          o[4 * c + 1] = fmaf(w, v[c][1], o[4 * c + 1] * f);
+          o[4 * c + 2] = fmaf(w, v[c][2], o[4 * c + 2] * f);
+          o[4 * c + 3] = fmaf(w, v[c][3], o[4 * c + 3] * f);
         }
       }
       const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
       const int t = row / a.G;
-      const int64_t out_row = (int64_t)(rp.q0 + t) * a.Hq + kvh * a.G + (row - t * a.G);
+      const int64_t out_row = (int64_t)(q0 + t) * a.Hq + kvh * a.G + (row - t * a.G);
       __bf16* op = (__bf16*)a.out + out_row * D + c0;
 #pragma unroll
       for (int c = 0; c < NC; c += 4)
         *reinterpret_cast<u32x2*>(op + c) =
             u32x2{pack_bf16x2(o[c] * inv, o[c + 1] * inv), pack_bf16x2(o[c + 2] * inv, o[c + 3] * inv)};
-      if ((lane & 15) == 0 && a.lse) a.lse[out_row] = wsum > 0.f ? M + __logf(wsum) : kNegInf;
+      if ((lane & 15) == 0 && a.lse) a.lse[out_row] = wsum > 0.f ? m + __logf(wsum) : kNegInf;
     }
   }
 }
@@ -1123,8 +1131,8 @@ FwdWorkspace fwd_workspace_layout(int B, int T, int Hkv, int G, int D) {
   off = align(off + (size_t)(B + 1) * sizeof(int32_t));
   w.items_off = off;
   off = align(off + (size_t)w.cap_slots * kItemInts * sizeof(int32_t));
-  w.merge_off = off;
-  off = align(off + (size_t)(B + 1) * sizeof(int32_t));
+  w.merges_off = off;
+  off = align(off + (size_t)B * Hkv * 4 * sizeof(int32_t));
   w.plse_off = off;
   off = align(off + (size_t)w.cap_slots * kDecodeRows * sizeof(float));
   w.po_off = off;
