@@ -252,7 +252,7 @@ def main():
         del full, pre
 
     if not args.no_extra:
-        xsteps = max(3, args.steps // 3)
+        xsteps = max(10, args.steps // 2)
         # ---- long-context split-KV decode: 16 sequences, L ~ U[32K, 128K], 16 partitions
         lb = workload.llama_long(batch=16, device=dev)
         S = 16
@@ -266,7 +266,7 @@ def main():
                                max_seq_len=max(lb.seq_lens_list))
             pa.pa_merge_lse(po, pl, out=lo)
 
-        s_step_ms, s_kern_ms = time_steps(sstep, xsteps, 2, lib)
+        s_step_ms, s_kern_ms = time_steps(sstep, xsteps, 5, lib)
         sbytes = workload.algorithmic_bytes(lb)
         result["split_kv"] = {
             "workload": "Llama-3.1-8B-shaped long-context decode, 16 sequences, L~U[32768,131072], "
@@ -289,7 +289,7 @@ def main():
             pa.mla_decode(mb.q, mb.k_cache, mb.block_table, mb.seq_lens, mb.scale, out=mout,
                           workspace=mws, max_seq_len=max(mb.seq_lens_list))
 
-        m_step_ms, m_kern_ms = time_steps(mstep, xsteps, 2, lib)
+        m_step_ms, m_kern_ms = time_steps(mstep, xsteps, 5, lib)
         mbytes = workload.algorithmic_bytes(mb)
         mflops = workload.algorithmic_flops(mb)
         result["mla"] = {

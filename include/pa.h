@@ -175,10 +175,15 @@ PA_API size_t mla_workspace_size(const pa_dims* dims, int32_t num_splits);
  *   q        bf16 [B, Hq, 576]
  *   kv_cache bf16 [num_pages, P, 576]
  *   out      bf16 [B, Hq, 512];  lse float32 [B, Hq] or NULL
- * The keys of each request are split into num_splits page-aligned partitions
- * (as in pa_decode_split; 0 picks a count from B and the capacities) and
- * merged by log-sum-exp.  Requires bf16, Hkv == 1, Dqk == 576, Dv == 512,
- * Hq a multiple of 16 up to 128, P a power of two in [8, 256], seq_len >= 1.
+ * num_splits > 0: the keys of each request are split into num_splits
+ * page-aligned partitions (as in pa_decode_split), one workgroup each, and
+ * merged by log-sum-exp.  num_splits == 0 (the default): balanced schedule;
+ * every request is cut into pieces of at most c key tiles of 32, c chosen on
+ * the device from seq_lens so that all pieces run at once, one per compute
+ * unit, whatever the length mix; requests in several pieces are merged by
+ * log-sum-exp ([TDD] section "Parallel tiled softmax (3D kernel)").
+ * Requires bf16, Hkv == 1, Dqk == 576, Dv == 512, Hq a multiple of 16 up to
+ * 128, P a power of two in [8, 256], seq_len >= 1.
  */
 PA_API pa_status mla_decode(const void* q, const void* kv_cache, const int32_t* block_table,
                      const int32_t* seq_lens, float scale, void* out, float* lse,

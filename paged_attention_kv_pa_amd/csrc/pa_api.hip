@@ -85,12 +85,20 @@ pa_status check_mha_support(const pa_dims* d) {
   return PA_OK;
 }
 
-int mla_auto_splits(const pa_dims* d, int cu_count) {
-  const int B = std::max(1, d->num_seqs);
-  int s = (2 * cu_count + B - 1) / B;
-  const int max_pages = (d->max_seq_len + d->page_size - 1) / d->page_size;
-  s = std::min(s, std::max(1, max_pages));
-  return std::max(1, std::min(s, 64));
+// Balanced schedule with at most `pieces` split pieces: partial log-sum-exps
+// [pieces, Hq], merge info [B, 2], partial rows [pieces, Hq, 512].
+struct MlaBalancedWs {
+  size_t lse_off, info_off, po_off, total;
+};
+MlaBalancedWs mla_balanced_ws(const pa_dims* d, int pieces) {
+  auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t slots = (size_t)pieces * d->num_q_heads;
+  MlaBalancedWs w;
+  w.lse_off = 0;
+  w.info_off = align(slots * sizeof(float));
+  w.po_off = w.info_off + align((size_t)2 * d->num_seqs * sizeof(int32_t));
+  w.total = w.po_off + slots * 512 * sizeof(float);
+  return w;
 }
 
 size_t mla_ws_bytes(const pa_dims* d, int S) {
@@ -333,13 +341,12 @@ pa_status pa_merge_lse(const float* part_out, const float* part_lse, int32_t num
 
 size_t mla_workspace_size(const pa_dims* d, int32_t num_splits) {
   if (check_mla(d) != PA_OK || num_splits < 0 || num_splits > 64) return 0;
-  int S = num_splits;
-  if (S == 0) {
+  if (num_splits == 0) {
     DevCfg cfg;
     if (device_config(&cfg) != PA_OK) return 0;
-    S = mla_auto_splits(d, cfg.cu_count);
+    return mla_balanced_ws(d, cfg.cu_count).total;
   }
-  return mla_ws_bytes(d, S);
+  return mla_ws_bytes(d, num_splits);
 }
 
 pa_status mla_decode(const void* q, const void* kv_cache, const int32_t* block_table,
@@ -351,13 +358,40 @@ pa_status mla_decode(const void* q, const void* kv_cache, const int32_t* block_t
   if (!q || !kv_cache || !block_table || !seq_lens || !out) return PA_ERR_INVALID_ARG;
   if (num_splits < 0 || num_splits > 64) return PA_ERR_INVALID_ARG;
   if (d->num_seqs == 0) return PA_OK;
-  int S = num_splits;
-  if (S == 0) {
+  hipStream_t s = (hipStream_t)stream;
+  if (num_splits == 0) {
+    // balanced schedule: one workgroup per compute unit
     DevCfg cfg;
     st = device_config(&cfg);
     if (st != PA_OK) return st;
-    S = mla_auto_splits(d, cfg.cu_count);
+    const MlaBalancedWs w = mla_balanced_ws(d, cfg.cu_count);
+    if (!workspace || workspace_bytes < w.total) return PA_ERR_WORKSPACE;
+    char* ws = (char*)workspace;
+    pa::MlaArgs a{};
+    a.q = q;
+    a.kv = kv_cache;
+    a.block_table = block_table;
+    a.seq_lens = seq_lens;
+    a.out = out;
+    a.lse = lse;
+    a.part_lse = (float*)(ws + w.lse_off);
+    a.merge_info = (int32_t*)(ws + w.info_off);
+    a.part_o = (float*)(ws + w.po_off);
+    a.scale = scale;
+    a.B = d->num_seqs;
+    a.Hq = d->num_q_heads;
+    a.P = d->page_size;
+    a.log2_page = __builtin_ctz((unsigned)d->page_size);
+    a.max_pages = d->max_pages_per_seq;
+    a.num_splits = 0;
+    a.max_pieces = cfg.cu_count;
+    hipError_t e = mark(g_ev_start, s);
+    if (e == hipSuccess) e = pa::launch_mla_balanced(a, std::max(cfg.cu_count, d->num_seqs), s);
+    if (e == hipSuccess) e = mark(g_ev_stop, s);
+    if (e == hipSuccess) e = pa::launch_mla_balanced_merge(a, s);
+    return e == hipSuccess ? PA_OK : hip_fail(e);
   }
+  const int S = num_splits;
   if ((int64_t)d->num_seqs * S > INT32_MAX) return PA_ERR_INVALID_ARG;
   const size_t need = mla_ws_bytes(d, S);
   if (S > 1 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
@@ -379,7 +413,6 @@ pa_status mla_decode(const void* q, const void* kv_cache, const int32_t* block_t
   a.log2_page = __builtin_ctz((unsigned)d->page_size);
   a.max_pages = d->max_pages_per_seq;
   a.num_splits = S;
-  hipStream_t s = (hipStream_t)stream;
   hipError_t e = mark(g_ev_start, s);
   if (e == hipSuccess) e = pa::launch_mla_split(a, s);
   if (e == hipSuccess) e = mark(g_ev_stop, s);

@@ -82,10 +82,12 @@ struct MlaArgs {
   const int32_t* seq_lens;
   void* out;                 // bf16 [B, Hq, 512] (num_splits == 1)
   float* lse;
-  float* part_o;             // [B, Hq, S, 512] (num_splits > 1)
-  float* part_lse;           // [B, Hq, S]
+  float* part_o;             // [B, Hq, S, 512] (num_splits > 1); balanced: [max_pieces, Hq, 512]
+  float* part_lse;           // [B, Hq, S]; balanced: [max_pieces, Hq]
+  int32_t* merge_info;       // balanced: [B, 2] first partial slot and piece count of each request
   float scale;
   int32_t B, Hq, P, log2_page, max_pages, num_splits;
+  int32_t max_pieces;        // balanced: pieces that run at once (one workgroup per compute unit)
 };
 
 // Device properties cached per device by the ABI layer.
@@ -112,5 +114,7 @@ hipError_t launch_merge(const float* po, const float* pl, int rows, int S, int D
 hipError_t launch_f32_forward(const F32Args& a, hipStream_t s);
 hipError_t launch_f32_split(const F32Args& a, hipStream_t s);
 hipError_t launch_mla_split(const MlaArgs& a, hipStream_t s);
+hipError_t launch_mla_balanced(const MlaArgs& a, int grid, hipStream_t s);
+hipError_t launch_mla_balanced_merge(const MlaArgs& a, hipStream_t s);
 
 }  // namespace pa

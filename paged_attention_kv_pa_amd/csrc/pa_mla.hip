@@ -29,6 +29,8 @@
 //     accumulator (256 registers per lane) is rarely touched by vector ALUs.
 // The keys of a request are cut into page-aligned partitions, one workgroup
 // each, combined by the log-sum-exp merge in a second launch.
+#include <atomic>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -89,19 +91,17 @@ __device__ __forceinline__ int kperm32(int m) {
   return 16 * (q >> 1) + 8 * h + 4 * (q & 1) + w;
 }
 
-__global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
-  extern __shared__ __align__(16) char mla_smem[];
+// Keys [t0k, t1k) of request b for all its heads, by one workgroup.  The
+// result rows go to the output (pbase < 0) or, normalised, to the partial
+// rows part_o / part_lse at index pbase + head * pstride.  Every thread of
+// the workgroup calls this together; LDS is free on entry and on return.
+__device__ __forceinline__ void mla_keys(const MlaArgs& a, char* mla_smem, int tid, int b,
+                                         int t0k, int t1k, int64_t pbase, int pstride) {
   constexpr int KS = kDqk / 16;  // 36 K-steps of S^T
   constexpr int DT = kDv / 32;   // 16 column tiles of O^T
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wave = tid >> 6, lane = tid & 63;
   const int n = lane & 31, h = lane >> 5;
-  const int S = a.num_splits;
-  const int s = blockIdx.x % S, b = blockIdx.x / S;
-  const int L = a.seq_lens[b], P = a.P, lp = a.log2_page;
-  const int pages = (L + P - 1) >> lp;
-  const long long per = (long long)P * ((pages + S - 1) / S);
-  const long long a0 = per * s, a1 = a0 + per;
-  const int t0k = a0 < L ? (int)a0 : L, t1k = a1 < L ? (int)a1 : L;
+  const int P = a.P, lp = a.log2_page;
   const int ntiles = (t1k - t0k + kMTK - 1) / kMTK;
 
   // The block table is read-only for the whole call: reading it through the
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
   const float inv = lrow > 0.f ? 1.f / lrow : 0.f;
   const float lse = lrow > 0.f ? m * a.scale + __log2f(lrow) * kLn2 : kNegInf;
   const int64_t bh = (int64_t)b * a.Hq + head;
-  if (S == 1) {
+  if (pbase < 0) {
     __bf16* op = (__bf16*)a.out + bh * kDv + 4 * h;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -325,7 +325,8 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
                   pack_bf16x2(acc[dt][4 * q + 2] * inv, acc[dt][4 * q + 3] * inv)};
     if (h == 0 && a.lse) a.lse[bh] = lse;
   } else {
-    float* op = a.part_o + (bh * S + s) * kDv + 4 * h;
+    const int64_t pi = pbase + (int64_t)head * pstride;
+    float* op = a.part_o + pi * kDv + 4 * h;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -334,18 +335,219 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
                 __builtin_bit_cast(u32x4, floatx4{acc[dt][4 * q] * inv, acc[dt][4 * q + 1] * inv,
                                                   acc[dt][4 * q + 2] * inv,
                                                   acc[dt][4 * q + 3] * inv}));
-    if (h == 0) a.part_lse[bh * S + s] = lse;
+    if (h == 0) a.part_lse[pi] = lse;
   }
 }
 
+// pa_decode_split-style partitions: workgroup (b, s) takes the s-th of
+// num_splits page-aligned key ranges of request b.
+__global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
+  extern __shared__ __align__(16) char mla_smem[];
+  const int S = a.num_splits;
+  const int s = blockIdx.x % S, b = blockIdx.x / S;
+  const int L = a.seq_lens[b], P = a.P;
+  const int pages = (L + P - 1) >> a.log2_page;
+  const long long per = (long long)P * ((pages + S - 1) / S);
+  const long long a0 = per * s, a1 = a0 + per;
+  const int t0k = a0 < L ? (int)a0 : L, t1k = a1 < L ? (int)a1 : L;
+  mla_keys(a, mla_smem, threadIdx.x, b, t0k, t1k, S > 1 ? (int64_t)b * a.Hq * S + s : -1, S);
+}
+
+// Tiles a request contributes to the balanced schedule (an empty request
+// still gets one, so that its zero output is written).
+__device__ __forceinline__ int mla_tiles(int L) { return L > kMTK ? (L + kMTK - 1) / kMTK : 1; }
+
+// Sum / maximum over the workgroup (every thread gets the result).
+__device__ __forceinline__ long long mla_block_sum(long long v, long long* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  __syncthreads();  // red is free
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  long long t = 0;
+#pragma unroll
+  for (int w = 0; w < kMlaThreads / 64; ++w) t += red[w];
+  return t;
+}
+
+__device__ __forceinline__ long long mla_block_max(long long v, long long* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  long long t = 0;
+#pragma unroll
+  for (int w = 0; w < kMlaThreads / 64; ++w) t = max(t, red[w]);
+  return t;
+}
+
+// Balanced schedule: every request is cut into pieces of at most c key tiles
+// (the last piece of a request may be shorter), c being the smallest cap the
+// search below finds for which all pieces fit in max_pieces workgroups (one
+// per compute unit), so that every workgroup streams at most c tiles whatever
+// the length mix.  Workgroup w takes piece w in request order; a request in
+// several pieces is finished by the merge kernel from the partial rows in
+// slots w0 .. w0 + n - 1, recorded in merge_info[2b] = w0, [2b + 1] = n.
+// When the requests outnumber the workgroups every request is one piece.
+// Each workgroup recomputes the (small) schedule from seq_lens.
+__global__ __launch_bounds__(kMlaThreads) void mla_balanced_kernel(MlaArgs a) {
+  extern __shared__ __align__(16) char mla_smem[];
+  __shared__ long long s_red[kMlaThreads / 64];
+  __shared__ int s_b, s_j, s_n;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const long long G = a.max_pieces;
+  long long T = 0, tmax = 1;
+  for (int b = tid; b < a.B; b += kMlaThreads) {
+    const long long t = mla_tiles(a.seq_lens[b]);
+    T += t;
+    tmax = max(tmax, t);
+  }
+  T = mla_block_sum(T, s_red);
+  tmax = mla_block_max(tmax, s_red);
+  // smallest cap found: start at the even share and raise it by the rounding
+  // overhead the last count showed (a handful of rounds)
+  long long c = (T + G - 1) / G;
+  if (c < 1) c = 1;
+  bool fits = false;
+  for (int round = 0; round < 32 && c < tmax; ++round) {
+    long long n = 0;
+    for (int b = tid; b < a.B; b += kMlaThreads) n += (mla_tiles(a.seq_lens[b]) + c - 1) / c;
+    n = mla_block_sum(n, s_red);
+    if (n <= G) {
+      fits = true;
+      break;
+    }
+    const long long extra = n - (T + c - 1) / c;
+    const long long next = G > extra ? (T + G - extra - 1) / (G - extra) : tmax;
+    c = next > c + 1 ? next : c + 1;
+  }
+  // no cap below the longest request found: one piece per request, none split
+  if (!fits || c > tmax) c = tmax;
+  // piece blockIdx.x: scan the per-request piece counts chunk by chunk
+  const long long w = blockIdx.x;
+  if (tid == 0) s_b = -1;
+  long long run = 0;
+  for (int base = 0; base < a.B; base += kMlaThreads) {
+    const int b = base + tid;
+    const long long n = b < a.B ? (mla_tiles(a.seq_lens[b]) + c - 1) / c : 0;
+    long long incl = n;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const long long y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    __syncthreads();  // s_red is free
+    if (lane == 63) s_red[wave] = incl;
+    __syncthreads();
+    long long before = run, tot = 0;
+#pragma unroll
+    for (int v = 0; v < kMlaThreads / 64; ++v) {
+      if (v < wave) before += s_red[v];
+      tot += s_red[v];
+    }
+    const long long ex = before + incl - n;
+    if (n > 0 && ex <= w && w < ex + n) {
+      s_b = b;
+      s_j = (int)(w - ex);
+      s_n = (int)n;
+    }
+    run += tot;
+    if (run > w) break;  // uniform
+  }
+  __syncthreads();
+  const int b = s_b;
+  if (b < 0) return;  // no piece left for this workgroup
+  const int j = s_j, n = s_n;
+  const int L = a.seq_lens[b];
+  const long long k0 = (long long)j * c * kMTK, k1 = k0 + c * kMTK;
+  const int t0k = k0 < L ? (int)k0 : L, t1k = k1 < L ? (int)k1 : L;
+  if (tid == 0 && j == 0) {
+    a.merge_info[2 * b] = (int)w;
+    a.merge_info[2 * b + 1] = n;
+  }
+  mla_keys(a, mla_smem, threadIdx.x, b, t0k, t1k, n > 1 ? w * (int64_t)a.Hq : -1, 1);
+}
+
+// Rows of the requests the balanced schedule cut: workgroup (b, 16 heads),
+// 16 lanes per row with 32 columns each, folding the pieces' partial rows
+// with a running log-sum-exp.
+__global__ __launch_bounds__(kMlaThreads) void mla_balanced_merge_kernel(MlaArgs a) {
+  const int hg_count = a.Hq / 16;
+  const int b = blockIdx.x / hg_count, hg = blockIdx.x % hg_count;
+  const int w0 = a.merge_info[2 * b], np = a.merge_info[2 * b + 1];
+  if (np <= 1) return;  // written whole by one workgroup
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int head = 16 * hg + 4 * wave + (lane >> 4);
+  const int c0 = (lane & 15) * 32;
+  float m = kNegInf, wsum = 0.f;
+  float o[32];
+#pragma unroll
+  for (int c = 0; c < 32; ++c) o[c] = 0.f;
+  for (int i = 0; i < np; ++i) {
+    const int64_t pi = (int64_t)(w0 + i) * a.Hq + head;
+    const float ls = a.part_lse[pi];
+    const floatx4* po = reinterpret_cast<const floatx4*>(a.part_o + pi * kDv + c0);
+    floatx4 v[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v[c] = po[c];
+    const float mn = fmaxf(m, ls);
+    const float f = mn == kNegInf ? 1.f : __expf(m - mn);
+    const float wt = ls == kNegInf ? 0.f : __expf(ls - mn);
+    m = mn;
+    wsum = fmaf(wsum, f, wt);
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[4 * c + e] = fmaf(wt, v[c][e], o[4 * c + e] * f);
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  const int64_t bh = (int64_t)b * a.Hq + head;
+  __bf16* op = (__bf16*)a.out + bh * kDv + c0;
+#pragma unroll
+  for (int c = 0; c < 32; c += 8)
+    store16(op + c, u32x4{pack_bf16x2(o[c] * inv, o[c + 1] * inv), pack_bf16x2(o[c + 2] * inv, o[c + 3] * inv),
+                          pack_bf16x2(o[c + 4] * inv, o[c + 5] * inv), pack_bf16x2(o[c + 6] * inv, o[c + 7] * inv)});
+  if ((lane & 15) == 0 && a.lse) a.lse[bh] = wsum > 0.f ? m + __logf(wsum) : kNegInf;
+}
+
+// Raises a kernel's dynamic-LDS limit once per device (a host-side runtime
+// call that need not be repeated on every launch).
+hipError_t allow_lds_once(const void* kernel, std::atomic<uint64_t>& done, size_t lds) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = 1ull << (dev & 63);
+  if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e == hipSuccess) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
+
+std::atomic<uint64_t> g_lds_balanced{0}, g_lds_split{0};
+
 }  // namespace
+
+hipError_t launch_mla_balanced(const MlaArgs& a, int grid, hipStream_t s) {
+  if (a.B <= 0 || grid <= 0) return hipSuccess;
+  const size_t lds = (size_t)kStages * kStageBytes + kQLdsBytes;
+  hipError_t e = allow_lds_once((const void*)mla_balanced_kernel, g_lds_balanced, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(mla_balanced_kernel, dim3(grid), dim3(kMlaThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_mla_balanced_merge(const MlaArgs& a, hipStream_t s) {
+  if (a.B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(mla_balanced_merge_kernel, dim3(a.B * (a.Hq / 16)), dim3(kMlaThreads), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_mla_split(const MlaArgs& a, hipStream_t s) {
   const int64_t blocks = (int64_t)a.B * a.num_splits;
   if (blocks <= 0) return hipSuccess;
   const size_t lds = (size_t)kStages * kStageBytes + kQLdsBytes;
-  hipError_t e = hipFuncSetAttribute((const void*)mla_split_kernel,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e = allow_lds_once((const void*)mla_split_kernel, g_lds_split, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(mla_split_kernel, dim3(blocks), dim3(kMlaThreads), lds, s, a);
   return hipGetLastError();

@@ -222,6 +222,23 @@ def test_mla_scaled(S):
     mla_parity(b, "mla scaled", S=S)
 
 
+def test_mla_balanced_many_short_requests():
+    # more tiles than workgroups: ranges hold several requests, some cut in two
+    b = workload.deepseek_mla(2, batch=600, lo=1, hi=40)
+    mla_parity(b, "mla balanced, 600 short requests", S=0)
+
+
+@pytest.mark.parametrize("page,heads", [(16, 64), (8, 16), (256, 128)])
+def test_mla_balanced_pages_and_heads(page, heads):
+    # fewer tiles than workgroups: most requests spread over several workgroups
+    lens = [1, 33, 700, 5, 2000, 64, 63, 32, 31]
+    b = workload.make_batch([1] * len(lens), [x - 1 for x in lens], num_q_heads=heads,
+                            num_kv_heads=1, head_dim_qk=576, head_dim_v=512, page_size=page,
+                            dtype=torch.bfloat16, layout="mla", scale=1.0 / math.sqrt(192.0),
+                            seed=41 + page, name="mla_pages")
+    mla_parity(b, "mla balanced page %d heads %d" % (page, heads), S=0)
+
+
 def test_mla_full_size_sampled_heads():
     b = workload.deepseek_mla(0)
     mla_parity(b, "mla full (heads 0,1,37,64,127)", heads=[0, 1, 37, 64, 127])
