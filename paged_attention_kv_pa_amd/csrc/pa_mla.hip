@@ -57,6 +57,7 @@ constexpr int kQLdsBytes = 128 * kQLdsStride;
 
 typedef __attribute__((ext_vector_type(4))) short short4v;
 typedef __attribute__((address_space(3))) short4v lds_short4;
+typedef __attribute__((address_space(3))) const char lds_cchar;
 
 // Swizzle of the chunk index inside its group of 8, by key.
 __device__ __forceinline__ int swz(int k) { return (k >> 1) & 7; }
@@ -144,6 +145,7 @@ __device__ __forceinline__ void mla_keys(const MlaArgs& a, char* mla_smem, int t
   const int head = 32 * wave + n;
   const bool row_ok = head < a.Hq;
   char* qlds = mla_smem + kStages * kStageBytes;
+  lds_cchar* qlds3 = (lds_cchar*)mla_smem + kStages * kStageBytes;
   bf16x8 qf[kQRegSteps];  // B operand of S^T: Q[head][16 ks + 8h .. +7]
   {
     const __bf16* qp = (const __bf16*)a.q + ((int64_t)b * a.Hq + head) * kDqk + 8 * h;
@@ -197,7 +199,9 @@ __device__ __forceinline__ void mla_keys(const MlaArgs& a, char* mla_smem, int t
     __syncthreads();  // tile ti is in LDS; stage (ti + 2) % 3 is no longer read
     if (ti + 2 < ntiles) issue_tile(ti + 2, (ti + 2) % kStages);
     const int t0 = t0k + ti * kMTK;
-    const char* stage = mla_smem + (ti % kStages) * kStageBytes;
+    // the stage as an LDS address: operand addresses stay 32-bit and their
+    // constant parts fold into the instructions' offsets
+    lds_cchar* stage = (lds_cchar*)mla_smem + (ti % kStages) * kStageBytes;
 
     // S^T (two accumulation chains: even / odd K-steps)
     floatx16 sa, sb;
@@ -207,11 +211,14 @@ __device__ __forceinline__ void mla_keys(const MlaArgs& a, char* mla_smem, int t
     // hand: left alone, the scheduler sinks each read next to its use)
     constexpr int kAhead = 2;
     auto kread = [&](int ks) {  // chunk 2 ks + h lives in group (2 ks + h) >> 3 = ks >> 2
-      return as_bf16x8(*reinterpret_cast<const u32x4*>(stage + koff[ks & 3] + (ks >> 2) * (kMTK * 8 * 16)));
+      const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+          stage + koff[ks & 3] + (ks >> 2) * (kMTK * 8 * 16));
+      return as_bf16x8(v);
     };
     auto qread = [&](int ks) {
-      return as_bf16x8(*reinterpret_cast<const u32x4*>(
-          qlds + head * kQLdsStride + (16 * (ks - kQRegSteps) + 8 * h) * 2));
+      const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+          qlds3 + head * kQLdsStride + (16 * (ks - kQRegSteps) + 8 * h) * 2);
+      return as_bf16x8(v);
     };
     bf16x8 kbuf[kAhead], qbuf[kAhead];
 #pragma unroll
@@ -234,9 +241,13 @@ __device__ __forceinline__ void mla_keys(const MlaArgs& a, char* mla_smem, int t
     // lane holds S[head][key] for keys 8h + v (v < 8) and 16 + 8h + (v - 8)
     float x[16];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int key = t0 + (v < 8 ? 8 * h + v : 16 + 8 * h + (v - 8));
-      x[v] = key < t1k ? sa[v] + sb[v] : kNegInf;
+    for (int v = 0; v < 16; ++v) x[v] = sa[v] + sb[v];
+    if (t0 + kMTK > t1k) {  // the last tile of the range: mask the keys past its end
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = t0 + (v < 8 ? 8 * h + v : 16 + 8 * h + (v - 8));
+        x[v] = key < t1k ? x[v] : kNegInf;
+      }
     }
     float tmax = x[0];
 #pragma unroll
