@@ -51,6 +51,17 @@ __device__ __forceinline__ void lds_dma16(const void* gsrc, const void* lds_wave
                : "memory", "m0");
 }
 
+// A pointer every lane holds the same value of, made visibly uniform (scalar
+// registers): loads through it with uniform indices become scalar loads,
+// which the copy waits do not count.
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Wait until at most N vector-memory operations of this wave are in flight.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

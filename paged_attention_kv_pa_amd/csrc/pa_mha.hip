@@ -351,7 +351,7 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
   using LY = PrefillLayout<D>;
   constexpr int KS = D / 16, DT = D / 32, NST = LY::kStages;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 31, h = lane >> 5;
-  const int G = a.G, P = a.P;
+  const int G = __builtin_amdgcn_readfirstlane(a.G), P = __builtin_amdgcn_readfirstlane(a.P);
   // item fields are workgroup-uniform: keep them in scalar registers so that
   // block-table reads become scalar loads
   const int b = __builtin_amdgcn_readfirstlane(it.seq);
@@ -398,10 +398,12 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
   for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qf[ks]));
   wait_vmcnt<0>();
 
-  const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
-  const int64_t page_elems = (int64_t)a.Hkv * P * D;
-  const char* kbase = (const char*)((const __bf16*)a.k_cache + (int64_t)kvh * P * D);
-  const char* vbase = (const char*)((const __bf16*)a.v_cache + (int64_t)kvh * D * P);
+  // (the arguments may live in vector registers here: the kernel also makes
+  // a real call with them; make the bases visibly uniform)
+  const int32_t* bt = uniform_ptr(a.block_table + (int64_t)b * a.max_pages);
+  const int64_t page_elems = (int64_t)__builtin_amdgcn_readfirstlane(a.Hkv * P * D);
+  const char* kbase = uniform_ptr((const char*)((const __bf16*)a.k_cache + (int64_t)kvh * P * D));
+  const char* vbase = uniform_ptr((const char*)((const __bf16*)a.v_cache + (int64_t)kvh * D * P));
 
   // Wave w copies, of each 64-key tile, half of the column chunks of K (the
   // half w & 1) for the 16 keys of group w / 2, and V^T of the 8-key chunk w.  Its
