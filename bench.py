@@ -124,6 +124,60 @@ def cpu_baseline(b, nbytes):
             "sample": "the whole timed batch (64 decode requests), %d pass(es), %.2f s each" % (reps, per)}
 
 
+def small_decode_cases(torch, pa, workload, dev, args, layers=32):
+    """Per-call time of the small Llama decode cases, replayed from a graph of
+    `layers` pa_forward calls that each read their own KV-cache copy."""
+    res = []
+    for case, name in ((0, "B1 L500"), (1, "B64 L500"), (2, "B1 L~U[500,8192]")):
+        b = workload.llama_decode(case, device=dev)
+        T, Hq = b.num_tokens, b.num_q_heads
+        maxL, maxq = max(b.seq_lens_list), max(b.q_lens)
+        kcs = [b.k_cache] + [b.k_cache.clone() for _ in range(layers - 1)]
+        vcs = [b.v_cache] + [b.v_cache.clone() for _ in range(layers - 1)]
+        outs = [torch.empty(T, Hq, b.head_dim_v, dtype=b.dtype, device=dev) for _ in range(layers)]
+        dims = pa.make_dims(b.q, b.k_cache, b.v_cache, b.block_table, b.seq_lens, T,
+                            max_seq_len=maxL, max_q_len=maxq)
+        ws = torch.empty(pa.pa_workspace_size(dims), dtype=torch.uint8, device=dev)
+
+        def step():
+            for i in range(layers):
+                pa.pa_forward(b.q, kcs[i], vcs[i], b.block_table, b.seq_lens, b.query_start_loc,
+                              b.scale, out=outs[i], workspace=ws, max_seq_len=maxL, max_q_len=maxq)
+
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()  # warm-up outside the capture
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        reps = max(5, args.steps // 3)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        per_call_ms = e0.elapsed_time(e1) / reps / layers
+        nbytes = workload.algorithmic_bytes(b)
+        kv_replay = 2 * b.k_cache.numel() * b.k_cache.element_size() * layers
+        res.append({"case": name, "us_per_call": round(per_call_ms * 1e3, 2),
+                    "gbs": round(nbytes / (per_call_ms * 1e-3) / 1e9, 1),
+                    "algorithmic_bytes": nbytes,
+                    # below 256 MB a replay's KV fits in the last-level cache
+                    "kv_bytes_per_replay": kv_replay})
+        del graph, kcs, vcs, outs, ws
+    return {"workload": "Llama-3.1-8B-shaped decode, small cases; each a graph of %d pa_forward "
+                        "calls over %d distinct KV-cache copies, time per call" % (layers, layers),
+            "cases": res}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -208,6 +262,12 @@ def main():
     }
     del ws, out, lse
     b_host_needed = not args.no_cpu_baseline
+
+    # ---- the small decode cases, each as one captured graph of 32 calls over
+    # 32 distinct copies of the KV cache (one decode step of a 32-layer model:
+    # every call reads KV that no earlier call of the replay touched)
+    if not args.no_extra:
+        result["small_decode"] = small_decode_cases(torch, pa, workload, dev, args)
 
     # ---- prefill half of the metric: the prefill + extend requests of the Qwen3-235B
     # mixed batch (requests 48..63), and the whole mixed batch in one call
