@@ -226,8 +226,11 @@ pa_status pa_forward(const void* q, const void* k_cache, const void* v_cache,
   pl.P = d->page_size;
   pl.max_pages = d->max_pages_per_seq;
   pl.target_items = std::max(1, pa::kItemsPerWorkgroup * grid);
-  hipError_t e = pa::launch_plan(pl, s);
-  if (e != hipSuccess) return hip_fail(e);
+  // decode-only calls of up to kFusedPlanMax requests: the persistent kernel
+  // plans itself and only a counter reset precedes it
+  const bool fused = decode_only && d->num_seqs <= pa::kFusedPlanMax;
+  hipError_t e = hipSuccess;
+  if (!fused && (e = pa::launch_plan(pl, s)) != hipSuccess) return hip_fail(e);
 
   pa::MhaArgs a{};
   a.q = q;
@@ -253,8 +256,11 @@ pa_status pa_forward(const void* q, const void* k_cache, const void* v_cache,
   a.P = d->page_size;
   a.max_pages = d->max_pages_per_seq;
   a.num_splits = 1;
+  a.target_items = pl.target_items;
+  if (fused && (e = pa::launch_reset_queue(ctrl, s)) != hipSuccess) return hip_fail(e);
   if ((e = mark(g_ev_start, s)) != hipSuccess) return hip_fail(e);
-  e = pa::launch_mha_forward(a, D, decode_only, grid, s);
+  e = fused ? pa::launch_mha_forward_fused(a, D, grid, s)
+            : pa::launch_mha_forward(a, D, decode_only, grid, s);
   if (e != hipSuccess) return hip_fail(e);
   if ((e = mark(g_ev_stop, s)) != hipSuccess) return hip_fail(e);
   e = pa::launch_mha_forward_merge(a, D, std::max(1, cfg.cu_count * 2), s);

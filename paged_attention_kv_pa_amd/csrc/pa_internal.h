@@ -24,6 +24,7 @@ constexpr int kTailDivisor = 2;        // ... get decode partitions kTailDivisor
 constexpr int kItemsPerWorkgroup = 4;  // decode work is cut into ~this many items per workgroup
 constexpr int kMaxSplits = 256;        // pa_decode_split / pa_merge_lse / mla_decode limit
 constexpr int kItemInts = 12;          // int32 words of one pa_forward work item
+constexpr int kFusedPlanMax = 1024;    // decode-only calls up to this many requests plan in-kernel
 
 struct MhaArgs {
   const void* q;
@@ -45,6 +46,7 @@ struct MhaArgs {
   int32_t num_seqs;
   int32_t Hq, Hkv, G, P, max_pages;
   int32_t num_splits;        // pa_decode_split only
+  int32_t target_items;      // pa_forward decode-only calls planned in the kernel
 };
 
 struct PlanArgs {
@@ -106,6 +108,8 @@ FwdWorkspace fwd_workspace_layout(int B, int T, int Hkv, int G, int D);
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_mha_forward(const MhaArgs& a, int D, bool decode_only, int grid, hipStream_t s);
+hipError_t launch_mha_forward_fused(const MhaArgs& a, int D, int grid, hipStream_t s);
+hipError_t launch_reset_queue(Control* ctrl, hipStream_t s);
 hipError_t launch_mha_forward_merge(const MhaArgs& a, int D, int grid, hipStream_t s);
 hipError_t launch_mha_split(const MhaArgs& a, int D, hipStream_t s);
 hipError_t mha_occupancy(int D, bool decode_only, int* blocks_per_cu);

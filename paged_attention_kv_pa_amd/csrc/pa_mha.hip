@@ -707,6 +707,171 @@ __device__ __noinline__ int run_decode_item_outlined(const MhaArgs& a, const Wor
   return run_decode_item<D, kPrefillWaves>(a, it, dst, sm, counter);
 }
 
+// ---------------------------------------------------------------------------
+// Work planning rules shared by the planner kernel and the persistent
+// kernel's own planning (decode-only calls of up to kFusedPlanMax requests).
+// ---------------------------------------------------------------------------
+// New-token count, key count and first query row of request b.  Requests
+// whose lengths are inconsistent (seq_len < q_len, or no key) get no work;
+// seq_len is capped at the block-table capacity so no item can index past a
+// table row.
+__device__ __forceinline__ void shape_of(const int32_t* qsl, const int32_t* seq_lens,
+                                         int max_pages, int P, int b, int* nq, int* L, int* q0) {
+  *q0 = qsl[b];
+  int q = qsl[b + 1] - *q0;
+  int l = seq_lens[b];
+  const long long cap = (long long)max_pages * P;
+  if (l > cap) l = (int)cap;
+  if (q < 0 || l < q || l < 1) q = 0;
+  *nq = q;
+  *L = l;
+}
+
+// Keys per decode partition: the decode work (keys x KV heads) spread over
+// about target_items items, at least kMinChunk keys, a multiple of 64.
+__device__ __forceinline__ long long decode_chunk(unsigned long long dec_keys, int Hkv,
+                                                  int target_items) {
+  const unsigned long long work = dec_keys * (unsigned long long)Hkv;
+  long long chunk = (long long)((work + target_items - 1) / (unsigned long long)target_items);
+  chunk = chunk < kMinChunk ? kMinChunk : chunk;
+  return (chunk + 63) & ~63LL;
+}
+
+// Partitions of a decode-mode request of L keys.  Items are handed out in
+// request order, so the last requests' items run last: cutting those finer
+// shortens the tail where workgroups finish at different times (the extra
+// partial rows stay few).
+__device__ __forceinline__ void decode_split(int L, long long chunk, bool tail, int* per,
+                                             int* nsplit) {
+  long long ck = chunk;
+  if (tail) {
+    ck = (chunk / kTailDivisor + 63) & ~63LL;
+    ck = ck < kMinChunk ? kMinChunk : ck;
+  }
+  long long sp = (L + ck - 1) / ck;
+  sp = sp < 1 ? 1 : (sp > kMaxFwdSplits ? kMaxFwdSplits : sp);
+  *per = 64 * (int)(((L + 63) / 64 + sp - 1) / sp);
+  *nsplit = (L + *per - 1) / *per;
+}
+
+__device__ __forceinline__ bool is_tail_request(int b, int B) { return b >= B - B / kTailFraction; }
+
+__device__ __forceinline__ int4 wave_inclusive_scan4(int4 v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int4 u = int4{__shfl_up(v.x, o), __shfl_up(v.y, o), __shfl_up(v.z, o), __shfl_up(v.w, o)};
+    if (lane >= o) v = int4{v.x + u.x, v.y + u.y, v.z + u.z, v.w + u.w};
+  }
+  return v;
+}
+
+// Exclusive scan over a workgroup of NT threads; *total gets the sum.
+template <int NT>
+__device__ int4 block_exclusive_scan4(int4 v, int4* wsum, int4* total) {
+  static_assert(NT % 64 == 0 && NT / 64 <= 64, "block size");
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int4 incl = wave_inclusive_scan4(v);
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  if (w == 0) {
+    int4 t = lane < NT / 64 ? wsum[lane] : int4{0, 0, 0, 0};
+    t = wave_inclusive_scan4(t);
+    if (lane < NT / 64) wsum[lane] = t;  // inclusive prefix of wave totals
+  }
+  __syncthreads();
+  const int4 before = w > 0 ? wsum[w - 1] : int4{0, 0, 0, 0};
+  *total = wsum[NT / 64 - 1];
+  __syncthreads();
+  return int4{before.x + incl.x - v.x, before.y + incl.y - v.y, before.z + incl.z - v.z,
+              before.w + incl.w - v.w};
+}
+
+// The persistent kernel's own plan of a decode-only call (every workgroup
+// computes it; workgroup 0 also writes the merge entries and their count):
+// per request its first item and first partial slot.
+struct FusedPlan {
+  int doff[kFusedPlanMax + 1];  // first decode item of each request; [B] = item count
+  int soff[kFusedPlanMax + 1];  // first partial slot
+  int4 wsum[kThreads / 64];
+  unsigned long long keys;
+};
+
+__device__ long long fused_plan(const MhaArgs& a, FusedPlan& fp) {
+  const int tid = threadIdx.x;
+  if (tid == 0) fp.keys = 0;
+  __syncthreads();
+  unsigned long long my_keys = 0;
+  for (int b = tid; b < a.num_seqs; b += kThreads) {
+    int nq, L, q0;
+    shape_of(a.qsl, a.seq_lens, a.max_pages, a.P, b, &nq, &L, &q0);
+    if (nq > 0) my_keys += (unsigned long long)L;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) my_keys += __shfl_xor(my_keys, o);
+  if ((tid & 63) == 0 && my_keys) atomicAdd(&fp.keys, my_keys);
+  __syncthreads();
+  const long long chunk = decode_chunk(fp.keys, a.Hkv, a.target_items);
+  int4 run = int4{0, 0, 0, 0};  // decode items, partial slots, merge entries
+  for (int base = 0; base < a.num_seqs; base += kThreads) {
+    const int b = base + tid;
+    int4 cnt = int4{0, 0, 0, 0};
+    int nq = 0, L = 0, q0 = 0, per = 0, nsplit = 0;
+    if (b < a.num_seqs) {
+      shape_of(a.qsl, a.seq_lens, a.max_pages, a.P, b, &nq, &L, &q0);
+      if (nq > 0) {
+        decode_split(L, chunk, is_tail_request(b, a.num_seqs), &per, &nsplit);
+        cnt.x = a.Hkv * nsplit;
+        if (nsplit > 1) {
+          cnt.y = a.Hkv * nsplit;
+          cnt.z = a.Hkv;
+        }
+      }
+    }
+    int4 tot;
+    const int4 ex = block_exclusive_scan4<kThreads>(cnt, fp.wsum, &tot);
+    if (b < a.num_seqs) {
+      fp.doff[b] = run.x + ex.x;
+      fp.soff[b] = run.y + ex.y;
+      if (blockIdx.x == 0 && nsplit > 1) {
+        int4* me = reinterpret_cast<int4*>(const_cast<int32_t*>(a.merges)) + run.z + ex.z;
+        const int slot0 = run.y + ex.y;
+        for (int kvh = 0; kvh < a.Hkv; ++kvh)
+          me[kvh] = int4{slot0 + kvh * nsplit, nsplit | (nq * a.G) << 16, q0, kvh};
+      }
+    }
+    run = int4{run.x + tot.x, run.y + tot.y, run.z + tot.z, 0};
+  }
+  if (tid == 0) {
+    fp.doff[a.num_seqs] = run.x;
+    if (blockIdx.x == 0) a.ctrl->n_merge = run.z;
+  }
+  __syncthreads();
+  return chunk;
+}
+
+// Decode item j of the kernel's own plan (the planner kernel's item layout).
+__device__ WorkItem fused_item(const MhaArgs& a, const FusedPlan& fp, long long chunk, int j) {
+  const int b = find_request(fp.doff, a.num_seqs, j);
+  int nq, L, q0, per, nsplit;
+  shape_of(a.qsl, a.seq_lens, a.max_pages, a.P, b, &nq, &L, &q0);
+  decode_split(L, chunk, is_tail_request(b, a.num_seqs), &per, &nsplit);
+  const int local = j - fp.doff[b];
+  const int kvh = local / nsplit, sp = local - kvh * nsplit;
+  WorkItem it;
+  it.seq = b;
+  it.kvh = kvh;
+  it.row0 = 0;
+  it.nrows = nq * a.G;
+  it.kv_begin = sp * per;
+  it.kv_end = min(L, sp * per + per);
+  it.part = nsplit > 1 ? fp.soff[b] + kvh * nsplit + sp : -1;
+  it.q0 = q0;
+  it.ctx = L - nq;
+  it.pad[0] = it.pad[1] = it.pad[2] = 0;
+  return it;
+}
+
 // Persistent forward kernel: a fixed grid; each workgroup takes items from
 // device counters until the planner's item count is reached.
 //
@@ -723,14 +888,29 @@ __device__ __noinline__ int run_decode_item_outlined(const MhaArgs& a, const Wor
 // A workgroup runs one loop over prefill-mode items and then one over
 // decode-mode items; the two loops keep the register allocation of the two
 // item kinds apart.
-template <int D, bool DECODE_ONLY>
+//
+// FUSED (decode-only calls of at most kFusedPlanMax requests): no planner
+// kernel runs before this one; every workgroup computes the plan itself
+// (fused_plan) and builds its items from it, and the only preceding launch
+// resets the queue counter.
+template <int D, bool DECODE_ONLY, bool FUSED = false>
 __global__ __launch_bounds__(DECODE_ONLY ? kThreads : kPrefillThreads, DECODE_ONLY ? 2 : 1)
 void mha_forward_kernel(MhaArgs a) {
+  static_assert(!FUSED || DECODE_ONLY, "the kernel plans only decode-only calls");
   __shared__ typename FwdLds<D, DECODE_ONLY>::type sm;
   __shared__ WorkItem s_item;
   __shared__ int s_idx;
-  const int n_items = a.ctrl->n_items;
-  const int n_pre = a.ctrl->n_pre;
+  __shared__ typename std::conditional<FUSED, FusedPlan, int>::type fp;
+  long long chunk = 0;
+  int n_items, n_pre;
+  if constexpr (FUSED) {
+    chunk = fused_plan(a, fp);
+    n_pre = 0;
+    n_items = fp.doff[a.num_seqs];
+  } else {
+    n_items = a.ctrl->n_items;
+    n_pre = a.ctrl->n_pre;
+  }
   const int n_dec = n_items - n_pre;
   // A decode-only grid starts workgroup w on decode-mode item w, so the queue
   // hands out the items after the first gridDim.x.
@@ -743,8 +923,15 @@ void mha_forward_kernel(MhaArgs a) {
   // wave 0: decode-mode item j into s_item, lane k copying word k
   auto fetch_decode = [&](int j) {
     const int lane = threadIdx.x;
-    if (j < n_dec && lane < kItemInts)
-      reinterpret_cast<int32_t*>(&s_item)[lane] = a.dec_items[(int64_t)j * kItemInts + lane];
+    if constexpr (FUSED) {
+      if (j < n_dec) {
+        const WorkItem w = fused_item(a, fp, chunk, j);
+        if (lane == 0) s_item = w;
+      }
+    } else {
+      if (j < n_dec && lane < kItemInts)
+        reinterpret_cast<int32_t*>(&s_item)[lane] = a.dec_items[(int64_t)j * kItemInts + lane];
+    }
     if (lane == 0) s_idx = n_pre + j;
   };
   auto publish = [&]() {
@@ -859,46 +1046,8 @@ constexpr int kPlanThreads = 1024;
 
 // Exclusive scan of one int4 per thread over the 1024-thread block: wave-level
 // scans with shuffles, then one wave scans the 16 wave totals.
-__device__ __forceinline__ int4 wave_inclusive_scan4(int4 v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int4 u = int4{__shfl_up(v.x, o), __shfl_up(v.y, o), __shfl_up(v.z, o), __shfl_up(v.w, o)};
-    if (lane >= o) v = int4{v.x + u.x, v.y + u.y, v.z + u.z, v.w + u.w};
-  }
-  return v;
-}
-
-__device__ int4 block_exclusive_scan4(int4 v, int4* wsum, int4* total) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int4 incl = wave_inclusive_scan4(v);
-  if (lane == 63) wsum[w] = incl;
-  __syncthreads();
-  if (w == 0) {
-    int4 t = lane < kPlanThreads / 64 ? wsum[lane] : int4{0, 0, 0, 0};
-    t = wave_inclusive_scan4(t);
-    if (lane < kPlanThreads / 64) wsum[lane] = t;  // inclusive prefix of wave totals
-  }
-  __syncthreads();
-  const int4 before = w > 0 ? wsum[w - 1] : int4{0, 0, 0, 0};
-  *total = wsum[kPlanThreads / 64 - 1];
-  __syncthreads();
-  return int4{before.x + incl.x - v.x, before.y + incl.y - v.y, before.z + incl.z - v.z,
-              before.w + incl.w - v.w};
-}
-
-// New-token count and key count of request b.  Requests whose lengths are
-// inconsistent (seq_len < q_len, or no key) get no work; seq_len is capped at
-// the block-table capacity so no item can index past a table row.
 __device__ __forceinline__ void request_shape(const PlanArgs& a, int b, int* nq, int* L, int* q0) {
-  *q0 = a.qsl[b];
-  int q = a.qsl[b + 1] - *q0;
-  int l = a.seq_lens[b];
-  const long long cap = (long long)a.max_pages * a.P;
-  if (l > cap) l = (int)cap;
-  if (q < 0 || l < q || l < 1) q = 0;
-  *nq = q;
-  *L = l;
+  shape_of(a.qsl, a.seq_lens, a.max_pages, a.P, b, nq, L, q0);
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
@@ -927,10 +1076,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   for (int o = 32; o >= 1; o >>= 1) my_keys += __shfl_xor(my_keys, o);
   if ((tid & 63) == 0 && my_keys) atomicAdd(&s_dec_keys, my_keys);
   __syncthreads();
-  const unsigned long long dec_work = s_dec_keys * (unsigned long long)Hkv;
-  long long chunk = (long long)((dec_work + a.target_items - 1) / (unsigned long long)a.target_items);
-  chunk = chunk < kMinChunk ? kMinChunk : chunk;
-  chunk = (chunk + 63) & ~63LL;
+  const long long chunk = decode_chunk(s_dec_keys, Hkv, a.target_items);
 
   // pass 2: per-request counts, exclusive scans, plans
   int4 run = int4{0, 0, 0, 0};  // prefill items, decode items, partial slots, merge entries
@@ -948,18 +1094,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       }
       const int rows = rp.nq * G;
       if (rp.nq > 0 && rows <= kDecodeRows) {
-        // Items are handed out in request order, so the last requests' items
-        // run last: cutting those finer shortens the tail where workgroups
-        // finish at different times (the extra partial rows stay few).
-        long long ck = chunk;
-        if (b >= a.B - a.B / kTailFraction) {
-          ck = (chunk / kTailDivisor + 63) & ~63LL;
-          ck = ck < kMinChunk ? kMinChunk : ck;
-        }
-        long long sp = (rp.L + ck - 1) / ck;
-        sp = sp < 1 ? 1 : (sp > kMaxFwdSplits ? kMaxFwdSplits : sp);
-        rp.per = 64 * (int)(((rp.L + 63) / 64 + sp - 1) / sp);
-        rp.nsplit = (rp.L + rp.per - 1) / rp.per;
+        decode_split(rp.L, chunk, is_tail_request(b, a.B), &rp.per, &rp.nsplit);
         cnt.y = Hkv * rp.nsplit;
         if (rp.nsplit > 1) {
           cnt.z = Hkv * rp.nsplit;
@@ -971,7 +1106,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       }
     }
     int4 tot;
-    const int4 ex = block_exclusive_scan4(cnt, sh, &tot);
+    const int4 ex = block_exclusive_scan4<kPlanThreads>(cnt, sh, &tot);
     if (b < a.B) {
       rp.slot0 = run.z + ex.z;
       a.req[b] = rp;
@@ -1074,6 +1209,13 @@ __global__ __launch_bounds__(kThreads) void mha_forward_merge_kernel(MhaArgs a) 
   }
 }
 
+// Queue counters of a pa_forward call whose persistent kernel plans itself
+// (a fill kernel rather than a memset, so a captured call replays it).
+__global__ __launch_bounds__(64) void reset_queue_kernel(Control* c) {
+  if (threadIdx.x == 0) c->work_counter = 0;
+  if (threadIdx.x < 8) c->xcd_counter[threadIdx.x] = 0;
+}
+
 }  // namespace
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
@@ -1097,6 +1239,17 @@ hipError_t launch_mha_forward(const MhaArgs& a, int D, bool decode_only, int gri
     if (decode_only) hipLaunchKernelGGL((mha_forward_kernel<64, true>), dim3(grid), dim3(kThreads), 0, s, a);
     else hipLaunchKernelGGL((mha_forward_kernel<64, false>), dim3(grid), dim3(kPrefillThreads), 0, s, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_reset_queue(Control* ctrl, hipStream_t s) {
+  hipLaunchKernelGGL(reset_queue_kernel, dim3(1), dim3(64), 0, s, ctrl);
+  return hipGetLastError();
+}
+
+hipError_t launch_mha_forward_fused(const MhaArgs& a, int D, int grid, hipStream_t s) {
+  if (D == 128) hipLaunchKernelGGL((mha_forward_kernel<128, true, true>), dim3(grid), dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL((mha_forward_kernel<64, true, true>), dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -108,6 +108,14 @@ def test_llama_decode_forward_full_size(case):
     forward_parity(b, "llama_decode/%d" % case)
 
 
+@pytest.mark.parametrize("batch", [1030, 2000])
+def test_decode_more_requests_than_the_kernel_plans(batch):
+    # decode-only batches above 1024 requests go through the planner kernel;
+    # smaller ones are planned inside the persistent kernel (the cases above)
+    b = workload.llama_decode(3, batch=batch, lo=1, hi=300)
+    forward_parity(b, "llama decode, %d short requests" % batch)
+
+
 @pytest.mark.parametrize("S", [1, 2, 7, 64, 200])
 def test_llama_decode_split_matches_oracle_partials(S):
     b = workload.llama_decode(3, batch=8)
