@@ -111,11 +111,13 @@ PA_API size_t pa_workspace_size(const pa_dims* dims);
  * prefill, extend and decode requests in one call ([TDD] sections
  * "Technical implementation of paged attention", "Q-block optimization",
  * "Persistent kernels and CUDA graphs"; [ROC] section "The challenge of
- * mixed inference workloads").  A planner kernel turns seq_lens and
- * query_start_loc into work items (query tokens x the query heads of one KV
- * head, over a key range); one persistent kernel with a fixed grid runs them;
- * decode rows whose key range was split are then merged by log-sum-exp
- * ([TDD] section "Parallel tiled softmax (3D kernel)").
+ * mixed inference workloads").  seq_lens and query_start_loc are turned into
+ * work items (query tokens x the query heads of one KV head, over a key
+ * range) on the device: by a planner kernel, or, for calls whose requests all
+ * decode (max_q_len x Hq / Hkv <= 16) and number at most 1024, by the
+ * persistent kernel itself.  One persistent kernel with a fixed grid runs the
+ * items; decode rows whose key range was split are then merged by
+ * log-sum-exp ([TDD] section "Parallel tiled softmax (3D kernel)").
  *
  * Supported: bf16 with Dqk == Dv in {64, 128}, P a multiple of 8 up to 256;
  * fp32 with Dqk, Dv <= 256 and any P >= 1.  Requires Hq % Hkv == 0.

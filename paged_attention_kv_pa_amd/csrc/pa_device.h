@@ -173,8 +173,8 @@ struct Control {
   int32_t n_pre;            // prefill-mode items; item indices [0, n_pre)
   int32_t n_items;          // all items; decode-mode items are [n_pre, n_items)
   int32_t n_merge;          // (request, KV head) pairs whose decode rows were split
-  int32_t work_counter;     // decode-mode items claimed from the queue (reset by the planner)
-  int32_t xcd_counter[8];   // next entry of each prefill-mode item queue (reset by the planner)
+  int32_t work_counter;     // decode-mode items claimed from the queue (reset before each call)
+  int32_t xcd_counter[8];   // next entry of each prefill-mode item queue (reset before each call)
   int32_t pad[52];
 };
 

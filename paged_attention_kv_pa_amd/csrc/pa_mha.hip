@@ -834,7 +834,7 @@ __device__ long long fused_plan(const MhaArgs& a, FusedPlan& fp) {
       fp.doff[b] = run.x + ex.x;
       fp.soff[b] = run.y + ex.y;
       if (blockIdx.x == 0 && nsplit > 1) {
-        int4* me = reinterpret_cast<int4*>(const_cast<int32_t*>(a.merges)) + run.z + ex.z;
+        int4* me = reinterpret_cast<int4*>(a.merges) + run.z + ex.z;
         const int slot0 = run.y + ex.y;
         for (int kvh = 0; kvh < a.Hkv; ++kvh)
           me[kvh] = int4{slot0 + kvh * nsplit, nsplit | (nq * a.G) << 16, q0, kvh};
