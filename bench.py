@@ -186,7 +186,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the split-KV and MLA measurements")
+                    help="skip the split-KV, MLA and small-case measurements")
+    ap.add_argument("--no-small", action="store_true",
+                    help="skip the small decode cases (their graph replays would dominate "
+                         "per-kernel profiler averages)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only time a plain 2 GiB device-to-device copy (HBM reference and the "
                          "byte-counter calibration kernel)")
@@ -266,7 +269,7 @@ def main():
     # ---- the small decode cases, each as one captured graph of 32 calls over
     # 32 distinct copies of the KV cache (one decode step of a 32-layer model:
     # every call reads KV that no earlier call of the replay touched)
-    if not args.no_extra:
+    if not args.no_extra and not args.no_small:
         result["small_decode"] = small_decode_cases(torch, pa, workload, dev, args)
 
     # ---- prefill half of the metric: the prefill + extend requests of the Qwen3-235B
