@@ -62,6 +62,14 @@ __device__ __forceinline__ T* uniform_ptr(T* p) {
   return (T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
+// lds_dma16 with the wave's LDS byte address already in a scalar register.
+__device__ __forceinline__ void lds_dma16_m0(const void* gsrc, uint32_t lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds_wave_base), "v"(gsrc)
+               : "memory", "m0");
+}
+
 // Wait until at most N vector-memory operations of this wave are in flight.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

@@ -109,35 +109,59 @@ __device__ __forceinline__ void mla_keys(const MlaArgs& a, char* mla_smem, int t
   // constant address space lets the uniform reads become scalar loads (a
   // vector load would make the compiler wait for every copy in flight).
   typedef const __attribute__((address_space(4))) int32_t* ConstI32Ptr;
-  const ConstI32Ptr bt = (ConstI32Ptr)(a.block_table + (int64_t)b * a.max_pages);
-  const char* kv = (const char*)a.kv;
+  // The request's table row and the cache base are workgroup-uniform: kept
+  // in scalar registers, the page lookups are scalar loads and nothing on
+  // the copy path has to be reloaded from spill slots (a vector reload there
+  // would wait for every copy in flight).
+  const ConstI32Ptr bt =
+      (ConstI32Ptr)uniform_ptr(a.block_table + (int64_t)__builtin_amdgcn_readfirstlane(b) * a.max_pages);
+  const char* kv = uniform_ptr((const char*)a.kv);
 
   // DMA of tile ti into stage st: thread tid copies key tid / 8, chunk slot
   // tid % 8 of each of the 9 groups; one wave instruction fills 64
   // consecutive chunk positions of a group.
-  const int dkey = tid >> 3;
-  const int dchunk = (tid & 7) ^ swz(dkey);
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(lds_cchar*)mla_smem + wave_s * 64 * 16);
   auto issue_tile = [&](int ti, int st) {
+    // The thread's key and chunk are recomputed from the lane index at every
+    // call (the empty asm keeps the compiler from hoisting them out of the
+    // tile loop): kept live across the loop they get spilled, and their
+    // reload would wait for the copies in flight.
+    int lane_now = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    asm volatile("" : "+v"(lane_now));
+    const int dt = wave_s * 64 + lane_now;
+    const int dkey = dt >> 3;
+    const int dchunk = (dt & 7) ^ swz(dkey);
+    const int lane_src = dkey * (kDqk * 2) + dchunk * 16;  // within a tile of one page
     const int t0 = t0k + ti * kMTK;
-    const int key = min(t0 + dkey, t1k - 1);  // clamped: real data, masked later
-    // pages of this tile, read through scalar loads (uniform indices)
-    const int last_pg = (t1k - 1) >> lp;
-    const int pg0 = __builtin_amdgcn_readfirstlane(t0 >> lp);
-    int page;
-    if (P >= kMTK) {
-      page = bt[pg0];
+    const char* src;
+    if (P >= kMTK && t0 + kMTK <= t1k) {
+      // all 32 keys real and in one page: a scalar page base plus a fixed
+      // per-lane offset
+      const int page = bt[t0 >> lp];
+      src = kv + (((int64_t)page << lp) + (t0 & (P - 1))) * (kDqk * 2) + lane_src;
     } else {
-      const int j = (key >> lp) - pg0;  // 0 .. 32 / P - 1
-      const int p0 = bt[pg0];
-      const int p1 = bt[min(pg0 + 1, last_pg)];
-      const int p2 = bt[min(pg0 + 2, last_pg)];
-      const int p3 = bt[min(pg0 + 3, last_pg)];
-      page = j == 0 ? p0 : (j == 1 ? p1 : (j == 2 ? p2 : p3));
+      const int key = min(t0 + dkey, t1k - 1);  // clamped: real data, masked later
+      // pages of this tile, read through scalar loads (uniform indices)
+      const int last_pg = (t1k - 1) >> lp;
+      const int pg0 = __builtin_amdgcn_readfirstlane(t0 >> lp);
+      int page;
+      if (P >= kMTK) {
+        page = bt[pg0];
+      } else {
+        const int j = (key >> lp) - pg0;  // 0 .. 32 / P - 1
+        const int p0 = bt[pg0];
+        const int p1 = bt[min(pg0 + 1, last_pg)];
+        const int p2 = bt[min(pg0 + 2, last_pg)];
+        const int p3 = bt[min(pg0 + 3, last_pg)];
+        page = j == 0 ? p0 : (j == 1 ? p1 : (j == 2 ? p2 : p3));
+      }
+      src = kv + (((int64_t)page << lp) + (key & (P - 1))) * (kDqk * 2) + dchunk * 16;
     }
-    const char* src = kv + (((int64_t)page << lp) + (key & (P - 1))) * (kDqk * 2) + dchunk * 16;
-    const char* dst = mla_smem + st * kStageBytes + wave * 64 * 16;
+    const uint32_t dst = lds_wave + st * kStageBytes;
 #pragma unroll
-    for (int j = 0; j < kGroups; ++j) lds_dma16(src + 128 * j, dst + j * kMTK * 8 * 16);
+    for (int j = 0; j < kGroups; ++j) lds_dma16_m0(src + 128 * j, dst + j * kMTK * 8 * 16);
   };
 
   // query fragments first (plain loads, waited for before the copies start):
