@@ -70,6 +70,12 @@ __device__ __forceinline__ void lds_dma16_m0(const void* gsrc, uint32_t lds_wave
                : "memory", "m0");
 }
 
+// s_waitcnt immediate for "no vector-memory operation in flight" (gfx9
+// encoding: vmcnt bits [3:0] and [15:14] zero, expcnt [6:4] and lgkmcnt [11:8]
+// at their maxima, i.e. not waited for).  Passed to __builtin_amdgcn_s_waitcnt,
+// which the compiler's own wait insertion takes into account.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 // Wait until at most N vector-memory operations of this wave are in flight.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

@@ -108,7 +108,7 @@ __device__ int run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest&
   constexpr int KS = D / 32, DT = D / 16;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
   const int b = it.seq, kvh = it.kvh, G = a.G, P = a.P;
-  const int kv_end = it.kv_end;
+  const int kv_end = __builtin_amdgcn_readfirstlane(it.kv_end);
 
   // this lane's query row
   const bool row_ok = r < it.nrows;
@@ -131,11 +131,18 @@ __device__ int run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest&
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
+  // The request's block-table row, read by scalar loads: a vector load of a
+  // table entry would be counted behind the K / V loads already in flight,
+  // and waiting for it would wait for all of them (one step of look-ahead
+  // instead of two).
+  typedef const __attribute__((address_space(4))) int32_t* ConstI32Ptr;
+  const ConstI32Ptr bt = (ConstI32Ptr)uniform_ptr(
+      a.block_table + (int64_t)__builtin_amdgcn_readfirstlane(b) * a.max_pages);
   const int64_t page_elems = (int64_t)a.Hkv * P * D;
   const __bf16* kbase = (const __bf16*)a.k_cache + (int64_t)kvh * P * D + 8 * g;
   const __bf16* vbase = (const __bf16*)a.v_cache + (int64_t)kvh * D * P + (int64_t)r * P;
   const int last8 = (kv_end - 1) & ~7;
+  const int last_pg = __builtin_amdgcn_readfirstlane((kv_end - 1) / P);
 
   // One 32-key step of this wave: load K / V^T operands, then update the
   // online softmax and the accumulator.  Steps are software-pipelined: the
@@ -145,18 +152,46 @@ __device__ int run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest&
     bf16x8 vf[DT];
   };
   auto load_step = [&](int t0, Step& st) {
+    // Pages of the step's four 8-key groups (P is a multiple of 8, so a group
+    // lies in one page); groups past the end take the last page, where their
+    // clamped keys are.
+    const int ts = __builtin_amdgcn_readfirstlane(t0);
+    int pidx = ts / P, off = ts - pidx * P;
+    auto next_group = [&]() {
+      off += 8;
+      if (off >= P) {
+        off -= P;
+        ++pidx;
+      }
+      return min(pidx, last_pg);
+    };
+    const int i0 = min(pidx, last_pg), i1 = next_group(), i2 = next_group(), i3 = next_group();
+    const int pg0 = bt[i0], pg1 = bt[i1], pg2 = bt[i2], pg3 = bt[i3];
+    // per-lane selects of the four scalars (written out: an indexed array
+    // would live in scratch memory)
+    auto pick = [](int j, int v0, int v1, int v2, int v3) {
+      int x = v0;
+      x = j == 1 ? v1 : x;
+      x = j == 2 ? v2 : x;
+      x = j == 3 ? v3 : x;
+      return x;
+    };
+    {
+      // K rows (group r / 4), clamped into the valid range (masked below)
+      const int page = pick(r >> 2, pg0, pg1, pg2, pg3);
+      const int kb = pick(r >> 2, i0, i1, i2, i3) * P;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {  // K rows, clamped into the valid range (masked below)
-      const int key = min(t0 + kperm(mt, r), kv_end - 1);
-      const int page = bt[key / P];
-      const __bf16* kp = kbase + (int64_t)page * page_elems + (key % P) * D;
+      for (int mt = 0; mt < 2; ++mt) {
+        const int key = min(t0 + kperm(mt, r), kv_end - 1);
+        const __bf16* kp = kbase + (int64_t)page * page_elems + (key - kb) * D;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) st.kf[mt][ks] = as_bf16x8(load16(kp + 32 * ks));
+        for (int ks = 0; ks < KS; ++ks) st.kf[mt][ks] = as_bf16x8(load16(kp + 32 * ks));
+      }
     }
     // V^T operand: keys t0+8g .. t0+8g+7 of column 16dt + r
     const int key8 = min(t0 + 8 * g, last8);
-    const int page = bt[key8 / P];
-    const __bf16* vp = vbase + (int64_t)page * page_elems + (key8 % P);
+    const int page = pick(g, pg0, pg1, pg2, pg3);
+    const __bf16* vp = vbase + (int64_t)page * page_elems + (key8 - pick(g, i0, i1, i2, i3) * P);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) st.vf[dt] = as_bf16x8(load16(vp + (int64_t)16 * dt * P));
   };
@@ -207,19 +242,34 @@ __device__ int run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest&
   };
 
   {
+    // The step bounds are wave-uniform (scalar branches), and the next step's
+    // loads are issued unconditionally (past the end they re-read the clamped
+    // last key, a cache hit): with a conditional issue the compiler cannot
+    // count the loads in flight and waits for all of them before every step
+    // (one step of look-ahead instead of two).  Every clamped key is a real
+    // key of the item (the wave's range is not empty).
     constexpr int kStride = 32 * NW;  // NW waves x 32 keys
-    int t0 = it.kv_begin + 32 * wave;
+    const int kv_begin = __builtin_amdgcn_readfirstlane(it.kv_begin);
+    int t0 = kv_begin + 32 * __builtin_amdgcn_readfirstlane(wave);
     Step sa, sb;
-    if (t0 < kv_end) load_step(t0, sa);
-    while (t0 < kv_end) {
-      if (t0 + kStride < kv_end) load_step(t0 + kStride, sb);
-      compute_step(t0, sa);
-      t0 += kStride;
-      if (t0 >= kv_end) break;
-      if (t0 + kStride < kv_end) load_step(t0 + kStride, sa);
-      compute_step(t0, sb);
-      t0 += kStride;
+    if (t0 < kv_end) {
+      load_step(t0, sa);
+      // Two steps per pass and a single exit test at the bottom (an exit
+      // between the two steps is merged by the compiler into a flow block
+      // whose fall-through path makes it wait for every load at the loop
+      // head).  The second step of the last pass may lie wholly past the
+      // end: its keys are masked and its values zeroed, so it adds nothing.
+      do {
+        load_step(t0 + kStride, sb);
+        compute_step(t0, sa);
+        load_step(t0 + 2 * kStride, sa);
+        compute_step(t0 + kStride, sb);
+        t0 += 2 * kStride;
+      } while (t0 < kv_end);
     }
+    // Drain the last look-ahead here, with a wait the compiler sees, so that
+    // no load is counted as in flight when the next item's loop starts.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   }
 
   int claim = 0;
@@ -906,7 +956,7 @@ void mha_forward_kernel(MhaArgs a) {
   if constexpr (FUSED) {
     chunk = fused_plan(a, fp);
     n_pre = 0;
-    n_items = fp.doff[a.num_seqs];
+    n_items = __builtin_amdgcn_readfirstlane(fp.doff[a.num_seqs]);
   } else {
     n_items = a.ctrl->n_items;
     n_pre = a.ctrl->n_pre;
@@ -934,10 +984,16 @@ void mha_forward_kernel(MhaArgs a) {
     }
     if (lane == 0) s_idx = n_pre + j;
   };
+  // Every thread reads the published item; the reads are made visibly
+  // uniform (scalar registers), so the item loop and the key loops inside an
+  // item compile to scalar branches.
   auto publish = [&]() {
     __syncthreads();
-    idx = s_idx;
-    it = s_item;
+    idx = __builtin_amdgcn_readfirstlane(s_idx);
+#pragma unroll
+    for (int k = 0; k < kItemInts; ++k)
+      reinterpret_cast<int32_t*>(&it)[k] =
+          __builtin_amdgcn_readfirstlane(reinterpret_cast<const int32_t*>(&s_item)[k]);
     __syncthreads();
   };
   // wave 0 takes the next index (lane 0's atomics, broadcast to the wave):

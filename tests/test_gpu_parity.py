@@ -116,6 +116,24 @@ def test_decode_more_requests_than_the_kernel_plans(batch):
     forward_parity(b, "llama decode, %d short requests" % batch)
 
 
+@pytest.mark.parametrize("P", [8, 24, 48])
+def test_decode_page_sizes(P):
+    # decode items and split partitions over pages that hold a multiple of 8
+    # keys, not always a power of two: one 32-key step can touch up to four
+    # pages, and ranges end anywhere inside a page
+    b = workload.make_batch([1] * 9, [0, 6, 7, 8, 30, 32, 199, 999, 2499], num_q_heads=32,
+                            num_kv_heads=8, head_dim_qk=128, page_size=P, seed=70 + P)
+    forward_parity(b, "decode pages P=%d" % P)
+    g = b.to(DEV)
+    say("case decode split pages P=%d" % P)
+    po, pl = pa.pa_decode_split(g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens, b.scale, 5)
+    torch.cuda.synchronize()
+    rpo, rpl = oracle.decode_split(b.q, b.k_cache, b.v_cache, b.block_table, b.seq_lens, b.scale,
+                                   5, b.num_kv_heads)
+    check_out(po.cpu().numpy(), rpo, torch.bfloat16, "bf16 partials P=%d" % P)
+    check_lse(pl.cpu().numpy(), rpl, "bf16 partial lse P=%d" % P)
+
+
 @pytest.mark.parametrize("S", [1, 2, 7, 64, 200])
 def test_llama_decode_split_matches_oracle_partials(S):
     b = workload.llama_decode(3, batch=8)
@@ -261,7 +279,8 @@ def test_edge_empty_requests_single_keys_and_exact_pages():
 
 
 @pytest.mark.parametrize("Hq,Hkv,D,P", [(32, 8, 64, 16), (64, 2, 128, 16), (16, 16, 128, 32),
-                                        (8, 1, 128, 64), (12, 4, 64, 8)])
+                                        (8, 1, 128, 64), (12, 4, 64, 8), (32, 8, 128, 24),
+                                        (16, 2, 64, 40)])
 def test_head_and_page_shapes(Hq, Hkv, D, P):
     b = workload.make_batch([1, 5, 40, 1, 130], [700, 100, 0, 3, 60], num_q_heads=Hq,
                             num_kv_heads=Hkv, head_dim_qk=D, page_size=P, seed=Hq * 7 + P)
