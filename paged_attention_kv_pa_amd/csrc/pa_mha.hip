@@ -464,15 +464,21 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
   // scalar loads.
   typedef const __attribute__((address_space(4))) int32_t* ConstI32Ptr;
   const ConstI32Ptr cbt = (ConstI32Ptr)bt;
-  const int kgroup = wave >> 1;
+  // Copy addressing is wave-uniform wherever it can be (scalar registers and
+  // scalar arithmetic): the per-lane part is one 32-bit offset per copy.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int kgroup = wave_u >> 1;
+  const uint32_t lds_stage0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)sm.stage[0]);
   struct TilePages {
     int pg0, first0;  // physical page and its first key, keys 16 (w / 2) + 0 .. 7
     int pg1, first1;  // the same for keys 16 (w / 2) + 8 .. 15
   };
   auto load_pages = [&](int t0) {
     TilePages tp;
-    const int i0 = __builtin_amdgcn_readfirstlane(min(t0 + 16 * kgroup, kv_end - 1) / P);
-    const int i1 = __builtin_amdgcn_readfirstlane(min(t0 + 16 * kgroup + 8, kv_end - 1) / P);
+    const int ts = __builtin_amdgcn_readfirstlane(t0);
+    const int i0 = min(ts + 16 * kgroup, kv_end - 1) / P;
+    const int i1 = min(ts + 16 * kgroup + 8, kv_end - 1) / P;
     tp.pg0 = cbt[i0];
     tp.pg1 = cbt[i1];
     tp.first0 = i0 * P;
@@ -480,34 +486,33 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
     return tp;
   };
   auto issue_tile = [&](int t0, int st, const TilePages& tp) {
-    char* stage = sm.stage[st];
+    const uint32_t stage = lds_stage0 + st * LY::kStageBytes;
+    const int ts = __builtin_amdgcn_readfirstlane(t0);
     {
       // four consecutive lanes copy 64 contiguous bytes of one key row (in
       // swizzled order), so a copy instruction reads 16 whole 64-byte pieces
       const int k16 = lane >> 2;
       const int cl = (lane & 3) ^ ((k16 >> 2) & 3);
       const bool hi = k16 >= 8;
-      const int key = min(t0 + 16 * kgroup + k16, kv_end - 1);
-      const int pg = hi ? tp.pg1 : tp.pg0;
-      const int first = hi ? tp.first1 : tp.first0;
-      const int c0 = (wave & 1) * (LY::kChunks / 2);  // first column chunk of this wave
-      const char* src = kbase + ((int64_t)pg * page_elems + (int64_t)(key - first) * D +
-                                 8 * (c0 + cl)) * 2;
+      const int key = min(ts + 16 * kgroup + k16, kv_end - 1);
+      const int c0 = (wave_u & 1) * (LY::kChunks / 2);  // first column chunk of this wave
+      const char* page0 = kbase + (int64_t)tp.pg0 * page_elems * 2;
+      const char* page1 = kbase + (int64_t)tp.pg1 * page_elems * 2;
+      const int off = ((key - (hi ? tp.first1 : tp.first0)) * D + 8 * (c0 + cl)) * 2;
+      const char* src = (hi ? page1 : page0) + off;
 #pragma unroll
       for (int j = 0; j < LY::kKCopies; ++j)
-        lds_dma16(src + 64 * j, stage + LY::koff(16 * kgroup, c0 + 4 * j));
+        lds_dma16_m0(src + 64 * j, stage + LY::koff(16 * kgroup, c0 + 4 * j));
     }
     {
-      const bool hi = wave & 1;
-      const int cs = min(t0 + 8 * wave, (kv_end - 1) & ~7);
+      const bool hi = wave_u & 1;
+      const int cs = min(ts + 8 * wave_u, (kv_end - 1) & ~7);
       const int pg = hi ? tp.pg1 : tp.pg0;
       const int slot = cs - (hi ? tp.first1 : tp.first0);
+      const char* vpage = vbase + ((int64_t)pg * page_elems + slot) * 2;
 #pragma unroll
-      for (int i = 0; i < LY::kVCopies; ++i) {
-        const int d = 64 * i + lane;
-        const char* src = vbase + ((int64_t)pg * page_elems + (int64_t)d * P + slot) * 2;
-        lds_dma16(src, stage + LY::voff(wave, 64 * i));
-      }
+      for (int i = 0; i < LY::kVCopies; ++i)
+        lds_dma16_m0(vpage + (64 * i + lane) * P * 2, stage + LY::voff(wave_u, 64 * i));
     }
   };
 
