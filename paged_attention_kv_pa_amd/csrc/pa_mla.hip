@@ -86,6 +86,20 @@ __device__ __forceinline__ void mfma32_acc_agpr(floatx16& acc, const bf16x8& a, 
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
+// s += A B (or s = A B) on v_mfma_f32_32x32x16_bf16 with s in vector
+// registers.  Written as inline assembly because, once the output
+// accumulators are pinned to AGPRs, the compiler selects the AGPR form for
+// every builtin matrix instruction: the score tiles then took AGPRs 0..31
+// and two output tiles were moved out to vector registers and back around
+// every key tile.  The caller pads hazards as for mfma32_acc_agpr, and reads
+// s only after the last instruction has retired.
+__device__ __forceinline__ void mfma32_vgpr(floatx16& s, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32_vgpr_first(floatx16& s, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "v"(b));
+}
+
 // Key held by M-row m of the K operand (see the file comment).
 __device__ __forceinline__ int kperm32(int m) {
   const int q = m >> 3, h = (m >> 2) & 1, w = m & 3;
@@ -227,13 +241,12 @@ __device__ __forceinline__ void mla_keys(const MlaArgs& a, char* mla_smem, int t
     // constant parts fold into the instructions' offsets
     lds_cchar* stage = (lds_cchar*)mla_smem + (ti % kStages) * kStageBytes;
 
-    // S^T (two accumulation chains: even / odd K-steps)
+    // S^T (two accumulation chains: even / odd K-steps, each started by an
+    // instruction with a zero addend)
     floatx16 sa, sb;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) sa[v] = sb[v] = 0.f;
     // operand reads run kAhead K-steps ahead of the matrix instructions (by
     // hand: left alone, the scheduler sinks each read next to its use)
-    constexpr int kAhead = 2;
+    constexpr int kAhead = 4;
     auto kread = [&](int ks) {  // chunk 2 ks + h lives in group (2 ks + h) >> 3 = ks >> 2
       const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
           stage + koff[ks & 3] + (ks >> 2) * (kMTK * 8 * 16));
@@ -254,14 +267,19 @@ __device__ __forceinline__ void mla_keys(const MlaArgs& a, char* mla_smem, int t
     for (int ks = 0; ks < KS; ++ks) {
       const bf16x8 kf = kbuf[ks % kAhead];
       const bf16x8 qv = ks < kQRegSteps ? qf[ks < kQRegSteps ? ks : 0] : qbuf[ks % kAhead];
-      if (ks & 1) sb = mfma32_bf16(kf, qv, sb);
-      else sa = mfma32_bf16(kf, qv, sa);
+      if (ks == 0) mfma32_vgpr_first(sa, kf, qv);
+      else if (ks == 1) mfma32_vgpr_first(sb, kf, qv);
+      else if (ks & 1) mfma32_vgpr(sb, kf, qv);
+      else mfma32_vgpr(sa, kf, qv);
       if (ks + kAhead < KS) {
         kbuf[ks % kAhead] = kread(ks + kAhead);
         if (ks + kAhead >= kQRegSteps) qbuf[ks % kAhead] = qread(ks + kAhead);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    // the last two matrix instructions (one per chain) must have retired
+    // before vector instructions read their results
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(sa), "+v"(sb));
     // lane holds S[head][key] for keys 8h + v (v < 8) and 16 + 8h + (v - 8)
     float x[16];
 #pragma unroll
@@ -317,7 +335,7 @@ __device__ __forceinline__ void mla_keys(const MlaArgs& a, char* mla_smem, int t
     // operands keep those writes before this point)
     asm volatile("s_nop 4" : "+v"(pf[0]), "+v"(pf[1]));
     // V^T operands: two transposing reads each, kAheadV instructions ahead
-    constexpr int kAheadV = 2;
+    constexpr int kAheadV = 4;
     auto vread = [&](int i) {  // i = 2 dt + kk
       const int dt = i >> 1, kk = i & 1;
       const int goff = (dt >> 1) * (kMTK * 8 * 16);  // chunk group of columns 32 dt ..
