@@ -57,6 +57,9 @@ def _load():
             lib.orc_attention.restype = i32
             lib.orc_decode_split.argtypes = [p, p, p, i32, p, p] + [i32] * 9 + [f32, i32, p, p, i32]
             lib.orc_decode_split.restype = i32
+            lib.orc_chunked_partials.argtypes = [p, p, p, i32, p, p, p] + [i32] * 9 + [f32, i32, i32,
+                                                                                    p, p, i32]
+            lib.orc_chunked_partials.restype = i32
             lib.orc_merge_lse.argtypes = [p, p, i32, i32, i32, p, p]
             lib.orc_merge_lse.restype = i32
             lib.orc_split_range.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32),
@@ -177,6 +180,39 @@ def decode_split(q, k_cache, v_cache, block_table, seq_lens, scale, num_splits,
     rc = lib.orc_decode_split(_ptr(qa), _ptr(ka), _ptr(va), dt, _ptr(bt), _ptr(sl), B, Hq,
                               int(num_kv_heads), Dqk, Dv, P, num_pages, bt.shape[1], layout,
                               float(scale), S, _ptr(po), _ptr(pl), nt)
+    _check(rc)
+    return po, pl
+
+
+def chunked_partials(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale,
+                     chunk_keys, num_chunks, num_kv_heads, head_dim_v=None, layout=LAYOUT_MHA,
+                     nthreads=None):
+    """Chunked-context partials of a varlen batch, in fp64 (see orc_chunked_partials).
+
+    Chunk s covers keys [s C, (s + 1) C) of every request; each row gets the partial
+    over the keys of the chunk it sees (zeros and -inf when there are none).
+    Returns (part_out [T, Hq, S, Dv], part_lse [T, Hq, S]).
+    """
+    lib = _load()
+    qa, dt = _raw(q)
+    ka, dk = _raw(k_cache)
+    va, dv = _raw(v_cache)
+    if not (dt == dk == dv) or dt is None:
+        raise TypeError("q, k_cache and v_cache must share one float dtype")
+    bt, sl, qs = _i32(block_table), _i32(seq_lens), _i32(query_start_loc)
+    T, Hq, Dqk = qa.shape
+    B = sl.shape[0]
+    if qs.shape[0] != B + 1 or bt.ndim != 2 or bt.shape[0] != B:
+        raise ValueError("inconsistent batch arrays")
+    Dv = Dqk if head_dim_v is None else int(head_dim_v)
+    num_pages, P = (ka.shape[0], ka.shape[2]) if layout == LAYOUT_MHA else (ka.shape[0], ka.shape[1])
+    S = int(num_chunks)
+    po = np.full((T, Hq, S, Dv), np.nan, dtype=np.float64)
+    pl = np.full((T, Hq, S), np.nan, dtype=np.float64)
+    nt = max_threads() if nthreads is None else int(nthreads)
+    rc = lib.orc_chunked_partials(_ptr(qa), _ptr(ka), _ptr(va), dt, _ptr(bt), _ptr(sl), _ptr(qs),
+                                  B, Hq, int(num_kv_heads), Dqk, Dv, P, num_pages, bt.shape[1],
+                                  layout, float(scale), int(chunk_keys), S, _ptr(po), _ptr(pl), nt)
     _check(rc)
     return po, pl
 

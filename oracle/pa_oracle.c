@@ -298,6 +298,87 @@ int orc_decode_split(const void* q, const void* kc, const void* vc, int dtype,
 }
 
 /*
+ * Chunked-context partials (ROCm backends, bullet "Chunked context
+ * processing": the context is processed a fixed number of keys at a time and
+ * the pieces are combined by their log-sum-exp).  The keys of every request
+ * are cut into chunks of C keys, chunk s covering [s C, (s + 1) C).  For new
+ * token j of request b (position c_b + j, as in orc_attention) and query head
+ * h, part_out[i, h, s, :] and part_lse[i, h, s] (i = qsl[b] + j) are plain
+ * attention over the keys of chunk s that the token sees:
+ *   [s C, min((s + 1) C, c_b + j + 1)).
+ * A chunk holding none of them gives zeros and -inf, so orc_merge_lse over
+ * the S chunks of a row gives that row of orc_attention.
+ *   part_out [T, Hq, S, Dv], part_lse [T, Hq, S], both double.
+ */
+int orc_chunked_partials(const void* q, const void* kc, const void* vc, int dtype,
+                         const int32_t* block_table, const int32_t* seq_lens,
+                         const int32_t* qsl, int B, int Hq, int Hkv, int Dqk,
+                         int Dv, int P, int num_pages, int max_pages, int layout,
+                         float scale, int C, int S, double* part_out,
+                         double* part_lse, int nthreads) {
+  int rc = check_common(B, Hq, Hkv, Dqk, Dv, P, max_pages, layout);
+  if (rc) return rc;
+  if (C <= 0 || S <= 0) return ORC_ERR_ARG;
+  const int g = Hq / Hkv;
+  const double sigma = (double)scale;
+  int err = ORC_OK;
+  if (nthreads <= 0) nthreads = 1;
+
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+  for (int64_t job = 0; job < (int64_t)B * Hkv; ++job) {
+    const int b = (int)(job / Hkv), h = (int)(job % Hkv);
+    const int i0 = qsl[b], nq = qsl[b + 1] - qsl[b], L = seq_lens[b];
+    if (nq <= 0) {
+      if (nq < 0) {
+#pragma omp atomic write
+        err = ORC_ERR_DATA;
+      }
+      continue;
+    }
+    if (L < nq || (L + P - 1) / P > max_pages) {
+#pragma omp atomic write
+      err = ORC_ERR_DATA;
+      continue;
+    }
+    const int c = L - nq;
+    double* Kd = malloc(sizeof(double) * (size_t)L * Dqk);
+    double* Vd = malloc(sizeof(double) * (size_t)L * Dv);
+    double* qrow = malloc(sizeof(double) * (size_t)Dqk);
+    double* s = malloc(sizeof(double) * (size_t)L);
+    if (!Kd || !Vd || !qrow || !s) {
+#pragma omp atomic write
+      err = ORC_ERR_NOMEM;
+      free(Kd); free(Vd); free(qrow); free(s);
+      continue;
+    }
+    if (gather(kc, vc, dtype, layout, block_table + (size_t)b * max_pages,
+               num_pages, L, h, Hkv, P, Dqk, Dv, Kd, Vd)) {
+#pragma omp atomic write
+      err = ORC_ERR_DATA;
+    } else {
+      for (int j = 0; j < nq; ++j) {
+        const int i = i0 + j;
+        const long seen = (long)c + j + 1;  /* keys 0 .. c + j */
+        for (int hh = h * g; hh < (h + 1) * g; ++hh) {
+          for (int d = 0; d < Dqk; ++d)
+            qrow[d] = load_elem(q, dtype, ((size_t)i * Hq + hh) * Dqk + d);
+          for (int sp = 0; sp < S; ++sp) {
+            long t0 = (long)sp * C, t1 = t0 + C;
+            if (t1 > seen) t1 = seen;
+            if (t0 > t1) t0 = t1;
+            size_t row = ((size_t)i * Hq + hh) * S + sp;
+            attend(qrow, Kd, Vd, (int)t0, (int)t1, Dqk, Dv, sigma, s,
+                   part_out + row * Dv, part_lse + row);
+          }
+        }
+      }
+    }
+    free(Kd); free(Vd); free(qrow); free(s);
+  }
+  return err;
+}
+
+/*
  * Log-sum-exp merge of S partials per row (rows are independent):
  *   M = max_s lse_s;  w_s = exp(lse_s - M) (0 when lse_s = -inf);
  *   out = sum w_s o_s / sum w_s;  lse = M + ln sum w_s.

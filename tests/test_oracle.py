@@ -136,6 +136,51 @@ def test_split_partials_match_sdpa_on_their_ranges():
         assert all(n == nonempty[0] for n in nonempty[:-1])
 
 
+# decode, decode, extend, prefill, extend: rows with few and many visible keys
+CHUNK_SPECS = [(1, 0), (1, 12), (4, 9), (6, 0), (3, 30)]
+
+
+@pytest.mark.parametrize("C", [1, 3, 4, 16, 64])
+def test_chunked_then_merge_equals_unchunked(C):
+    """Chunked-context partials merged by LSE give plain attention; a chunk past
+    every request's keys is empty (zeros, -inf) for every row."""
+    c = _build_case(31, CHUNK_SPECS, 4, 2, 8, 8, 4)
+    out, lse = _run(c, 0.35, 2, 8)
+    S = max((int(L) + C - 1) // C for L in c["seq"]) + 1
+    po, pl = oracle.chunked_partials(c["q"], c["kc"], c["vc"], c["bt"], c["seq"], c["qsl"], 0.35,
+                                     C, S, 2, head_dim_v=8)
+    mo, ml = oracle.merge_lse(po, pl)
+    np.testing.assert_allclose(mo, out, atol=TOL, rtol=0)
+    np.testing.assert_allclose(ml, lse, atol=TOL, rtol=0)
+    assert np.all(np.isneginf(pl[:, :, S - 1])) and np.all(po[:, :, S - 1] == 0)
+
+
+def test_chunked_partials_match_sdpa_on_visible_keys():
+    """Each chunk partial of a row is attention over the chunk's keys that the row's
+    token sees (SDPA on the dense keys); chunks it cannot see are empty."""
+    specs = [(5, 7), (1, 20), (9, 0)]
+    c = _build_case(33, specs, 4, 2, 8, 8, 4)
+    C, S = 6, 6
+    po, pl = oracle.chunked_partials(c["q"], c["kc"], c["vc"], c["bt"], c["seq"], c["qsl"], 0.5,
+                                     C, S, 2, head_dim_v=8)
+    i = 0
+    empty = 0
+    for b, (nq, ctx) in enumerate(specs):
+        for j in range(nq):
+            pos = ctx + j
+            for s in range(S):
+                t0, t1 = s * C, min(s * C + C, pos + 1)
+                if t1 <= t0:
+                    assert np.all(np.isneginf(pl[i, :, s])) and np.all(po[i, :, s] == 0)
+                    empty += 1
+                    continue
+                ro, rl = sdpa_reference(c["qs"][b][j:j + 1], c["Ks"][b][t0:t1], c["Vs"][b][t0:t1], 0.5)
+                np.testing.assert_allclose(po[i, :, s], ro[0], atol=TOL, rtol=0)
+                np.testing.assert_allclose(pl[i, :, s], rl[0], atol=TOL, rtol=0)
+            i += 1
+    assert empty > 0 and i == c["q"].shape[0]
+
+
 def test_constant_value_rows_sum_to_one():
     """V = const => out = const for every row (softmax rows sum to 1)."""
     specs = [(1, 30), (4, 5), (9, 0)]

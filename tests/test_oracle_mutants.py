@@ -42,6 +42,8 @@ MUTANTS = {
                                "  if (layout == ORC_LAYOUT_MLA) return ((size_t)page * P + slot) * Dqk + d + (Dqk - Dv);\n"
                                "  return (((size_t)page * Hkv + head) * Dv + d) * P + slot;"),
     "merge_weight_sum_skipped": ("      wsum += w;\n", "      wsum += 1.0;\n"),
+    "chunk_ignores_causal_limit": ("            if (t1 > seen) t1 = seen;", "            if (t1 > L) t1 = L;"),
+    "chunk_start_one_chunk_late": ("long t0 = (long)sp * C, t1 = t0 + C;", "long t0 = (long)(sp + 1) * C, t1 = t0 + C;"),
 }
 
 
@@ -53,8 +55,11 @@ def _battery():
             out.append(("sdpa", lambda c=case, d=dt: pins.test_bruteforce_against_torch_sdpa(c, d)))
     for S in (1, 2, 3, 7, 64):
         out.append(("split", lambda s=S: pins.test_split_then_merge_equals_unsplit(s)))
+    for C in (1, 3, 4, 16, 64):
+        out.append(("chunked", lambda c=C: pins.test_chunked_then_merge_equals_unchunked(c)))
     for name in ("test_page_permutation_is_bitwise_invariant",
                  "test_split_partials_match_sdpa_on_their_ranges",
+                 "test_chunked_partials_match_sdpa_on_visible_keys",
                  "test_constant_value_rows_sum_to_one", "test_length_one_context_returns_v0",
                  "test_equal_keys_give_mean_of_visible_values",
                  "test_zero_query_gives_mean_and_log_count",
