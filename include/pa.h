@@ -149,6 +149,36 @@ PA_API pa_status pa_decode_split(const void* q, const void* k_cache, const void*
                           float* part_lse, const pa_dims* dims, void* stream);
 
 /*
+ * pa_forward_chunked — chunked-context processing of a varlen batch ([ROC]
+ * bullet "Chunked context processing"): the keys of every request are taken
+ * a fixed budget of chunk_keys at a time, and each chunk yields per-row
+ * partials that pa_merge_lse combines.  Chunk s of request b covers keys
+ * [s * chunk_keys, (s + 1) * chunk_keys); new token j of request b (at
+ * position c_b + j, c_b = seq_lens[b] - q_b, causal as in pa_forward) sees
+ * the keys of the chunk below c_b + j + 1.  For output row i * Hq + h
+ * (token i = query_start_loc[b] + j, query head h):
+ *   part_out[i, h, s, :]  float32 [T, Hq, num_chunks, Dv]  attention over the
+ *                         keys of chunk s the token sees (zeros if none)
+ *   part_lse[i, h, s]     float32 [T, Hq, num_chunks]      their log-sum-exp
+ *                         (-inf if none)
+ * pa_merge_lse(part_out, part_lse, T * Hq, num_chunks, Dv, out, lse, PA_BF16)
+ * then gives pa_forward's out and lse.  One workgroup runs each (request, KV
+ * head, block of up to 256 rows, chunk), so a long context is spread over
+ * num_chunks workgroups whatever its number of new tokens.
+ * chunk_keys: a positive multiple of 64; num_chunks in [1, 256] with
+ * chunk_keys * num_chunks >= dims->max_seq_len.  bf16 only, Dqk == Dv in
+ * {64, 128}, P a multiple of 8 up to 256.  Rows of requests with no new token
+ * or with seq_len < q_len are not written.  Buffers are caller-owned device
+ * memory; nothing is allocated.  Returns PA_OK, PA_ERR_INVALID_ARG,
+ * PA_ERR_UNSUPPORTED or PA_ERR_HIP.
+ */
+PA_API pa_status pa_forward_chunked(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    const int32_t* query_start_loc, float scale,
+                                    int32_t chunk_keys, int32_t num_chunks, float* part_out,
+                                    float* part_lse, const pa_dims* dims, void* stream);
+
+/*
  * pa_merge_lse — second launch: log-sum-exp merge of split partials ([TDD]
  * section "Parallel tiled softmax (3D kernel)"; [ROC] bullet "Chunked context
  * processing").  For each of num_rows rows:

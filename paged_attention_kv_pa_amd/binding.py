@@ -62,6 +62,8 @@ def library():
             lib.pa_forward.restype = i32
             lib.pa_decode_split.argtypes = [p, p, p, p, p, f32, i32, p, p, dp, p]
             lib.pa_decode_split.restype = i32
+            lib.pa_forward_chunked.argtypes = [p, p, p, p, p, p, f32, i32, i32, p, p, dp, p]
+            lib.pa_forward_chunked.restype = i32
             lib.pa_merge_lse.argtypes = [p, p, i32, i32, i32, p, p, i32, p]
             lib.pa_merge_lse.restype = i32
             lib.mla_workspace_size.argtypes = [dp, i32]
@@ -220,6 +222,43 @@ def pa_decode_split(q, k_cache, v_cache, block_table, seq_lens, scale, num_split
                                    _ptr(seq_lens), float(scale), S, _ptr(part_out),
                                    _ptr(part_lse), ctypes.byref(dims), _stream(q.device, stream))
     _check(st, "pa_decode_split")
+    return part_out, part_lse
+
+
+def pa_forward_chunked(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale,
+                       chunk_keys, num_chunks=None, part_out=None, part_lse=None, max_seq_len=None,
+                       max_q_len=None, stream=None):
+    """Chunked-context partials (see pa_forward_chunked in include/pa.h).
+
+    num_chunks defaults to ceil(max_seq_len / chunk_keys).  Returns
+    (part_out [T, Hq, S, D] fp32, part_lse [T, Hq, S] fp32); pa_merge_lse of the pair
+    gives pa_forward's output.
+    """
+    _check_common(q, k_cache, v_cache, block_table, seq_lens)
+    _need(query_start_loc.dtype == torch.int32 and query_start_loc.is_contiguous()
+          and query_start_loc.device == q.device, "query_start_loc must be contiguous int32 on q's device")
+    _need(q.dim() == 3 and k_cache.dim() == 4 and v_cache.dim() == 4, "bad tensor ranks")
+    _need(query_start_loc.shape[0] == seq_lens.shape[0] + 1, "query_start_loc must have B + 1 entries")
+    T = int(q.shape[0])
+    dims = make_dims(q, k_cache, v_cache, block_table, seq_lens, T, max_seq_len=max_seq_len,
+                     max_q_len=max_q_len)
+    C = int(chunk_keys)
+    S = (dims.max_seq_len + C - 1) // C if num_chunks is None else int(num_chunks)
+    S = max(S, 1)
+    shape = (T, dims.num_q_heads, S, dims.head_dim_v)
+    if part_out is None:
+        part_out = torch.empty(shape, dtype=torch.float32, device=q.device)
+    if part_lse is None:
+        part_lse = torch.empty(shape[:3], dtype=torch.float32, device=q.device)
+    _need(tuple(part_out.shape) == shape and part_out.dtype == torch.float32 and part_out.is_contiguous(),
+          "bad part_out")
+    _need(tuple(part_lse.shape) == shape[:3] and part_lse.dtype == torch.float32 and part_lse.is_contiguous(),
+          "bad part_lse")
+    st = library().pa_forward_chunked(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                      _ptr(seq_lens), _ptr(query_start_loc), float(scale), C, S,
+                                      _ptr(part_out), _ptr(part_lse), ctypes.byref(dims),
+                                      _stream(q.device, stream))
+    _check(st, "pa_forward_chunked")
     return part_out, part_lse
 
 

@@ -332,6 +332,54 @@ pa_status pa_decode_split(const void* q, const void* k_cache, const void* v_cach
   return e == hipSuccess ? PA_OK : hip_fail(e);
 }
 
+pa_status pa_forward_chunked(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             const int32_t* query_start_loc, float scale, int32_t chunk_keys,
+                             int32_t num_chunks, float* part_out, float* part_lse,
+                             const pa_dims* d, void* stream) {
+  pa_status st = check_dims(d);
+  if (st != PA_OK) return st;
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !query_start_loc || !part_out ||
+      !part_lse)
+    return PA_ERR_INVALID_ARG;
+  if (chunk_keys < 64 || chunk_keys % 64 != 0) return PA_ERR_INVALID_ARG;
+  if (num_chunks < 1 || num_chunks > pa::kMaxSplits) return PA_ERR_INVALID_ARG;
+  if ((int64_t)chunk_keys * num_chunks < d->max_seq_len) return PA_ERR_INVALID_ARG;
+  if (d->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  st = check_mha_support(d);
+  if (st != PA_OK) return st;
+  if (d->num_seqs == 0 || d->num_tokens == 0 || d->max_q_len == 0) return PA_OK;
+  if ((int64_t)d->num_tokens * d->num_q_heads * num_chunks > INT32_MAX) return PA_ERR_INVALID_ARG;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  const int64_t row_blocks = ((int64_t)d->max_q_len * G + pa::kPrefillRows - 1) / pa::kPrefillRows;
+  if ((int64_t)d->num_seqs * d->num_kv_heads * row_blocks * num_chunks > INT32_MAX)
+    return PA_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  pa::MhaArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.qsl = query_start_loc;
+  a.part_o = part_out;
+  a.part_lse = part_lse;
+  a.scale = scale;
+  a.num_seqs = d->num_seqs;
+  a.Hq = d->num_q_heads;
+  a.Hkv = d->num_kv_heads;
+  a.G = G;
+  a.P = d->page_size;
+  a.max_pages = d->max_pages_per_seq;
+  a.num_splits = num_chunks;
+  a.chunk_keys = chunk_keys;
+  a.row_blocks = (int32_t)row_blocks;
+  hipError_t e = mark(g_ev_start, s);
+  if (e == hipSuccess) e = pa::launch_mha_chunked(a, d->head_dim_qk, s);
+  if (e == hipSuccess) e = mark(g_ev_stop, s);
+  return e == hipSuccess ? PA_OK : hip_fail(e);
+}
+
 pa_status pa_merge_lse(const float* part_out, const float* part_lse, int32_t num_rows,
                        int32_t num_splits, int32_t head_dim_v, void* out, float* lse,
                        int32_t out_dtype, void* stream) {

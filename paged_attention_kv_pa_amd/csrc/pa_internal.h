@@ -46,8 +46,10 @@ struct MhaArgs {
   float scale;
   int32_t num_seqs;
   int32_t Hq, Hkv, G, P, max_pages;
-  int32_t num_splits;        // pa_decode_split only
+  int32_t num_splits;        // pa_decode_split: partitions; pa_forward_chunked: chunks
   int32_t target_items;      // pa_forward decode-only calls planned in the kernel
+  int32_t chunk_keys;        // pa_forward_chunked: keys per chunk
+  int32_t row_blocks;        // pa_forward_chunked: row blocks of the longest request
 };
 
 struct PlanArgs {
@@ -113,6 +115,7 @@ hipError_t launch_mha_forward_fused(const MhaArgs& a, int D, int grid, hipStream
 hipError_t launch_reset_queue(Control* ctrl, hipStream_t s);
 hipError_t launch_mha_forward_merge(const MhaArgs& a, int D, int grid, hipStream_t s);
 hipError_t launch_mha_split(const MhaArgs& a, int D, hipStream_t s);
+hipError_t launch_mha_chunked(const MhaArgs& a, int D, hipStream_t s);
 hipError_t mha_occupancy(int D, bool decode_only, int* blocks_per_cu);
 hipError_t launch_merge(const float* po, const float* pl, int rows, int S, int Dv, void* out,
                         bool out_bf16, float* lse, hipStream_t s);

@@ -42,10 +42,13 @@ constexpr int kTK = 64;  // keys per LDS tile in prefill mode
 __device__ __forceinline__ int kperm(int mt, int m) { return 8 * (m >> 2) + 4 * mt + (m & 3); }
 
 // Where the rows of an item go.
+// Partial row `row` of an item (output row out_row) goes to
+// part_o[po_base + row po_row + out_row po_out ..] and
+// part_lse[pl_base + row pl_row + out_row pl_out].
 struct Dest {
   bool partial;
-  int64_t po_base, po_row;  // partial output offsets (elements)
-  int64_t pl_base, pl_row;
+  int64_t po_base, po_row, po_out;  // partial output offsets (elements)
+  int64_t pl_base, pl_row, pl_out;
 };
 
 template <int D, int NW>
@@ -63,7 +66,7 @@ __device__ __forceinline__ void store_row_chunk(const MhaArgs& a, const Dest& ds
                                                 int64_t out_row, int c0, const float* o) {
   static_assert(N == 2 || N == 4 || N == 8, "columns per store");
   if (dst.partial) {
-    float* p = a.part_o + dst.po_base + (int64_t)row * dst.po_row + c0;
+    float* p = a.part_o + dst.po_base + (int64_t)row * dst.po_row + out_row * dst.po_out + c0;
     if constexpr (N == 2) {
       *reinterpret_cast<u32x2*>(p) = u32x2{__float_as_uint(o[0]), __float_as_uint(o[1])};
     } else {
@@ -87,7 +90,7 @@ __device__ __forceinline__ void store_row_chunk(const MhaArgs& a, const Dest& ds
 __device__ __forceinline__ void store_lse(const MhaArgs& a, const Dest& dst, int row,
                                           int64_t out_row, float v) {
   if (dst.partial) {
-    a.part_lse[dst.pl_base + (int64_t)row * dst.pl_row] = v;
+    a.part_lse[dst.pl_base + (int64_t)row * dst.pl_row + out_row * dst.pl_out] = v;
   } else if (a.lse) {
     a.lse[out_row] = v;
   }
@@ -1037,8 +1040,10 @@ void mha_forward_kernel(MhaArgs a) {
     dst.partial = it.part >= 0;
     dst.po_base = (int64_t)it.part * kDecodeRows * D;
     dst.po_row = D;
+    dst.po_out = 0;
     dst.pl_base = (int64_t)it.part * kDecodeRows;
     dst.pl_row = 1;
+    dst.pl_out = 0;
     return dst;
   };
   if constexpr (DECODE_ONLY) {
@@ -1076,8 +1081,10 @@ void mha_split_kernel(MhaArgs a) {
   dst.partial = true;
   dst.po_base = ((int64_t)(b * a.Hq + kvh * a.G) * S + s) * D;
   dst.po_row = (int64_t)S * D;
+  dst.po_out = 0;
   dst.pl_base = (int64_t)(b * a.Hq + kvh * a.G) * S + s;
   dst.pl_row = S;
+  dst.pl_out = 0;
   if (t1 <= t0) {  // empty partition: zeros and -inf
     for (int i = threadIdx.x; i < a.G * D; i += blockDim.x)
       a.part_o[dst.po_base + (int64_t)(i / D) * dst.po_row + (i % D)] = 0.f;
@@ -1098,6 +1105,68 @@ void mha_split_kernel(MhaArgs a) {
   it.pad[0] = it.pad[1] = it.pad[2] = 0;
   if constexpr (DEC) run_decode_item<D, 4>(a, it, dst, sm, nullptr);
   else run_prefill_item<D>(a, it, dst, sm);
+}
+
+// pa_forward_chunked: chunked-context processing ("vLLM AMD ROCm Attention
+// Backend Optimization", bullet "Chunked context processing").  Workgroup
+// (request b, KV head, row block, chunk s) runs the prefill-mode item of the
+// block's rows (up to 256: query tokens x the G heads of the KV head) over
+// the keys of chunk s, [s C, (s + 1) C), cut at the causal limit of the
+// block's last row.  Its partials are indexed by output row:
+// part_o[(out_row S + s) D ..] and part_lse[out_row S + s].  A row that sees
+// no key of the chunk gets zeros and -inf: inside the item when another row
+// of the block sees the chunk, here when none does.  Requests with no work
+// (no new token, or inconsistent lengths) write nothing.
+template <int D>
+__global__ __launch_bounds__(kPrefillThreads, 1) void mha_chunked_kernel(MhaArgs a) {
+  __shared__ LdsPrefill<D> sm;
+  const int S = a.num_splits, nblk = a.row_blocks;
+  int idx = blockIdx.x;
+  const int s = idx % S;
+  idx /= S;
+  const int blk = idx % nblk;
+  idx /= nblk;
+  const int kvh = idx % a.Hkv, b = idx / a.Hkv;
+  int nq, L, q0;
+  shape_of(a.qsl, a.seq_lens, a.max_pages, a.P, b, &nq, &L, &q0);
+  const int G = a.G, rows = nq * G, row0 = blk * kPrefillRows;
+  if (row0 >= rows) return;
+  const int nrows = min(kPrefillRows, rows - row0);
+  const int ctx = L - nq;
+  const long long t0 = (long long)s * a.chunk_keys;
+  const long long last_lim = (long long)ctx + (row0 + nrows - 1) / G + 1;
+  const long long t1 = min(last_lim, t0 + a.chunk_keys);
+  if (t1 <= t0) {
+    constexpr int C4 = D / 4;
+    for (int i = threadIdx.x; i < nrows * C4; i += kPrefillThreads) {
+      const int r = i / C4, c = 4 * (i - r * C4);
+      const int rid = row0 + r, t = rid / G;
+      const int64_t out_row = (int64_t)(q0 + t) * a.Hq + kvh * G + (rid - t * G);
+      store16(a.part_o + (out_row * S + s) * D + c, u32x4{0, 0, 0, 0});
+      if (c == 0) a.part_lse[out_row * S + s] = kNegInf;
+    }
+    return;
+  }
+  Dest dst;
+  dst.partial = true;
+  dst.po_base = (int64_t)s * D;
+  dst.po_row = 0;
+  dst.po_out = (int64_t)S * D;
+  dst.pl_base = s;
+  dst.pl_row = 0;
+  dst.pl_out = S;
+  WorkItem it;
+  it.seq = b;
+  it.kvh = kvh;
+  it.row0 = row0;
+  it.nrows = nrows;
+  it.kv_begin = (int)t0;
+  it.kv_end = (int)t1;
+  it.part = 0;
+  it.q0 = q0;
+  it.ctx = ctx;
+  it.pad[0] = it.pad[1] = it.pad[2] = 0;
+  run_prefill_item<D>(a, it, dst, sm);
 }
 
 // Planner: one workgroup of 1024 threads turns (seq_lens, query_start_loc)
@@ -1331,6 +1400,16 @@ hipError_t launch_mha_split(const MhaArgs& a, int D, hipStream_t s) {
     if (dec) hipLaunchKernelGGL((mha_split_kernel<64, true>), dim3(blocks), dim3(kThreads), 0, s, a);
     else hipLaunchKernelGGL((mha_split_kernel<64, false>), dim3(blocks), dim3(kPrefillThreads), 0, s, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_mha_chunked(const MhaArgs& a, int D, hipStream_t s) {
+  const int64_t blocks = (int64_t)a.num_seqs * a.Hkv * a.row_blocks * a.num_splits;
+  if (blocks <= 0) return hipSuccess;
+  if (D == 128)
+    hipLaunchKernelGGL((mha_chunked_kernel<128>), dim3(blocks), dim3(kPrefillThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((mha_chunked_kernel<64>), dim3(blocks), dim3(kPrefillThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -23,7 +23,8 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     names = set(_declared())
-    assert {"pa_forward", "pa_decode_split", "pa_merge_lse", "mla_decode", "pa_workspace_size",
+    assert {"pa_forward", "pa_forward_chunked", "pa_decode_split", "pa_merge_lse", "mla_decode",
+            "pa_workspace_size",
             "mla_workspace_size", "pa_validate", "pa_status_string", "pa_last_hip_error"} <= names
 
 
@@ -116,6 +117,25 @@ def test_decode_split_argument_checks():
     assert call(4, _dims(num_tokens=5)) == binding.PA_ERR_INVALID_ARG  # T != B
     assert call(4, _dims(head_dim_qk=80, head_dim_v=80)) == binding.PA_ERR_UNSUPPORTED
     assert call(4, _dims(num_seqs=0, num_tokens=0)) == binding.PA_OK
+
+
+def test_chunked_argument_checks():
+    lib = pa.library()
+    d = _dims(num_tokens=40, max_q_len=37)
+
+    def call(C, S, dd=d, qsl=FAKE):
+        return lib.pa_forward_chunked(FAKE, FAKE, FAKE, FAKE, FAKE, qsl, 0.1, C, S, FAKE, FAKE,
+                                      ctypes.byref(dd), None)
+    bad = binding.PA_ERR_INVALID_ARG
+    assert call(0, 8) == bad and call(32, 10) == bad and call(100, 4) == bad  # not a multiple of 64
+    assert call(64, 0) == bad and call(64, 257) == bad
+    assert call(64, 4) == bad  # 4 chunks of 64 keys do not cover max_seq_len = 320
+    assert call(64, 5, qsl=None) == bad
+    assert call(64, 5, _dims(num_tokens=40, max_q_len=37, dtype=binding.PA_F32)) == binding.PA_ERR_UNSUPPORTED
+    assert call(64, 5, _dims(num_tokens=40, max_q_len=37, head_dim_qk=80, head_dim_v=80)) == \
+        binding.PA_ERR_UNSUPPORTED
+    assert call(64, 5, _dims(num_seqs=0, num_tokens=0, max_q_len=0)) == binding.PA_OK
+    assert call(64, 5, _dims(num_tokens=0, max_q_len=0)) == binding.PA_OK
 
 
 def test_merge_argument_checks():

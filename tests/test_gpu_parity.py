@@ -200,6 +200,66 @@ def test_long_context_split_full_size(batch, S, lengths):
     check_lse(glse, rlse, "long pa_forward B=%d" % batch)
 
 
+# ------------------------------------------- chunked-context processing
+
+def chunked_parity(b, C, what, S=None, rows=None):
+    """pa_forward_chunked partials against the oracle's chunk partials, and their
+    pa_merge_lse against plain attention (rows: optional sample of output rows)."""
+    g = b.to(DEV)
+    Lmax = max(b.seq_lens_list + [1])
+    S = (Lmax + C - 1) // C if S is None else S
+    say("case %s: B=%d T=%d keys=%d C=%d S=%d" % (what, b.num_seqs, b.num_tokens,
+                                                  sum(b.seq_lens_list), C, S))
+    po, pl = pa.pa_forward_chunked(g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens,
+                                   g.query_start_loc, b.scale, C, num_chunks=S, max_seq_len=Lmax,
+                                   max_q_len=max(b.q_lens + [1]))
+    lse = torch.empty(pl.shape[:2], dtype=torch.float32, device=DEV)
+    out = pa.pa_merge_lse(po, pl, lse=lse)
+    torch.cuda.synchronize()
+    po, pl = po.cpu().numpy(), pl.cpu().numpy()
+    got, glse = out.float().cpu().numpy(), lse.cpu().numpy()
+    if rows is None:
+        rpo, rpl = oracle.chunked_partials(b.q, b.k_cache, b.v_cache, b.block_table, b.seq_lens,
+                                           b.query_start_loc, b.scale, C, S, b.num_kv_heads)
+        check_out(po, rpo, torch.bfloat16, "%s partials" % what)
+        check_lse(pl, rpl, "%s partial lse" % what)
+    ref, rlse = oracle_forward(b, rows)
+    if rows is not None:
+        sel = np.asarray(rows, dtype=bool)
+        got, ref, glse, rlse = got[sel], ref[sel], glse[sel], rlse[sel]
+    check_out(got, ref, torch.bfloat16, "%s merged" % what)
+    check_lse(glse, rlse, "%s merged" % what)
+
+
+@pytest.mark.parametrize("C", [64, 256, 1024])
+def test_chunked_mixed_batch_matches_oracle(C):
+    # decode, short decode, extend, prefill, prefill over several row blocks
+    b = workload.make_batch([1, 1, 300, 37, 520], [900, 50, 700, 0, 0], num_q_heads=32,
+                            num_kv_heads=8, head_dim_qk=128, page_size=16, seed=500 + C)
+    chunked_parity(b, C, "chunked mixed")
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,P,C", [(32, 4, 64, 16, 128), (32, 8, 128, 8, 64),
+                                          (64, 4, 128, 32, 192), (16, 16, 128, 16, 320)])
+def test_chunked_head_and_page_shapes(Hq, Hkv, D, P, C):
+    b = workload.make_batch([70, 1, 129], [400, 333, 64], num_q_heads=Hq, num_kv_heads=Hkv,
+                            head_dim_qk=D, page_size=P, seed=Hq + Hkv + D + P + C)
+    chunked_parity(b, C, "chunked Hq=%d Hkv=%d D=%d P=%d" % (Hq, Hkv, D, P))
+
+
+def test_chunked_extra_chunks_are_empty():
+    b = workload.make_batch([5, 1], [60, 190], num_q_heads=32, num_kv_heads=8, head_dim_qk=128,
+                            page_size=16, seed=77)
+    chunked_parity(b, 64, "chunked extra chunks", S=9)  # 4 chunks would cover 196 keys
+
+
+def test_chunked_long_context_extend():
+    # the case chunking is for: a long cached context under few new tokens
+    b = workload.make_batch([200, 1, 64], [20000, 30000, 9000], num_q_heads=32, num_kv_heads=8,
+                            head_dim_qk=128, page_size=16, seed=91)
+    chunked_parity(b, 4096, "chunked long extend")
+
+
 # --------------------------------------------------- Qwen3 mixed batch (MHA)
 
 def test_qwen3_mixed_scaled_all_rows():
