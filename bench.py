@@ -365,6 +365,45 @@ def main():
             "ms_per_step": round(m_step_ms, 4), "kernel_ms": round(m_kern_ms, 4),
             "algorithmic_bytes": mbytes, "algorithmic_flops": mflops}
         del mb, mout, mws
+        # ---- chunked-context extend: 256 new tokens on 131072 cached tokens, 8192-key chunks,
+        # against the same request in one pa_forward call
+        cb = workload.llama_long_extend(0, device=dev)
+        cL, cq, C = max(cb.seq_lens_list), max(cb.q_lens), 8192
+        cS = (cL + C - 1) // C
+        cpo = torch.empty(cb.num_tokens, cb.num_q_heads, cS, cb.head_dim_v, dtype=torch.float32,
+                          device=dev)
+        cpl = torch.empty(cb.num_tokens, cb.num_q_heads, cS, dtype=torch.float32, device=dev)
+        cout = torch.empty(cb.num_tokens, cb.num_q_heads, cb.head_dim_v, dtype=cb.dtype, device=dev)
+        cdims = pa.make_dims(cb.q, cb.k_cache, cb.v_cache, cb.block_table, cb.seq_lens,
+                             cb.num_tokens, max_seq_len=cL, max_q_len=cq)
+        cws = torch.empty(max(1, pa.pa_workspace_size(cdims)), dtype=torch.uint8, device=dev)
+
+        def cstep():
+            pa.pa_forward_chunked(cb.q, cb.k_cache, cb.v_cache, cb.block_table, cb.seq_lens,
+                                  cb.query_start_loc, cb.scale, C, num_chunks=cS, part_out=cpo,
+                                  part_lse=cpl, max_seq_len=cL, max_q_len=cq)
+            pa.pa_merge_lse(cpo, cpl, out=cout)
+
+        def fstep():
+            pa.pa_forward(cb.q, cb.k_cache, cb.v_cache, cb.block_table, cb.seq_lens,
+                          cb.query_start_loc, cb.scale, out=cout, workspace=cws, max_seq_len=cL,
+                          max_q_len=cq)
+
+        c_step_ms, c_kern_ms = time_steps(cstep, xsteps, 3, lib)
+        f_step_ms, f_kern_ms = time_steps(fstep, xsteps, 3, lib)
+        cflops = workload.algorithmic_flops(cb)
+        result["chunked_extend"] = {
+            "workload": "Llama-3.1-8B-shaped extend, 256 new tokens on 131072 cached tokens, "
+                        "page 16: pa_forward_chunked (8192-key chunks) + pa_merge_lse, against "
+                        "one pa_forward call",
+            "chunk_keys": C, "chunks": cS,
+            "tflops": round(cflops / (c_step_ms * 1e-3) / 1e12, 2),
+            "frac": round(cflops / (c_step_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "ms_per_step": round(c_step_ms, 4), "kernel_ms": round(c_kern_ms, 4),
+            "pa_forward_ms_per_step": round(f_step_ms, 4),
+            "pa_forward_tflops": round(cflops / (f_step_ms * 1e-3) / 1e12, 2),
+            "algorithmic_flops": cflops}
+        del cb, cpo, cpl, cout, cws
 
     if b_host_needed:
         result["cpu_baseline"] = cpu_baseline(b, nbytes)

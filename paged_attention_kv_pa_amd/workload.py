@@ -250,6 +250,15 @@ def llama_long(batch: int = 1, case: int = 0, device="cpu", lengths: Optional[Se
                       name="llama_long/%d" % case)
 
 
+def llama_long_extend(case: int = 0, device="cpu", new_tokens: int = 256,
+                      cached: int = 131072) -> Batch:
+    """Long-context extend with Llama-3.1-8B heads: new_tokens new tokens on a cached
+    context of `cached` tokens (one request), page 16, bf16."""
+    return make_batch([new_tokens], [cached], num_q_heads=32, num_kv_heads=8, head_dim_qk=128,
+                      page_size=16, dtype=BF16, seed=case_seed(3, 100 + case), device=device,
+                      name="llama_long_extend/%d" % case)
+
+
 def qwen3_mixed(case: int = 0, device="cpu", n_decode: int = 48, n_extend: int = 8,
                 n_prefill: int = 8, dec=(1024, 16384), ext_q=(256, 2048),
                 ext_c=(4096, 32768), pre_q=(512, 8192)) -> Batch:

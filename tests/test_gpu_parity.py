@@ -260,6 +260,14 @@ def test_chunked_long_context_extend():
     chunked_parity(b, 4096, "chunked long extend")
 
 
+def test_chunked_long_extend_full_size_sampled_rows():
+    # the bench's chunked-extend workload: 256 new tokens on 131072 cached tokens
+    b = workload.llama_long_extend(0)
+    rows = np.zeros((b.num_tokens, b.num_q_heads), dtype=bool)
+    rows[[0, 100, 255], :] = True
+    chunked_parity(b, 8192, "chunked long extend full size (sampled rows)", rows=rows)
+
+
 # --------------------------------------------------- Qwen3 mixed batch (MHA)
 
 def test_qwen3_mixed_scaled_all_rows():
