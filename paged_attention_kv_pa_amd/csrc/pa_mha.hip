@@ -458,9 +458,13 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
   const char* kbase = uniform_ptr((const char*)((const __bf16*)a.k_cache + (int64_t)kvh * P * D));
   const char* vbase = uniform_ptr((const char*)((const __bf16*)a.v_cache + (int64_t)kvh * D * P));
 
-  // Wave w copies, of each 64-key tile, half of the column chunks of K (the
-  // half w & 1) for the 16 keys of group w / 2, and V^T of the 8-key chunk w.  Its
-  // keys lie in the two 8-key groups of key group w / 2, one page each; keys
+  // The copies are issued by the four waves of group A (waves 0-3, which
+  // start every step with their matrix products, see the schedule below):
+  // wave w copies, of each 64-key tile, all column chunks of K for the 16
+  // keys of group w and V^T of the 8-key chunks 2w and 2w + 1.  Issued by
+  // all eight waves they cost the softmax group time on its critical path
+  // (measured 4.6% slower for the Qwen3 prefill + extend batch).  The keys
+  // of group w lie in two 8-key groups, one page each; keys
   // at or past kv_end are clamped to kv_end - 1 (real data, masked or zeroed
   // later).  The block table is read-only for the whole call: reading it
   // through the constant address space lets these uniform reads become
@@ -470,12 +474,13 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
   // Copy addressing is wave-uniform wherever it can be (scalar registers and
   // scalar arithmetic): the per-lane part is one 32-bit offset per copy.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int kgroup = wave_u >> 1;
+  const bool copier = wave_u < kPrefillWaves / 2;  // group A
+  const int kgroup = wave_u & (kPrefillWaves / 2 - 1);
   const uint32_t lds_stage0 = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)sm.stage[0]);
   struct TilePages {
-    int pg0, first0;  // physical page and its first key, keys 16 (w / 2) + 0 .. 7
-    int pg1, first1;  // the same for keys 16 (w / 2) + 8 .. 15
+    int pg0, first0;  // physical page and its first key, keys 16 kgroup + 0 .. 7
+    int pg1, first1;  // the same for keys 16 kgroup + 8 .. 15
   };
   auto load_pages = [&](int t0) {
     TilePages tp;
@@ -489,33 +494,38 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
     return tp;
   };
   auto issue_tile = [&](int t0, int st, const TilePages& tp) {
+    if (!copier) return;
     const uint32_t stage = lds_stage0 + st * LY::kStageBytes;
     const int ts = __builtin_amdgcn_readfirstlane(t0);
-    {
-      // four consecutive lanes copy 64 contiguous bytes of one key row (in
-      // swizzled order), so a copy instruction reads 16 whole 64-byte pieces
-      const int k16 = lane >> 2;
-      const int cl = (lane & 3) ^ ((k16 >> 2) & 3);
-      const bool hi = k16 >= 8;
-      const int key = min(ts + 16 * kgroup + k16, kv_end - 1);
-      const int c0 = (wave_u & 1) * (LY::kChunks / 2);  // first column chunk of this wave
-      const char* page0 = kbase + (int64_t)tp.pg0 * page_elems * 2;
-      const char* page1 = kbase + (int64_t)tp.pg1 * page_elems * 2;
-      const int off = ((key - (hi ? tp.first1 : tp.first0)) * D + 8 * (c0 + cl)) * 2;
-      const char* src = (hi ? page1 : page0) + off;
 #pragma unroll
-      for (int j = 0; j < LY::kKCopies; ++j)
-        lds_dma16_m0(src + 64 * j, stage + LY::koff(16 * kgroup, c0 + 4 * j));
-    }
-    {
-      const bool hi = wave_u & 1;
-      const int cs = min(ts + 8 * wave_u, (kv_end - 1) & ~7);
-      const int pg = hi ? tp.pg1 : tp.pg0;
-      const int slot = cs - (hi ? tp.first1 : tp.first0);
-      const char* vpage = vbase + ((int64_t)pg * page_elems + slot) * 2;
+    for (int half = 0; half < 2; ++half) {  // the two 8-key halves of the group
+      {
+        // four consecutive lanes copy 64 contiguous bytes of one key row (in
+        // swizzled order), so a copy instruction reads 16 whole 64-byte pieces
+        const int k16 = lane >> 2;
+        const int cl = (lane & 3) ^ ((k16 >> 2) & 3);
+        const bool hi = k16 >= 8;
+        const int key = min(ts + 16 * kgroup + k16, kv_end - 1);
+        const int c0 = half * (LY::kChunks / 2);  // first column chunk of this half
+        const char* page0 = kbase + (int64_t)tp.pg0 * page_elems * 2;
+        const char* page1 = kbase + (int64_t)tp.pg1 * page_elems * 2;
+        const int off = ((key - (hi ? tp.first1 : tp.first0)) * D + 8 * (c0 + cl)) * 2;
+        const char* src = (hi ? page1 : page0) + off;
 #pragma unroll
-      for (int i = 0; i < LY::kVCopies; ++i)
-        lds_dma16_m0(vpage + (64 * i + lane) * P * 2, stage + LY::voff(wave_u, 64 * i));
+        for (int j = 0; j < LY::kKCopies; ++j)
+          lds_dma16_m0(src + 64 * j, stage + LY::koff(16 * kgroup, c0 + 4 * j));
+      }
+      {
+        const bool hi = half;
+        const int vch = 2 * kgroup + half;  // the 8-key chunk
+        const int cs = min(ts + 8 * vch, (kv_end - 1) & ~7);
+        const int pg = hi ? tp.pg1 : tp.pg0;
+        const int slot = cs - (hi ? tp.first1 : tp.first0);
+        const char* vpage = vbase + ((int64_t)pg * page_elems + slot) * 2;
+#pragma unroll
+        for (int i = 0; i < LY::kVCopies; ++i)
+          lds_dma16_m0(vpage + (64 * i + lane) * P * 2, stage + LY::voff(vch, 64 * i));
+      }
     }
   };
 
@@ -645,7 +655,7 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
   if (ntiles > 0) issue_tile(kv_begin, 0, load_pages(kv_begin));
   if (ntiles > 1) {
     issue_tile(kv_begin + kTK, 1, load_pages(kv_begin + kTK));
-    wait_vmcnt<LY::kCopies>();
+    if (copier) wait_vmcnt<2 * LY::kCopies>();
   } else {
     wait_vmcnt<0>();
   }
@@ -678,8 +688,11 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
     if (group_b) gemm_phase(t);
     else softmax_phase(t);
     // this thread's part of tile t + 1 is in LDS (tile t + 2 may stay in flight)
-    if (t + 2 < ntiles) wait_vmcnt<LY::kCopies>();
-    else wait_vmcnt<0>();
+    if (t + 2 < ntiles) {
+      if (copier) wait_vmcnt<2 * LY::kCopies>();
+    } else {
+      wait_vmcnt<0>();
+    }
     __syncthreads();
   }
   __syncthreads();  // every wave is done with the ring before the next item
