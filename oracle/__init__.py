@@ -29,6 +29,7 @@ _LIB = os.path.join(_HERE, "libpa_oracle.so")
 
 F32, BF16 = 0, 1
 LAYOUT_MHA, LAYOUT_MLA = 0, 1
+MASK_CAUSAL, MASK_FULL, MASK_PREFIX = 0, 1, 2
 _ERRORS = {1: "invalid sizes", 2: "invalid request data (lengths or block table)",
            3: "out of memory"}
 
@@ -55,6 +56,9 @@ def _load():
             p, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
             lib.orc_attention.argtypes = [p, p, p, i32, p, p, p] + [i32] * 9 + [f32, p, p, p, i32]
             lib.orc_attention.restype = i32
+            lib.orc_attention_masked.argtypes = [p, p, p, i32, p, p, p] + [i32] * 9 + [f32, i32, p,
+                                                                                     p, p, p, i32]
+            lib.orc_attention_masked.restype = i32
             lib.orc_decode_split.argtypes = [p, p, p, i32, p, p] + [i32] * 9 + [f32, i32, p, p, i32]
             lib.orc_decode_split.restype = i32
             lib.orc_chunked_partials.argtypes = [p, p, p, i32, p, p, p] + [i32] * 9 + [f32, i32, i32,
@@ -119,8 +123,9 @@ def _check(rc):
 
 def attention(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale,
               num_kv_heads, head_dim_v=None, layout=LAYOUT_MHA, rows=None,
-              nthreads=None):
-    """Paged causal attention over a varlen batch, in fp64.
+              nthreads=None, mask=MASK_CAUSAL, prefix_lens=None):
+    """Paged attention over a varlen batch, in fp64: causal, or MASK_FULL / MASK_PREFIX
+    (prefix_lens int32 [B]) as defined in pa_oracle.c.
 
     q: [T, Hq, Dqk]; k_cache / v_cache in the layouts of pa_oracle.c
     (for LAYOUT_MLA pass the latent cache as both); block_table [B, max_pages];
@@ -150,9 +155,20 @@ def attention(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale
     if rows is not None:
         sel = np.ascontiguousarray(np.asarray(rows, dtype=np.uint8).reshape(T, Hq))
     nt = max_threads() if nthreads is None else int(nthreads)
-    rc = lib.orc_attention(_ptr(qa), _ptr(ka), _ptr(va), dt, _ptr(bt), _ptr(sl), _ptr(qs),
-                           B, Hq, int(num_kv_heads), Dqk, Dv, P, num_pages, bt.shape[1],
-                           layout, float(scale), _ptr(sel), _ptr(out), _ptr(lse), nt)
+    if mask == MASK_CAUSAL and prefix_lens is None:
+        rc = lib.orc_attention(_ptr(qa), _ptr(ka), _ptr(va), dt, _ptr(bt), _ptr(sl), _ptr(qs),
+                               B, Hq, int(num_kv_heads), Dqk, Dv, P, num_pages, bt.shape[1],
+                               layout, float(scale), _ptr(sel), _ptr(out), _ptr(lse), nt)
+    else:
+        pfx = None
+        if prefix_lens is not None:
+            pfx = _i32(prefix_lens)
+            if pfx.shape != (B,):
+                raise ValueError("prefix_lens must have B entries")
+        rc = lib.orc_attention_masked(_ptr(qa), _ptr(ka), _ptr(va), dt, _ptr(bt), _ptr(sl),
+                                      _ptr(qs), B, Hq, int(num_kv_heads), Dqk, Dv, P, num_pages,
+                                      bt.shape[1], layout, float(scale), int(mask), _ptr(pfx),
+                                      _ptr(sel), _ptr(out), _ptr(lse), nt)
     _check(rc)
     return out, lse
 

@@ -24,6 +24,14 @@
  *     q_b new tokens on top of c_b = L_b - q_b cached ones.  Causality is
  *     aligned to the end of the sequence: new token j sits at position
  *     c_b + j and sees keys 0 .. c_b + j.
+ *   - Masks other than causal (Triton deep dive, section on the backend's
+ *     use cases: encoder / decoder attention and multimodal prefix
+ *     attention, named there without formulas).  ORC_MASK_FULL: every new
+ *     token of a request sees all L_b keys (encoder self-attention, or
+ *     cross-attention onto a cached encoder output).  ORC_MASK_PREFIX: the
+ *     first prefix_lens[b] key positions form a bidirectional prefix, the
+ *     rest stays causal; the token at position p sees keys
+ *     0 .. max(p, prefix_lens[b] - 1), at most L_b - 1.
  *   - Split-KV partials and their log-sum-exp merge (Triton deep dive,
  *     section "Parallel tiled softmax (3D kernel)"; ROCm backends, bullet
  *     "Chunked context processing"): the key range is cut into contiguous
@@ -54,6 +62,7 @@
 
 enum { ORC_F32 = 0, ORC_BF16 = 1 };
 enum { ORC_LAYOUT_MHA = 0, ORC_LAYOUT_MLA = 1 };
+enum { ORC_MASK_CAUSAL = 0, ORC_MASK_FULL = 1, ORC_MASK_PREFIX = 2 };
 enum { ORC_OK = 0, ORC_ERR_ARG = 1, ORC_ERR_DATA = 2, ORC_ERR_NOMEM = 3 };
 
 /* Read element idx of an array of the given dtype, widened to double. */
@@ -143,7 +152,8 @@ static int check_common(int B, int Hq, int Hkv, int Dqk, int Dv, int P,
 }
 
 /*
- * Paged causal attention over a varlen continuous batch.
+ * Paged attention over a varlen continuous batch, causal or with one of the
+ * other masks above (mask; prefix_lens [B] is read for ORC_MASK_PREFIX only).
  *   q        [T, Hq, Dqk] (dtype), T = qsl[B]
  *   out      [T, Hq, Dv] double;  lse [T, Hq] double (may be NULL)
  *   row_sel  optional [T * Hq] bytes; when given, only rows with a nonzero
@@ -151,14 +161,18 @@ static int check_common(int B, int Hq, int Hkv, int Dqk, int Dv, int P,
  * Returns ORC_OK, ORC_ERR_ARG (bad sizes) or ORC_ERR_DATA (a request with
  * seq_len < q_len, a negative count, or a table entry out of range).
  */
-int orc_attention(const void* q, const void* kc, const void* vc, int dtype,
-                  const int32_t* block_table, const int32_t* seq_lens,
-                  const int32_t* qsl, int B, int Hq, int Hkv, int Dqk, int Dv,
-                  int P, int num_pages, int max_pages, int layout, float scale,
-                  const uint8_t* row_sel, double* out, double* lse,
-                  int nthreads) {
+int orc_attention_masked(const void* q, const void* kc, const void* vc, int dtype,
+                         const int32_t* block_table, const int32_t* seq_lens,
+                         const int32_t* qsl, int B, int Hq, int Hkv, int Dqk, int Dv,
+                         int P, int num_pages, int max_pages, int layout, float scale,
+                         int mask, const int32_t* prefix_lens,
+                         const uint8_t* row_sel, double* out, double* lse,
+                         int nthreads) {
   int rc = check_common(B, Hq, Hkv, Dqk, Dv, P, max_pages, layout);
   if (rc) return rc;
+  if (mask != ORC_MASK_CAUSAL && mask != ORC_MASK_FULL && mask != ORC_MASK_PREFIX)
+    return ORC_ERR_ARG;
+  if (mask == ORC_MASK_PREFIX && !prefix_lens) return ORC_ERR_ARG;
   const int g = Hq / Hkv;
   const double sigma = (double)scale;
   int err = ORC_OK;
@@ -210,8 +224,13 @@ int orc_attention(const void* q, const void* kc, const void* vc, int dtype,
           if (row_sel && !row_sel[(size_t)i * Hq + hh]) continue;
           for (int d = 0; d < Dqk; ++d)
             qrow[d] = load_elem(q, dtype, ((size_t)i * Hq + hh) * Dqk + d);
+          /* keys [0, end) are visible: causal end = pos + 1 */
+          int end = pos + 1;
+          if (mask == ORC_MASK_FULL) end = L;
+          if (mask == ORC_MASK_PREFIX && prefix_lens[b] > end)
+            end = prefix_lens[b] < L ? prefix_lens[b] : L;
           double l_out;
-          attend(qrow, Kd, Vd, 0, pos + 1, Dqk, Dv, sigma, s,
+          attend(qrow, Kd, Vd, 0, end, Dqk, Dv, sigma, s,
                  out + ((size_t)i * Hq + hh) * Dv, &l_out);
           if (lse) lse[(size_t)i * Hq + hh] = l_out;
         }
@@ -220,6 +239,19 @@ int orc_attention(const void* q, const void* kc, const void* vc, int dtype,
     free(Kd); free(Vd); free(qrow); free(s);
   }
   return err;
+}
+
+/* Causal paged attention (orc_attention_masked with ORC_MASK_CAUSAL). */
+int orc_attention(const void* q, const void* kc, const void* vc, int dtype,
+                  const int32_t* block_table, const int32_t* seq_lens,
+                  const int32_t* qsl, int B, int Hq, int Hkv, int Dqk, int Dv,
+                  int P, int num_pages, int max_pages, int layout, float scale,
+                  const uint8_t* row_sel, double* out, double* lse,
+                  int nthreads) {
+  return orc_attention_masked(q, kc, vc, dtype, block_table, seq_lens, qsl, B,
+                              Hq, Hkv, Dqk, Dv, P, num_pages, max_pages,
+                              layout, scale, ORC_MASK_CAUSAL, NULL, row_sel,
+                              out, lse, nthreads);
 }
 
 /*

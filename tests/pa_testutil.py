@@ -78,8 +78,14 @@ def causal_mask(nq, L):
     return t <= c + j
 
 
-def sdpa_reference(q, K, V, scale):
-    """float64 torch SDPA (GQA via enable_gqa) with the end-aligned causal mask.
+def prefix_mask(nq, L, prefix):
+    """Bool [nq, L]: causal, plus keys 0 .. prefix - 1 visible to every query."""
+    return causal_mask(nq, L) | (torch.arange(L).unsqueeze(0) < prefix)
+
+
+def sdpa_reference(q, K, V, scale, mask=None):
+    """float64 torch SDPA (GQA via enable_gqa) with the end-aligned causal mask, or
+    with `mask` (bool [nq, L], True = visible) when given.
 
     q [nq, Hq, Dqk], K [L, Hkv, Dqk], V [L, Hkv, Dv] -> out [nq, Hq, Dv], lse [nq, Hq].
     """
@@ -87,7 +93,7 @@ def sdpa_reference(q, K, V, scale):
     qd = q.double().permute(1, 0, 2).unsqueeze(0)
     kd = K.double().permute(1, 0, 2).unsqueeze(0)
     vd = V.double().permute(1, 0, 2).unsqueeze(0)
-    mask = causal_mask(nq, L)
+    mask = causal_mask(nq, L) if mask is None else mask
     out = F.scaled_dot_product_attention(qd, kd, vd, attn_mask=mask, scale=scale, enable_gqa=True)
     g = q.shape[1] // K.shape[1]
     kx = kd.repeat_interleave(g, dim=1)

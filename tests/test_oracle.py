@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import oracle
-from pa_testutil import dense_request, scatter_pages, sdpa_reference
+from pa_testutil import dense_request, prefix_mask, scatter_pages, sdpa_reference
 
 TOL = 1e-12
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -179,6 +179,62 @@ def test_chunked_partials_match_sdpa_on_visible_keys():
                 np.testing.assert_allclose(pl[i, :, s], rl[0], atol=TOL, rtol=0)
             i += 1
     assert empty > 0 and i == c["q"].shape[0]
+
+
+MASK_SPECS = [(1, 0), (1, 12), (4, 9), (6, 0), (3, 30), (7, 5)]
+
+
+def _masked(c, mask, prefix=None, scale=0.45):
+    lay = oracle.LAYOUT_MHA
+    return oracle.attention(c["q"], c["kc"], c["vc"], c["bt"], c["seq"], c["qsl"], scale, 2,
+                            head_dim_v=8, layout=lay, mask=mask,
+                            prefix_lens=None if prefix is None else np.asarray(prefix, np.int32))
+
+
+def test_full_mask_equals_unmasked_sdpa():
+    """MASK_FULL: every new token sees all keys of its request (SDPA with no mask)."""
+    c = _build_case(41, MASK_SPECS, 4, 2, 8, 8, 4)
+    out, lse = _masked(c, oracle.MASK_FULL)
+    i0 = 0
+    for (nq, ctx), q, K, V in zip(MASK_SPECS, c["qs"], c["Ks"], c["Vs"]):
+        full = torch.ones(nq, nq + ctx, dtype=torch.bool)
+        ro, rl = sdpa_reference(q, K, V, float(np.float32(0.45)), mask=full)
+        np.testing.assert_allclose(out[i0:i0 + nq], ro, atol=TOL, rtol=0)
+        np.testing.assert_allclose(lse[i0:i0 + nq], rl, atol=TOL, rtol=0)
+        i0 += nq
+
+
+@pytest.mark.parametrize("prefixes", [[0, 5, 9, 3, 20, 2], [1, 13, 13, 6, 33, 12], [2, 40, 1, 4, 7, 11]])
+def test_prefix_mask_matches_sdpa(prefixes):
+    """MASK_PREFIX: causal plus a bidirectional prefix of prefix_lens[b] keys (lengths
+    below, inside and past the new tokens, and past the end of the request)."""
+    c = _build_case(43, MASK_SPECS, 4, 2, 8, 8, 4)
+    out, lse = _masked(c, oracle.MASK_PREFIX, prefixes)
+    i0 = 0
+    for (nq, ctx), q, K, V, pf in zip(MASK_SPECS, c["qs"], c["Ks"], c["Vs"], prefixes):
+        m = prefix_mask(nq, nq + ctx, pf)
+        ro, rl = sdpa_reference(q, K, V, float(np.float32(0.45)), mask=m)
+        np.testing.assert_allclose(out[i0:i0 + nq], ro, atol=TOL, rtol=0)
+        np.testing.assert_allclose(lse[i0:i0 + nq], rl, atol=TOL, rtol=0)
+        i0 += nq
+
+
+def test_mask_special_cases_reduce_to_causal_or_full():
+    """An empty prefix is causal and a prefix covering every key is full, bit for
+    bit; decode rows (one new token) see every key under all three masks."""
+    c = _build_case(45, MASK_SPECS, 4, 2, 8, 8, 4)
+    causal = _masked(c, oracle.MASK_CAUSAL)
+    full = _masked(c, oracle.MASK_FULL)
+    zero = _masked(c, oracle.MASK_PREFIX, [0] * len(MASK_SPECS))
+    big = _masked(c, oracle.MASK_PREFIX, [10 ** 6] * len(MASK_SPECS))
+    for a, b in ((causal, zero), (full, big)):
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    qsl = c["qsl"]
+    for i, (nq, ctx) in enumerate(MASK_SPECS):
+        if nq == 1:
+            r = qsl[i]
+            assert np.array_equal(causal[0][r], full[0][r])
+    assert not np.allclose(causal[0], full[0])
 
 
 def test_constant_value_rows_sum_to_one():

@@ -20,7 +20,12 @@ SRC = os.path.join(os.path.dirname(real_oracle.__file__), "pa_oracle.c")
 INIT = os.path.join(os.path.dirname(real_oracle.__file__), "__init__.py")
 
 MUTANTS = {
-    "causal_off_by_one": ("attend(qrow, Kd, Vd, 0, pos + 1,", "attend(qrow, Kd, Vd, 0, pos,"),
+    "causal_off_by_one": ("          int end = pos + 1;", "          int end = pos;"),
+    "full_mask_still_causal": ("          if (mask == ORC_MASK_FULL) end = L;", ""),
+    "prefix_capped_one_short": ("            end = prefix_lens[b] < L ? prefix_lens[b] : L;",
+                                "            end = prefix_lens[b] < L ? prefix_lens[b] : L - 1;"),
+    "prefix_off_by_one": ("if (mask == ORC_MASK_PREFIX && prefix_lens[b] > end)\n            end = prefix_lens[b] < L ? prefix_lens[b] : L;",
+                          "if (mask == ORC_MASK_PREFIX && prefix_lens[b] > end)\n            end = prefix_lens[b] + 1 < L ? prefix_lens[b] + 1 : L;"),
     "scale_dropped": ("s[t] = sigma * dot;", "s[t] = dot;"),
     "gqa_head_ignored": ("key_index(layout, page, slot, h, d, Hkv, P, Dqk)",
                          "key_index(layout, page, slot, 0, d, Hkv, P, Dqk)"),
@@ -55,11 +60,15 @@ def _battery():
             out.append(("sdpa", lambda c=case, d=dt: pins.test_bruteforce_against_torch_sdpa(c, d)))
     for S in (1, 2, 3, 7, 64):
         out.append(("split", lambda s=S: pins.test_split_then_merge_equals_unsplit(s)))
+    for pf in ([0, 5, 9, 3, 20, 2], [1, 13, 13, 6, 33, 12], [2, 40, 1, 4, 7, 11]):
+        out.append(("prefix", lambda p=pf: pins.test_prefix_mask_matches_sdpa(p)))
     for C in (1, 3, 4, 16, 64):
         out.append(("chunked", lambda c=C: pins.test_chunked_then_merge_equals_unchunked(c)))
     for name in ("test_page_permutation_is_bitwise_invariant",
                  "test_split_partials_match_sdpa_on_their_ranges",
                  "test_chunked_partials_match_sdpa_on_visible_keys",
+                 "test_full_mask_equals_unmasked_sdpa",
+                 "test_mask_special_cases_reduce_to_causal_or_full",
                  "test_constant_value_rows_sum_to_one", "test_length_one_context_returns_v0",
                  "test_equal_keys_give_mean_of_visible_values",
                  "test_zero_query_gives_mean_and_log_count",
