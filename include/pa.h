@@ -83,6 +83,17 @@ typedef enum pa_status {
 
 typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
 
+/*
+ * Which keys a new token sees (pa_forward_masked).  With c_b = seq_lens[b] -
+ * q_b cached keys, new token j of request b sits at position c_b + j.
+ *   PA_MASK_CAUSAL  keys 0 .. c_b + j (pa_forward)
+ *   PA_MASK_FULL    every key of the request (encoder / decoder attention)
+ *   PA_MASK_PREFIX  keys 0 .. max(c_b + j, prefix_lens[b] - 1), at most
+ *                   seq_lens[b] - 1: the first prefix_lens[b] positions are
+ *                   a bidirectional prefix (multimodal prefix attention)
+ */
+typedef enum pa_mask { PA_MASK_CAUSAL = 0, PA_MASK_FULL = 1, PA_MASK_PREFIX = 2 } pa_mask;
+
 /* Shapes and host-side capacities of one call.  Capacities (max_*) size the
  * workspace and the launch grids without reading device memory. */
 typedef struct pa_dims {
@@ -129,6 +140,23 @@ PA_API pa_status pa_forward(const void* q, const void* k_cache, const void* v_ca
                      const int32_t* query_start_loc, float scale, void* out,
                      float* lse, const pa_dims* dims, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/*
+ * pa_forward_masked — pa_forward with another mask than causal ([TDD]
+ * section on the backend's use cases, which names encoder / decoder
+ * attention and multimodal prefix attention): mask is a pa_mask;
+ * prefix_lens is an int32 [B] device array for PA_MASK_PREFIX (any values;
+ * negative ones act as 0) and must be NULL for the other masks.  Everything
+ * else, including the workspace, is as for pa_forward, which is this call
+ * with PA_MASK_CAUSAL.  Returns PA_ERR_INVALID_ARG for an unknown mask or a
+ * prefix_lens that does not match it.
+ */
+PA_API pa_status pa_forward_masked(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* block_table, const int32_t* seq_lens,
+                                   const int32_t* query_start_loc, int32_t mask,
+                                   const int32_t* prefix_lens, float scale, void* out,
+                                   float* lse, const pa_dims* dims, void* workspace,
+                                   size_t workspace_bytes, void* stream);
 
 /*
  * pa_decode_split — first launch of split-KV decode ([TDD] section

@@ -6,12 +6,14 @@ declared in ``include/pa.h``.  Functions carry the names of the C entry
 points.  The library is loaded on first use and a missing or unloadable
 library raises — there is no fallback.
 """
-from .binding import (PaError, pa_decode_split, pa_forward, pa_forward_chunked, pa_merge_lse,
+from .binding import (PA_MASK_CAUSAL, PA_MASK_FULL, PA_MASK_PREFIX, PaError, pa_decode_split,
+                      pa_forward, pa_forward_chunked, pa_forward_masked, pa_merge_lse,
                       pa_status_string,
                       pa_validate, pa_workspace_size, mla_decode, mla_workspace_size,
                       library, library_path, make_dims)
 
-__all__ = ["PaError", "pa_forward", "pa_forward_chunked", "pa_decode_split", "pa_merge_lse",
+__all__ = ["PaError", "pa_forward", "pa_forward_masked", "pa_forward_chunked", "pa_decode_split",
+           "pa_merge_lse", "PA_MASK_CAUSAL", "PA_MASK_FULL", "PA_MASK_PREFIX",
            "mla_decode",
            "pa_workspace_size", "mla_workspace_size", "pa_validate", "pa_status_string",
            "library", "library_path", "make_dims"]

@@ -60,6 +60,8 @@ def library():
             lib.pa_workspace_size.restype = sz
             lib.pa_forward.argtypes = [p, p, p, p, p, p, f32, p, p, dp, p, sz, p]
             lib.pa_forward.restype = i32
+            lib.pa_forward_masked.argtypes = [p, p, p, p, p, p, i32, p, f32, p, p, dp, p, sz, p]
+            lib.pa_forward_masked.restype = i32
             lib.pa_decode_split.argtypes = [p, p, p, p, p, f32, i32, p, p, dp, p]
             lib.pa_decode_split.restype = i32
             lib.pa_forward_chunked.argtypes = [p, p, p, p, p, p, f32, i32, i32, p, p, dp, p]
@@ -163,6 +165,9 @@ def mla_workspace_size(dims: PaDims, num_splits: int = 0) -> int:
     return int(library().mla_workspace_size(ctypes.byref(dims), int(num_splits)))
 
 
+PA_MASK_CAUSAL, PA_MASK_FULL, PA_MASK_PREFIX = 0, 1, 2
+
+
 def pa_forward(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale, out=None,
                lse=None, workspace=None, max_seq_len=None, max_q_len=None, stream=None):
     """Paged causal attention over a varlen batch (see pa_forward in include/pa.h).
@@ -171,6 +176,25 @@ def pa_forward(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scal
     block_table int32 [B, max_pages]; seq_lens int32 [B]; query_start_loc int32 [B+1].
     Returns out ([T, Hq, D], allocated if not given).
     """
+    return _forward(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale, out, lse,
+                    workspace, max_seq_len, max_q_len, stream, None, None)
+
+
+def pa_forward_masked(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale, mask,
+                      prefix_lens=None, out=None, lse=None, workspace=None, max_seq_len=None,
+                      max_q_len=None, stream=None):
+    """pa_forward with mask PA_MASK_CAUSAL, PA_MASK_FULL or PA_MASK_PREFIX (prefix_lens
+    int32 [B] on the device for the last); see pa_forward_masked in include/pa.h."""
+    if prefix_lens is not None:
+        _need(prefix_lens.dtype == torch.int32 and prefix_lens.is_contiguous()
+              and prefix_lens.device == q.device and tuple(prefix_lens.shape) == (int(seq_lens.shape[0]),),
+              "prefix_lens must be contiguous int32 [B] on q's device")
+    return _forward(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale, out, lse,
+                    workspace, max_seq_len, max_q_len, stream, int(mask), prefix_lens)
+
+
+def _forward(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale, out, lse,
+             workspace, max_seq_len, max_q_len, stream, mask, prefix_lens):
     _check_common(q, k_cache, v_cache, block_table, seq_lens)
     _need(query_start_loc.dtype == torch.int32 and query_start_loc.is_contiguous()
           and query_start_loc.device == q.device, "query_start_loc must be contiguous int32 on q's device")
@@ -189,11 +213,20 @@ def pa_forward(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scal
     need = pa_workspace_size(dims)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    st = library().pa_forward(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
-                              _ptr(seq_lens), _ptr(query_start_loc), float(scale), _ptr(out),
-                              _ptr(lse), ctypes.byref(dims), _ptr(workspace),
-                              workspace.numel() * workspace.element_size(), _stream(q.device, stream))
-    _check(st, "pa_forward")
+    nbytes = workspace.numel() * workspace.element_size()
+    if mask is None:
+        st = library().pa_forward(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                  _ptr(seq_lens), _ptr(query_start_loc), float(scale), _ptr(out),
+                                  _ptr(lse), ctypes.byref(dims), _ptr(workspace), nbytes,
+                                  _stream(q.device, stream))
+        _check(st, "pa_forward")
+    else:
+        st = library().pa_forward_masked(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                         _ptr(seq_lens), _ptr(query_start_loc), mask,
+                                         _ptr(prefix_lens), float(scale), _ptr(out), _ptr(lse),
+                                         ctypes.byref(dims), _ptr(workspace), nbytes,
+                                         _stream(q.device, stream))
+        _check(st, "pa_forward_masked")
     return out
 
 

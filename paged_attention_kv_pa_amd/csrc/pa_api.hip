@@ -158,10 +158,28 @@ pa_status pa_forward(const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* block_table, const int32_t* seq_lens,
                      const int32_t* query_start_loc, float scale, void* out, float* lse,
                      const pa_dims* d, void* workspace, size_t workspace_bytes, void* stream) {
+  return pa_forward_masked(q, k_cache, v_cache, block_table, seq_lens, query_start_loc,
+                           PA_MASK_CAUSAL, nullptr, scale, out, lse, d, workspace,
+                           workspace_bytes, stream);
+}
+
+static_assert(PA_MASK_CAUSAL == pa::kMaskCausal && PA_MASK_FULL == pa::kMaskFull &&
+                  PA_MASK_PREFIX == pa::kMaskPrefix,
+              "mask codes");
+
+pa_status pa_forward_masked(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_table, const int32_t* seq_lens,
+                            const int32_t* query_start_loc, int32_t mask,
+                            const int32_t* prefix_lens, float scale, void* out, float* lse,
+                            const pa_dims* d, void* workspace, size_t workspace_bytes,
+                            void* stream) {
   pa_status st = check_dims(d);
   if (st != PA_OK) return st;
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !query_start_loc || !out)
     return PA_ERR_INVALID_ARG;
+  if (mask != PA_MASK_CAUSAL && mask != PA_MASK_FULL && mask != PA_MASK_PREFIX)
+    return PA_ERR_INVALID_ARG;
+  if ((mask == PA_MASK_PREFIX) != (prefix_lens != nullptr)) return PA_ERR_INVALID_ARG;
   st = check_mha_support(d);
   if (st != PA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
@@ -189,6 +207,8 @@ pa_status pa_forward(const void* q, const void* k_cache, const void* v_cache,
     a.P = d->page_size;
     a.max_pages = d->max_pages_per_seq;
     a.num_splits = 1;
+    a.mask = mask;
+    a.prefix_lens = prefix_lens;
     hipError_t e = mark(g_ev_start, s);
     if (e == hipSuccess) e = pa::launch_f32_forward(a, s);
     if (e == hipSuccess) e = mark(g_ev_stop, s);
@@ -257,6 +277,8 @@ pa_status pa_forward(const void* q, const void* k_cache, const void* v_cache,
   a.max_pages = d->max_pages_per_seq;
   a.num_splits = 1;
   a.target_items = pl.target_items;
+  a.mask = mask;
+  a.prefix_lens = prefix_lens;
   if (fused && (e = pa::launch_reset_queue(ctrl, s)) != hipSuccess) return hip_fail(e);
   if ((e = mark(g_ev_start, s)) != hipSuccess) return hip_fail(e);
   e = fused ? pa::launch_mha_forward_fused(a, D, grid, s)

@@ -17,7 +17,7 @@ namespace {
 
 constexpr int kF32MaxD = 256;
 
-// One query row over keys [k0, k1) (k1 already capped by the causal limit).
+// One query row over keys [k0, k1) (k1 already capped by the row's visible limit).
 // Writes out[0..Dv) (normalised) and *lse; an empty range gives 0 and -inf.
 __device__ void f32_row(const F32Args& a, int b, int kvh, const float* qrow, int k0, int k1,
                         float* out, float* lse_out) {
@@ -88,8 +88,9 @@ __global__ __launch_bounds__(64) void f32_forward_kernel(F32Args a) {
   const int b = lo;
   const int nq = a.qsl[b + 1] - a.qsl[b];
   const int L = a.seq_lens[b];
-  const int pos = L - nq + (i - a.qsl[b]);
-  f32_row(a, b, h / a.G, a.q + row * a.Dqk, 0, pos + 1, a.out + row * a.Dv,
+  const int pfx = a.mask == kMaskPrefix ? a.prefix_lens[b] : 0;
+  const int end = min(visible_end(a.mask, L - nq, i - a.qsl[b], pfx), L);
+  f32_row(a, b, h / a.G, a.q + row * a.Dqk, 0, end, a.out + row * a.Dv,
           a.lse ? a.lse + row : nullptr);
 }
 

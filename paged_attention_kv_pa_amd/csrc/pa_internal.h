@@ -26,6 +26,19 @@ constexpr int kMaxSplits = 256;        // pa_decode_split / pa_merge_lse / mla_d
 constexpr int kItemInts = 12;          // int32 words of one pa_forward work item
 constexpr int kFusedPlanMax = 1024;    // decode-only calls up to this many requests plan in-kernel
 
+// Masks (pa_mask in include/pa.h).
+constexpr int kMaskCausal = 0, kMaskFull = 1, kMaskPrefix = 2;
+
+// End (exclusive) of the keys new token t of a request with ctx cached keys
+// sees: ctx + t + 1 under the causal mask; every key under the full mask
+// (the caller caps it at the key count); under the prefix mask at least the
+// request's first `prefix` keys.
+__device__ __forceinline__ int visible_end(int mask, int ctx, int t, int prefix) {
+  const int causal = ctx + t + 1;
+  if (mask == kMaskFull) return 0x7fffffff;
+  return mask == kMaskPrefix ? (prefix > causal ? prefix : causal) : causal;
+}
+
 struct MhaArgs {
   const void* q;
   const void* k_cache;
@@ -50,6 +63,8 @@ struct MhaArgs {
   int32_t target_items;      // pa_forward decode-only calls planned in the kernel
   int32_t chunk_keys;        // pa_forward_chunked: keys per chunk
   int32_t row_blocks;        // pa_forward_chunked: row blocks of the longest request
+  int32_t mask;              // kMaskCausal / kMaskFull / kMaskPrefix
+  const int32_t* prefix_lens;  // [B], read under kMaskPrefix only
 };
 
 struct PlanArgs {
@@ -78,6 +93,8 @@ struct F32Args {
   float* part_lse;
   float scale;
   int32_t B, T, Hq, Hkv, G, Dqk, Dv, P, max_pages, num_splits;
+  int32_t mask;                // forward mode: kMaskCausal / kMaskFull / kMaskPrefix
+  const int32_t* prefix_lens;  // [B], read under kMaskPrefix only
 };
 
 struct MlaArgs {

@@ -118,7 +118,8 @@ __device__ int run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest&
   const int ridx = it.row0 + r;
   const int tok = ridx / G;
   const int head = kvh * G + (ridx - tok * G);
-  const int lim = row_ok ? min(it.ctx + tok + 1, kv_end) : it.kv_begin;
+  const int pfx = a.mask == kMaskPrefix ? a.prefix_lens[b] : 0;
+  const int lim = row_ok ? min(visible_end(a.mask, it.ctx, tok, pfx), kv_end) : it.kv_begin;
 
   bf16x8 qf[KS];
   {
@@ -415,6 +416,8 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
   const int row0 = __builtin_amdgcn_readfirstlane(it.row0);
   const int ctx = __builtin_amdgcn_readfirstlane(it.ctx);
   const int q0 = __builtin_amdgcn_readfirstlane(it.q0);
+  const int mask = __builtin_amdgcn_readfirstlane(a.mask);
+  const int pfx = mask == kMaskPrefix ? __builtin_amdgcn_readfirstlane(a.prefix_lens[b]) : 0;
 
   // this lane's row
   const int row = 32 * wave + n;
@@ -427,7 +430,7 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
     const int t = rid / G;
     const int head = kvh * G + (rid - t * G);
     out_row = (int64_t)(q0 + t) * a.Hq + head;
-    lim = row_ok ? min(ctx + t + 1, kv_end) : kv_begin;
+    lim = row_ok ? min(visible_end(mask, ctx, t, pfx), kv_end) : kv_begin;
     const __bf16* qp = (const __bf16*)a.q + out_row * D + 8 * h;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -439,8 +442,8 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
   {
     const int first = 32 * wave, last = min(32 * wave + 32, nrows) - 1;
     if (last >= first) {
-      wave_min = min(ctx + (row0 + first) / G + 1, kv_end);
-      wave_lim = min(ctx + (row0 + last) / G + 1, kv_end);
+      wave_min = min(visible_end(mask, ctx, (row0 + first) / G, pfx), kv_end);
+      wave_lim = min(visible_end(mask, ctx, (row0 + last) / G, pfx), kv_end);
     }
   }
   // q must be in registers before the copies start counting; tying the
@@ -760,7 +763,8 @@ __device__ WorkItem make_prefill_item(const MhaArgs& a, int idx) {
   it.nrows = min(kPrefillRows, rows - it.row0);
   it.ctx = rp.L - rp.nq;
   it.kv_begin = 0;
-  it.kv_end = it.ctx + (it.row0 + it.nrows - 1) / G + 1;
+  const int pfx = a.mask == kMaskPrefix ? a.prefix_lens[b] : 0;
+  it.kv_end = min(rp.L, visible_end(a.mask, it.ctx, (it.row0 + it.nrows - 1) / G, pfx));
   it.part = -1;
   it.q0 = rp.q0;
   it.pad[0] = it.pad[1] = it.pad[2] = 0;

@@ -23,7 +23,8 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     names = set(_declared())
-    assert {"pa_forward", "pa_forward_chunked", "pa_decode_split", "pa_merge_lse", "mla_decode",
+    assert {"pa_forward", "pa_forward_masked", "pa_forward_chunked", "pa_decode_split",
+            "pa_merge_lse", "mla_decode",
             "pa_workspace_size",
             "mla_workspace_size", "pa_validate", "pa_status_string", "pa_last_hip_error"} <= names
 
@@ -117,6 +118,23 @@ def test_decode_split_argument_checks():
     assert call(4, _dims(num_tokens=5)) == binding.PA_ERR_INVALID_ARG  # T != B
     assert call(4, _dims(head_dim_qk=80, head_dim_v=80)) == binding.PA_ERR_UNSUPPORTED
     assert call(4, _dims(num_seqs=0, num_tokens=0)) == binding.PA_OK
+
+
+def test_masked_forward_argument_checks():
+    lib = pa.library()
+    d = _dims()
+
+    def call(mask, prefix, dd=d):
+        return lib.pa_forward_masked(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, mask, prefix, 0.1, FAKE,
+                                     None, ctypes.byref(dd), FAKE, 1 << 40, None)
+    bad = binding.PA_ERR_INVALID_ARG
+    assert call(3, None) == bad and call(-1, None) == bad
+    assert call(binding.PA_MASK_PREFIX, None) == bad   # prefix mask without prefix lengths
+    assert call(binding.PA_MASK_FULL, FAKE) == bad     # prefix lengths with another mask
+    assert call(binding.PA_MASK_CAUSAL, FAKE) == bad
+    empty = _dims(num_seqs=0, num_tokens=0)
+    assert call(binding.PA_MASK_FULL, None, empty) == binding.PA_OK
+    assert call(binding.PA_MASK_PREFIX, FAKE, empty) == binding.PA_OK
 
 
 def test_chunked_argument_checks():

@@ -200,6 +200,82 @@ def test_long_context_split_full_size(batch, S, lengths):
     check_lse(glse, rlse, "long pa_forward B=%d" % batch)
 
 
+# ------------------------------------------------------ full and prefix masks
+
+def masked_parity(b, mask, prefixes, what):
+    say("case %s: B=%d T=%d keys=%d mask=%d prefixes=%s" % (what, b.num_seqs, b.num_tokens,
+                                                           sum(b.seq_lens_list), mask, prefixes))
+    g = b.to(DEV)
+    pl = None if prefixes is None else torch.tensor(prefixes, dtype=torch.int32, device=DEV)
+    lse = torch.full((b.num_tokens, b.num_q_heads), float("nan"), dtype=torch.float32, device=DEV)
+    out = pa.pa_forward_masked(g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens,
+                               g.query_start_loc, b.scale, mask, prefix_lens=pl, lse=lse,
+                               max_seq_len=max(b.seq_lens_list + [1]),
+                               max_q_len=max(b.q_lens + [1]))
+    torch.cuda.synchronize()
+    ref, rlse = oracle.attention(b.q, b.k_cache, b.v_cache, b.block_table, b.seq_lens,
+                                 b.query_start_loc, b.scale, b.num_kv_heads, mask=mask,
+                                 prefix_lens=None if prefixes is None else np.asarray(prefixes, np.int32))
+    got = out.float().cpu().numpy()
+    check_out(got, ref, b.dtype, what)
+    check_lse(lse.cpu().numpy(), rlse, what)
+    return got
+
+
+# decode, a two-token request (8 decode-mode rows), extend, prefill, prefill over 3 row blocks
+MASK_Q, MASK_C = [1, 2, 300, 37, 190], [900, 40, 700, 0, 0]
+
+
+@pytest.mark.parametrize("mask,prefixes", [
+    (pa.PA_MASK_FULL, None),
+    (pa.PA_MASK_PREFIX, [0, 41, 750, 20, 100]),     # inside the new tokens / the cache / none
+    (pa.PA_MASK_PREFIX, [5000, 10, 1000, 37, 190]),  # past the end, covering every key
+    (pa.PA_MASK_PREFIX, [-3, 42, 1, 64, 129]),
+])
+def test_masked_forward_matches_oracle(mask, prefixes):
+    b = workload.make_batch(MASK_Q, MASK_C, num_q_heads=32, num_kv_heads=8, head_dim_qk=128,
+                            page_size=16, seed=601)
+    masked_parity(b, mask, prefixes, "masked bf16")
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,P", [(32, 4, 64, 16), (64, 4, 128, 8), (16, 16, 128, 32)])
+def test_masked_forward_shapes(Hq, Hkv, D, P):
+    b = workload.make_batch([3, 1, 270], [50, 500, 260], num_q_heads=Hq, num_kv_heads=Hkv,
+                            head_dim_qk=D, page_size=P, seed=Hq + Hkv + D + P)
+    masked_parity(b, pa.PA_MASK_FULL, None, "full Hq=%d Hkv=%d D=%d P=%d" % (Hq, Hkv, D, P))
+    masked_parity(b, pa.PA_MASK_PREFIX, [40, 0, 400], "prefix Hq=%d Hkv=%d D=%d P=%d" % (Hq, Hkv, D, P))
+
+
+@pytest.mark.parametrize("mask,prefixes", [(pa.PA_MASK_FULL, None), (pa.PA_MASK_PREFIX, [3, 9, 0])])
+def test_masked_forward_f32(mask, prefixes):
+    b = workload.make_batch([4, 1, 7], [20, 33, 0], num_q_heads=8, num_kv_heads=2, head_dim_qk=64,
+                            page_size=16, dtype=torch.float32, seed=607)
+    masked_parity(b, mask, prefixes, "masked fp32")
+
+
+def test_masked_causal_is_pa_forward_bitwise():
+    b = workload.make_batch(MASK_Q, MASK_C, num_q_heads=32, num_kv_heads=8, head_dim_qk=128,
+                            page_size=16, seed=611)
+    g = b.to(DEV)
+    kw = dict(max_seq_len=max(b.seq_lens_list), max_q_len=max(b.q_lens))
+    a = pa.pa_forward(g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens, g.query_start_loc,
+                      b.scale, **kw)
+    c = pa.pa_forward_masked(g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens,
+                             g.query_start_loc, b.scale, pa.PA_MASK_CAUSAL, **kw)
+    z = pa.pa_forward_masked(g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens,
+                             g.query_start_loc, b.scale, pa.PA_MASK_PREFIX,
+                             prefix_lens=torch.zeros(b.num_seqs, dtype=torch.int32, device=DEV), **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+    assert torch.equal(a.view(torch.int16), z.view(torch.int16))
+
+
+def test_full_mask_qwen3_scaled():
+    b = workload.qwen3_mixed(1, n_decode=6, n_extend=2, n_prefill=2, dec=(1024, 4096),
+                             ext_q=(256, 600), ext_c=(4096, 8192), pre_q=(512, 1500))
+    masked_parity(b, pa.PA_MASK_FULL, None, "full mask qwen3 scaled")
+
+
 # ------------------------------------------- chunked-context processing
 
 def chunked_parity(b, C, what, S=None, rows=None):
