@@ -277,7 +277,7 @@ def main():
     if not args.no_prefill:
         full = workload.qwen3_mixed(0, device=dev)
 
-        def timed_forward(m, steps):
+        def timed_forward(m, steps, mask=None):
             Tm = m.num_tokens
             mo = torch.empty(Tm, m.num_q_heads, m.head_dim_v, dtype=m.dtype, device=dev)
             mmaxL, mmaxq = max(m.seq_lens_list), max(m.q_lens)
@@ -286,9 +286,14 @@ def main():
             mws = torch.empty(pa.pa_workspace_size(mdims), dtype=torch.uint8, device=dev)
 
             def pstep():
-                pa.pa_forward(m.q, m.k_cache, m.v_cache, m.block_table, m.seq_lens,
-                              m.query_start_loc, m.scale, out=mo, workspace=mws,
-                              max_seq_len=mmaxL, max_q_len=mmaxq)
+                if mask is None:
+                    pa.pa_forward(m.q, m.k_cache, m.v_cache, m.block_table, m.seq_lens,
+                                  m.query_start_loc, m.scale, out=mo, workspace=mws,
+                                  max_seq_len=mmaxL, max_q_len=mmaxq)
+                else:
+                    pa.pa_forward_masked(m.q, m.k_cache, m.v_cache, m.block_table, m.seq_lens,
+                                         m.query_start_loc, m.scale, mask, out=mo, workspace=mws,
+                                         max_seq_len=mmaxL, max_q_len=mmaxq)
 
             return time_steps(pstep, steps, 2, lib)
 
@@ -304,6 +309,18 @@ def main():
             "value": round(tf, 2), "unit": "TFLOP/s", "peak": BF16_PEAK_TFLOPS,
             "frac": round(tf / BF16_PEAK_TFLOPS, 4), "kernel_ms": round(p_kern_ms, 4),
             "ms_per_step": round(p_step_ms, 4), "algorithmic_flops": flops, "steps": psteps}
+        # the same sub-batch under the full mask (every new token sees all keys of its
+        # request, as in encoder or cross-attention): pairs = q_b * L_b per request
+        f_step_ms, f_kern_ms = timed_forward(pre, psteps, mask=pa.PA_MASK_FULL)
+        fflops = sum(4 * q * L * pre.num_q_heads * pre.head_dim_qk
+                     for q, L in zip(pre.q_lens, pre.seq_lens_list))
+        ftf = fflops / (f_kern_ms * 1e-3) / 1e12
+        result["prefill_full_mask"] = {
+            "workload": "the prefill + extend sub-batch above through pa_forward_masked with "
+                        "PA_MASK_FULL (no causal mask)",
+            "value": round(ftf, 2), "unit": "TFLOP/s", "frac": round(ftf / BF16_PEAK_TFLOPS, 4),
+            "kernel_ms": round(f_kern_ms, 4), "ms_per_step": round(f_step_ms, 4),
+            "algorithmic_flops": fflops}
         m_step_ms, m_kern_ms = timed_forward(full, psteps)
         result["mixed_batch"] = {
             "workload": "Qwen3-235B-shaped mixed batch, all 64 requests [48 decode : 8 extend : "
