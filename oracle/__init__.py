@@ -57,7 +57,7 @@ def _load():
             lib.orc_attention.argtypes = [p, p, p, i32, p, p, p] + [i32] * 9 + [f32, p, p, p, i32]
             lib.orc_attention.restype = i32
             lib.orc_attention_masked.argtypes = [p, p, p, i32, p, p, p] + [i32] * 9 + [f32, i32, p,
-                                                                                     p, p, p, i32]
+                                                                                     p, p, p, p, i32]
             lib.orc_attention_masked.restype = i32
             lib.orc_decode_split.argtypes = [p, p, p, i32, p, p] + [i32] * 9 + [f32, i32, p, p, i32]
             lib.orc_decode_split.restype = i32
@@ -123,9 +123,10 @@ def _check(rc):
 
 def attention(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale,
               num_kv_heads, head_dim_v=None, layout=LAYOUT_MHA, rows=None,
-              nthreads=None, mask=MASK_CAUSAL, prefix_lens=None):
+              nthreads=None, mask=MASK_CAUSAL, prefix_lens=None, sinks=None):
     """Paged attention over a varlen batch, in fp64: causal, or MASK_FULL / MASK_PREFIX
-    (prefix_lens int32 [B]) as defined in pa_oracle.c.
+    (prefix_lens int32 [B]) as defined in pa_oracle.c; sinks: optional float32 [Hq]
+    sink logits.
 
     q: [T, Hq, Dqk]; k_cache / v_cache in the layouts of pa_oracle.c
     (for LAYOUT_MLA pass the latent cache as both); block_table [B, max_pages];
@@ -155,7 +156,7 @@ def attention(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale
     if rows is not None:
         sel = np.ascontiguousarray(np.asarray(rows, dtype=np.uint8).reshape(T, Hq))
     nt = max_threads() if nthreads is None else int(nthreads)
-    if mask == MASK_CAUSAL and prefix_lens is None:
+    if mask == MASK_CAUSAL and prefix_lens is None and sinks is None:
         rc = lib.orc_attention(_ptr(qa), _ptr(ka), _ptr(va), dt, _ptr(bt), _ptr(sl), _ptr(qs),
                                B, Hq, int(num_kv_heads), Dqk, Dv, P, num_pages, bt.shape[1],
                                layout, float(scale), _ptr(sel), _ptr(out), _ptr(lse), nt)
@@ -165,10 +166,15 @@ def attention(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale
             pfx = _i32(prefix_lens)
             if pfx.shape != (B,):
                 raise ValueError("prefix_lens must have B entries")
+        snk = None
+        if sinks is not None:
+            snk = np.ascontiguousarray(np.asarray(sinks, dtype=np.float32))
+            if snk.shape != (Hq,):
+                raise ValueError("sinks must have Hq entries")
         rc = lib.orc_attention_masked(_ptr(qa), _ptr(ka), _ptr(va), dt, _ptr(bt), _ptr(sl),
                                       _ptr(qs), B, Hq, int(num_kv_heads), Dqk, Dv, P, num_pages,
                                       bt.shape[1], layout, float(scale), int(mask), _ptr(pfx),
-                                      _ptr(sel), _ptr(out), _ptr(lse), nt)
+                                      _ptr(snk), _ptr(sel), _ptr(out), _ptr(lse), nt)
     _check(rc)
     return out, lse
 

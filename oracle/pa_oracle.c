@@ -32,6 +32,10 @@
  *     first prefix_lens[b] key positions form a bidirectional prefix, the
  *     rest stays causal; the token at position p sees keys
  *     0 .. max(p, prefix_lens[b] - 1), at most L_b - 1.
+ *   - Sink tokens (Triton deep dive, same list of use cases; named there
+ *     for GPT-OSS without a formula): a per-query-head logit sinks[h] joins
+ *     the softmax of every row of head h as one more key whose value is
+ *     zero, so it only adds e^{sinks[h]} to the denominator.
  *   - Split-KV partials and their log-sum-exp merge (Triton deep dive,
  *     section "Parallel tiled softmax (3D kernel)"; ROCm backends, bullet
  *     "Chunked context processing"): the key range is cut into contiguous
@@ -165,7 +169,7 @@ int orc_attention_masked(const void* q, const void* kc, const void* vc, int dtyp
                          const int32_t* block_table, const int32_t* seq_lens,
                          const int32_t* qsl, int B, int Hq, int Hkv, int Dqk, int Dv,
                          int P, int num_pages, int max_pages, int layout, float scale,
-                         int mask, const int32_t* prefix_lens,
+                         int mask, const int32_t* prefix_lens, const float* sinks,
                          const uint8_t* row_sel, double* out, double* lse,
                          int nthreads) {
   int rc = check_common(B, Hq, Hkv, Dqk, Dv, P, max_pages, layout);
@@ -232,6 +236,18 @@ int orc_attention_masked(const void* q, const void* kc, const void* vc, int dtyp
           double l_out;
           attend(qrow, Kd, Vd, 0, end, Dqk, Dv, sigma, s,
                  out + ((size_t)i * Hq + hh) * Dv, &l_out);
+          if (sinks) {
+            /* one more logit, sinks[hh], with a zero value: the row's weights
+               shrink by e^{lse} / (e^{lse} + e^{sink}) */
+            const double sk = (double)sinks[hh];
+            const double mx = l_out > sk ? l_out : sk;
+            if (mx > -INFINITY) {
+              const double wr = exp(l_out - mx), ws = exp(sk - mx);
+              double* o = out + ((size_t)i * Hq + hh) * Dv;
+              for (int d = 0; d < Dv; ++d) o[d] *= wr / (wr + ws);
+              l_out = mx + log(wr + ws);
+            }
+          }
           if (lse) lse[(size_t)i * Hq + hh] = l_out;
         }
       }
@@ -250,7 +266,7 @@ int orc_attention(const void* q, const void* kc, const void* vc, int dtype,
                   int nthreads) {
   return orc_attention_masked(q, kc, vc, dtype, block_table, seq_lens, qsl, B,
                               Hq, Hkv, Dqk, Dv, P, num_pages, max_pages,
-                              layout, scale, ORC_MASK_CAUSAL, NULL, row_sel,
+                              layout, scale, ORC_MASK_CAUSAL, NULL, NULL, row_sel,
                               out, lse, nthreads);
 }
 

@@ -237,6 +237,52 @@ def test_mask_special_cases_reduce_to_causal_or_full():
     assert not np.allclose(causal[0], full[0])
 
 
+def _sdpa_with_sink(q, K, V, scale, sinks):
+    """float64 attention with the causal mask and, per query head h, one extra key of
+    zero key and value whose logit is sinks[h] (an additive bias on SDPA)."""
+    nq, L, Hkv = q.shape[0], K.shape[0], K.shape[1]
+    Kx = torch.cat([K.double(), torch.zeros(1, Hkv, K.shape[2], dtype=torch.float64)], 0)
+    Vx = torch.cat([V.double(), torch.zeros(1, Hkv, V.shape[2], dtype=torch.float64)], 0)
+    Hq = q.shape[1]
+    bias = torch.full((Hq, nq, L + 1), float("-inf"), dtype=torch.float64)
+    vis = torch.cat([torch.ones(nq, L, dtype=torch.bool), torch.zeros(nq, 1, dtype=torch.bool)], 1)
+    vis[:, :L] = torch.arange(L).unsqueeze(0) <= (L - nq + torch.arange(nq)).unsqueeze(1)
+    bias[:, vis] = 0.0
+    bias[:, :, L] = torch.as_tensor(np.asarray(sinks, np.float64)).unsqueeze(1)
+    qd = q.double().permute(1, 0, 2).unsqueeze(0)
+    kd = Kx.permute(1, 0, 2).unsqueeze(0)
+    vd = Vx.permute(1, 0, 2).unsqueeze(0)
+    out = torch.nn.functional.scaled_dot_product_attention(qd, kd, vd, attn_mask=bias.unsqueeze(0),
+                                                           scale=scale, enable_gqa=True)
+    g = Hq // Hkv
+    s = torch.matmul(qd, kd.repeat_interleave(g, dim=1).transpose(-1, -2)) * scale + bias.unsqueeze(0)
+    lse = torch.logsumexp(s, dim=-1)
+    return out[0].permute(1, 0, 2).numpy(), lse[0].permute(1, 0).numpy()
+
+
+def test_sinks_match_sdpa_with_an_extra_zero_key():
+    """A sink logit per query head acts as one more key with zero value (checked with
+    SDPA and an additive bias), for sinks far below, near and far above the scores."""
+    c = _build_case(47, MASK_SPECS, 4, 2, 8, 8, 4)
+    sinks = np.array([-30.0, -0.7, 1.3, 25.0], dtype=np.float32)
+    out, lse = oracle.attention(c["q"], c["kc"], c["vc"], c["bt"], c["seq"], c["qsl"], 0.45, 2,
+                                head_dim_v=8, sinks=sinks)
+    i0 = 0
+    for (nq, ctx), q, K, V in zip(MASK_SPECS, c["qs"], c["Ks"], c["Vs"]):
+        ro, rl = _sdpa_with_sink(q, K, V, float(np.float32(0.45)), sinks)
+        np.testing.assert_allclose(out[i0:i0 + nq], ro, atol=TOL, rtol=0)
+        np.testing.assert_allclose(lse[i0:i0 + nq], rl, atol=TOL, rtol=0)
+        i0 += nq
+
+
+def test_minus_infinite_sinks_change_nothing():
+    c = _build_case(49, MASK_SPECS, 4, 2, 8, 8, 4)
+    a = oracle.attention(c["q"], c["kc"], c["vc"], c["bt"], c["seq"], c["qsl"], 0.45, 2, head_dim_v=8)
+    b = oracle.attention(c["q"], c["kc"], c["vc"], c["bt"], c["seq"], c["qsl"], 0.45, 2, head_dim_v=8,
+                         sinks=np.full(4, -np.inf, np.float32))
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
 def test_constant_value_rows_sum_to_one():
     """V = const => out = const for every row (softmax rows sum to 1)."""
     specs = [(1, 30), (4, 5), (9, 0)]

@@ -22,6 +22,10 @@ INIT = os.path.join(os.path.dirname(real_oracle.__file__), "__init__.py")
 MUTANTS = {
     "causal_off_by_one": ("          int end = pos + 1;", "          int end = pos;"),
     "full_mask_still_causal": ("          if (mask == ORC_MASK_FULL) end = L;", ""),
+    "sink_weights_not_shrunk": ("              for (int d = 0; d < Dv; ++d) o[d] *= wr / (wr + ws);\n", ""),
+    "sink_lse_unchanged": ("              l_out = mx + log(wr + ws);\n", ""),
+    "sink_without_max_shift": ("const double wr = exp(l_out - mx), ws = exp(sk - mx);",
+                               "const double wr = exp(l_out), ws = exp(sk);"),
     "prefix_capped_one_short": ("            end = prefix_lens[b] < L ? prefix_lens[b] : L;",
                                 "            end = prefix_lens[b] < L ? prefix_lens[b] : L - 1;"),
     "prefix_off_by_one": ("if (mask == ORC_MASK_PREFIX && prefix_lens[b] > end)\n            end = prefix_lens[b] < L ? prefix_lens[b] : L;",
@@ -69,6 +73,8 @@ def _battery():
                  "test_chunked_partials_match_sdpa_on_visible_keys",
                  "test_full_mask_equals_unmasked_sdpa",
                  "test_mask_special_cases_reduce_to_causal_or_full",
+                 "test_sinks_match_sdpa_with_an_extra_zero_key",
+                 "test_minus_infinite_sinks_change_nothing",
                  "test_constant_value_rows_sum_to_one", "test_length_one_context_returns_v0",
                  "test_equal_keys_give_mean_of_visible_values",
                  "test_zero_query_gives_mean_and_log_count",
