@@ -142,20 +142,25 @@ PA_API pa_status pa_forward(const void* q, const void* k_cache, const void* v_ca
                      size_t workspace_bytes, void* stream);
 
 /*
- * pa_forward_masked — pa_forward with another mask than causal ([TDD]
- * section on the backend's use cases, which names encoder / decoder
- * attention and multimodal prefix attention): mask is a pa_mask;
- * prefix_lens is an int32 [B] device array for PA_MASK_PREFIX (any values;
- * negative ones act as 0) and must be NULL for the other masks.  Everything
- * else, including the workspace, is as for pa_forward, which is this call
- * with PA_MASK_CAUSAL.  Returns PA_ERR_INVALID_ARG for an unknown mask or a
- * prefix_lens that does not match it.
+ * pa_forward_masked — pa_forward with another mask than causal and / or
+ * sink tokens ([TDD] section on the backend's use cases, which names
+ * encoder / decoder attention, multimodal prefix attention and sink tokens).
+ * mask is a pa_mask; prefix_lens is an int32 [B] device array for
+ * PA_MASK_PREFIX (any values; negative ones act as 0) and must be NULL for
+ * the other masks.  sinks (nullable) is a float32 [Hq] device array of sink
+ * logits: for query head h, one more softmax key with logit sinks[h] (in
+ * the units of the scaled scores, natural log) and a zero value, so
+ *   out = sum_t e^{s_t} v_t / (e^{sinks[h]} + sum_t e^{s_t}),
+ *   lse = ln(e^{sinks[h]} + sum_t e^{s_t});  -inf means no sink.
+ * Everything else, including the workspace, is as for pa_forward, which is
+ * this call with PA_MASK_CAUSAL and no sinks.  Returns PA_ERR_INVALID_ARG for
+ * an unknown mask or a prefix_lens that does not match it.
  */
 PA_API pa_status pa_forward_masked(const void* q, const void* k_cache, const void* v_cache,
                                    const int32_t* block_table, const int32_t* seq_lens,
                                    const int32_t* query_start_loc, int32_t mask,
-                                   const int32_t* prefix_lens, float scale, void* out,
-                                   float* lse, const pa_dims* dims, void* workspace,
+                                   const int32_t* prefix_lens, const float* sinks, float scale,
+                                   void* out, float* lse, const pa_dims* dims, void* workspace,
                                    size_t workspace_bytes, void* stream);
 
 /*

@@ -60,7 +60,7 @@ def library():
             lib.pa_workspace_size.restype = sz
             lib.pa_forward.argtypes = [p, p, p, p, p, p, f32, p, p, dp, p, sz, p]
             lib.pa_forward.restype = i32
-            lib.pa_forward_masked.argtypes = [p, p, p, p, p, p, i32, p, f32, p, p, dp, p, sz, p]
+            lib.pa_forward_masked.argtypes = [p, p, p, p, p, p, i32, p, p, f32, p, p, dp, p, sz, p]
             lib.pa_forward_masked.restype = i32
             lib.pa_decode_split.argtypes = [p, p, p, p, p, f32, i32, p, p, dp, p]
             lib.pa_decode_split.restype = i32
@@ -177,24 +177,28 @@ def pa_forward(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scal
     Returns out ([T, Hq, D], allocated if not given).
     """
     return _forward(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale, out, lse,
-                    workspace, max_seq_len, max_q_len, stream, None, None)
+                    workspace, max_seq_len, max_q_len, stream, None, None, None)
 
 
 def pa_forward_masked(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale, mask,
-                      prefix_lens=None, out=None, lse=None, workspace=None, max_seq_len=None,
-                      max_q_len=None, stream=None):
+                      prefix_lens=None, sinks=None, out=None, lse=None, workspace=None,
+                      max_seq_len=None, max_q_len=None, stream=None):
     """pa_forward with mask PA_MASK_CAUSAL, PA_MASK_FULL or PA_MASK_PREFIX (prefix_lens
-    int32 [B] on the device for the last); see pa_forward_masked in include/pa.h."""
+    int32 [B] on the device for the last) and optional sink logits (float32 [Hq] on the
+    device); see pa_forward_masked in include/pa.h."""
+    if sinks is not None:
+        _need(sinks.dtype == torch.float32 and sinks.is_contiguous() and sinks.device == q.device
+              and tuple(sinks.shape) == (int(q.shape[1]),), "sinks must be contiguous float32 [Hq]")
     if prefix_lens is not None:
         _need(prefix_lens.dtype == torch.int32 and prefix_lens.is_contiguous()
               and prefix_lens.device == q.device and tuple(prefix_lens.shape) == (int(seq_lens.shape[0]),),
               "prefix_lens must be contiguous int32 [B] on q's device")
     return _forward(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale, out, lse,
-                    workspace, max_seq_len, max_q_len, stream, int(mask), prefix_lens)
+                    workspace, max_seq_len, max_q_len, stream, int(mask), prefix_lens, sinks)
 
 
 def _forward(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale, out, lse,
-             workspace, max_seq_len, max_q_len, stream, mask, prefix_lens):
+             workspace, max_seq_len, max_q_len, stream, mask, prefix_lens, sinks):
     _check_common(q, k_cache, v_cache, block_table, seq_lens)
     _need(query_start_loc.dtype == torch.int32 and query_start_loc.is_contiguous()
           and query_start_loc.device == q.device, "query_start_loc must be contiguous int32 on q's device")
@@ -223,7 +227,8 @@ def _forward(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale,
     else:
         st = library().pa_forward_masked(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
                                          _ptr(seq_lens), _ptr(query_start_loc), mask,
-                                         _ptr(prefix_lens), float(scale), _ptr(out), _ptr(lse),
+                                         _ptr(prefix_lens), _ptr(sinks), float(scale), _ptr(out),
+                                         _ptr(lse),
                                          ctypes.byref(dims), _ptr(workspace), nbytes,
                                          _stream(q.device, stream))
         _check(st, "pa_forward_masked")

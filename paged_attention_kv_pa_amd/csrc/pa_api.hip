@@ -159,7 +159,7 @@ pa_status pa_forward(const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* query_start_loc, float scale, void* out, float* lse,
                      const pa_dims* d, void* workspace, size_t workspace_bytes, void* stream) {
   return pa_forward_masked(q, k_cache, v_cache, block_table, seq_lens, query_start_loc,
-                           PA_MASK_CAUSAL, nullptr, scale, out, lse, d, workspace,
+                           PA_MASK_CAUSAL, nullptr, nullptr, scale, out, lse, d, workspace,
                            workspace_bytes, stream);
 }
 
@@ -170,9 +170,9 @@ static_assert(PA_MASK_CAUSAL == pa::kMaskCausal && PA_MASK_FULL == pa::kMaskFull
 pa_status pa_forward_masked(const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* block_table, const int32_t* seq_lens,
                             const int32_t* query_start_loc, int32_t mask,
-                            const int32_t* prefix_lens, float scale, void* out, float* lse,
-                            const pa_dims* d, void* workspace, size_t workspace_bytes,
-                            void* stream) {
+                            const int32_t* prefix_lens, const float* sinks, float scale,
+                            void* out, float* lse, const pa_dims* d, void* workspace,
+                            size_t workspace_bytes, void* stream) {
   pa_status st = check_dims(d);
   if (st != PA_OK) return st;
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !query_start_loc || !out)
@@ -209,6 +209,7 @@ pa_status pa_forward_masked(const void* q, const void* k_cache, const void* v_ca
     a.num_splits = 1;
     a.mask = mask;
     a.prefix_lens = prefix_lens;
+    a.sinks = sinks;
     hipError_t e = mark(g_ev_start, s);
     if (e == hipSuccess) e = pa::launch_f32_forward(a, s);
     if (e == hipSuccess) e = mark(g_ev_stop, s);
@@ -279,6 +280,7 @@ pa_status pa_forward_masked(const void* q, const void* k_cache, const void* v_ca
   a.target_items = pl.target_items;
   a.mask = mask;
   a.prefix_lens = prefix_lens;
+  a.sinks = sinks;
   if (fused && (e = pa::launch_reset_queue(ctrl, s)) != hipSuccess) return hip_fail(e);
   if ((e = mark(g_ev_start, s)) != hipSuccess) return hip_fail(e);
   e = fused ? pa::launch_mha_forward_fused(a, D, grid, s)

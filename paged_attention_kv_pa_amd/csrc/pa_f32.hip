@@ -19,8 +19,9 @@ constexpr int kF32MaxD = 256;
 
 // One query row over keys [k0, k1) (k1 already capped by the row's visible limit).
 // Writes out[0..Dv) (normalised) and *lse; an empty range gives 0 and -inf.
+// sink: a sink logit folded into the row (-inf: none).
 __device__ void f32_row(const F32Args& a, int b, int kvh, const float* qrow, int k0, int k1,
-                        float* out, float* lse_out) {
+                        float* out, float* lse_out, float sink) {
   __shared__ float qs[kF32MaxD];
   __shared__ float ps[64];
   const int lane = threadIdx.x;
@@ -65,13 +66,15 @@ __device__ void f32_row(const F32Args& a, int b, int kvh, const float* qrow, int
     }
     __syncthreads();
   }
-  const float inv = l > 0.f ? 1.f / l : 0.f;
+  float inv = l > 0.f ? 1.f / l : 0.f;
+  float lse = l > 0.f ? m + __logf(l) : kNegInf;
+  if (sink != kNegInf) inv *= fold_sink(sink, &lse);
 #pragma unroll
   for (int c = 0; c < kF32MaxD / 64; ++c) {
     const int d = lane + 64 * c;
     if (d < Dv) out[d] = acc[c] * inv;
   }
-  if (lane == 0 && lse_out) *lse_out = l > 0.f ? m + __logf(l) : kNegInf;
+  if (lane == 0 && lse_out) *lse_out = lse;
 }
 
 // pa_forward, fp32: one workgroup (one wave) per (query row, head).
@@ -91,7 +94,7 @@ __global__ __launch_bounds__(64) void f32_forward_kernel(F32Args a) {
   const int pfx = a.mask == kMaskPrefix ? a.prefix_lens[b] : 0;
   const int end = min(visible_end(a.mask, L - nq, i - a.qsl[b], pfx), L);
   f32_row(a, b, h / a.G, a.q + row * a.Dqk, 0, end, a.out + row * a.Dv,
-          a.lse ? a.lse + row : nullptr);
+          a.lse ? a.lse + row : nullptr, a.sinks ? a.sinks[h] : kNegInf);
 }
 
 // pa_decode_split, fp32: one workgroup per (request, head, partition).
@@ -106,7 +109,7 @@ __global__ __launch_bounds__(64) void f32_split_kernel(F32Args a) {
   const long long per = (long long)a.P * ((pages + S - 1) / S);
   const long long a0 = per * s, a1 = a0 + per;
   const int t0 = a0 < L ? (int)a0 : L, t1 = a1 < L ? (int)a1 : L;
-  f32_row(a, b, h / a.G, a.q + bh * a.Dqk, t0, t1, a.part_o + id * a.Dv, a.part_lse + id);
+  f32_row(a, b, h / a.G, a.q + bh * a.Dqk, t0, t1, a.part_o + id * a.Dv, a.part_lse + id, kNegInf);
 }
 
 }  // namespace

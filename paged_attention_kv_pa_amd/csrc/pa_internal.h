@@ -39,6 +39,18 @@ __device__ __forceinline__ int visible_end(int mask, int ctx, int t, int prefix)
   return mask == kMaskPrefix ? (prefix > causal ? prefix : causal) : causal;
 }
 
+// Folds a sink logit s (natural-log units, -inf for none) into a finished
+// row whose keys gave log-sum-exp *lse (-inf if it saw no key): the sink is
+// one more softmax key with a zero value.  Returns the factor the row's
+// normalised output is multiplied by; *lse becomes that of keys and sink.
+__device__ __forceinline__ float fold_sink(float s, float* lse) {
+  const float mx = fmaxf(*lse, s);
+  if (mx == kNegInf) return 1.f;
+  const float wr = __expf(*lse - mx), ws = __expf(s - mx);
+  *lse = mx + __logf(wr + ws);
+  return wr / (wr + ws);
+}
+
 struct MhaArgs {
   const void* q;
   const void* k_cache;
@@ -65,6 +77,7 @@ struct MhaArgs {
   int32_t row_blocks;        // pa_forward_chunked: row blocks of the longest request
   int32_t mask;              // kMaskCausal / kMaskFull / kMaskPrefix
   const int32_t* prefix_lens;  // [B], read under kMaskPrefix only
+  const float* sinks;        // [Hq] sink logits or NULL (pa_forward_masked only)
 };
 
 struct PlanArgs {
@@ -95,6 +108,7 @@ struct F32Args {
   int32_t B, T, Hq, Hkv, G, Dqk, Dv, P, max_pages, num_splits;
   int32_t mask;                // forward mode: kMaskCausal / kMaskFull / kMaskPrefix
   const int32_t* prefix_lens;  // [B], read under kMaskPrefix only
+  const float* sinks;          // forward mode: [Hq] sink logits or NULL
 };
 
 struct MlaArgs {

@@ -310,15 +310,18 @@ __device__ int run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest&
       }
     }
     if (row < it.nrows) {
-      const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-#pragma unroll
-      for (int e = 0; e < NC; ++e) o[e] *= inv;
       const int rid = it.row0 + row;
       const int t = rid / G;
-      const int64_t out_row = (int64_t)(it.q0 + t) * a.Hq + kvh * G + (rid - t * G);
+      const int head = kvh * G + (rid - t * G);
+      const int64_t out_row = (int64_t)(it.q0 + t) * a.Hq + head;
+      float lse = wsum > 0.f ? M * a.scale + __log2f(wsum) * kLn2 : kNegInf;
+      float f = wsum > 0.f ? 1.f / wsum : 0.f;
+      // a sink enters finished rows only (split rows get it in their merge)
+      if (a.sinks && !dst.partial) f *= fold_sink(a.sinks[head], &lse);
+#pragma unroll
+      for (int e = 0; e < NC; ++e) o[e] *= f;
       store_row_chunk<D, NC>(a, dst, row, out_row, c0, o);
-      if (tid % TPR == 0)
-        store_lse(a, dst, row, out_row, wsum > 0.f ? M * a.scale + __log2f(wsum) * kLn2 : kNegInf);
+      if (tid % TPR == 0) store_lse(a, dst, row, out_row, lse);
     }
   }
   __syncthreads();
@@ -703,7 +706,10 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
   // epilogue: element v of acc[dt] is O[row][32 dt + 8 (v / 4) + 4 h + v % 4]
   const float lrow = l + __shfl_xor(l, 32);
   if (!row_ok) return;
-  const float inv = lrow > 0.f ? 1.f / lrow : 0.f;
+  float lse = lrow > 0.f ? (m + __log2f(lrow)) * kLn2 : kNegInf;
+  float inv = lrow > 0.f ? 1.f / lrow : 0.f;
+  // a sink enters finished rows only (partial rows get it in their merge)
+  if (a.sinks && !dst.partial) inv *= fold_sink(a.sinks[out_row % a.Hq], &lse);
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -712,8 +718,7 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
                           acc[dt][4 * q + 2] * inv, acc[dt][4 * q + 3] * inv};
       store_row_chunk<D, 4>(a, dst, row, out_row, 32 * dt + 8 * q + 4 * h, o);
     }
-  if (h == 0)
-    store_lse(a, dst, row, out_row, lrow > 0.f ? (m + __log2f(lrow)) * kLn2 : kNegInf);
+  if (h == 0) store_lse(a, dst, row, out_row, lse);
 }
 
 template <int D, bool DECODE_ONLY>
@@ -1343,15 +1348,18 @@ __global__ __launch_bounds__(kThreads) void mha_forward_merge_kernel(MhaArgs a) 
           o[4 * c + 3] = fmaf(w, v[c][3], o[4 * c + 3] * f);
         }
       }
-      const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+      float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+      float lse = wsum > 0.f ? m + __logf(wsum) : kNegInf;
       const int t = row / a.G;
-      const int64_t out_row = (int64_t)(q0 + t) * a.Hq + kvh * a.G + (row - t * a.G);
+      const int head = kvh * a.G + (row - t * a.G);
+      const int64_t out_row = (int64_t)(q0 + t) * a.Hq + head;
+      if (a.sinks) inv *= fold_sink(a.sinks[head], &lse);
       __bf16* op = (__bf16*)a.out + out_row * D + c0;
 #pragma unroll
       for (int c = 0; c < NC; c += 4)
         *reinterpret_cast<u32x2*>(op + c) =
             u32x2{pack_bf16x2(o[c] * inv, o[c + 1] * inv), pack_bf16x2(o[c + 2] * inv, o[c + 3] * inv)};
-      if ((lane & 15) == 0 && a.lse) a.lse[out_row] = wsum > 0.f ? m + __logf(wsum) : kNegInf;
+      if ((lane & 15) == 0 && a.lse) a.lse[out_row] = lse;
     }
   }
 }

@@ -125,8 +125,8 @@ def test_masked_forward_argument_checks():
     d = _dims()
 
     def call(mask, prefix, dd=d):
-        return lib.pa_forward_masked(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, mask, prefix, 0.1, FAKE,
-                                     None, ctypes.byref(dd), FAKE, 1 << 40, None)
+        return lib.pa_forward_masked(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, mask, prefix, None, 0.1,
+                                     FAKE, None, ctypes.byref(dd), FAKE, 1 << 40, None)
     bad = binding.PA_ERR_INVALID_ARG
     assert call(3, None) == bad and call(-1, None) == bad
     assert call(binding.PA_MASK_PREFIX, None) == bad   # prefix mask without prefix lengths

@@ -202,20 +202,22 @@ def test_long_context_split_full_size(batch, S, lengths):
 
 # ------------------------------------------------------ full and prefix masks
 
-def masked_parity(b, mask, prefixes, what):
-    say("case %s: B=%d T=%d keys=%d mask=%d prefixes=%s" % (what, b.num_seqs, b.num_tokens,
-                                                           sum(b.seq_lens_list), mask, prefixes))
+def masked_parity(b, mask, prefixes, what, sinks=None):
+    say("case %s: B=%d T=%d keys=%d mask=%d prefixes=%s sinks=%s" % (
+        what, b.num_seqs, b.num_tokens, sum(b.seq_lens_list), mask, prefixes, sinks is not None))
     g = b.to(DEV)
     pl = None if prefixes is None else torch.tensor(prefixes, dtype=torch.int32, device=DEV)
+    sk = None if sinks is None else torch.tensor(sinks, dtype=torch.float32, device=DEV)
     lse = torch.full((b.num_tokens, b.num_q_heads), float("nan"), dtype=torch.float32, device=DEV)
     out = pa.pa_forward_masked(g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens,
-                               g.query_start_loc, b.scale, mask, prefix_lens=pl, lse=lse,
+                               g.query_start_loc, b.scale, mask, prefix_lens=pl, sinks=sk, lse=lse,
                                max_seq_len=max(b.seq_lens_list + [1]),
                                max_q_len=max(b.q_lens + [1]))
     torch.cuda.synchronize()
     ref, rlse = oracle.attention(b.q, b.k_cache, b.v_cache, b.block_table, b.seq_lens,
                                  b.query_start_loc, b.scale, b.num_kv_heads, mask=mask,
-                                 prefix_lens=None if prefixes is None else np.asarray(prefixes, np.int32))
+                                 prefix_lens=None if prefixes is None else np.asarray(prefixes, np.int32),
+                                 sinks=sinks)
     got = out.float().cpu().numpy()
     check_out(got, ref, b.dtype, what)
     check_lse(lse.cpu().numpy(), rlse, what)
@@ -268,6 +270,35 @@ def test_masked_causal_is_pa_forward_bitwise():
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), c.view(torch.int16))
     assert torch.equal(a.view(torch.int16), z.view(torch.int16))
+
+
+def sink_logits(Hq, seed):
+    """Sink logits far below, near and far above the scaled scores, and one -inf."""
+    g = np.random.default_rng(seed)
+    s = g.normal(0.0, 2.0, Hq).astype(np.float32)
+    s[0], s[1], s[2] = -40.0, 30.0, -np.inf
+    return s
+
+
+@pytest.mark.parametrize("mask,prefixes", [(pa.PA_MASK_CAUSAL, None), (pa.PA_MASK_FULL, None),
+                                           (pa.PA_MASK_PREFIX, [0, 41, 750, 20, 100])])
+def test_sinks_forward_matches_oracle(mask, prefixes):
+    b = workload.make_batch(MASK_Q, MASK_C, num_q_heads=32, num_kv_heads=8, head_dim_qk=128,
+                            page_size=16, seed=613)
+    masked_parity(b, mask, prefixes, "sinks bf16", sinks=sink_logits(32, 1))
+
+
+def test_sinks_on_split_decode_rows():
+    # few long decode requests: pa_forward splits their keys, and the sink enters
+    # in the merge of the partial rows
+    b = workload.llama_decode(3, batch=4)
+    masked_parity(b, pa.PA_MASK_CAUSAL, None, "sinks split decode", sinks=sink_logits(32, 2))
+
+
+def test_sinks_f32():
+    b = workload.make_batch([4, 1, 7], [20, 33, 0], num_q_heads=8, num_kv_heads=2, head_dim_qk=64,
+                            page_size=16, dtype=torch.float32, seed=617)
+    masked_parity(b, pa.PA_MASK_CAUSAL, None, "sinks fp32", sinks=sink_logits(8, 3))
 
 
 def test_full_mask_qwen3_scaled():
