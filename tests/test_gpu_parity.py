@@ -565,6 +565,88 @@ def test_graph_capture_replay_with_new_lengths():
             check_lse(g_lse, rlse, "graph batch %d" % i)
 
 
+def test_graph_replay_masked_sinks_and_chunked():
+    """A captured pa_forward_masked (prefix mask, sinks) and a captured pa_forward_chunked +
+    pa_merge_lse, replayed after rewriting the batch, the prefix lengths and the sinks."""
+    Hq, Hkv, D, P = 32, 8, 128, 16
+    specs = [([1, 9, 130], [700, 40, 200]), ([3, 1, 60], [10, 1500, 90])]
+    batches = [workload.make_batch(q, c, num_q_heads=Hq, num_kv_heads=Hkv, head_dim_qk=D,
+                                   page_size=P, seed=200 + i, max_pages_per_seq=120,
+                                   pool_pages=300) for i, (q, c) in enumerate(specs)]
+    prefixes = [[5, 30, 100], [0, 2000, 77]]
+    sinks = [sink_logits(Hq, 5), sink_logits(Hq, 6)]
+    T, C, S = max(b.num_tokens for b in batches), 256, 8
+    q = torch.zeros(T, Hq, D, dtype=torch.bfloat16, device=DEV)
+    kc = batches[0].k_cache.to(DEV).clone()
+    vc = batches[0].v_cache.to(DEV).clone()
+    bt = torch.zeros(3, 120, dtype=torch.int32, device=DEV)
+    sl = torch.zeros(3, dtype=torch.int32, device=DEV)
+    qsl = torch.zeros(4, dtype=torch.int32, device=DEV)
+    pl = torch.zeros(3, dtype=torch.int32, device=DEV)
+    sk = torch.zeros(Hq, dtype=torch.float32, device=DEV)
+    out = torch.zeros(T, Hq, D, dtype=torch.bfloat16, device=DEV)
+    cout = torch.zeros(T, Hq, D, dtype=torch.bfloat16, device=DEV)
+    po = torch.zeros(T, Hq, S, D, dtype=torch.float32, device=DEV)
+    plse = torch.zeros(T, Hq, S, dtype=torch.float32, device=DEV)
+    kw = dict(max_seq_len=120 * P, max_q_len=T)
+    ws = torch.empty(pa.pa_workspace_size(pa.make_dims(q, kc, vc, bt, sl, T, **kw)),
+                     dtype=torch.uint8, device=DEV)
+
+    def load(i):
+        b = batches[i]
+        q.zero_()
+        q[:b.num_tokens].copy_(b.q)
+        kc.copy_(b.k_cache)
+        vc.copy_(b.v_cache)
+        bt.copy_(b.block_table)
+        sl.copy_(b.seq_lens)
+        qsl.copy_(b.query_start_loc)
+        pl.copy_(torch.tensor(prefixes[i], dtype=torch.int32))
+        sk.copy_(torch.from_numpy(sinks[i]))
+
+    def call():
+        pa.pa_forward_masked(q, kc, vc, bt, sl, qsl, batches[0].scale, pa.PA_MASK_PREFIX,
+                             prefix_lens=pl, sinks=sk, out=out, workspace=ws, **kw)
+        pa.pa_forward_chunked(q, kc, vc, bt, sl, qsl, batches[0].scale, C, num_chunks=S,
+                              part_out=po, part_lse=plse, **kw)
+        pa.pa_merge_lse(po, plse, out=cout)
+
+    load(0)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        call()
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for i, b in enumerate(batches):
+            say("masked / chunked graph replay %d batch %d" % (rep, i))
+            load(i)
+            out.fill_(float("nan"))
+            cout.fill_(float("nan"))
+            graph.replay()
+            torch.cuda.synchronize()
+            g = out[:b.num_tokens].float().cpu().numpy()
+            gc = cout[:b.num_tokens].float().cpu().numpy()
+            ref, _ = oracle.attention(b.q, b.k_cache, b.v_cache, b.block_table, b.seq_lens,
+                                      b.query_start_loc, b.scale, b.num_kv_heads,
+                                      mask=oracle.MASK_PREFIX,
+                                      prefix_lens=np.asarray(prefixes[i], np.int32), sinks=sinks[i])
+            check_out(g, ref, torch.bfloat16, "graph masked batch %d" % i)
+            cref, _ = oracle_forward(b)
+            check_out(gc, cref, torch.bfloat16, "graph chunked batch %d" % i)
+
+
+def test_sinks_llama_decode_full_size():
+    # the headline decode batch (B 64, L~U[500,8192]) with sink logits
+    b = workload.llama_decode(3)
+    masked_parity(b, pa.PA_MASK_CAUSAL, None, "sinks llama decode full size", sinks=sink_logits(32, 4))
+
+
 def test_validate_reports_bad_rows():
     b = workload.make_batch([1, 2], [10, 30], num_q_heads=32, num_kv_heads=8, head_dim_qk=128,
                             page_size=16, seed=17)
