@@ -108,6 +108,51 @@ size_t mla_ws_bytes(const pa_dims* d, int S) {
   return lse_bytes + rows * S * 512 * sizeof(float);
 }
 
+// Chunked route of a pa_forward call (chunked-context processing, "vLLM AMD
+// ROCm Attention Backend Optimization", bullet "Chunked context
+// processing"), decided from the dims alone so that pa_workspace_size can
+// size it.  A causal bf16 call with prefill-mode rows whose prefill items
+// cannot fill the GPU (at most kRouteItems (request, KV head, 256-row block)
+// items by the capacities) and whose contexts reach kRouteMinKeys keys runs
+// as chunk partials plus a merge: S chunks of C keys, S chosen so that
+// items x S is about kRouteTargetItems while the fp32 partials stay under
+// kRouteMaxBytes.
+constexpr int64_t kRouteItems = 128, kRouteTargetItems = 1024, kRouteMinKeys = 8192,
+                  kRouteMinChunk = 2048, kRouteMaxBytes = 256ll << 20;
+struct ChunkRoute {
+  bool on = false;
+  int C = 0, S = 0, row_blocks = 0;
+  size_t po_bytes = 0, pl_bytes = 0;
+};
+ChunkRoute chunk_route(const pa_dims* d) {
+  ChunkRoute r;
+  if (d->dtype != PA_BF16 || d->head_dim_qk != d->head_dim_v) return r;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if ((int64_t)d->max_q_len * G <= pa::kDecodeRows) return r;  // decode-only calls split their own way
+  if (d->max_seq_len < kRouteMinKeys) return r;
+  const int64_t blocks = ((int64_t)d->max_q_len * G + pa::kPrefillRows - 1) / pa::kPrefillRows;
+  const int64_t items = (int64_t)d->num_seqs * d->num_kv_heads * blocks;
+  if (items < 1 || items > kRouteItems) return r;
+  const int64_t rows = (int64_t)d->num_tokens * d->num_q_heads;
+  const int64_t row_bytes = ((int64_t)d->head_dim_v + 1) * 4;
+  int64_t S = (kRouteTargetItems + items - 1) / items;
+  S = std::min<int64_t>(S, kRouteMaxBytes / std::max<int64_t>(1, rows * row_bytes));
+  S = std::min<int64_t>(S, pa::kMaxSplits);
+  if (S < 2) return r;
+  int64_t C = (d->max_seq_len + S - 1) / S;
+  C = std::max<int64_t>(kRouteMinChunk, (C + 63) & ~63LL);
+  S = (d->max_seq_len + C - 1) / C;
+  if (S < 2 || items * S > INT32_MAX) return r;
+  auto align = [](int64_t x) { return (size_t)((x + 255) & ~255LL); };
+  r.on = true;
+  r.C = (int)C;
+  r.S = (int)S;
+  r.row_blocks = (int)blocks;
+  r.po_bytes = align(rows * S * d->head_dim_v * 4);
+  r.pl_bytes = align(rows * S * 4);
+  return r;
+}
+
 pa_status check_mla(const pa_dims* d) {
   pa_status st = check_dims(d);
   if (st != PA_OK) return st;
@@ -150,8 +195,10 @@ size_t pa_workspace_size(const pa_dims* d) {
   if (check_dims(d) != PA_OK) return 0;
   if (d->dtype == PA_F32) return 256;
   const int G = d->num_q_heads / d->num_kv_heads;
+  const ChunkRoute r = chunk_route(d);
   return pa::fwd_workspace_layout(d->num_seqs, d->num_tokens, d->num_kv_heads, G, d->head_dim_v)
-      .total;
+             .total +
+         r.po_bytes + r.pl_bytes;
 }
 
 pa_status pa_forward(const void* q, const void* k_cache, const void* v_cache,
@@ -219,6 +266,40 @@ pa_status pa_forward_masked(const void* q, const void* k_cache, const void* v_ca
   const int D = d->head_dim_qk;
   const pa::FwdWorkspace w = pa::fwd_workspace_layout(d->num_seqs, d->num_tokens,
                                                       d->num_kv_heads, G, D);
+  const ChunkRoute route = chunk_route(d);
+  if (route.on && mask == PA_MASK_CAUSAL && !sinks) {
+    // few long requests: chunk partials and their merge instead of the
+    // persistent kernel, whose prefill items alone could not fill the GPU
+    if (!workspace || workspace_bytes < w.total + route.po_bytes + route.pl_bytes)
+      return PA_ERR_WORKSPACE;
+    char* ws = (char*)workspace;
+    pa::MhaArgs a{};
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_table = block_table;
+    a.seq_lens = seq_lens;
+    a.qsl = query_start_loc;
+    a.part_o = (float*)(ws + w.total);
+    a.part_lse = (float*)(ws + w.total + route.po_bytes);
+    a.scale = scale;
+    a.num_seqs = d->num_seqs;
+    a.Hq = d->num_q_heads;
+    a.Hkv = d->num_kv_heads;
+    a.G = G;
+    a.P = d->page_size;
+    a.max_pages = d->max_pages_per_seq;
+    a.num_splits = route.S;
+    a.chunk_keys = route.C;
+    a.row_blocks = route.row_blocks;
+    hipError_t e = mark(g_ev_start, s);
+    if (e == hipSuccess) e = pa::launch_mha_chunked(a, D, s);
+    if (e == hipSuccess) e = mark(g_ev_stop, s);
+    if (e == hipSuccess)
+      e = pa::launch_merge(a.part_o, a.part_lse, d->num_tokens * d->num_q_heads, route.S,
+                           d->head_dim_v, out, true, lse, s);
+    return e == hipSuccess ? PA_OK : hip_fail(e);
+  }
   if (!workspace || workspace_bytes < w.total) return PA_ERR_WORKSPACE;
   DevCfg cfg;
   st = device_config(&cfg);

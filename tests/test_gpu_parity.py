@@ -367,6 +367,21 @@ def test_chunked_long_context_extend():
     chunked_parity(b, 4096, "chunked long extend")
 
 
+def test_forward_runs_few_long_extends_as_chunks():
+    # few long requests with new tokens: pa_forward itself runs them as chunk
+    # partials + merge (its prefill items alone could not fill the GPU)
+    b = workload.make_batch([200, 1, 64], [20000, 30000, 9000], num_q_heads=32, num_kv_heads=8,
+                            head_dim_qk=128, page_size=16, seed=93)
+    forward_parity(b, "pa_forward on few long extends")
+
+
+def test_forward_long_extend_full_size_sampled_rows():
+    b = workload.llama_long_extend(0)
+    rows = np.zeros((b.num_tokens, b.num_q_heads), dtype=bool)
+    rows[[0, 100, 255], :] = True
+    forward_parity(b, "pa_forward long extend full size (sampled rows)", rows=rows)
+
+
 def test_chunked_long_extend_full_size_sampled_rows():
     # the bench's chunked-extend workload: 256 new tokens on 131072 cached tokens
     b = workload.llama_long_extend(0)
