@@ -411,8 +411,8 @@ def main():
         cflops = workload.algorithmic_flops(cb)
         result["chunked_extend"] = {
             "workload": "Llama-3.1-8B-shaped extend, 256 new tokens on 131072 cached tokens, "
-                        "page 16: pa_forward_chunked (8192-key chunks) + pa_merge_lse, against "
-                        "one pa_forward call",
+                        "page 16: pa_forward_chunked (8192-key chunks) + pa_merge_lse, and the "
+                        "same request through pa_forward (which runs such calls as chunks too)",
             "chunk_keys": C, "chunks": cS,
             "tflops": round(cflops / (c_step_ms * 1e-3) / 1e12, 2),
             "frac": round(cflops / (c_step_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
