@@ -111,7 +111,7 @@ size_t mla_ws_bytes(const pa_dims* d, int S) {
 // Chunked route of a pa_forward call (chunked-context processing, "vLLM AMD
 // ROCm Attention Backend Optimization", bullet "Chunked context
 // processing"), decided from the dims alone so that pa_workspace_size can
-// size it.  A causal bf16 call with prefill-mode rows whose prefill items
+// size it.  A bf16 call with prefill-mode rows whose prefill items
 // cannot fill the GPU (at most kRouteItems (request, KV head, 256-row block)
 // items by the capacities) and whose contexts reach kRouteMinKeys keys runs
 // as chunk partials plus a merge: S chunks of C keys, S chosen so that
@@ -267,7 +267,7 @@ pa_status pa_forward_masked(const void* q, const void* k_cache, const void* v_ca
   const pa::FwdWorkspace w = pa::fwd_workspace_layout(d->num_seqs, d->num_tokens,
                                                       d->num_kv_heads, G, D);
   const ChunkRoute route = chunk_route(d);
-  if (route.on && mask == PA_MASK_CAUSAL && !sinks) {
+  if (route.on) {
     // few long requests: chunk partials and their merge instead of the
     // persistent kernel, whose prefill items alone could not fill the GPU
     if (!workspace || workspace_bytes < w.total + route.po_bytes + route.pl_bytes)
@@ -292,12 +292,14 @@ pa_status pa_forward_masked(const void* q, const void* k_cache, const void* v_ca
     a.num_splits = route.S;
     a.chunk_keys = route.C;
     a.row_blocks = route.row_blocks;
+    a.mask = mask;
+    a.prefix_lens = prefix_lens;
     hipError_t e = mark(g_ev_start, s);
     if (e == hipSuccess) e = pa::launch_mha_chunked(a, D, s);
     if (e == hipSuccess) e = mark(g_ev_stop, s);
     if (e == hipSuccess)
       e = pa::launch_merge(a.part_o, a.part_lse, d->num_tokens * d->num_q_heads, route.S,
-                           d->head_dim_v, out, true, lse, s);
+                           d->head_dim_v, out, true, lse, s, sinks, d->num_q_heads);
     return e == hipSuccess ? PA_OK : hip_fail(e);
   }
   if (!workspace || workspace_bytes < w.total) return PA_ERR_WORKSPACE;

@@ -149,7 +149,8 @@ hipError_t launch_mha_split(const MhaArgs& a, int D, hipStream_t s);
 hipError_t launch_mha_chunked(const MhaArgs& a, int D, hipStream_t s);
 hipError_t mha_occupancy(int D, bool decode_only, int* blocks_per_cu);
 hipError_t launch_merge(const float* po, const float* pl, int rows, int S, int Dv, void* out,
-                        bool out_bf16, float* lse, hipStream_t s);
+                        bool out_bf16, float* lse, hipStream_t s, const float* sinks = nullptr,
+                        int Hq = 1);
 hipError_t launch_f32_forward(const F32Args& a, hipStream_t s);
 hipError_t launch_f32_split(const F32Args& a, hipStream_t s);
 hipError_t launch_mla_split(const MlaArgs& a, hipStream_t s);

@@ -6,6 +6,8 @@
 // processing": the pieces are combined by log-sum-exp for stability):
 //   M = max_s lse_s;  w_s = exp(lse_s - M), 0 for an empty partition;
 //   out = sum_s w_s o_s / sum_s w_s;  lse = M + ln sum_s w_s.
+// With sink logits (pa_forward's chunked route), row r of head r % Hq folds
+// sinks[r % Hq] in as one more zero-valued key (fold_sink).
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -19,7 +21,9 @@ constexpr int kMergeThreads = 256;
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __restrict__ po,
                                                               const float* __restrict__ pl,
                                                               int rows, int S, int Dv, void* out,
-                                                              int out_bf16, float* lse) {
+                                                              int out_bf16, float* lse,
+                                                              const float* __restrict__ sinks,
+                                                              int Hq) {
   __shared__ float wts[kMergeThreads / 64][kMaxSplits];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t row = (int64_t)blockIdx.x * (kMergeThreads / 64) + wv;
@@ -40,7 +44,9 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
   wsum = wave_sum(wsum);
   __syncthreads();
   if (!valid) return;
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  float lrow = wsum > 0.f ? M + __logf(wsum) : kNegInf;
+  if (sinks) inv *= fold_sink(sinks[row % Hq], &lrow);
   const float* o = po + row * S * Dv;
   for (int d = lane; d < Dv; d += 64) {
     float acc = 0.f;
@@ -52,17 +58,17 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
     if (out_bf16) ((__bf16*)out)[row * Dv + d] = (__bf16)acc;
     else ((float*)out)[row * Dv + d] = acc;
   }
-  if (lane == 0 && lse) lse[row] = wsum > 0.f ? M + __logf(wsum) : kNegInf;
+  if (lane == 0 && lse) lse[row] = lrow;
 }
 
 }  // namespace
 
 hipError_t launch_merge(const float* po, const float* pl, int rows, int S, int Dv, void* out,
-                        bool out_bf16, float* lse, hipStream_t s) {
+                        bool out_bf16, float* lse, hipStream_t s, const float* sinks, int Hq) {
   if (rows <= 0) return hipSuccess;
   const int blocks = (rows + kMergeThreads / 64 - 1) / (kMergeThreads / 64);
   hipLaunchKernelGGL(merge_kernel, dim3(blocks), dim3(kMergeThreads), 0, s, po, pl, rows, S, Dv,
-                     out, out_bf16 ? 1 : 0, lse);
+                     out, out_bf16 ? 1 : 0, lse, sinks, Hq > 0 ? Hq : 1);
   return hipGetLastError();
 }
 

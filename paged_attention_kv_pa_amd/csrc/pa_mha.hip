@@ -1133,8 +1133,9 @@ void mha_split_kernel(MhaArgs a) {
 // Backend Optimization", bullet "Chunked context processing").  Workgroup
 // (request b, KV head, row block, chunk s) runs the prefill-mode item of the
 // block's rows (up to 256: query tokens x the G heads of the KV head) over
-// the keys of chunk s, [s C, (s + 1) C), cut at the causal limit of the
-// block's last row.  Its partials are indexed by output row:
+// the keys of chunk s, [s C, (s + 1) C), cut at the key limit of the
+// block's last row (causal for pa_forward_chunked; pa_forward's chunked route
+// passes its mask).  Its partials are indexed by output row:
 // part_o[(out_row S + s) D ..] and part_lse[out_row S + s].  A row that sees
 // no key of the chunk gets zeros and -inf: inside the item when another row
 // of the block sees the chunk, here when none does.  Requests with no work
@@ -1156,7 +1157,8 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void mha_chunked_kernel(MhaArgs
   const int nrows = min(kPrefillRows, rows - row0);
   const int ctx = L - nq;
   const long long t0 = (long long)s * a.chunk_keys;
-  const long long last_lim = (long long)ctx + (row0 + nrows - 1) / G + 1;
+  const int pfx = a.mask == kMaskPrefix ? a.prefix_lens[b] : 0;
+  const long long last_lim = min(L, visible_end(a.mask, ctx, (row0 + nrows - 1) / G, pfx));
   const long long t1 = min(last_lim, t0 + a.chunk_keys);
   if (t1 <= t0) {
     constexpr int C4 = D / 4;

@@ -375,6 +375,18 @@ def test_forward_runs_few_long_extends_as_chunks():
     forward_parity(b, "pa_forward on few long extends")
 
 
+@pytest.mark.parametrize("mask,prefixes,with_sinks", [(pa.PA_MASK_FULL, None, True),
+                                                      (pa.PA_MASK_PREFIX, [20100, 5, 9030], False),
+                                                      (pa.PA_MASK_CAUSAL, None, True)])
+def test_forward_chunked_route_masks_and_sinks(mask, prefixes, with_sinks):
+    # the same few long extends under the other masks and with sinks: the chunk
+    # kernel takes the mask, the merge folds the sinks in
+    b = workload.make_batch([200, 1, 64], [20000, 30000, 9000], num_q_heads=32, num_kv_heads=8,
+                            head_dim_qk=128, page_size=16, seed=95)
+    masked_parity(b, mask, prefixes, "routed mask %d" % mask,
+                  sinks=sink_logits(32, 9) if with_sinks else None)
+
+
 def test_forward_long_extend_full_size_sampled_rows():
     b = workload.llama_long_extend(0)
     rows = np.zeros((b.num_tokens, b.num_q_heads), dtype=bool)
