@@ -480,6 +480,20 @@ def test_edge_empty_requests_single_keys_and_exact_pages():
     forward_parity(b, "edge mix")
 
 
+def test_edge_empty_requests_in_chunked_masked_and_routed_calls():
+    # requests with no new token (one of them with no key at all) between real ones
+    b = workload.make_batch([1, 0, 40, 0, 3], [0, 5, 100, 0, 13], num_q_heads=32, num_kv_heads=8,
+                            head_dim_qk=128, page_size=16, seed=13)
+    chunked_parity(b, 64, "edge chunked")
+    masked_parity(b, pa.PA_MASK_FULL, None, "edge full mask", sinks=sink_logits(32, 7))
+    masked_parity(b, pa.PA_MASK_PREFIX, [0, 3, 120, 0, 16], "edge prefix mask")
+    # the same shape of batch with long contexts, so that pa_forward takes its chunked route
+    r = workload.make_batch([1, 0, 40, 0, 3], [9000, 5, 10000, 0, 13], num_q_heads=32,
+                            num_kv_heads=8, head_dim_qk=128, page_size=16, seed=14)
+    forward_parity(r, "edge routed")
+    masked_parity(r, pa.PA_MASK_PREFIX, [0, 3, 9500, 0, 16], "edge routed prefix", sinks=sink_logits(32, 8))
+
+
 @pytest.mark.parametrize("Hq,Hkv,D,P", [(32, 8, 64, 16), (64, 2, 128, 16), (16, 16, 128, 32),
                                         (8, 1, 128, 64), (12, 4, 64, 8), (32, 8, 128, 24),
                                         (16, 2, 64, 40)])
