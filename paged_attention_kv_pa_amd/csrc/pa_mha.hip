@@ -1144,11 +1144,17 @@ template <int D>
 __global__ __launch_bounds__(kPrefillThreads, 1) void mha_chunked_kernel(MhaArgs a) {
   __shared__ LdsPrefill<D> sm;
   const int S = a.num_splits, nblk = a.row_blocks;
-  int idx = blockIdx.x;
-  const int s = idx % S;
-  idx /= S;
+  // Workgroups go to the 8 chiplets (XCDs, each with its own L2) round-robin
+  // by index.  The index is remapped so that consecutive logical indices sit
+  // on one XCD and are dispatched together, and the row blocks of one
+  // (request, KV head, chunk), which read the same keys, are consecutive.
+  const int n = gridDim.x, q8 = n >> 3, r8 = n & 7;
+  const int x = blockIdx.x & 7, p = blockIdx.x >> 3;
+  int idx = x * q8 + min(x, r8) + p;
   const int blk = idx % nblk;
   idx /= nblk;
+  const int s = idx % S;
+  idx /= S;
   const int kvh = idx % a.Hkv, b = idx / a.Hkv;
   int nq, L, q0;
   shape_of(a.qsl, a.seq_lens, a.max_pages, a.P, b, &nq, &L, &q0);
