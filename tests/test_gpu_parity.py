@@ -474,6 +474,16 @@ def test_mla_full_size_sampled_heads():
 
 # --------------------------------------------------------------- edge cases
 
+@pytest.mark.parametrize("Hq,Hkv", [(16, 16), (32, 8)])
+def test_f32_unequal_head_dims(Hq, Hkv):
+    # non-absorbed MLA-shaped heads (query/key 192 = 128 + 64 rotary, value 128) on the
+    # fp32 path: prefill, extend and decode rows
+    b = workload.make_batch([1, 37, 130], [300, 0, 90], num_q_heads=Hq, num_kv_heads=Hkv,
+                            head_dim_qk=192, head_dim_v=128, page_size=16,
+                            dtype=torch.float32, seed=701 + Hq)
+    forward_parity(b, "fp32 Dqk 192 Dv 128 Hq=%d Hkv=%d" % (Hq, Hkv))
+
+
 def test_edge_empty_requests_single_keys_and_exact_pages():
     b = workload.make_batch([1, 0, 1, 3, 0, 16, 1, 1], [0, 5, 15, 13, 0, 0, 31, 47],
                             num_q_heads=32, num_kv_heads=8, head_dim_qk=128, page_size=16, seed=11)
