@@ -64,6 +64,9 @@ def _load():
             lib.orc_chunked_partials.argtypes = [p, p, p, i32, p, p, p] + [i32] * 9 + [f32, i32, i32,
                                                                                     p, p, i32]
             lib.orc_chunked_partials.restype = i32
+            lib.orc_chunked_partials_masked.argtypes = ([p, p, p, i32, p, p, p] + [i32] * 9 +
+                                                        [f32, i32, i32, i32, p, p, p, i32])
+            lib.orc_chunked_partials_masked.restype = i32
             lib.orc_merge_lse.argtypes = [p, p, i32, i32, i32, p, p]
             lib.orc_merge_lse.restype = i32
             lib.orc_split_range.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32),
@@ -208,7 +211,7 @@ def decode_split(q, k_cache, v_cache, block_table, seq_lens, scale, num_splits,
 
 def chunked_partials(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale,
                      chunk_keys, num_chunks, num_kv_heads, head_dim_v=None, layout=LAYOUT_MHA,
-                     nthreads=None):
+                     nthreads=None, mask=MASK_CAUSAL, prefix_lens=None):
     """Chunked-context partials of a varlen batch, in fp64 (see orc_chunked_partials).
 
     Chunk s covers keys [s C, (s + 1) C) of every request; each row gets the partial
@@ -232,9 +235,18 @@ def chunked_partials(q, k_cache, v_cache, block_table, seq_lens, query_start_loc
     po = np.full((T, Hq, S, Dv), np.nan, dtype=np.float64)
     pl = np.full((T, Hq, S), np.nan, dtype=np.float64)
     nt = max_threads() if nthreads is None else int(nthreads)
-    rc = lib.orc_chunked_partials(_ptr(qa), _ptr(ka), _ptr(va), dt, _ptr(bt), _ptr(sl), _ptr(qs),
-                                  B, Hq, int(num_kv_heads), Dqk, Dv, P, num_pages, bt.shape[1],
-                                  layout, float(scale), int(chunk_keys), S, _ptr(po), _ptr(pl), nt)
+    if mask == MASK_CAUSAL and prefix_lens is None:
+        rc = lib.orc_chunked_partials(_ptr(qa), _ptr(ka), _ptr(va), dt, _ptr(bt), _ptr(sl),
+                                      _ptr(qs), B, Hq, int(num_kv_heads), Dqk, Dv, P, num_pages,
+                                      bt.shape[1], layout, float(scale), int(chunk_keys), S,
+                                      _ptr(po), _ptr(pl), nt)
+    else:
+        pfx = None if prefix_lens is None else _i32(prefix_lens)
+        rc = lib.orc_chunked_partials_masked(_ptr(qa), _ptr(ka), _ptr(va), dt, _ptr(bt), _ptr(sl),
+                                             _ptr(qs), B, Hq, int(num_kv_heads), Dqk, Dv, P,
+                                             num_pages, bt.shape[1], layout, float(scale),
+                                             int(chunk_keys), S, int(mask), _ptr(pfx), _ptr(po),
+                                             _ptr(pl), nt)
     _check(rc)
     return po, pl
 

@@ -355,18 +355,24 @@ int orc_decode_split(const void* q, const void* kc, const void* vc, int dtype,
  * attention over the keys of chunk s that the token sees:
  *   [s C, min((s + 1) C, c_b + j + 1)).
  * A chunk holding none of them gives zeros and -inf, so orc_merge_lse over
- * the S chunks of a row gives that row of orc_attention.
+ * the S chunks of a row gives that row of orc_attention.  With mask /
+ * prefix_lens (as in orc_attention_masked) a token sees the chunk's keys
+ * below its visible end instead.
  *   part_out [T, Hq, S, Dv], part_lse [T, Hq, S], both double.
  */
-int orc_chunked_partials(const void* q, const void* kc, const void* vc, int dtype,
-                         const int32_t* block_table, const int32_t* seq_lens,
-                         const int32_t* qsl, int B, int Hq, int Hkv, int Dqk,
-                         int Dv, int P, int num_pages, int max_pages, int layout,
-                         float scale, int C, int S, double* part_out,
-                         double* part_lse, int nthreads) {
+int orc_chunked_partials_masked(const void* q, const void* kc, const void* vc,
+                                int dtype, const int32_t* block_table,
+                                const int32_t* seq_lens, const int32_t* qsl, int B,
+                                int Hq, int Hkv, int Dqk, int Dv, int P, int num_pages,
+                                int max_pages, int layout, float scale, int C, int S,
+                                int mask, const int32_t* prefix_lens,
+                                double* part_out, double* part_lse, int nthreads) {
   int rc = check_common(B, Hq, Hkv, Dqk, Dv, P, max_pages, layout);
   if (rc) return rc;
   if (C <= 0 || S <= 0) return ORC_ERR_ARG;
+  if (mask != ORC_MASK_CAUSAL && mask != ORC_MASK_FULL && mask != ORC_MASK_PREFIX)
+    return ORC_ERR_ARG;
+  if (mask == ORC_MASK_PREFIX && !prefix_lens) return ORC_ERR_ARG;
   const int g = Hq / Hkv;
   const double sigma = (double)scale;
   int err = ORC_OK;
@@ -406,7 +412,10 @@ int orc_chunked_partials(const void* q, const void* kc, const void* vc, int dtyp
     } else {
       for (int j = 0; j < nq; ++j) {
         const int i = i0 + j;
-        const long seen = (long)c + j + 1;  /* keys 0 .. c + j */
+        long seen = (long)c + j + 1;  /* keys 0 .. c + j under the causal mask */
+        if (mask == ORC_MASK_FULL) seen = L;
+        if (mask == ORC_MASK_PREFIX && prefix_lens[b] > seen)
+          seen = prefix_lens[b] < L ? prefix_lens[b] : L;
         for (int hh = h * g; hh < (h + 1) * g; ++hh) {
           for (int d = 0; d < Dqk; ++d)
             qrow[d] = load_elem(q, dtype, ((size_t)i * Hq + hh) * Dqk + d);
@@ -424,6 +433,19 @@ int orc_chunked_partials(const void* q, const void* kc, const void* vc, int dtyp
     free(Kd); free(Vd); free(qrow); free(s);
   }
   return err;
+}
+
+/* Causal chunk partials (orc_chunked_partials_masked with ORC_MASK_CAUSAL). */
+int orc_chunked_partials(const void* q, const void* kc, const void* vc, int dtype,
+                         const int32_t* block_table, const int32_t* seq_lens,
+                         const int32_t* qsl, int B, int Hq, int Hkv, int Dqk,
+                         int Dv, int P, int num_pages, int max_pages, int layout,
+                         float scale, int C, int S, double* part_out,
+                         double* part_lse, int nthreads) {
+  return orc_chunked_partials_masked(q, kc, vc, dtype, block_table, seq_lens, qsl,
+                                     B, Hq, Hkv, Dqk, Dv, P, num_pages, max_pages,
+                                     layout, scale, C, S, ORC_MASK_CAUSAL, NULL,
+                                     part_out, part_lse, nthreads);
 }
 
 /*

@@ -155,6 +155,21 @@ def test_chunked_then_merge_equals_unchunked(C):
     assert np.all(np.isneginf(pl[:, :, S - 1])) and np.all(po[:, :, S - 1] == 0)
 
 
+@pytest.mark.parametrize("mask,prefix", [(oracle.MASK_FULL, None), (oracle.MASK_PREFIX, [0, 4, 11, 30, 15, 2])])
+def test_masked_chunks_merge_to_masked_attention(mask, prefix):
+    """Chunk partials under the full and prefix masks merge to the masked attention."""
+    specs = [(1, 0), (1, 12), (4, 9), (6, 0), (3, 30), (7, 5)]
+    c = _build_case(35, specs, 4, 2, 8, 8, 4)
+    pfx = None if prefix is None else np.asarray(prefix, np.int32)
+    out, lse = oracle.attention(c["q"], c["kc"], c["vc"], c["bt"], c["seq"], c["qsl"], 0.35, 2,
+                                head_dim_v=8, mask=mask, prefix_lens=pfx)
+    po, pl = oracle.chunked_partials(c["q"], c["kc"], c["vc"], c["bt"], c["seq"], c["qsl"], 0.35,
+                                     5, 8, 2, head_dim_v=8, mask=mask, prefix_lens=pfx)
+    mo, ml = oracle.merge_lse(po, pl)
+    np.testing.assert_allclose(mo, out, atol=TOL, rtol=0)
+    np.testing.assert_allclose(ml, lse, atol=TOL, rtol=0)
+
+
 def test_chunked_partials_match_sdpa_on_visible_keys():
     """Each chunk partial of a row is attention over the chunk's keys that the row's
     token sees (SDPA on the dense keys); chunks it cannot see are empty."""
