@@ -203,6 +203,8 @@ PA_API pa_status pa_decode_split(const void* q, const void* k_cache, const void*
  * then gives pa_forward's out and lse.  One workgroup runs each (request, KV
  * head, block of up to 256 rows, chunk), so a long context is spread over
  * num_chunks workgroups whatever its number of new tokens.
+ * mask / prefix_lens as for pa_forward_masked (PA_MASK_CAUSAL and NULL for
+ * causal attention): a token sees the chunk's keys below its mask's limit.
  * chunk_keys: a positive multiple of 64; num_chunks in [1, 256] with
  * chunk_keys * num_chunks >= dims->max_seq_len.  bf16 only, Dqk == Dv in
  * {64, 128}, P a multiple of 8 up to 256.  Rows of requests with no new token
@@ -214,7 +216,8 @@ PA_API pa_status pa_forward_chunked(const void* q, const void* k_cache, const vo
                                     const int32_t* block_table, const int32_t* seq_lens,
                                     const int32_t* query_start_loc, float scale,
                                     int32_t chunk_keys, int32_t num_chunks, float* part_out,
-                                    float* part_lse, const pa_dims* dims, void* stream);
+                                    float* part_lse, int32_t mask, const int32_t* prefix_lens,
+                                    const pa_dims* dims, void* stream);
 
 /*
  * pa_merge_lse — second launch: log-sum-exp merge of split partials ([TDD]

@@ -64,7 +64,7 @@ def library():
             lib.pa_forward_masked.restype = i32
             lib.pa_decode_split.argtypes = [p, p, p, p, p, f32, i32, p, p, dp, p]
             lib.pa_decode_split.restype = i32
-            lib.pa_forward_chunked.argtypes = [p, p, p, p, p, p, f32, i32, i32, p, p, dp, p]
+            lib.pa_forward_chunked.argtypes = [p, p, p, p, p, p, f32, i32, i32, p, p, i32, p, dp, p]
             lib.pa_forward_chunked.restype = i32
             lib.pa_merge_lse.argtypes = [p, p, i32, i32, i32, p, p, i32, p]
             lib.pa_merge_lse.restype = i32
@@ -265,7 +265,7 @@ def pa_decode_split(q, k_cache, v_cache, block_table, seq_lens, scale, num_split
 
 def pa_forward_chunked(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale,
                        chunk_keys, num_chunks=None, part_out=None, part_lse=None, max_seq_len=None,
-                       max_q_len=None, stream=None):
+                       max_q_len=None, stream=None, mask=PA_MASK_CAUSAL, prefix_lens=None):
     """Chunked-context partials (see pa_forward_chunked in include/pa.h).
 
     num_chunks defaults to ceil(max_seq_len / chunk_keys).  Returns
@@ -294,8 +294,8 @@ def pa_forward_chunked(q, k_cache, v_cache, block_table, seq_lens, query_start_l
           "bad part_lse")
     st = library().pa_forward_chunked(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
                                       _ptr(seq_lens), _ptr(query_start_loc), float(scale), C, S,
-                                      _ptr(part_out), _ptr(part_lse), ctypes.byref(dims),
-                                      _stream(q.device, stream))
+                                      _ptr(part_out), _ptr(part_lse), int(mask), _ptr(prefix_lens),
+                                      ctypes.byref(dims), _stream(q.device, stream))
     _check(st, "pa_forward_chunked")
     return part_out, part_lse
 

@@ -443,13 +443,17 @@ pa_status pa_forward_chunked(const void* q, const void* k_cache, const void* v_c
                              const int32_t* block_table, const int32_t* seq_lens,
                              const int32_t* query_start_loc, float scale, int32_t chunk_keys,
                              int32_t num_chunks, float* part_out, float* part_lse,
-                             const pa_dims* d, void* stream) {
+                             int32_t mask, const int32_t* prefix_lens, const pa_dims* d,
+                             void* stream) {
   pa_status st = check_dims(d);
   if (st != PA_OK) return st;
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !query_start_loc || !part_out ||
       !part_lse)
     return PA_ERR_INVALID_ARG;
   if (chunk_keys < 64 || chunk_keys % 64 != 0) return PA_ERR_INVALID_ARG;
+  if (mask != PA_MASK_CAUSAL && mask != PA_MASK_FULL && mask != PA_MASK_PREFIX)
+    return PA_ERR_INVALID_ARG;
+  if ((mask == PA_MASK_PREFIX) != (prefix_lens != nullptr)) return PA_ERR_INVALID_ARG;
   if (num_chunks < 1 || num_chunks > pa::kMaxSplits) return PA_ERR_INVALID_ARG;
   if ((int64_t)chunk_keys * num_chunks < d->max_seq_len) return PA_ERR_INVALID_ARG;
   if (d->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
@@ -481,6 +485,8 @@ pa_status pa_forward_chunked(const void* q, const void* k_cache, const void* v_c
   a.num_splits = num_chunks;
   a.chunk_keys = chunk_keys;
   a.row_blocks = (int32_t)row_blocks;
+  a.mask = mask;
+  a.prefix_lens = prefix_lens;
   hipError_t e = mark(g_ev_start, s);
   if (e == hipSuccess) e = pa::launch_mha_chunked(a, d->head_dim_qk, s);
   if (e == hipSuccess) e = mark(g_ev_stop, s);

@@ -143,7 +143,7 @@ def test_chunked_argument_checks():
 
     def call(C, S, dd=d, qsl=FAKE):
         return lib.pa_forward_chunked(FAKE, FAKE, FAKE, FAKE, FAKE, qsl, 0.1, C, S, FAKE, FAKE,
-                                      ctypes.byref(dd), None)
+                                      binding.PA_MASK_CAUSAL, None, ctypes.byref(dd), None)
     bad = binding.PA_ERR_INVALID_ARG
     assert call(0, 8) == bad and call(32, 10) == bad and call(100, 4) == bad  # not a multiple of 64
     assert call(64, 0) == bad and call(64, 257) == bad
@@ -152,6 +152,11 @@ def test_chunked_argument_checks():
     assert call(64, 5, _dims(num_tokens=40, max_q_len=37, dtype=binding.PA_F32)) == binding.PA_ERR_UNSUPPORTED
     assert call(64, 5, _dims(num_tokens=40, max_q_len=37, head_dim_qk=80, head_dim_v=80)) == \
         binding.PA_ERR_UNSUPPORTED
+    dd = _dims(num_tokens=40, max_q_len=37)
+    masked = lambda m, pfx: lib.pa_forward_chunked(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, 64, 5,
+                                                   FAKE, FAKE, m, pfx, ctypes.byref(dd), None)
+    assert masked(3, None) == bad and masked(binding.PA_MASK_PREFIX, None) == bad
+    assert masked(binding.PA_MASK_FULL, FAKE) == bad
     assert call(64, 5, _dims(num_seqs=0, num_tokens=0, max_q_len=0)) == binding.PA_OK
     assert call(64, 5, _dims(num_tokens=0, max_q_len=0)) == binding.PA_OK
 

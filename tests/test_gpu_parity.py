@@ -309,17 +309,19 @@ def test_full_mask_qwen3_scaled():
 
 # ------------------------------------------- chunked-context processing
 
-def chunked_parity(b, C, what, S=None, rows=None):
+def chunked_parity(b, C, what, S=None, rows=None, mask=pa.PA_MASK_CAUSAL, prefixes=None):
     """pa_forward_chunked partials against the oracle's chunk partials, and their
     pa_merge_lse against plain attention (rows: optional sample of output rows)."""
     g = b.to(DEV)
+    pfx = None if prefixes is None else np.asarray(prefixes, np.int32)
+    dpfx = None if prefixes is None else torch.tensor(prefixes, dtype=torch.int32, device=DEV)
     Lmax = max(b.seq_lens_list + [1])
     S = (Lmax + C - 1) // C if S is None else S
     say("case %s: B=%d T=%d keys=%d C=%d S=%d" % (what, b.num_seqs, b.num_tokens,
                                                   sum(b.seq_lens_list), C, S))
     po, pl = pa.pa_forward_chunked(g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens,
                                    g.query_start_loc, b.scale, C, num_chunks=S, max_seq_len=Lmax,
-                                   max_q_len=max(b.q_lens + [1]))
+                                   max_q_len=max(b.q_lens + [1]), mask=mask, prefix_lens=dpfx)
     lse = torch.empty(pl.shape[:2], dtype=torch.float32, device=DEV)
     out = pa.pa_merge_lse(po, pl, lse=lse)
     torch.cuda.synchronize()
@@ -327,10 +329,13 @@ def chunked_parity(b, C, what, S=None, rows=None):
     got, glse = out.float().cpu().numpy(), lse.cpu().numpy()
     if rows is None:
         rpo, rpl = oracle.chunked_partials(b.q, b.k_cache, b.v_cache, b.block_table, b.seq_lens,
-                                           b.query_start_loc, b.scale, C, S, b.num_kv_heads)
+                                           b.query_start_loc, b.scale, C, S, b.num_kv_heads,
+                                           mask=mask, prefix_lens=pfx)
         check_out(po, rpo, torch.bfloat16, "%s partials" % what)
         check_lse(pl, rpl, "%s partial lse" % what)
-    ref, rlse = oracle_forward(b, rows)
+    ref, rlse = oracle.attention(b.q, b.k_cache, b.v_cache, b.block_table, b.seq_lens,
+                                 b.query_start_loc, b.scale, b.num_kv_heads, rows=rows,
+                                 mask=mask, prefix_lens=pfx)
     if rows is not None:
         sel = np.asarray(rows, dtype=bool)
         got, ref, glse, rlse = got[sel], ref[sel], glse[sel], rlse[sel]
@@ -352,6 +357,14 @@ def test_chunked_head_and_page_shapes(Hq, Hkv, D, P, C):
     b = workload.make_batch([70, 1, 129], [400, 333, 64], num_q_heads=Hq, num_kv_heads=Hkv,
                             head_dim_qk=D, page_size=P, seed=Hq + Hkv + D + P + C)
     chunked_parity(b, C, "chunked Hq=%d Hkv=%d D=%d P=%d" % (Hq, Hkv, D, P))
+
+
+@pytest.mark.parametrize("mask,prefixes", [(pa.PA_MASK_FULL, None),
+                                           (pa.PA_MASK_PREFIX, [0, 60, 800, 20, 300])])
+def test_chunked_masks_match_oracle(mask, prefixes):
+    b = workload.make_batch([1, 1, 300, 37, 520], [900, 50, 700, 0, 0], num_q_heads=32,
+                            num_kv_heads=8, head_dim_qk=128, page_size=16, seed=531)
+    chunked_parity(b, 256, "chunked mask %d" % mask, mask=mask, prefixes=prefixes)
 
 
 def test_chunked_extra_chunks_are_empty():
