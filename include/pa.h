@@ -228,11 +228,15 @@ PA_API pa_status pa_forward_chunked(const void* q, const void* k_cache, const vo
  * a row whose partitions are all empty gives zeros and -inf.
  *   part_out float32 [num_rows, S, Dv], part_lse float32 [num_rows, S]
  *   out      [num_rows, Dv] in out_dtype (pa_dtype), lse float32 [num_rows] or NULL
+ * sinks (nullable): float32 [num_q_heads] sink logits as in pa_forward_masked;
+ * row r belongs to query head r % num_q_heads (rows ordered [T, Hq]) and
+ * gets sinks[r % num_q_heads] folded in as one more zero-valued key.
  * num_splits in [1, 256], head_dim_v in [1, 1024].
  */
 PA_API pa_status pa_merge_lse(const float* part_out, const float* part_lse, int32_t num_rows,
                        int32_t num_splits, int32_t head_dim_v, void* out, float* lse,
-                       int32_t out_dtype, void* stream);
+                       int32_t out_dtype, const float* sinks, int32_t num_q_heads,
+                       void* stream);
 
 /*
  * Bytes of workspace mla_decode needs for these dims and num_splits

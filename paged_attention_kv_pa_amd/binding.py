@@ -66,7 +66,7 @@ def library():
             lib.pa_decode_split.restype = i32
             lib.pa_forward_chunked.argtypes = [p, p, p, p, p, p, f32, i32, i32, p, p, i32, p, dp, p]
             lib.pa_forward_chunked.restype = i32
-            lib.pa_merge_lse.argtypes = [p, p, i32, i32, i32, p, p, i32, p]
+            lib.pa_merge_lse.argtypes = [p, p, i32, i32, i32, p, p, i32, p, i32, p]
             lib.pa_merge_lse.restype = i32
             lib.mla_workspace_size.argtypes = [dp, i32]
             lib.mla_workspace_size.restype = sz
@@ -300,7 +300,8 @@ def pa_forward_chunked(q, k_cache, v_cache, block_table, seq_lens, query_start_l
     return part_out, part_lse
 
 
-def pa_merge_lse(part_out, part_lse, out=None, lse=None, out_dtype=torch.bfloat16, stream=None):
+def pa_merge_lse(part_out, part_lse, out=None, lse=None, out_dtype=torch.bfloat16, stream=None,
+                 sinks=None):
     """Log-sum-exp merge of partials over the split axis (see pa_merge_lse in include/pa.h).
 
     part_out [..., S, Dv] fp32, part_lse [..., S] fp32 -> out [..., Dv] in out_dtype.
@@ -319,8 +320,14 @@ def pa_merge_lse(part_out, part_lse, out=None, lse=None, out_dtype=torch.bfloat1
     code = _dtype_code(out)
     if lse is not None:
         _need(lse.dtype == torch.float32 and lse.is_contiguous() and tuple(lse.shape) == lead, "bad lse")
+    Hq = 0
+    if sinks is not None:
+        _need(part_lse.dim() >= 2, "sinks need partials shaped [..., Hq, S]")
+        Hq = int(part_lse.shape[-2])
+        _need(sinks.dtype == torch.float32 and sinks.is_contiguous() and tuple(sinks.shape) == (Hq,)
+              and sinks.device == part_out.device, "sinks must be contiguous float32 [Hq]")
     st = library().pa_merge_lse(_ptr(part_out), _ptr(part_lse), rows, S, Dv, _ptr(out), _ptr(lse),
-                                code, _stream(part_out.device, stream))
+                                code, _ptr(sinks), Hq, _stream(part_out.device, stream))
     _check(st, "pa_merge_lse")
     return out
 

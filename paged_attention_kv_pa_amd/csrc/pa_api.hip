@@ -495,14 +495,17 @@ pa_status pa_forward_chunked(const void* q, const void* k_cache, const void* v_c
 
 pa_status pa_merge_lse(const float* part_out, const float* part_lse, int32_t num_rows,
                        int32_t num_splits, int32_t head_dim_v, void* out, float* lse,
-                       int32_t out_dtype, void* stream) {
+                       int32_t out_dtype, const float* sinks, int32_t num_q_heads,
+                       void* stream) {
   if (!part_out || !part_lse || !out) return PA_ERR_INVALID_ARG;
+  if (sinks && num_q_heads < 1) return PA_ERR_INVALID_ARG;
   if (num_rows < 0 || num_splits < 1 || num_splits > pa::kMaxSplits || head_dim_v < 1 ||
       head_dim_v > 1024)
     return PA_ERR_INVALID_ARG;
   if (out_dtype != PA_F32 && out_dtype != PA_BF16) return PA_ERR_INVALID_ARG;
   hipError_t e = pa::launch_merge(part_out, part_lse, num_rows, num_splits, head_dim_v, out,
-                                  out_dtype == PA_BF16, lse, (hipStream_t)stream);
+                                  out_dtype == PA_BF16, lse, (hipStream_t)stream, sinks,
+                                  num_q_heads);
   return e == hipSuccess ? PA_OK : hip_fail(e);
 }
 

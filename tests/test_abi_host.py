@@ -163,14 +163,16 @@ def test_chunked_argument_checks():
 
 def test_merge_argument_checks():
     lib = pa.library()
-    m = lambda rows, S, Dv, dt: lib.pa_merge_lse(FAKE, FAKE, rows, S, Dv, FAKE, None, dt, None)
+    m = lambda rows, S, Dv, dt: lib.pa_merge_lse(FAKE, FAKE, rows, S, Dv, FAKE, None, dt, None, 0,
+                                                 None)
     assert m(-1, 4, 128, 1) == binding.PA_ERR_INVALID_ARG
     assert m(4, 0, 128, 1) == binding.PA_ERR_INVALID_ARG
     assert m(4, 300, 128, 1) == binding.PA_ERR_INVALID_ARG
     assert m(4, 4, 0, 1) == binding.PA_ERR_INVALID_ARG
     assert m(4, 4, 128, 5) == binding.PA_ERR_INVALID_ARG
     assert m(0, 4, 128, 1) == binding.PA_OK
-    assert lib.pa_merge_lse(None, FAKE, 4, 4, 128, FAKE, None, 1, None) == binding.PA_ERR_INVALID_ARG
+    assert lib.pa_merge_lse(None, FAKE, 4, 4, 128, FAKE, None, 1, None, 0, None) == binding.PA_ERR_INVALID_ARG
+    assert lib.pa_merge_lse(FAKE, FAKE, 4, 4, 128, FAKE, None, 1, FAKE, 0, None) == binding.PA_ERR_INVALID_ARG
 
 
 def test_mla_argument_checks():

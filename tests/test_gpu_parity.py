@@ -288,6 +288,21 @@ def test_sinks_forward_matches_oracle(mask, prefixes):
     masked_parity(b, mask, prefixes, "sinks bf16", sinks=sink_logits(32, 1))
 
 
+def test_sinks_in_split_decode_merge():
+    # pa_decode_split partials merged by pa_merge_lse with sink logits
+    b = workload.llama_decode(3, batch=8)
+    g = b.to(DEV)
+    sk = sink_logits(32, 11)
+    po, pl = pa.pa_decode_split(g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens, b.scale, 7)
+    lse = torch.empty(pl.shape[:2], dtype=torch.float32, device=DEV)
+    out = pa.pa_merge_lse(po, pl, lse=lse, sinks=torch.from_numpy(sk).to(DEV))
+    torch.cuda.synchronize()
+    ref, rlse = oracle.attention(b.q, b.k_cache, b.v_cache, b.block_table, b.seq_lens,
+                                 b.query_start_loc, b.scale, b.num_kv_heads, sinks=sk)
+    check_out(out.float().cpu().numpy(), ref, torch.bfloat16, "split merge with sinks")
+    check_lse(lse.cpu().numpy(), rlse, "split merge with sinks")
+
+
 def test_sinks_on_split_decode_rows():
     # few long decode requests: pa_forward splits their keys, and the sink enters
     # in the merge of the partial rows
