@@ -129,7 +129,7 @@ PA_API size_t pa_workspace_size(const pa_dims* dims);
  * persistent kernel itself.  One persistent kernel with a fixed grid runs the
  * items; decode rows whose key range was split are then merged by
  * log-sum-exp ([TDD] section "Parallel tiled softmax (3D kernel)").  A bf16
- * call whose prefill-mode items could not fill the GPU (judged from the dims:
+ * call whose prefill-mode items could not fill the GPU (decided from the dims:
  * at most 128 (request, KV head, 256-row block) items, max_seq_len >= 8192)
  * runs instead as the chunk partials of pa_forward_chunked plus their merge
  * ([ROC] bullet "Chunked context processing"); pa_workspace_size then
