@@ -42,13 +42,24 @@ __device__ __forceinline__ floatx16 mfma32_bf16(const bf16x8& a, const bf16x8& b
 // the whole wave.  Issued through inline assembly so that the compiler neither
 // waits for these copies at every barrier nor counts them: the caller waits
 // with wait_vmcnt<N>() and must not expect compiler-inserted waits for them.
-__device__ __forceinline__ void lds_dma16(const void* gsrc, const void* lds_wave_base) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)lds_wave_base);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(base), "v"(gsrc)
-               : "memory", "m0");
+//
+// The instruction takes its LDS address from m0, a register the compiler
+// reserves (a clobber of m0 is ignored).  So the statement saves m0 in a
+// scalar register of its own, writes the address, waits the one wait state an
+// SALU write of m0 needs before an LDS-DMA instruction reads it, issues the
+// copy and puts the saved value back: whatever the compiler keeps in m0
+// survives.
+__device__ __forceinline__ void lds_dma16_m0(const void* gsrc, uint32_t lds_wave_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_wave_base), "v"(gsrc)
+      : "memory");
 }
 
 // A pointer every lane holds the same value of, made visibly uniform (scalar
@@ -60,14 +71,6 @@ __device__ __forceinline__ T* uniform_ptr(T* p) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
   return (T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
-}
-
-// lds_dma16 with the wave's LDS byte address already in a scalar register.
-__device__ __forceinline__ void lds_dma16_m0(const void* gsrc, uint32_t lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(lds_wave_base), "v"(gsrc)
-               : "memory", "m0");
 }
 
 // s_waitcnt immediate for "no vector-memory operation in flight" (gfx9
@@ -183,13 +186,23 @@ struct ReqPlan {
 };
 
 // Control block at the start of the pa_forward workspace.
+//
+// The queue counters are zero when a call starts: the planner kernel zeroes
+// them, and the merge kernel that ends every call zeroes them again for the
+// next call and then writes kQueueReady into `ready`.  A decode-only call,
+// which runs no planner, claims items from the counter only when it finds
+// that marker (a workspace the library has not used yet holds anything);
+// without it every workgroup takes the fixed sequence of items w, w + grid,
+// w + 2 grid ... instead, which needs no counter.
+constexpr uint32_t kQueueReady = 0x51a9e7c3u;
 struct Control {
   int32_t n_pre;            // prefill-mode items; item indices [0, n_pre)
   int32_t n_items;          // all items; decode-mode items are [n_pre, n_items)
   int32_t n_merge;          // (request, KV head) pairs whose decode rows were split
-  int32_t work_counter;     // decode-mode items claimed from the queue (reset before each call)
-  int32_t xcd_counter[8];   // next entry of each prefill-mode item queue (reset before each call)
-  int32_t pad[52];
+  int32_t work_counter;     // decode-mode items claimed from the queue
+  int32_t xcd_counter[8];   // next entry of each prefill-mode item queue
+  uint32_t ready;           // kQueueReady: the counters above are zero
+  int32_t pad[51];
 };
 
 }  // namespace pa
