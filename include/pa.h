@@ -14,8 +14,13 @@
  *    frees or synchronises on these calls; work is enqueued on `stream`
  *    (a hipStream_t; NULL means the null stream) and the call returns at
  *    once.  Scratch memory comes from the caller as `workspace`, sized with
- *    the matching *_workspace_size() function (contents need no
- *    initialisation and are overwritten).
+ *    the matching *_workspace_size() function.  Its contents need no
+ *    initialisation.  pa_forward leaves a little state in the first 256
+ *    bytes of its workspace for the next call on it (queue counters left at
+ *    zero and a marker that says so; a workspace without the marker is run
+ *    without the counters); a caller that writes into a workspace between
+ *    calls, or reuses one after a PA_ERR_HIP, must zero those 256 bytes or
+ *    overwrite them as a whole.
  *  - Sizes, dtypes and capacities are checked on the host before anything is
  *    launched; a failed check returns an error code and launches nothing.
  *    A launch failure returns PA_ERR_HIP (pa_last_hip_error() gives the
@@ -178,8 +183,9 @@ PA_API pa_status pa_forward_masked(const void* q, const void* k_cache, const voi
  *   part_out[b, h, s, :]  float32 [B, Hq, S, Dv]  softmax-normalised within
  *                         the partition (zeros if empty)
  *   part_lse[b, h, s]     float32 [B, Hq, S]      its log-sum-exp (-inf if empty)
- * num_splits in [1, 256].  Same dtype / shape support as pa_forward.
- * Every seq_len must be >= 1.
+ * num_splits in [1, 256].  Same dtype / shape support as pa_forward; a bf16
+ * call also needs Hq / Hkv <= 256 (one partition runs as one work item of at
+ * most 256 rows), else PA_ERR_UNSUPPORTED.  Every seq_len must be >= 1.
  */
 PA_API pa_status pa_decode_split(const void* q, const void* k_cache, const void* v_cache,
                           const int32_t* block_table, const int32_t* seq_lens,

@@ -117,8 +117,16 @@ def _need(cond, msg):
 
 
 def make_dims(q, k_cache, v_cache, block_table, seq_lens, num_tokens, *, layout="mha",
-              head_dim_v=None, max_seq_len=None, max_q_len=None) -> PaDims:
-    """Fill a pa_dims from tensor shapes and host-side capacities."""
+              head_dim_v=None, max_seq_len=None, max_q_len=None, query_start_loc=None) -> PaDims:
+    """Fill a pa_dims from tensor shapes and host-side capacities.
+
+    max_seq_len defaults to the block-table capacity (max_pages * P).  max_q_len
+    defaults to the longest request of query_start_loc when that is given (one
+    small device-to-host copy of the B + 1 offsets, which waits for the stream),
+    else to num_tokens.  The default matters for speed: a batch whose requests
+    all decode (max_q_len * Hq / Hkv <= 16) runs the decode-only kernel, which
+    an over-estimated max_q_len would turn off.
+    """
     B = int(seq_lens.shape[0])
     Hq, Dqk = int(q.shape[1]), int(q.shape[2])
     if layout == "mla":
@@ -140,7 +148,13 @@ def make_dims(q, k_cache, v_cache, block_table, seq_lens, num_tokens, *, layout=
     d.num_pages = num_pages
     d.max_pages_per_seq = maxp
     d.max_seq_len = int(max_seq_len) if max_seq_len is not None else maxp * P
-    d.max_q_len = int(max_q_len) if max_q_len is not None else min(int(num_tokens), d.max_seq_len)
+    if max_q_len is not None:
+        d.max_q_len = int(max_q_len)
+    elif query_start_loc is not None and int(query_start_loc.shape[0]) > 1:
+        qs = query_start_loc.detach().to("cpu", torch.int64)
+        d.max_q_len = max(0, int((qs[1:] - qs[:-1]).max()))
+    else:
+        d.max_q_len = min(int(num_tokens), d.max_seq_len)
     d.dtype = _dtype_code(q)
     return d
 
@@ -206,7 +220,7 @@ def _forward(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale,
     _need(query_start_loc.shape[0] == seq_lens.shape[0] + 1, "query_start_loc must have B + 1 entries")
     T = int(q.shape[0])
     dims = make_dims(q, k_cache, v_cache, block_table, seq_lens, T, max_seq_len=max_seq_len,
-                     max_q_len=max_q_len)
+                     max_q_len=max_q_len, query_start_loc=query_start_loc)
     if out is None:
         out = torch.empty(T, dims.num_q_heads, dims.head_dim_v, dtype=q.dtype, device=q.device)
     _need(out.is_contiguous() and out.dtype == q.dtype and out.shape == (T, dims.num_q_heads, dims.head_dim_v),
@@ -279,7 +293,7 @@ def pa_forward_chunked(q, k_cache, v_cache, block_table, seq_lens, query_start_l
     _need(query_start_loc.shape[0] == seq_lens.shape[0] + 1, "query_start_loc must have B + 1 entries")
     T = int(q.shape[0])
     dims = make_dims(q, k_cache, v_cache, block_table, seq_lens, T, max_seq_len=max_seq_len,
-                     max_q_len=max_q_len)
+                     max_q_len=max_q_len, query_start_loc=query_start_loc)
     C = int(chunk_keys)
     S = (dims.max_seq_len + C - 1) // C if num_chunks is None else int(num_chunks)
     S = max(S, 1)

@@ -299,7 +299,8 @@ pa_status pa_forward_masked(const void* q, const void* k_cache, const void* v_ca
     if (e == hipSuccess) e = mark(g_ev_stop, s);
     if (e == hipSuccess)
       e = pa::launch_merge(a.part_o, a.part_lse, d->num_tokens * d->num_q_heads, route.S,
-                           d->head_dim_v, out, true, lse, s, sinks, d->num_q_heads);
+                           d->head_dim_v, out, true, lse, s, sinks, d->num_q_heads,
+                           query_start_loc + d->num_seqs);
     return e == hipSuccess ? PA_OK : hip_fail(e);
   }
   if (!workspace || workspace_bytes < w.total) return PA_ERR_WORKSPACE;
@@ -331,7 +332,7 @@ pa_status pa_forward_masked(const void* q, const void* k_cache, const void* v_ca
   pl.max_pages = d->max_pages_per_seq;
   pl.target_items = std::max(1, pa::kItemsPerWorkgroup * grid);
   // decode-only calls of up to kFusedPlanMax requests: the persistent kernel
-  // plans itself and only a counter reset precedes it
+  // plans itself, so the call is two launches (attention kernel, merge)
   const bool fused = decode_only && d->num_seqs <= pa::kFusedPlanMax;
   hipError_t e = hipSuccess;
   if (!fused && (e = pa::launch_plan(pl, s)) != hipSuccess) return hip_fail(e);
@@ -364,13 +365,16 @@ pa_status pa_forward_masked(const void* q, const void* k_cache, const void* v_ca
   a.mask = mask;
   a.prefix_lens = prefix_lens;
   a.sinks = sinks;
-  if (fused && (e = pa::launch_reset_queue(ctrl, s)) != hipSuccess) return hip_fail(e);
   if ((e = mark(g_ev_start, s)) != hipSuccess) return hip_fail(e);
   e = fused ? pa::launch_mha_forward_fused(a, D, grid, s)
             : pa::launch_mha_forward(a, D, decode_only, grid, s);
   if (e != hipSuccess) return hip_fail(e);
   if ((e = mark(g_ev_stop, s)) != hipSuccess) return hip_fail(e);
-  e = pa::launch_mha_forward_merge(a, D, std::max(1, cfg.cu_count * 2), s);
+  // the merge also leaves the queue counters zeroed for the next call; one
+  // wave per (request, KV head) pair with split rows, at most B * Hkv of them
+  const int64_t pairs = (int64_t)d->num_seqs * d->num_kv_heads;
+  e = pa::launch_mha_forward_merge(
+      a, D, (int)std::max<int64_t>(1, std::min<int64_t>(cfg.cu_count * 2, (pairs + 3) / 4)), s);
   if (e != hipSuccess) return hip_fail(e);
   return PA_OK;
 }
@@ -387,10 +391,12 @@ pa_status pa_decode_split(const void* q, const void* k_cache, const void* v_cach
   if (d->num_tokens != d->num_seqs) return PA_ERR_INVALID_ARG;
   st = check_mha_support(d);
   if (st != PA_OK) return st;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  // a bf16 partition runs one work item, which holds at most kPrefillRows rows
+  if (d->dtype == PA_BF16 && G > pa::kPrefillRows) return PA_ERR_UNSUPPORTED;
   if (d->num_seqs == 0) return PA_OK;
   if ((int64_t)d->num_seqs * d->num_q_heads * num_splits > INT32_MAX) return PA_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
-  const int G = d->num_q_heads / d->num_kv_heads;
   hipError_t e = mark(g_ev_start, s);
   if (e != hipSuccess) return hip_fail(e);
   if (d->dtype == PA_F32) {

@@ -143,14 +143,16 @@ FwdWorkspace fwd_workspace_layout(int B, int T, int Hkv, int G, int D);
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_mha_forward(const MhaArgs& a, int D, bool decode_only, int grid, hipStream_t s);
 hipError_t launch_mha_forward_fused(const MhaArgs& a, int D, int grid, hipStream_t s);
-hipError_t launch_reset_queue(Control* ctrl, hipStream_t s);
 hipError_t launch_mha_forward_merge(const MhaArgs& a, int D, int grid, hipStream_t s);
 hipError_t launch_mha_split(const MhaArgs& a, int D, hipStream_t s);
 hipError_t launch_mha_chunked(const MhaArgs& a, int D, hipStream_t s);
 hipError_t mha_occupancy(int D, bool decode_only, int* blocks_per_cu);
+// Rows are ordered [token, head] with Hq heads per token; tok_end (a device
+// int, may be NULL) stops the merge at token *tok_end: later rows are left
+// untouched.
 hipError_t launch_merge(const float* po, const float* pl, int rows, int S, int Dv, void* out,
                         bool out_bf16, float* lse, hipStream_t s, const float* sinks = nullptr,
-                        int Hq = 1);
+                        int Hq = 1, const int32_t* tok_end = nullptr);
 hipError_t launch_f32_forward(const F32Args& a, hipStream_t s);
 hipError_t launch_f32_split(const F32Args& a, hipStream_t s);
 hipError_t launch_mla_split(const MlaArgs& a, hipStream_t s);

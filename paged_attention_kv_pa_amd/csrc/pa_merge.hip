@@ -23,11 +23,14 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
                                                               int rows, int S, int Dv, void* out,
                                                               int out_bf16, float* lse,
                                                               const float* __restrict__ sinks,
-                                                              int Hq) {
+                                                              int Hq,
+                                                              const int32_t* __restrict__ tok_end) {
   __shared__ float wts[kMergeThreads / 64][kMaxSplits];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t row = (int64_t)blockIdx.x * (kMergeThreads / 64) + wv;
-  const bool valid = row < rows;  // every wave reaches the barrier below
+  // rows of tokens at or past *tok_end (when given) are left untouched
+  const bool valid = row < rows && (!tok_end || row < (int64_t)tok_end[0] * Hq);
+  // (every wave reaches the barrier below)
   const float* ls = pl + (valid ? row : 0) * S;
   float M = kNegInf;
   if (valid)
@@ -64,11 +67,12 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
 }  // namespace
 
 hipError_t launch_merge(const float* po, const float* pl, int rows, int S, int Dv, void* out,
-                        bool out_bf16, float* lse, hipStream_t s, const float* sinks, int Hq) {
+                        bool out_bf16, float* lse, hipStream_t s, const float* sinks, int Hq,
+                        const int32_t* tok_end) {
   if (rows <= 0) return hipSuccess;
   const int blocks = (rows + kMergeThreads / 64 - 1) / (kMergeThreads / 64);
   hipLaunchKernelGGL(merge_kernel, dim3(blocks), dim3(kMergeThreads), 0, s, po, pl, rows, S, Dv,
-                     out, out_bf16 ? 1 : 0, lse, sinks, Hq > 0 ? Hq : 1);
+                     out, out_bf16 ? 1 : 0, lse, sinks, Hq > 0 ? Hq : 1, tok_end);
   return hipGetLastError();
 }
 

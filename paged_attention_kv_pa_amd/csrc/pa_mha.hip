@@ -995,7 +995,12 @@ void mha_forward_kernel(MhaArgs a) {
   // A decode-only grid starts workgroup w on decode-mode item w, so the queue
   // hands out the items after the first gridDim.x.
   const int dec_base = DECODE_ONLY ? (int)gridDim.x : 0;
-  int32_t* const counter = &a.ctrl->work_counter;
+  // The planner zeroes the counter; a call that plans itself finds it zeroed
+  // by the previous call's merge kernel, or else takes a fixed item sequence
+  // (see Control).  `ready` is not written while this kernel runs, so every
+  // workgroup reads the same value.
+  const bool queue = !FUSED || __builtin_amdgcn_readfirstlane(a.ctrl->ready) == kQueueReady;
+  int32_t* const counter = queue ? &a.ctrl->work_counter : nullptr;
   int idx;
   WorkItem it;
   const int home = blockIdx.x & 7;
@@ -1076,11 +1081,13 @@ void mha_forward_kernel(MhaArgs a) {
     for (; idx < n_pre && idx < n_items; next()) run_prefill_item<D>(a, it, dest(), sm.pre);
   }
   // decode-mode items: each one claims its successor while its epilogue runs
+  // (without the queue: the item gridDim.x further on)
   while (idx < n_items) {
     int j;
     if constexpr (DECODE_ONLY) j = run_decode_item<D, 4>(a, it, dest(), sm, counter);
     else j = run_decode_item_outlined<D>(a, it, dest(), sm.dec, counter);
-    if (threadIdx.x < 64) fetch_decode(__shfl(j, 0) + dec_base);
+    if (threadIdx.x < 64)
+      fetch_decode(queue ? __shfl(j, 0) + dec_base : idx - n_pre + (int)gridDim.x);
     publish();
   }
 }
@@ -1324,6 +1331,13 @@ __global__ __launch_bounds__(kThreads) void mha_forward_merge_kernel(MhaArgs a) 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int rsub = lane >> 4, c0 = (lane & 15) * NC;
   const int n_merge = a.ctrl->n_merge;
+  // The attention kernel of this call is done with the queue counters: zero
+  // them for the next call and mark them so (see Control).
+  if (blockIdx.x == 0 && threadIdx.x < 64) {
+    if (threadIdx.x == 0) a.ctrl->work_counter = 0;
+    if (threadIdx.x < 8) a.ctrl->xcd_counter[threadIdx.x] = 0;
+    if (threadIdx.x == 0) a.ctrl->ready = kQueueReady;  // seen with the zeros by the next kernel
+  }
   const int stride = gridDim.x * (kThreads / 64);
   for (int e = blockIdx.x * (kThreads / 64) + wv; e < n_merge; e += stride) {
     const int4 me = reinterpret_cast<const int4*>(a.merges)[e];
@@ -1372,13 +1386,6 @@ __global__ __launch_bounds__(kThreads) void mha_forward_merge_kernel(MhaArgs a) 
   }
 }
 
-// Queue counters of a pa_forward call whose persistent kernel plans itself
-// (a fill kernel rather than a memset, so a captured call replays it).
-__global__ __launch_bounds__(64) void reset_queue_kernel(Control* c) {
-  if (threadIdx.x == 0) c->work_counter = 0;
-  if (threadIdx.x < 8) c->xcd_counter[threadIdx.x] = 0;
-}
-
 }  // namespace
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
@@ -1402,11 +1409,6 @@ hipError_t launch_mha_forward(const MhaArgs& a, int D, bool decode_only, int gri
     if (decode_only) hipLaunchKernelGGL((mha_forward_kernel<64, true>), dim3(grid), dim3(kThreads), 0, s, a);
     else hipLaunchKernelGGL((mha_forward_kernel<64, false>), dim3(grid), dim3(kPrefillThreads), 0, s, a);
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_reset_queue(Control* ctrl, hipStream_t s) {
-  hipLaunchKernelGGL(reset_queue_kernel, dim3(1), dim3(64), 0, s, ctrl);
   return hipGetLastError();
 }
 

@@ -118,6 +118,28 @@ def test_decode_split_argument_checks():
     assert call(4, _dims(num_tokens=5)) == binding.PA_ERR_INVALID_ARG  # T != B
     assert call(4, _dims(head_dim_qk=80, head_dim_v=80)) == binding.PA_ERR_UNSUPPORTED
     assert call(4, _dims(num_seqs=0, num_tokens=0)) == binding.PA_OK
+    # a bf16 partition is one work item of at most 256 rows: wider groups are refused
+    assert call(4, _dims(num_q_heads=512, num_kv_heads=1)) == binding.PA_ERR_UNSUPPORTED
+    assert call(4, _dims(num_q_heads=512, num_kv_heads=1, num_seqs=0, num_tokens=0)) == \
+        binding.PA_ERR_UNSUPPORTED
+
+
+def test_make_dims_takes_max_q_len_from_query_start_loc():
+    # without max_q_len the binding reads the longest request off query_start_loc, so
+    # a decode batch keeps the decode-only kernel (max_q_len * Hq / Hkv <= 16)
+    b = workload.make_batch([1] * 6, [3000] * 6, num_q_heads=32, num_kv_heads=8, head_dim_qk=128,
+                            page_size=16, seed=5, poison=False)
+    d = binding.make_dims(b.q, b.k_cache, b.v_cache, b.block_table, b.seq_lens, b.num_tokens,
+                          query_start_loc=b.query_start_loc)
+    assert d.max_q_len == 1
+    m = workload.make_batch([1, 7, 0, 3], [20, 5, 9, 0], num_q_heads=8, num_kv_heads=2,
+                            head_dim_qk=64, page_size=16, seed=6, poison=False)
+    d = binding.make_dims(m.q, m.k_cache, m.v_cache, m.block_table, m.seq_lens, m.num_tokens,
+                          query_start_loc=m.query_start_loc)
+    assert d.max_q_len == 7
+    d = binding.make_dims(m.q, m.k_cache, m.v_cache, m.block_table, m.seq_lens, m.num_tokens,
+                          max_q_len=9, query_start_loc=m.query_start_loc)
+    assert d.max_q_len == 9
 
 
 def test_masked_forward_argument_checks():
