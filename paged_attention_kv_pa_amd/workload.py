@@ -195,6 +195,27 @@ def sub_batch(b: Batch, requests: Sequence[int]) -> Batch:
         name=b.name + "[%d:%d]" % (r[0], r[-1] + 1))
 
 
+def permute_requests(b: Batch, order: Sequence[int]) -> Batch:
+    """The requests of `b` in the given order (same cache pool): request i of the
+    result is request order[i] of `b`, with its query rows, block-table row and
+    lengths.  Returns the batch and, as a LongTensor, the row of `b` each result
+    token comes from."""
+    order = [int(i) for i in order]
+    assert sorted(order) == list(range(b.num_seqs)), "order must be a permutation"
+    qsl = [int(x) for x in b.query_start_loc.cpu()]
+    src = torch.tensor([t for i in order for t in range(qsl[i], qsl[i + 1])], dtype=torch.int64)
+    q_lens = [b.q_lens[i] for i in order]
+    new_qsl = torch.zeros(b.num_seqs + 1, dtype=torch.int32)
+    new_qsl[1:] = torch.cumsum(torch.tensor(q_lens, dtype=torch.int64), 0).to(torch.int32)
+    idx = torch.tensor(order, dtype=torch.int64, device=b.block_table.device)
+    pb = dataclasses.replace(
+        b, q=b.q[src.to(b.q.device)].contiguous(), block_table=b.block_table[idx].contiguous(),
+        seq_lens=b.seq_lens[idx.to(b.seq_lens.device)].contiguous(),
+        query_start_loc=new_qsl.to(b.query_start_loc.device), q_lens=q_lens,
+        ctx_lens=[b.ctx_lens[i] for i in order], name=b.name + "[permuted]")
+    return pb, src
+
+
 def _randint(gen, lo, hi, n):
     """n integers uniform in [lo, hi] (inclusive)."""
     return [int(x) for x in torch.randint(int(lo), int(hi) + 1, (n,), generator=gen)]

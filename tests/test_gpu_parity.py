@@ -61,10 +61,11 @@ def oracle_forward(b, rows=None):
                             head_dim_v=b.head_dim_v, layout=lay, rows=rows)
 
 
-def forward_parity(b, what, rows=None):
+def forward_parity(b, what, rows=None, ref=None):
+    """pa_forward against the oracle (ref: a precomputed oracle (out, lse) of b)."""
     say("case %s: B=%d T=%d keys=%d" % (what, b.num_seqs, b.num_tokens, sum(b.seq_lens_list)))
     got, glse = run_forward(b)
-    ref, rlse = oracle_forward(b, rows)
+    ref, rlse = oracle_forward(b, rows) if ref is None else ref
     if rows is not None:
         sel = np.asarray(rows, dtype=bool)
         got, ref, glse, rlse = got[sel], ref[sel], glse[sel], rlse[sel]
@@ -324,9 +325,11 @@ def test_full_mask_qwen3_scaled():
 
 # ------------------------------------------- chunked-context processing
 
-def chunked_parity(b, C, what, S=None, rows=None, mask=pa.PA_MASK_CAUSAL, prefixes=None):
+def chunked_parity(b, C, what, S=None, rows=None, mask=pa.PA_MASK_CAUSAL, prefixes=None,
+                   ref=None, partials=True):
     """pa_forward_chunked partials against the oracle's chunk partials, and their
-    pa_merge_lse against plain attention (rows: optional sample of output rows)."""
+    pa_merge_lse against plain attention (rows: optional sample of output rows;
+    ref: a precomputed oracle (out, lse); partials=False skips the partials)."""
     g = b.to(DEV)
     pfx = None if prefixes is None else np.asarray(prefixes, np.int32)
     dpfx = None if prefixes is None else torch.tensor(prefixes, dtype=torch.int32, device=DEV)
@@ -342,15 +345,18 @@ def chunked_parity(b, C, what, S=None, rows=None, mask=pa.PA_MASK_CAUSAL, prefix
     torch.cuda.synchronize()
     po, pl = po.cpu().numpy(), pl.cpu().numpy()
     got, glse = out.float().cpu().numpy(), lse.cpu().numpy()
-    if rows is None:
+    if rows is None and partials:
         rpo, rpl = oracle.chunked_partials(b.q, b.k_cache, b.v_cache, b.block_table, b.seq_lens,
                                            b.query_start_loc, b.scale, C, S, b.num_kv_heads,
                                            mask=mask, prefix_lens=pfx)
         check_out(po, rpo, torch.bfloat16, "%s partials" % what)
         check_lse(pl, rpl, "%s partial lse" % what)
-    ref, rlse = oracle.attention(b.q, b.k_cache, b.v_cache, b.block_table, b.seq_lens,
-                                 b.query_start_loc, b.scale, b.num_kv_heads, rows=rows,
-                                 mask=mask, prefix_lens=pfx)
+    if ref is None:
+        ref, rlse = oracle.attention(b.q, b.k_cache, b.v_cache, b.block_table, b.seq_lens,
+                                     b.query_start_loc, b.scale, b.num_kv_heads, rows=rows,
+                                     mask=mask, prefix_lens=pfx)
+    else:
+        ref, rlse = ref
     if rows is not None:
         sel = np.asarray(rows, dtype=bool)
         got, ref, glse, rlse = got[sel], ref[sel], glse[sel], rlse[sel]
@@ -415,19 +421,67 @@ def test_forward_chunked_route_masks_and_sinks(mask, prefixes, with_sinks):
                   sinks=sink_logits(32, 9) if with_sinks else None)
 
 
-def test_forward_long_extend_full_size_sampled_rows():
-    b = workload.llama_long_extend(0)
-    rows = np.zeros((b.num_tokens, b.num_q_heads), dtype=bool)
-    rows[[0, 100, 255], :] = True
-    forward_parity(b, "pa_forward long extend full size (sampled rows)", rows=rows)
+_LONG_EXTEND = {}
 
 
-def test_chunked_long_extend_full_size_sampled_rows():
-    # the bench's chunked-extend workload: 256 new tokens on 131072 cached tokens
-    b = workload.llama_long_extend(0)
-    rows = np.zeros((b.num_tokens, b.num_q_heads), dtype=bool)
-    rows[[0, 100, 255], :] = True
-    chunked_parity(b, 8192, "chunked long extend full size (sampled rows)", rows=rows)
+def long_extend_case():
+    """The bench's chunked-extend workload (256 new tokens on 131072 cached tokens,
+    Llama-3.1-8B heads) and its oracle result over every row, computed once."""
+    if not _LONG_EXTEND:
+        b = workload.llama_long_extend(0)
+        say("oracle: long extend, all %d rows x %d heads" % (b.num_tokens, b.num_q_heads))
+        _LONG_EXTEND["b"] = b
+        _LONG_EXTEND["ref"] = oracle_forward(b)
+    return _LONG_EXTEND["b"], _LONG_EXTEND["ref"]
+
+
+def test_forward_long_extend_full_size_all_rows():
+    b, ref = long_extend_case()
+    forward_parity(b, "pa_forward long extend full size (all rows)", ref=ref)
+
+
+def test_chunked_long_extend_full_size_all_rows():
+    # partials are compared at smaller sizes (test_chunked_long_context_extend)
+    b, ref = long_extend_case()
+    chunked_parity(b, 8192, "chunked long extend full size (all rows)", ref=ref, partials=False)
+
+
+def padded_call(b, route_expected):
+    """pa_forward with 7 padding rows past query_start_loc[B] in q, out and lse: the
+    padding rows of out / lse must keep their sentinel bytes."""
+    g = b.to(DEV)
+    T, Hq, D = b.num_tokens, b.num_q_heads, b.head_dim_v
+    qp = torch.cat([g.q, torch.full((7, Hq, b.head_dim_qk), float("nan"), dtype=b.dtype,
+                                    device=DEV)]).contiguous()
+    out = torch.full((T + 7, Hq, D), 3.0, dtype=b.dtype, device=DEV)
+    lse = torch.full((T + 7, Hq), -7.0, dtype=torch.float32, device=DEV)
+    maxL, maxq = max(b.seq_lens_list), max(b.q_lens)
+    dims = pa.make_dims(qp, g.k_cache, g.v_cache, g.block_table, g.seq_lens, T + 7,
+                        max_seq_len=maxL, max_q_len=maxq)
+    # the chunked route adds its partials to the workspace of the same dims
+    decode_dims = pa.make_dims(qp, g.k_cache, g.v_cache, g.block_table, g.seq_lens, T + 7,
+                               max_seq_len=maxL, max_q_len=1)
+    assert (pa.pa_workspace_size(dims) > pa.pa_workspace_size(decode_dims)) == route_expected
+    pa.pa_forward(qp, g.k_cache, g.v_cache, g.block_table, g.seq_lens, g.query_start_loc,
+                  b.scale, out=out, lse=lse, max_seq_len=maxL, max_q_len=maxq)
+    torch.cuda.synchronize()
+    assert torch.all(out[T:].float() == 3.0), "padding rows of out were written"
+    assert torch.all(lse[T:] == -7.0), "padding rows of lse were written"
+    ref, rlse = oracle_forward(b)
+    check_out(out[:T].float().cpu().numpy(), ref, b.dtype, "padded call (route %s)" % route_expected)
+    check_lse(lse[:T].cpu().numpy(), rlse, "padded call (route %s)" % route_expected)
+
+
+def test_padding_rows_untouched_on_the_chunked_route():
+    b = workload.make_batch([200, 1, 64], [20000, 30000, 9000], num_q_heads=32, num_kv_heads=8,
+                            head_dim_qk=128, page_size=16, seed=97)
+    padded_call(b, True)
+
+
+def test_padding_rows_untouched_on_the_persistent_path():
+    b = workload.make_batch([1, 37, 130, 1], [300, 0, 90, 2000], num_q_heads=32, num_kv_heads=8,
+                            head_dim_qk=128, page_size=16, seed=98)
+    padded_call(b, False)
 
 
 # --------------------------------------------------- Qwen3 mixed batch (MHA)
@@ -495,9 +549,9 @@ def test_mla_balanced_pages_and_heads(page, heads):
     mla_parity(b, "mla balanced page %d heads %d" % (page, heads), S=0)
 
 
-def test_mla_full_size_sampled_heads():
+def test_mla_full_size_all_heads():
     b = workload.deepseek_mla(0)
-    mla_parity(b, "mla full (heads 0,1,37,64,127)", heads=[0, 1, 37, 64, 127])
+    mla_parity(b, "mla full size, all 128 heads")
 
 
 # --------------------------------------------------------------- edge cases
@@ -539,6 +593,74 @@ def test_head_and_page_shapes(Hq, Hkv, D, P):
     b = workload.make_batch([1, 5, 40, 1, 130], [700, 100, 0, 3, 60], num_q_heads=Hq,
                             num_kv_heads=Hkv, head_dim_qk=D, page_size=P, seed=Hq * 7 + P)
     forward_parity(b, "shapes Hq=%d Hkv=%d D=%d P=%d" % (Hq, Hkv, D, P))
+
+
+def test_request_order_permutation_bitwise():
+    # [decode : extend : prefill] reordered: every request's rows move with it and
+    # come out bit for bit the same (the decode items' key partitions of this batch
+    # do not depend on a request's place in it)
+    b = workload.make_batch([1, 1, 1, 300, 37, 1, 520, 2], [900, 50, 2500, 700, 0, 4000, 0, 30],
+                            num_q_heads=32, num_kv_heads=8, head_dim_qk=128, page_size=16,
+                            seed=1201)
+    order = [6, 3, 0, 7, 5, 1, 4, 2]
+    pb, src = workload.permute_requests(b, order)
+    say("case request order %s" % order)
+    got, glse = run_forward(b)
+    pgot, plse = run_forward(pb)
+    # (bf16 outputs widened exactly to fp32: equal floats are equal bit patterns)
+    assert np.array_equal(pgot, got[src.numpy()]), "permuted outputs differ"
+    assert np.array_equal(plse, glse[src.numpy()])
+    ref, rlse = oracle_forward(pb)
+    check_out(pgot, ref, b.dtype, "permuted batch")
+    check_lse(plse, rlse, "permuted batch")
+
+
+def test_request_order_permutation_large_batch():
+    # a decode batch large enough that the last requests get finer key partitions:
+    # reversing it changes the partitions, so outputs permute within tolerance
+    b = workload.llama_decode(3, batch=48)
+    order = list(range(47, -1, -1))
+    pb, src = workload.permute_requests(b, order)
+    got, glse = run_forward(b)
+    pgot, plse = run_forward(pb)
+    ref, rlse = oracle_forward(pb)
+    check_out(pgot, ref, b.dtype, "reversed decode batch")
+    check_lse(plse, rlse, "reversed decode batch")
+    mx = float(np.max(np.abs(pgot - got[src.numpy()])))
+    say("reversed decode batch: max |permuted - original| = %.3e" % mx)
+    assert mx <= 2 * BF16_MAX
+
+
+@pytest.mark.parametrize("fill", [0x00, 0xAB])
+def test_decode_workspace_state_between_calls(fill):
+    # A decode-only call plans itself and takes its items from a queue counter
+    # that the previous call's merge left at zero, next to a marker.  A fresh
+    # workspace (any bytes) has no marker: that call takes a fixed item sequence.
+    # Both kinds of call, and a call after a prefill call on the same workspace,
+    # give the same bits.
+    b = workload.llama_decode(3, batch=40)
+    g = b.to(DEV)
+    kw = dict(max_seq_len=max(b.seq_lens_list), max_q_len=1)
+    dims = pa.make_dims(g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens, b.num_tokens, **kw)
+    ws = torch.full((pa.pa_workspace_size(dims),), fill, dtype=torch.uint8, device=DEV)
+    outs = []
+    for _ in range(3):
+        outs.append(pa.pa_forward(g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens,
+                                  g.query_start_loc, b.scale, workspace=ws, **kw))
+    m = workload.make_batch([1, 37, 130], [300, 0, 90], num_q_heads=32, num_kv_heads=8,
+                            head_dim_qk=128, page_size=16, seed=5).to(DEV)
+    mws = ws[:pa.pa_workspace_size(pa.make_dims(m.q, m.k_cache, m.v_cache, m.block_table,
+                                                m.seq_lens, m.num_tokens, max_seq_len=220,
+                                                max_q_len=130))]
+    pa.pa_forward(m.q, m.k_cache, m.v_cache, m.block_table, m.seq_lens, m.query_start_loc,
+                  m.scale, workspace=mws, max_seq_len=220, max_q_len=130)
+    outs.append(pa.pa_forward(g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens,
+                              g.query_start_loc, b.scale, workspace=ws, **kw))
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+    ref, _ = oracle_forward(b)
+    check_out(outs[0].float().cpu().numpy(), ref, b.dtype, "decode, workspace filled 0x%02x" % fill)
 
 
 def test_page_permutation_invariance_bitwise():
