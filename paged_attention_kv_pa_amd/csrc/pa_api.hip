@@ -36,6 +36,7 @@ struct DevCfg {
 std::mutex g_mu;
 std::map<int, DevCfg> g_cfg;
 
+
 pa_status device_config(DevCfg* out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -153,6 +154,23 @@ ChunkRoute chunk_route(const pa_dims* d) {
   return r;
 }
 
+// Persistent grid of a bf16 pa_forward call and the number of decode items its
+// planner aims at (the workspace is sized from the same numbers).
+struct FwdGeom {
+  bool decode_only = false;
+  int grid = 0, target = 0;
+};
+pa_status fwd_geometry(const pa_dims* d, FwdGeom* g) {
+  DevCfg cfg;
+  const pa_status st = device_config(&cfg);
+  if (st != PA_OK) return st;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  g->decode_only = (int64_t)d->max_q_len * G <= pa::kDecodeRows;
+  g->grid = cfg.cu_count * cfg.occ[d->head_dim_qk == 128][g->decode_only ? 1 : 0];
+  g->target = std::max(1, pa::kItemsPerWorkgroup * g->grid);
+  return PA_OK;
+}
+
 pa_status check_mla(const pa_dims* d) {
   pa_status st = check_dims(d);
   if (st != PA_OK) return st;
@@ -194,10 +212,12 @@ pa_status pa_set_kernel_events(void* start, void* stop) {
 size_t pa_workspace_size(const pa_dims* d) {
   if (check_dims(d) != PA_OK) return 0;
   if (d->dtype == PA_F32) return 256;
-  const int G = d->num_q_heads / d->num_kv_heads;
+  // the decode-item bound needs the current device's grid; without a device
+  // the bound of kMaxFwdSplits partitions per (request, KV head) is used
+  FwdGeom geo;
+  const int target = fwd_geometry(d, &geo) == PA_OK ? geo.target : INT32_MAX / 4;
   const ChunkRoute r = chunk_route(d);
-  return pa::fwd_workspace_layout(d->num_seqs, d->num_tokens, d->num_kv_heads, G, d->head_dim_v)
-             .total +
+  return pa::fwd_workspace_layout(d->num_seqs, d->num_kv_heads, d->head_dim_v, target).total +
          r.po_bytes + r.pl_bytes;
 }
 
@@ -264,8 +284,13 @@ pa_status pa_forward_masked(const void* q, const void* k_cache, const void* v_ca
   }
 
   const int D = d->head_dim_qk;
-  const pa::FwdWorkspace w = pa::fwd_workspace_layout(d->num_seqs, d->num_tokens,
-                                                      d->num_kv_heads, G, D);
+  // (without a device the workspace is checked against the device-free bound
+  // pa_workspace_size gives, and the device error is reported after the
+  // host checks)
+  FwdGeom geo;
+  const pa_status geo_st = fwd_geometry(d, &geo);
+  const pa::FwdWorkspace w = pa::fwd_workspace_layout(
+      d->num_seqs, d->num_kv_heads, d->head_dim_v, geo_st == PA_OK ? geo.target : INT32_MAX / 4);
   const ChunkRoute route = chunk_route(d);
   if (route.on) {
     // few long requests: chunk partials and their merge instead of the
@@ -304,11 +329,12 @@ pa_status pa_forward_masked(const void* q, const void* k_cache, const void* v_ca
     return e == hipSuccess ? PA_OK : hip_fail(e);
   }
   if (!workspace || workspace_bytes < w.total) return PA_ERR_WORKSPACE;
+  if (geo_st != PA_OK) return geo_st;
   DevCfg cfg;
   st = device_config(&cfg);
   if (st != PA_OK) return st;
-  const bool decode_only = (int64_t)d->max_q_len * G <= pa::kDecodeRows;
-  const int grid = cfg.cu_count * cfg.occ[D == 128][decode_only ? 1 : 0];
+  const bool decode_only = geo.decode_only;
+  const int grid = geo.grid;
 
   char* ws = (char*)workspace;
   pa::Control* ctrl = (pa::Control*)(ws + w.ctrl_off);
@@ -330,7 +356,7 @@ pa_status pa_forward_masked(const void* q, const void* k_cache, const void* v_ca
   pl.G = G;
   pl.P = d->page_size;
   pl.max_pages = d->max_pages_per_seq;
-  pl.target_items = std::max(1, pa::kItemsPerWorkgroup * grid);
+  pl.target_items = geo.target;
   // decode-only calls of up to kFusedPlanMax requests: the persistent kernel
   // plans itself, so the call is two launches (attention kernel, merge)
   const bool fused = decode_only && d->num_seqs <= pa::kFusedPlanMax;

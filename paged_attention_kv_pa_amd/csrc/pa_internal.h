@@ -138,7 +138,9 @@ struct FwdWorkspace {
   size_t ctrl_off, req_off, pre_off, items_off, merges_off, plse_off, po_off, total;
   int64_t cap_slots;
 };
-FwdWorkspace fwd_workspace_layout(int B, int T, int Hkv, int G, int D);
+// target_items: the decode work of a call is cut into about this many items
+// (kItemsPerWorkgroup x the persistent grid).
+FwdWorkspace fwd_workspace_layout(int B, int Hkv, int D, int target_items);
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_mha_forward(const MhaArgs& a, int D, bool decode_only, int grid, hipStream_t s);

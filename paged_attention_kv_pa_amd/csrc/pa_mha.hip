@@ -27,6 +27,7 @@
 //     O[r][16 dt + 4g + i].
 // Softmax runs in base 2 on fp32 scores (scale * log2 e folded into one FMA);
 // the probabilities are rounded to bf16 for the value product.
+#include <algorithm>
 #include <type_traits>
 
 #include "pa_device.h"
@@ -1448,12 +1449,15 @@ hipError_t launch_mha_chunked(const MhaArgs& a, int D, hipStream_t s) {
   return hipGetLastError();
 }
 
-FwdWorkspace fwd_workspace_layout(int B, int T, int Hkv, int G, int D) {
-  (void)T;
-  (void)G;
+FwdWorkspace fwd_workspace_layout(int B, int Hkv, int D, int target_items) {
   FwdWorkspace w;
   auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  w.cap_slots = (int64_t)Hkv * B * kMaxFwdSplits;
+  // Decode-mode items (and so partial slots) of one call: a (request, KV head)
+  // pair of L keys gets at most ceil(L / ck) <= L / ck + 1 partitions, with
+  // ck >= chunk / 2 (the tail rule) and chunk >= the call's decode keys x Hkv
+  // / target_items; summed over the pairs, at most 2 target_items + B Hkv.
+  w.cap_slots = std::min<int64_t>((int64_t)Hkv * B * kMaxFwdSplits,
+                                  2 * (int64_t)target_items + (int64_t)Hkv * B);
   size_t off = 0;
   w.ctrl_off = off;
   off = align(off + sizeof(Control));
