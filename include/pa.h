@@ -174,6 +174,28 @@ PA_API pa_status pa_forward_masked(const void* q, const void* k_cache, const voi
                                    size_t workspace_bytes, void* stream);
 
 /*
+ * pa_forward_noalloc — pa_forward for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same arguments, results and
+ * kernels as pa_forward, but the workspace is a device array inside the
+ * library of pa_noalloc_max_workspace() bytes (64 MiB), one copy per GPU, held
+ * until the process ends; the call itself allocates and frees nothing.
+ * Returns PA_ERR_WORKSPACE when pa_workspace_size(dims) exceeds that size
+ * (for instance a long-context call that pa_forward would run as chunk
+ * partials of several hundred MiB).  Every call on one GPU shares that GPU's
+ * array: calls that can overlap on one GPU (other streams, other threads)
+ * race on it and must be serialised by the caller.  The array keeps the last
+ * call's contents, which the next call needs no clearing of.
+ */
+PA_API pa_status pa_forward_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    const int32_t* query_start_loc, float scale, void* out,
+                                    float* lse, const pa_dims* dims, void* stream);
+
+/* Size in bytes of pa_forward_noalloc's per-GPU workspace. */
+PA_API size_t pa_noalloc_max_workspace(void);
+
+/*
  * pa_decode_split — first launch of split-KV decode ([TDD] section
  * "Parallel tiled softmax (3D kernel)"): every request has exactly one query
  * token (T == B, q is [B, Hq, Dqk]; query_start_loc is not taken).  The keys

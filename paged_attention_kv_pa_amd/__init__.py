@@ -7,12 +7,14 @@ points.  The library is loaded on first use and a missing or unloadable
 library raises — there is no fallback.
 """
 from .binding import (PA_MASK_CAUSAL, PA_MASK_FULL, PA_MASK_PREFIX, PaError, pa_decode_split,
-                      pa_forward, pa_forward_chunked, pa_forward_masked, pa_merge_lse,
+                      pa_forward, pa_forward_chunked, pa_forward_masked, pa_forward_noalloc,
+                      pa_merge_lse, pa_noalloc_max_workspace,
                       pa_status_string,
                       pa_validate, pa_workspace_size, mla_decode, mla_workspace_size,
                       library, library_path, make_dims)
 
 __all__ = ["PaError", "pa_forward", "pa_forward_masked", "pa_forward_chunked", "pa_decode_split",
+           "pa_forward_noalloc", "pa_noalloc_max_workspace",
            "pa_merge_lse", "PA_MASK_CAUSAL", "PA_MASK_FULL", "PA_MASK_PREFIX",
            "mla_decode",
            "pa_workspace_size", "mla_workspace_size", "pa_validate", "pa_status_string",

@@ -62,6 +62,10 @@ def library():
             lib.pa_forward.restype = i32
             lib.pa_forward_masked.argtypes = [p, p, p, p, p, p, i32, p, p, f32, p, p, dp, p, sz, p]
             lib.pa_forward_masked.restype = i32
+            lib.pa_forward_noalloc.argtypes = [p, p, p, p, p, p, f32, p, p, dp, p]
+            lib.pa_forward_noalloc.restype = i32
+            lib.pa_noalloc_max_workspace.argtypes = []
+            lib.pa_noalloc_max_workspace.restype = sz
             lib.pa_decode_split.argtypes = [p, p, p, p, p, f32, i32, p, p, dp, p]
             lib.pa_decode_split.restype = i32
             lib.pa_forward_chunked.argtypes = [p, p, p, p, p, p, f32, i32, i32, p, p, i32, p, dp, p]
@@ -247,6 +251,35 @@ def _forward(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale,
                                          _stream(q.device, stream))
         _check(st, "pa_forward_masked")
     return out
+
+
+def pa_forward_noalloc(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale, out,
+                       lse=None, max_seq_len=None, max_q_len=None, stream=None):
+    """pa_forward on the library's own per-GPU workspace (see pa_forward_noalloc in
+    include/pa.h): nothing is allocated, so `out` must be given."""
+    _check_common(q, k_cache, v_cache, block_table, seq_lens)
+    _need(query_start_loc.dtype == torch.int32 and query_start_loc.is_contiguous()
+          and query_start_loc.device == q.device, "query_start_loc must be contiguous int32 on q's device")
+    _need(q.dim() == 3 and k_cache.dim() == 4 and v_cache.dim() == 4, "bad tensor ranks")
+    _need(query_start_loc.shape[0] == seq_lens.shape[0] + 1, "query_start_loc must have B + 1 entries")
+    T = int(q.shape[0])
+    dims = make_dims(q, k_cache, v_cache, block_table, seq_lens, T, max_seq_len=max_seq_len,
+                     max_q_len=max_q_len, query_start_loc=query_start_loc)
+    _need(out is not None and out.is_contiguous() and out.dtype == q.dtype
+          and tuple(out.shape) == (T, dims.num_q_heads, dims.head_dim_v), "bad out tensor")
+    if lse is not None:
+        _need(lse.dtype == torch.float32 and lse.is_contiguous() and lse.shape == (T, dims.num_q_heads),
+              "bad lse tensor")
+    st = library().pa_forward_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                      _ptr(seq_lens), _ptr(query_start_loc), float(scale),
+                                      _ptr(out), _ptr(lse), ctypes.byref(dims),
+                                      _stream(q.device, stream))
+    _check(st, "pa_forward_noalloc")
+    return out
+
+
+def pa_noalloc_max_workspace() -> int:
+    return int(library().pa_noalloc_max_workspace())
 
 
 def pa_decode_split(q, k_cache, v_cache, block_table, seq_lens, scale, num_splits, part_out=None,

@@ -36,6 +36,31 @@ struct DevCfg {
 std::mutex g_mu;
 std::map<int, DevCfg> g_cfg;
 
+// Workspace of pa_forward_noalloc: a device array of the library, one copy on
+// every GPU it runs on, held until the process ends.  Host code never uses
+// the array's name as an address (on the host it only stands for the device
+// symbol): the per-device address comes from hipGetSymbolAddress, called
+// once per device with that device current.
+constexpr size_t kScratchBytes = 64ull << 20;
+__device__ __align__(256) char scratch[kScratchBytes];
+std::map<int, void*> g_scratch;  // device -> address of its copy (under g_mu)
+
+pa_status scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_scratch.find(dev);
+  if (it == g_scratch.end()) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    if (!ptr) return hip_fail(hipErrorInvalidSymbol);
+    it = g_scratch.emplace(dev, ptr).first;
+  }
+  *out = it->second;
+  return PA_OK;
+}
 
 pa_status device_config(DevCfg* out) {
   int dev = 0;
@@ -403,6 +428,24 @@ pa_status pa_forward_masked(const void* q, const void* k_cache, const void* v_ca
       a, D, (int)std::max<int64_t>(1, std::min<int64_t>(cfg.cu_count * 2, (pairs + 3) / 4)), s);
   if (e != hipSuccess) return hip_fail(e);
   return PA_OK;
+}
+
+size_t pa_noalloc_max_workspace(void) { return kScratchBytes; }
+
+pa_status pa_forward_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             const int32_t* query_start_loc, float scale, void* out, float* lse,
+                             const pa_dims* d, void* stream) {
+  pa_status st = check_dims(d);
+  if (st != PA_OK) return st;
+  const size_t need = pa_workspace_size(d);
+  if (need == 0 || need > kScratchBytes) return PA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != PA_OK) return st;
+  return pa_forward_masked(q, k_cache, v_cache, block_table, seq_lens, query_start_loc,
+                           PA_MASK_CAUSAL, nullptr, nullptr, scale, out, lse, d, ws,
+                           kScratchBytes, stream);
 }
 
 pa_status pa_decode_split(const void* q, const void* k_cache, const void* v_cache,
