@@ -140,8 +140,12 @@ PA_API size_t pa_workspace_size(const pa_dims* dims);
  * ([ROC] bullet "Chunked context processing"); pa_workspace_size then
  * includes those partials.
  *
- * Supported: bf16 with Dqk == Dv in {64, 128}, P a multiple of 8 up to 256;
- * fp32 with Dqk, Dv <= 256 and any P >= 1.  Requires Hq % Hkv == 0.
+ * Supported: bf16 with (Dqk, Dv) = (64, 64), (128, 128) or (192, 128) (the
+ * last is MLA's prefill / extend on the uncompressed representation, query
+ * and key 128 + 64 rotary columns, value 128: [ROC] sections "Hybrid
+ * processing strategy" and "Prefill/Extend (Non-Absorbed)"), P a multiple of 8
+ * up to 256; fp32 with Dqk, Dv <= 256 and any P >= 1.  Requires
+ * Hq % Hkv == 0.
  * Returns PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE or
  * PA_ERR_HIP.
  */
@@ -234,8 +238,8 @@ PA_API pa_status pa_decode_split(const void* q, const void* k_cache, const void*
  * mask / prefix_lens as for pa_forward_masked (PA_MASK_CAUSAL and NULL for
  * causal attention): a token sees the chunk's keys below its mask's limit.
  * chunk_keys: a positive multiple of 64; num_chunks in [1, 256] with
- * chunk_keys * num_chunks >= dims->max_seq_len.  bf16 only, Dqk == Dv in
- * {64, 128}, P a multiple of 8 up to 256.  Rows of requests with no new token
+ * chunk_keys * num_chunks >= dims->max_seq_len.  bf16 only, with the head
+ * dims and page sizes of pa_forward.  Rows of requests with no new token
  * or with seq_len < q_len are not written.  Buffers are caller-owned device
  * memory; nothing is allocated.  Returns PA_OK, PA_ERR_INVALID_ARG,
  * PA_ERR_UNSUPPORTED or PA_ERR_HIP.

@@ -30,7 +30,7 @@ pa_status hip_fail(hipError_t e) {
 
 struct DevCfg {
   int cu_count = 0;
-  int occ[2][2] = {{0, 0}, {0, 0}};  // [D == 128][decode_only]
+  int occ[pa::kMhaVariants][2] = {};  // persistent workgroups per CU [variant][decode_only]
 };
 
 std::mutex g_mu;
@@ -72,9 +72,9 @@ pa_status device_config(DevCfg* out) {
     DevCfg c;
     e = hipDeviceGetAttribute(&c.cu_count, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return hip_fail(e);
-    for (int di = 0; di < 2; ++di)
+    for (int di = 0; di < pa::kMhaVariants; ++di)
       for (int dd = 0; dd < 2; ++dd) {
-        e = pa::mha_occupancy(di ? 128 : 64, dd != 0, &c.occ[di][dd]);
+        e = pa::mha_occupancy(di, dd != 0, &c.occ[di][dd]);
         if (e != hipSuccess) return hip_fail(e);
         if (c.occ[di][dd] < 1) c.occ[di][dd] = 1;
       }
@@ -102,8 +102,7 @@ pa_status check_dims(const pa_dims* d) {
 // Support check for the MHA kernels (pa_forward / pa_decode_split).
 pa_status check_mha_support(const pa_dims* d) {
   if (d->dtype == PA_BF16) {
-    if (d->head_dim_qk != d->head_dim_v) return PA_ERR_UNSUPPORTED;
-    if (d->head_dim_qk != 64 && d->head_dim_qk != 128) return PA_ERR_UNSUPPORTED;
+    if (pa::mha_variant(d->head_dim_qk, d->head_dim_v) < 0) return PA_ERR_UNSUPPORTED;
     if (d->page_size % 8 != 0 || d->page_size > 256) return PA_ERR_UNSUPPORTED;
   } else {
     if (d->head_dim_qk > 256 || d->head_dim_v > 256) return PA_ERR_UNSUPPORTED;
@@ -152,7 +151,7 @@ struct ChunkRoute {
 };
 ChunkRoute chunk_route(const pa_dims* d) {
   ChunkRoute r;
-  if (d->dtype != PA_BF16 || d->head_dim_qk != d->head_dim_v) return r;
+  if (d->dtype != PA_BF16 || pa::mha_variant(d->head_dim_qk, d->head_dim_v) < 0) return r;
   const int G = d->num_q_heads / d->num_kv_heads;
   if ((int64_t)d->max_q_len * G <= pa::kDecodeRows) return r;  // decode-only calls split their own way
   if (d->max_seq_len < kRouteMinKeys) return r;
@@ -191,7 +190,8 @@ pa_status fwd_geometry(const pa_dims* d, FwdGeom* g) {
   if (st != PA_OK) return st;
   const int G = d->num_q_heads / d->num_kv_heads;
   g->decode_only = (int64_t)d->max_q_len * G <= pa::kDecodeRows;
-  g->grid = cfg.cu_count * cfg.occ[d->head_dim_qk == 128][g->decode_only ? 1 : 0];
+  g->grid = cfg.cu_count * cfg.occ[pa::mha_variant(d->head_dim_qk, d->head_dim_v)]
+                                   [g->decode_only ? 1 : 0];
   g->target = std::max(1, pa::kItemsPerWorkgroup * g->grid);
   return PA_OK;
 }
@@ -308,7 +308,7 @@ pa_status pa_forward_masked(const void* q, const void* k_cache, const void* v_ca
     return e == hipSuccess ? PA_OK : hip_fail(e);
   }
 
-  const int D = d->head_dim_qk;
+  const int variant = pa::mha_variant(d->head_dim_qk, d->head_dim_v);
   // (without a device the workspace is checked against the device-free bound
   // pa_workspace_size gives, and the device error is reported after the
   // host checks)
@@ -345,7 +345,7 @@ pa_status pa_forward_masked(const void* q, const void* k_cache, const void* v_ca
     a.mask = mask;
     a.prefix_lens = prefix_lens;
     hipError_t e = mark(g_ev_start, s);
-    if (e == hipSuccess) e = pa::launch_mha_chunked(a, D, s);
+    if (e == hipSuccess) e = pa::launch_mha_chunked(a, variant, s);
     if (e == hipSuccess) e = mark(g_ev_stop, s);
     if (e == hipSuccess)
       e = pa::launch_merge(a.part_o, a.part_lse, d->num_tokens * d->num_q_heads, route.S,
@@ -417,15 +417,19 @@ pa_status pa_forward_masked(const void* q, const void* k_cache, const void* v_ca
   a.prefix_lens = prefix_lens;
   a.sinks = sinks;
   if ((e = mark(g_ev_start, s)) != hipSuccess) return hip_fail(e);
-  e = fused ? pa::launch_mha_forward_fused(a, D, grid, s)
-            : pa::launch_mha_forward(a, D, decode_only, grid, s);
+  e = fused ? pa::launch_mha_forward_fused(a, variant, grid, s)
+            : pa::launch_mha_forward(a, variant, decode_only, grid, s);
   if (e != hipSuccess) return hip_fail(e);
   if ((e = mark(g_ev_stop, s)) != hipSuccess) return hip_fail(e);
   // the merge also leaves the queue counters zeroed for the next call; one
-  // wave per (request, KV head) pair with split rows, at most B * Hkv of them
+  // wave per 4 rows of a (request, KV head) pair with split rows (at most
+  // B * Hkv pairs of up to 16 rows), four waves per workgroup
   const int64_t pairs = (int64_t)d->num_seqs * d->num_kv_heads;
+  a.merge_groups =
+      (int)((std::min<int64_t>(std::max(1, d->max_q_len) * (int64_t)G, pa::kDecodeRows) + 3) / 4);
+  const int64_t units = pairs * a.merge_groups;
   e = pa::launch_mha_forward_merge(
-      a, D, (int)std::max<int64_t>(1, std::min<int64_t>(cfg.cu_count * 2, (pairs + 3) / 4)), s);
+      a, d->head_dim_v, (int)std::max<int64_t>(1, std::min<int64_t>(cfg.cu_count * 4, (units + 3) / 4)), s);
   if (e != hipSuccess) return hip_fail(e);
   return PA_OK;
 }
@@ -508,7 +512,7 @@ pa_status pa_decode_split(const void* q, const void* k_cache, const void* v_cach
     a.P = d->page_size;
     a.max_pages = d->max_pages_per_seq;
     a.num_splits = num_splits;
-    e = pa::launch_mha_split(a, d->head_dim_qk, s);
+    e = pa::launch_mha_split(a, pa::mha_variant(d->head_dim_qk, d->head_dim_v), s);
   }
   if (e == hipSuccess) e = mark(g_ev_stop, s);
   return e == hipSuccess ? PA_OK : hip_fail(e);
@@ -563,7 +567,8 @@ pa_status pa_forward_chunked(const void* q, const void* k_cache, const void* v_c
   a.mask = mask;
   a.prefix_lens = prefix_lens;
   hipError_t e = mark(g_ev_start, s);
-  if (e == hipSuccess) e = pa::launch_mha_chunked(a, d->head_dim_qk, s);
+  if (e == hipSuccess)
+    e = pa::launch_mha_chunked(a, pa::mha_variant(d->head_dim_qk, d->head_dim_v), s);
   if (e == hipSuccess) e = mark(g_ev_stop, s);
   return e == hipSuccess ? PA_OK : hip_fail(e);
 }

@@ -75,6 +75,7 @@ struct MhaArgs {
   int32_t target_items;      // pa_forward decode-only calls planned in the kernel
   int32_t chunk_keys;        // pa_forward_chunked: keys per chunk
   int32_t row_blocks;        // pa_forward_chunked: row blocks of the longest request
+  int32_t merge_groups;      // pa_forward's merge: groups of 4 rows of the widest split pair
   int32_t mask;              // kMaskCausal / kMaskFull / kMaskPrefix
   const int32_t* prefix_lens;  // [B], read under kMaskPrefix only
   const float* sinks;        // [Hq] sink logits or NULL (pa_forward_masked only)
@@ -126,13 +127,6 @@ struct MlaArgs {
   int32_t max_pieces;        // balanced: pieces that run at once (one workgroup per compute unit)
 };
 
-// Device properties cached per device by the ABI layer.
-struct DeviceInfo {
-  int cu_count;
-  int fwd_blocks_per_cu_mixed[2];   // [D == 128] persistent kernel occupancy
-  int fwd_blocks_per_cu_decode[2];
-};
-
 // Workspace layout of pa_forward.
 struct FwdWorkspace {
   size_t ctrl_off, req_off, pre_off, items_off, merges_off, plse_off, po_off, total;
@@ -143,12 +137,17 @@ struct FwdWorkspace {
 FwdWorkspace fwd_workspace_layout(int B, int Hkv, int D, int target_items);
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
-hipError_t launch_mha_forward(const MhaArgs& a, int D, bool decode_only, int grid, hipStream_t s);
-hipError_t launch_mha_forward_fused(const MhaArgs& a, int D, int grid, hipStream_t s);
-hipError_t launch_mha_forward_merge(const MhaArgs& a, int D, int grid, hipStream_t s);
-hipError_t launch_mha_split(const MhaArgs& a, int D, hipStream_t s);
-hipError_t launch_mha_chunked(const MhaArgs& a, int D, hipStream_t s);
-hipError_t mha_occupancy(int D, bool decode_only, int* blocks_per_cu);
+// bf16 MHA kernels exist for (Dqk, Dv) = (64, 64), (128, 128) and (192, 128):
+// variant 0, 1, 2; mha_variant gives -1 for other pairs.
+constexpr int kMhaVariants = 3;
+int mha_variant(int dk, int dv);
+hipError_t launch_mha_forward(const MhaArgs& a, int variant, bool decode_only, int grid,
+                              hipStream_t s);
+hipError_t launch_mha_forward_fused(const MhaArgs& a, int variant, int grid, hipStream_t s);
+hipError_t launch_mha_forward_merge(const MhaArgs& a, int Dv, int grid, hipStream_t s);
+hipError_t launch_mha_split(const MhaArgs& a, int variant, hipStream_t s);
+hipError_t launch_mha_chunked(const MhaArgs& a, int variant, hipStream_t s);
+hipError_t mha_occupancy(int variant, bool decode_only, int* blocks_per_cu);
 // Rows are ordered [token, head] with Hq heads per token; tok_end (a device
 // int, may be NULL) stops the merge at token *tok_end: later rows are left
 // untouched.

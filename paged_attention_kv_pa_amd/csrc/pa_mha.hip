@@ -106,10 +106,10 @@ __device__ __forceinline__ void store_lse(const MhaArgs& a, const Dest& dst, int
 // `counter` (may be NULL): thread 0 takes the workgroup's next item index from
 // it once the keys are done, so the round trip overlaps the epilogue; the
 // index is returned in thread 0.
-template <int D, int NW>
+template <int DK, int DV, int NW>
 __device__ int run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest& dst,
-                               LdsDecode<D, NW>& sm, int32_t* counter) {
-  constexpr int KS = D / 32, DT = D / 16;
+                               LdsDecode<DV, NW>& sm, int32_t* counter) {
+  constexpr int KS = DK / 32, DT = DV / 16;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
   const int b = it.seq, kvh = it.kvh, G = a.G, P = a.P;
   const int kv_end = __builtin_amdgcn_readfirstlane(it.kv_end);
@@ -124,7 +124,7 @@ __device__ int run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest&
 
   bf16x8 qf[KS];
   {
-    const __bf16* qp = (const __bf16*)a.q + ((int64_t)(it.q0 + tok) * a.Hq + head) * D + 8 * g;
+    const __bf16* qp = (const __bf16*)a.q + ((int64_t)(it.q0 + tok) * a.Hq + head) * DK + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       qf[ks] = row_ok ? as_bf16x8(load16(qp + 32 * ks)) : as_bf16x8(u32x4{0, 0, 0, 0});
@@ -143,9 +143,9 @@ __device__ int run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest&
   typedef const __attribute__((address_space(4))) int32_t* ConstI32Ptr;
   const ConstI32Ptr bt = (ConstI32Ptr)uniform_ptr(
       a.block_table + (int64_t)__builtin_amdgcn_readfirstlane(b) * a.max_pages);
-  const int64_t page_elems = (int64_t)a.Hkv * P * D;
-  const __bf16* kbase = (const __bf16*)a.k_cache + (int64_t)kvh * P * D + 8 * g;
-  const __bf16* vbase = (const __bf16*)a.v_cache + (int64_t)kvh * D * P + (int64_t)r * P;
+  const int64_t kpage_elems = (int64_t)a.Hkv * P * DK, vpage_elems = (int64_t)a.Hkv * DV * P;
+  const __bf16* kbase = (const __bf16*)a.k_cache + (int64_t)kvh * P * DK + 8 * g;
+  const __bf16* vbase = (const __bf16*)a.v_cache + (int64_t)kvh * DV * P + (int64_t)r * P;
   const int last8 = (kv_end - 1) & ~7;
   const int last_pg = __builtin_amdgcn_readfirstlane((kv_end - 1) / P);
 
@@ -188,7 +188,7 @@ __device__ int run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest&
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         const int key = min(t0 + kperm(mt, r), kv_end - 1);
-        const __bf16* kp = kbase + (int64_t)page * page_elems + (key - kb) * D;
+        const __bf16* kp = kbase + (int64_t)page * kpage_elems + (key - kb) * DK;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) st.kf[mt][ks] = as_bf16x8(load16(kp + 32 * ks));
       }
@@ -196,7 +196,7 @@ __device__ int run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest&
     // V^T operand: keys t0+8g .. t0+8g+7 of column 16dt + r
     const int key8 = min(t0 + 8 * g, last8);
     const int page = pick(g, pg0, pg1, pg2, pg3);
-    const __bf16* vp = vbase + (int64_t)page * page_elems + (key8 - pick(g, i0, i1, i2, i3) * P);
+    const __bf16* vp = vbase + (int64_t)page * vpage_elems + (key8 - pick(g, i0, i1, i2, i3) * P);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) st.vf[dt] = as_bf16x8(load16(vp + (int64_t)16 * dt * P));
   };
@@ -292,7 +292,7 @@ __device__ int run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest&
   __syncthreads();
   {
     constexpr int TPR = 4 * NW;   // threads per row
-    constexpr int NC = D / TPR;   // columns per thread
+    constexpr int NC = DV / TPR;  // columns per thread
     const int row = tid / TPR, c0 = (tid % TPR) * NC;
     float M = kNegInf;
 #pragma unroll
@@ -321,7 +321,7 @@ __device__ int run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest&
       if (a.sinks && !dst.partial) f *= fold_sink(a.sinks[head], &lse);
 #pragma unroll
       for (int e = 0; e < NC; ++e) o[e] *= f;
-      store_row_chunk<D, NC>(a, dst, row, out_row, c0, o);
+      store_row_chunk<DV, NC>(a, dst, row, out_row, c0, o);
       if (tid % TPR == 0) store_lse(a, dst, row, out_row, lse);
     }
   }
@@ -377,16 +377,27 @@ __device__ __forceinline__ void pipeline_reads_and_mfma() {
   __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
 }
 
-template <int D>
+// The K and V^T tiles live in two rings: K of tile t is read in step t only,
+// V^T of tile t in step t + 1 (see the schedule in run_prefill_item), and the
+// copy of tile t + 2 starts at the beginning of step t.  So the K ring needs
+// the 3 stages of tiles t .. t + 2 and the V^T ring the 4 of tiles t - 1 ..
+// t + 2 (for DK = 192 one 4-stage ring of both would not fit in LDS).
+template <int DK, int DV>
 struct PrefillLayout {
-  static constexpr int kStages = 4;
-  static constexpr int kChunks = D / 8;                  // 16-byte chunks per key row
-  static constexpr int kKBytes = kTK * D * 2;            // K tile
-  static constexpr int kVBytes = kTK * D * 2;            // V^T tile
-  static constexpr int kStageBytes = kKBytes + kVBytes;
+  static constexpr int kKStages = 3, kVStages = 4;
+  static constexpr int kChunks = DK / 8;                 // 16-byte chunks per key row
+  static constexpr int kKBytes = kTK * DK * 2;           // K tile
+  static constexpr int kVBytes = kTK * DV * 2;           // V^T tile
+  static constexpr int kRingBytes = kKStages * kKBytes + kVStages * kVBytes;
   static constexpr int kKCopies = kChunks / 8;           // K copies per wave per tile
-  static constexpr int kVCopies = D / 64;                // V copies per wave per tile
+  static constexpr int kVCopies = DV / 64;               // V copies per wave per tile
   static constexpr int kCopies = kKCopies + kVCopies;    // copy instructions per thread per tile
+  static_assert(kChunks % 8 == 0 && DV % 64 == 0, "head dims");
+  // byte offsets of tile t's K and V^T stages in the ring
+  __device__ static __forceinline__ int kstage(int t) { return (t % kKStages) * kKBytes; }
+  __device__ static __forceinline__ int vstage(int t) {
+    return kKStages * kKBytes + (t % kVStages) * kVBytes;
+  }
   // byte offset of column chunk c of tile key k in the K tile: blocks of
   // 16 keys x 4 chunks (1 KiB, one copy instruction), key-major inside, the
   // chunk position XOR-swizzled by key bits 2..3
@@ -395,19 +406,19 @@ struct PrefillLayout {
             ((c & 3) ^ ((k >> 2) & 3))) * 16;
   }
   // byte offset of key chunk c (keys 8c .. 8c + 7), column d in the V^T tile
-  __device__ static __forceinline__ int voff(int c, int d) { return kKBytes + (c * D + d) * 16; }
+  __device__ static __forceinline__ int voff(int c, int d) { return (c * DV + d) * 16; }
 };
 
-template <int D>
+template <int DK, int DV>
 struct alignas(16) LdsPrefill {
-  char stage[PrefillLayout<D>::kStages][PrefillLayout<D>::kStageBytes];
+  char ring[PrefillLayout<DK, DV>::kRingBytes];
 };
 
-template <int D>
+template <int DK, int DV>
 __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Dest& dst,
-                                 LdsPrefill<D>& sm) {
-  using LY = PrefillLayout<D>;
-  constexpr int KS = D / 16, DT = D / 32, NST = LY::kStages;
+                                 LdsPrefill<DK, DV>& sm) {
+  using LY = PrefillLayout<DK, DV>;
+  constexpr int KS = DK / 16, DT = DV / 32;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 31, h = lane >> 5;
   const int G = __builtin_amdgcn_readfirstlane(a.G), P = __builtin_amdgcn_readfirstlane(a.P);
   // item fields are workgroup-uniform: keep them in scalar registers so that
@@ -435,7 +446,7 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
     const int head = kvh * G + (rid - t * G);
     out_row = (int64_t)(q0 + t) * a.Hq + head;
     lim = row_ok ? min(visible_end(mask, ctx, t, pfx), kv_end) : kv_begin;
-    const __bf16* qp = (const __bf16*)a.q + out_row * D + 8 * h;
+    const __bf16* qp = (const __bf16*)a.q + out_row * DK + 8 * h;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       qf[ks] = row_ok ? as_bf16x8(load16(qp + 16 * ks)) : as_bf16x8(u32x4{0, 0, 0, 0});
@@ -461,9 +472,10 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
   // (the arguments may live in vector registers here: the kernel also makes
   // a real call with them; make the bases visibly uniform)
   const int32_t* bt = uniform_ptr(a.block_table + (int64_t)b * a.max_pages);
-  const int64_t page_elems = (int64_t)__builtin_amdgcn_readfirstlane(a.Hkv * P * D);
-  const char* kbase = uniform_ptr((const char*)((const __bf16*)a.k_cache + (int64_t)kvh * P * D));
-  const char* vbase = uniform_ptr((const char*)((const __bf16*)a.v_cache + (int64_t)kvh * D * P));
+  const int64_t kpage_elems = (int64_t)__builtin_amdgcn_readfirstlane(a.Hkv * P * DK);
+  const int64_t vpage_elems = (int64_t)__builtin_amdgcn_readfirstlane(a.Hkv * DV * P);
+  const char* kbase = uniform_ptr((const char*)((const __bf16*)a.k_cache + (int64_t)kvh * P * DK));
+  const char* vbase = uniform_ptr((const char*)((const __bf16*)a.v_cache + (int64_t)kvh * DV * P));
 
   // The copies are issued by the four waves of group A (waves 0-3, which
   // start every step with their matrix products, see the schedule below):
@@ -483,8 +495,8 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const bool copier = wave_u < kPrefillWaves / 2;  // group A
   const int kgroup = wave_u & (kPrefillWaves / 2 - 1);
-  const uint32_t lds_stage0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)sm.stage[0]);
+  const uint32_t lds_ring = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)sm.ring);
   struct TilePages {
     int pg0, first0;  // physical page and its first key, keys 16 kgroup + 0 .. 7
     int pg1, first1;  // the same for keys 16 kgroup + 8 .. 15
@@ -500,9 +512,9 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
     tp.first1 = i1 * P;
     return tp;
   };
-  auto issue_tile = [&](int t0, int st, const TilePages& tp) {
+  auto issue_tile = [&](int t0, int tile, const TilePages& tp) {
     if (!copier) return;
-    const uint32_t stage = lds_stage0 + st * LY::kStageBytes;
+    const uint32_t kst = lds_ring + LY::kstage(tile), vst = lds_ring + LY::vstage(tile);
     const int ts = __builtin_amdgcn_readfirstlane(t0);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {  // the two 8-key halves of the group
@@ -514,13 +526,13 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
         const bool hi = k16 >= 8;
         const int key = min(ts + 16 * kgroup + k16, kv_end - 1);
         const int c0 = half * (LY::kChunks / 2);  // first column chunk of this half
-        const char* page0 = kbase + (int64_t)tp.pg0 * page_elems * 2;
-        const char* page1 = kbase + (int64_t)tp.pg1 * page_elems * 2;
-        const int off = ((key - (hi ? tp.first1 : tp.first0)) * D + 8 * (c0 + cl)) * 2;
+        const char* page0 = kbase + (int64_t)tp.pg0 * kpage_elems * 2;
+        const char* page1 = kbase + (int64_t)tp.pg1 * kpage_elems * 2;
+        const int off = ((key - (hi ? tp.first1 : tp.first0)) * DK + 8 * (c0 + cl)) * 2;
         const char* src = (hi ? page1 : page0) + off;
 #pragma unroll
         for (int j = 0; j < LY::kKCopies; ++j)
-          lds_dma16_m0(src + 64 * j, stage + LY::koff(16 * kgroup, c0 + 4 * j));
+          lds_dma16_m0(src + 64 * j, kst + LY::koff(16 * kgroup, c0 + 4 * j));
       }
       {
         const bool hi = half;
@@ -528,10 +540,10 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
         const int cs = min(ts + 8 * vch, (kv_end - 1) & ~7);
         const int pg = hi ? tp.pg1 : tp.pg0;
         const int slot = cs - (hi ? tp.first1 : tp.first0);
-        const char* vpage = vbase + ((int64_t)pg * page_elems + slot) * 2;
+        const char* vpage = vbase + ((int64_t)pg * vpage_elems + slot) * 2;
 #pragma unroll
         for (int i = 0; i < LY::kVCopies; ++i)
-          lds_dma16_m0(vpage + (64 * i + lane) * P * 2, stage + LY::voff(vch, 64 * i));
+          lds_dma16_m0(vpage + (64 * i + lane) * P * 2, vst + LY::voff(vch, 64 * i));
       }
     }
   };
@@ -559,7 +571,7 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
   constexpr int kAhead = 4;
   auto gemm_phase = [&](int t) {
     if (t < wave_tiles) {
-      const char* stage = sm.stage[t % NST];
+      const char* stage = sm.ring + LY::kstage(t);
       auto kread = [&](int i) {  // operand i = (ks, kb) = (i / 2, i % 2)
         return as_bf16x8(*reinterpret_cast<const u32x4*>(
             stage + LY::koff(32 * (i & 1) + krow, 2 * (i >> 1) + h)));
@@ -579,7 +591,7 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
       }
     }
     if (t >= 1 && t - 1 < wave_tiles) {
-      const char* stage = sm.stage[(t - 1) % NST];
+      const char* stage = sm.ring + LY::vstage(t - 1);
       auto vread = [&](int i) {  // operand i = (kc, dt) = (i / DT, i % DT)
         return as_bf16x8(*reinterpret_cast<const u32x4*>(
             stage + LY::voff(2 * (i / DT) + h, 32 * (i % DT) + n)));
@@ -655,9 +667,9 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
   // vector ALU.  Every step ends with a workgroup barrier.  Step t:
   //   even phase: A gemm(t)       B softmax(t - 1)   (copy of tile t + 2 starts)
   //   odd phase:  A softmax(t)    B gemm(t)          (copy of tile t + 1 waited)
-  // Tile t is read in steps t and t + 1; tile t + 2 lands in stage
-  // (t + 2) % 4, last read in step t - 1.
-  static_assert(NST == 4, "two tiles in flight ahead of the two being read");
+  // K of tile t is read in step t and its V^T in step t + 1; tile t + 2 lands
+  // in the stages of tiles t - 1 (K) and t - 2 (V^T), last read in step t - 1.
+  static_assert(LY::kKStages == 3 && LY::kVStages == 4, "two tiles in flight ahead");
   const bool group_b = wave >= kPrefillWaves / 2;
   if (ntiles > 0) issue_tile(kv_begin, 0, load_pages(kv_begin));
   if (ntiles > 1) {
@@ -670,7 +682,7 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
   TilePages next_pages;
   if (ntiles > 2) next_pages = load_pages(kv_begin + 2 * kTK);
   for (int t = 0; t <= ntiles; ++t) {
-    if (t + 2 < ntiles) issue_tile(kv_begin + (t + 2) * kTK, (t + 2) % NST, next_pages);
+    if (t + 2 < ntiles) issue_tile(kv_begin + (t + 2) * kTK, t + 2, next_pages);
     if (group_b) softmax_phase(t - 1);
     else gemm_phase(t);
     // (no barrier between the two phases: they share no LDS data; the groups
@@ -681,10 +693,10 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
       // last tile: zero the values of keys >= kv_end before their first use
       // in the next step (their slots may hold anything, and 0 * NaN would
       // reach the output)
-      char* stage = sm.stage[t % NST];
+      char* stage = sm.ring + LY::vstage(t);
       const int t0 = kv_begin + t * kTK;
-      for (int e = tid; e < 8 * D; e += kPrefillThreads) {
-        const int c = e / D, d = e - c * D;
+      for (int e = tid; e < 8 * DV; e += kPrefillThreads) {
+        const int c = e / DV, d = e - c * DV;
         const int k0 = t0 + 8 * c;
         if (k0 + 8 > kv_end) {
           u32x4* pz = reinterpret_cast<u32x4*>(stage + LY::voff(c, d));
@@ -717,18 +729,18 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
     for (int q = 0; q < 4; ++q) {
       const float o[4] = {acc[dt][4 * q] * inv, acc[dt][4 * q + 1] * inv,
                           acc[dt][4 * q + 2] * inv, acc[dt][4 * q + 3] * inv};
-      store_row_chunk<D, 4>(a, dst, row, out_row, 32 * dt + 8 * q + 4 * h, o);
+      store_row_chunk<DV, 4>(a, dst, row, out_row, 32 * dt + 8 * q + 4 * h, o);
     }
   if (h == 0) store_lse(a, dst, row, out_row, lse);
 }
 
-template <int D, bool DECODE_ONLY>
+template <int DK, int DV, bool DECODE_ONLY>
 struct FwdLds {
   union U {
-    LdsDecode<D, kPrefillWaves> dec;
-    LdsPrefill<D> pre;
+    LdsDecode<DV, kPrefillWaves> dec;
+    LdsPrefill<DK, DV> pre;
   };
-  typedef typename std::conditional<DECODE_ONLY, LdsDecode<D, 4>, U>::type type;
+  typedef typename std::conditional<DECODE_ONLY, LdsDecode<DV, 4>, U>::type type;
 };
 
 // Largest b in [0, B) with off[b] <= idx (off is non-decreasing, off[0] = 0):
@@ -780,12 +792,12 @@ __device__ WorkItem make_prefill_item(const MhaArgs& a, int idx) {
 // The decode item as a real call, for the kernel that also runs prefill
 // items: this keeps the decode code's register allocation out of the prefill
 // loop (a call costs little next to a decode item's key loads).
-template <int D>
+template <int DK, int DV>
 __device__ __noinline__ int run_decode_item_outlined(const MhaArgs& a, const WorkItem& it,
                                                      const Dest& dst,
-                                                     LdsDecode<D, kPrefillWaves>& sm,
+                                                     LdsDecode<DV, kPrefillWaves>& sm,
                                                      int32_t* counter) {
-  return run_decode_item<D, kPrefillWaves>(a, it, dst, sm, counter);
+  return run_decode_item<DK, DV, kPrefillWaves>(a, it, dst, sm, counter);
 }
 
 // ---------------------------------------------------------------------------
@@ -974,11 +986,15 @@ __device__ WorkItem fused_item(const MhaArgs& a, const FusedPlan& fp, long long 
 // kernel runs before this one; every workgroup computes the plan itself
 // (fused_plan) and builds its items from it, and the only preceding launch
 // resets the queue counter.
-template <int D, bool DECODE_ONLY, bool FUSED = false>
-__global__ __launch_bounds__(DECODE_ONLY ? kThreads : kPrefillThreads, DECODE_ONLY ? 2 : 1)
+// (Decode-only grids run two workgroups per compute unit, except with 192-wide
+// keys: their decode item's two steps of key operands in flight need more
+// registers than a half share of the register file.)
+template <int DK, int DV, bool DECODE_ONLY, bool FUSED = false>
+__global__ __launch_bounds__(DECODE_ONLY ? kThreads : kPrefillThreads,
+                             (DECODE_ONLY && DK <= 128) ? 2 : 1)
 void mha_forward_kernel(MhaArgs a) {
   static_assert(!FUSED || DECODE_ONLY, "the kernel plans only decode-only calls");
-  __shared__ typename FwdLds<D, DECODE_ONLY>::type sm;
+  __shared__ typename FwdLds<DK, DV, DECODE_ONLY>::type sm;
   __shared__ WorkItem s_item;
   __shared__ int s_idx;
   __shared__ typename std::conditional<FUSED, FusedPlan, int>::type fp;
@@ -1066,8 +1082,8 @@ void mha_forward_kernel(MhaArgs a) {
   auto dest = [&]() {
     Dest dst;
     dst.partial = it.part >= 0;
-    dst.po_base = (int64_t)it.part * kDecodeRows * D;
-    dst.po_row = D;
+    dst.po_base = (int64_t)it.part * kDecodeRows * DV;
+    dst.po_row = DV;
     dst.po_out = 0;
     dst.pl_base = (int64_t)it.part * kDecodeRows;
     dst.pl_row = 1;
@@ -1079,14 +1095,14 @@ void mha_forward_kernel(MhaArgs a) {
     publish();
   } else {
     next();
-    for (; idx < n_pre && idx < n_items; next()) run_prefill_item<D>(a, it, dest(), sm.pre);
+    for (; idx < n_pre && idx < n_items; next()) run_prefill_item<DK, DV>(a, it, dest(), sm.pre);
   }
   // decode-mode items: each one claims its successor while its epilogue runs
   // (without the queue: the item gridDim.x further on)
   while (idx < n_items) {
     int j;
-    if constexpr (DECODE_ONLY) j = run_decode_item<D, 4>(a, it, dest(), sm, counter);
-    else j = run_decode_item_outlined<D>(a, it, dest(), sm.dec, counter);
+    if constexpr (DECODE_ONLY) j = run_decode_item<DK, DV, 4>(a, it, dest(), sm, counter);
+    else j = run_decode_item_outlined<DK, DV>(a, it, dest(), sm.dec, counter);
     if (threadIdx.x < 64)
       fetch_decode(queue ? __shfl(j, 0) + dec_base : idx - n_pre + (int)gridDim.x);
     publish();
@@ -1094,10 +1110,11 @@ void mha_forward_kernel(MhaArgs a) {
 }
 
 // pa_decode_split: one workgroup per (request, KV head, partition).
-template <int D, bool DEC>
+template <int DK, int DV, bool DEC>
 __global__ __launch_bounds__(DEC ? kThreads : kPrefillThreads, DEC ? 2 : 1)
 void mha_split_kernel(MhaArgs a) {
-  __shared__ typename std::conditional<DEC, LdsDecode<D, 4>, LdsPrefill<D>>::type sm;
+  constexpr int D = DV;
+  __shared__ typename std::conditional<DEC, LdsDecode<DV, 4>, LdsPrefill<DK, DV>>::type sm;
   const int S = a.num_splits;
   const int s = blockIdx.x % S;
   const int bk = blockIdx.x / S;
@@ -1133,8 +1150,8 @@ void mha_split_kernel(MhaArgs a) {
   it.q0 = b;
   it.ctx = L - 1;
   it.pad[0] = it.pad[1] = it.pad[2] = 0;
-  if constexpr (DEC) run_decode_item<D, 4>(a, it, dst, sm, nullptr);
-  else run_prefill_item<D>(a, it, dst, sm);
+  if constexpr (DEC) run_decode_item<DK, DV, 4>(a, it, dst, sm, nullptr);
+  else run_prefill_item<DK, DV>(a, it, dst, sm);
 }
 
 // pa_forward_chunked: chunked-context processing ("vLLM AMD ROCm Attention
@@ -1148,9 +1165,10 @@ void mha_split_kernel(MhaArgs a) {
 // no key of the chunk gets zeros and -inf: inside the item when another row
 // of the block sees the chunk, here when none does.  Requests with no work
 // (no new token, or inconsistent lengths) write nothing.
-template <int D>
+template <int DK, int DV>
 __global__ __launch_bounds__(kPrefillThreads, 1) void mha_chunked_kernel(MhaArgs a) {
-  __shared__ LdsPrefill<D> sm;
+  constexpr int D = DV;
+  __shared__ LdsPrefill<DK, DV> sm;
   const int S = a.num_splits, nblk = a.row_blocks;
   // Workgroups go to the 8 chiplets (XCDs, each with its own L2) round-robin
   // by index.  The index is remapped so that consecutive logical indices sit
@@ -1204,7 +1222,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void mha_chunked_kernel(MhaArgs
   it.q0 = q0;
   it.ctx = ctx;
   it.pad[0] = it.pad[1] = it.pad[2] = 0;
-  run_prefill_item<D>(a, it, dst, sm);
+  run_prefill_item<DK, DV>(a, it, dst, sm);
 }
 
 // Planner: one workgroup of 1024 threads turns (seq_lens, query_start_loc)
@@ -1321,11 +1339,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   }
 }
 
-// Merge of pa_forward's split decode rows.  One wave takes a (request, KV
-// head) pair whose rows were split and handles 4 rows at a time: 16 lanes per
-// row, each with D / 16 consecutive columns, folding the partitions in one
-// pass with a running log-sum-exp (max, rescaled weight sum, rescaled sum);
-// the loads of several partitions are in flight together.
+// Merge of pa_forward's split decode rows.  One wave takes 4 rows of a
+// (request, KV head) pair whose rows were split (unit e = pair x
+// merge_groups + row group; a pair has at most merge_groups x 4 <= 16 rows,
+// fixed on the host from max_q_len): 16 lanes per row, each with
+// D / 16 consecutive columns, folding the partitions in one pass with a
+// running log-sum-exp (max, rescaled weight sum, rescaled sum); the loads of
+// several partitions are in flight together.
 template <int D>
 __global__ __launch_bounds__(kThreads) void mha_forward_merge_kernel(MhaArgs a) {
   constexpr int NC = D / 16;
@@ -1339,12 +1359,13 @@ __global__ __launch_bounds__(kThreads) void mha_forward_merge_kernel(MhaArgs a) 
     if (threadIdx.x < 8) a.ctrl->xcd_counter[threadIdx.x] = 0;
     if (threadIdx.x == 0) a.ctrl->ready = kQueueReady;  // seen with the zeros by the next kernel
   }
+  const int groups = a.merge_groups;
   const int stride = gridDim.x * (kThreads / 64);
-  for (int e = blockIdx.x * (kThreads / 64) + wv; e < n_merge; e += stride) {
-    const int4 me = reinterpret_cast<const int4*>(a.merges)[e];
+  for (int e = blockIdx.x * (kThreads / 64) + wv; e < n_merge * groups; e += stride) {
+    const int4 me = reinterpret_cast<const int4*>(a.merges)[e / groups];
     const int slot0 = me.x, S = me.y & 0xffff, nrows = me.y >> 16, q0 = me.z, kvh = me.w;
-    for (int r0 = 0; r0 < nrows; r0 += 4) {
-      const int row = r0 + rsub;
+    {
+      const int row = 4 * (e % groups) + rsub;
       if (row >= nrows) continue;
       float m = kNegInf, wsum = 0.f;
       float o[NC];
@@ -1394,59 +1415,87 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t mha_occupancy(int D, bool decode_only, int* blocks_per_cu) {
-  const void* f;
-  if (D == 128) f = decode_only ? (const void*)mha_forward_kernel<128, true> : (const void*)mha_forward_kernel<128, false>;
-  else f = decode_only ? (const void*)mha_forward_kernel<64, true> : (const void*)mha_forward_kernel<64, false>;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, f,
-                                                      decode_only ? kThreads : kPrefillThreads, 0);
-}
-
-hipError_t launch_mha_forward(const MhaArgs& a, int D, bool decode_only, int grid, hipStream_t s) {
-  if (D == 128) {
-    if (decode_only) hipLaunchKernelGGL((mha_forward_kernel<128, true>), dim3(grid), dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((mha_forward_kernel<128, false>), dim3(grid), dim3(kPrefillThreads), 0, s, a);
-  } else {
-    if (decode_only) hipLaunchKernelGGL((mha_forward_kernel<64, true>), dim3(grid), dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((mha_forward_kernel<64, false>), dim3(grid), dim3(kPrefillThreads), 0, s, a);
+// The bf16 head-dim pairs (Dqk, Dv) the MHA kernels are built for, by variant
+// index (see mha_variant).
+template <typename F>
+hipError_t with_dims(int variant, F&& f) {
+  switch (variant) {
+    case 0: return f(std::integral_constant<int, 64>(), std::integral_constant<int, 64>());
+    case 1: return f(std::integral_constant<int, 128>(), std::integral_constant<int, 128>());
+    case 2: return f(std::integral_constant<int, 192>(), std::integral_constant<int, 128>());
   }
+  return hipErrorInvalidValue;
+}
+
+int mha_variant(int dk, int dv) {
+  if (dk == 64 && dv == 64) return 0;
+  if (dk == 128 && dv == 128) return 1;
+  if (dk == 192 && dv == 128) return 2;
+  return -1;
+}
+
+hipError_t mha_occupancy(int variant, bool decode_only, int* blocks_per_cu) {
+  return with_dims(variant, [&](auto dk, auto dv) {
+    constexpr int DK = decltype(dk)::value, DV = decltype(dv)::value;
+    const void* f = decode_only ? (const void*)mha_forward_kernel<DK, DV, true>
+                                : (const void*)mha_forward_kernel<DK, DV, false>;
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, f,
+                                                        decode_only ? kThreads : kPrefillThreads, 0);
+  });
+}
+
+hipError_t launch_mha_forward(const MhaArgs& a, int variant, bool decode_only, int grid,
+                              hipStream_t s) {
+  return with_dims(variant, [&](auto dk, auto dv) {
+    constexpr int DK = decltype(dk)::value, DV = decltype(dv)::value;
+    if (decode_only)
+      hipLaunchKernelGGL((mha_forward_kernel<DK, DV, true>), dim3(grid), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((mha_forward_kernel<DK, DV, false>), dim3(grid), dim3(kPrefillThreads), 0,
+                         s, a);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_mha_forward_fused(const MhaArgs& a, int variant, int grid, hipStream_t s) {
+  return with_dims(variant, [&](auto dk, auto dv) {
+    constexpr int DK = decltype(dk)::value, DV = decltype(dv)::value;
+    hipLaunchKernelGGL((mha_forward_kernel<DK, DV, true, true>), dim3(grid), dim3(kThreads), 0, s,
+                       a);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_mha_forward_merge(const MhaArgs& a, int Dv, int grid, hipStream_t s) {
+  if (Dv == 128) hipLaunchKernelGGL(mha_forward_merge_kernel<128>, dim3(grid), dim3(kThreads), 0, s, a);
+  else if (Dv == 64) hipLaunchKernelGGL(mha_forward_merge_kernel<64>, dim3(grid), dim3(kThreads), 0, s, a);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
-hipError_t launch_mha_forward_fused(const MhaArgs& a, int D, int grid, hipStream_t s) {
-  if (D == 128) hipLaunchKernelGGL((mha_forward_kernel<128, true, true>), dim3(grid), dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL((mha_forward_kernel<64, true, true>), dim3(grid), dim3(kThreads), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_mha_forward_merge(const MhaArgs& a, int D, int grid, hipStream_t s) {
-  if (D == 128) hipLaunchKernelGGL(mha_forward_merge_kernel<128>, dim3(grid), dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL(mha_forward_merge_kernel<64>, dim3(grid), dim3(kThreads), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_mha_split(const MhaArgs& a, int D, hipStream_t s) {
+hipError_t launch_mha_split(const MhaArgs& a, int variant, hipStream_t s) {
   const int64_t blocks = (int64_t)a.num_seqs * a.Hkv * a.num_splits;
   if (blocks <= 0) return hipSuccess;
   const bool dec = a.G <= kDecodeRows;
-  if (D == 128) {
-    if (dec) hipLaunchKernelGGL((mha_split_kernel<128, true>), dim3(blocks), dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((mha_split_kernel<128, false>), dim3(blocks), dim3(kPrefillThreads), 0, s, a);
-  } else {
-    if (dec) hipLaunchKernelGGL((mha_split_kernel<64, true>), dim3(blocks), dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((mha_split_kernel<64, false>), dim3(blocks), dim3(kPrefillThreads), 0, s, a);
-  }
-  return hipGetLastError();
+  return with_dims(variant, [&](auto dk, auto dv) {
+    constexpr int DK = decltype(dk)::value, DV = decltype(dv)::value;
+    if (dec)
+      hipLaunchKernelGGL((mha_split_kernel<DK, DV, true>), dim3(blocks), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((mha_split_kernel<DK, DV, false>), dim3(blocks), dim3(kPrefillThreads), 0,
+                         s, a);
+    return hipGetLastError();
+  });
 }
 
-hipError_t launch_mha_chunked(const MhaArgs& a, int D, hipStream_t s) {
+hipError_t launch_mha_chunked(const MhaArgs& a, int variant, hipStream_t s) {
   const int64_t blocks = (int64_t)a.num_seqs * a.Hkv * a.row_blocks * a.num_splits;
   if (blocks <= 0) return hipSuccess;
-  if (D == 128)
-    hipLaunchKernelGGL((mha_chunked_kernel<128>), dim3(blocks), dim3(kPrefillThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((mha_chunked_kernel<64>), dim3(blocks), dim3(kPrefillThreads), 0, s, a);
-  return hipGetLastError();
+  return with_dims(variant, [&](auto dk, auto dv) {
+    constexpr int DK = decltype(dk)::value, DV = decltype(dv)::value;
+    hipLaunchKernelGGL((mha_chunked_kernel<DK, DV>), dim3(blocks), dim3(kPrefillThreads), 0, s, a);
+    return hipGetLastError();
+  });
 }
 
 FwdWorkspace fwd_workspace_layout(int B, int Hkv, int D, int target_items) {

@@ -311,6 +311,25 @@ def deepseek_mla(case: int = 0, device="cpu", batch: int = 64, lo: int = 1024,
                       name="deepseek_mla/%d" % case)
 
 
+def deepseek_mha_prefill(case: int = 0, device="cpu", n_extend: int = 8, n_prefill: int = 8,
+                         ext_q=(256, 2048), ext_c=(4096, 32768), pre_q=(512, 8192),
+                         heads: int = 128, page_size: int = 64) -> Batch:
+    """DeepSeek-R1 MLA prefill / extend on the uncompressed representation
+    ("Hybrid processing strategy": prefill and extend run non-absorbed, as MHA):
+    `heads` query heads each with its own key / value head, query / key 192 wide
+    (128 + 64 rotary), value 128 wide, page 64, bf16, scale 1/sqrt(192); requests
+    ordered [extend : prefill] with the extend / prefill lengths of the Qwen3 mix."""
+    seed = case_seed(6, case)
+    g = torch.Generator().manual_seed(seed + 7)
+    eq = _randint(g, ext_q[0], ext_q[1], n_extend)
+    ec = _randint(g, ext_c[0], ext_c[1], n_extend)
+    pq = _randint(g, pre_q[0], pre_q[1], n_prefill)
+    return make_batch(eq + pq, ec + [0] * n_prefill, num_q_heads=heads, num_kv_heads=heads,
+                      head_dim_qk=192, head_dim_v=128, page_size=page_size, dtype=BF16,
+                      scale=1.0 / math.sqrt(192.0), seed=seed, device=device,
+                      name="deepseek_mha_prefill/%d" % case)
+
+
 def algorithmic_bytes(b: Batch) -> int:
     """Bytes a perfect kernel moves: each visible K/V element once (the MLA latent
     once), q, out, lse (fp32) and 4 bytes per used block-table entry."""

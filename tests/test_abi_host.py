@@ -89,10 +89,20 @@ def test_forward_rejects_null_pointers_and_dims():
 
 
 @pytest.mark.parametrize("kw", [dict(head_dim_qk=96, head_dim_v=96), dict(head_dim_v=64),
+                                dict(head_dim_qk=192, head_dim_v=192),
+                                dict(head_dim_qk=128, head_dim_v=192),
                                 dict(page_size=12, max_pages_per_seq=30), dict(page_size=512, max_pages_per_seq=20),
                                 dict(dtype=binding.PA_F32, head_dim_qk=512, head_dim_v=512)])
 def test_forward_reports_unsupported(kw):
     assert _fwd(_dims(**kw)) == binding.PA_ERR_UNSUPPORTED
+
+
+def test_forward_accepts_the_non_absorbed_mla_head_dims():
+    # query / key 192 (128 + 64 rotary), value 128: supported in bf16; the call gets
+    # past every host check (the workspace check is the last one)
+    d = _dims(head_dim_qk=192, head_dim_v=128, num_q_heads=16, num_kv_heads=16)
+    assert pa.pa_workspace_size(d) > 0
+    assert _fwd(d, ws_bytes=0) == binding.PA_ERR_WORKSPACE
 
 
 def test_forward_checks_workspace_before_launch():

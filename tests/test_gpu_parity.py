@@ -218,7 +218,7 @@ def masked_parity(b, mask, prefixes, what, sinks=None):
     ref, rlse = oracle.attention(b.q, b.k_cache, b.v_cache, b.block_table, b.seq_lens,
                                  b.query_start_loc, b.scale, b.num_kv_heads, mask=mask,
                                  prefix_lens=None if prefixes is None else np.asarray(prefixes, np.int32),
-                                 sinks=sinks)
+                                 sinks=sinks, head_dim_v=b.head_dim_v)
     got = out.float().cpu().numpy()
     check_out(got, ref, b.dtype, what)
     check_lse(lse.cpu().numpy(), rlse, what)
@@ -348,13 +348,13 @@ def chunked_parity(b, C, what, S=None, rows=None, mask=pa.PA_MASK_CAUSAL, prefix
     if rows is None and partials:
         rpo, rpl = oracle.chunked_partials(b.q, b.k_cache, b.v_cache, b.block_table, b.seq_lens,
                                            b.query_start_loc, b.scale, C, S, b.num_kv_heads,
-                                           mask=mask, prefix_lens=pfx)
+                                           mask=mask, prefix_lens=pfx, head_dim_v=b.head_dim_v)
         check_out(po, rpo, torch.bfloat16, "%s partials" % what)
         check_lse(pl, rpl, "%s partial lse" % what)
     if ref is None:
         ref, rlse = oracle.attention(b.q, b.k_cache, b.v_cache, b.block_table, b.seq_lens,
                                      b.query_start_loc, b.scale, b.num_kv_heads, rows=rows,
-                                     mask=mask, prefix_lens=pfx)
+                                     mask=mask, prefix_lens=pfx, head_dim_v=b.head_dim_v)
     else:
         ref, rlse = ref
     if rows is not None:
@@ -564,6 +564,73 @@ def test_f32_unequal_head_dims(Hq, Hkv):
                             head_dim_qk=192, head_dim_v=128, page_size=16,
                             dtype=torch.float32, seed=701 + Hq)
     forward_parity(b, "fp32 Dqk 192 Dv 128 Hq=%d Hkv=%d" % (Hq, Hkv))
+
+
+# ------------------- MLA prefill / extend, non-absorbed (query/key 192, value 128)
+
+F2 = dict(head_dim_qk=192, head_dim_v=128, scale=1.0 / math.sqrt(192.0))
+
+
+@pytest.mark.parametrize("Hq,Hkv,P", [(16, 16, 64), (16, 4, 16), (8, 1, 8)])
+def test_f2_mixed_forward(Hq, Hkv, P):
+    # decode, a 3-token request, extend, prefill and a prefill over 3 row blocks (G = 1)
+    b = workload.make_batch([1, 3, 300, 40, 520], [900, 50, 700, 0, 0], num_q_heads=Hq,
+                            num_kv_heads=Hkv, page_size=P, seed=900 + Hq + Hkv + P, **F2)
+    forward_parity(b, "bf16 Dqk 192 Dv 128 Hq=%d Hkv=%d P=%d" % (Hq, Hkv, P))
+
+
+def test_f2_all_128_heads():
+    b = workload.make_batch([1, 130, 64], [200, 100, 0], num_q_heads=128, num_kv_heads=128,
+                            page_size=64, seed=931, **F2)
+    forward_parity(b, "bf16 Dqk 192 Dv 128, 128 heads")
+
+
+def test_f2_deepseek_prefill_scaled():
+    b = workload.deepseek_mha_prefill(1, n_extend=2, n_prefill=2, ext_q=(200, 400),
+                                      ext_c=(1000, 3000), pre_q=(300, 700), heads=16)
+    forward_parity(b, "deepseek non-absorbed prefill + extend, scaled, 16 heads")
+
+
+def test_f2_decode_only_batch():
+    b = workload.make_batch([1] * 7, [5, 900, 3000, 64, 127, 2000, 40], num_q_heads=32,
+                            num_kv_heads=8, page_size=16, seed=941, **F2)
+    forward_parity(b, "bf16 Dqk 192 Dv 128 decode-only")
+
+
+@pytest.mark.parametrize("mask,prefixes,with_sinks", [(pa.PA_MASK_FULL, None, False),
+                                                      (pa.PA_MASK_PREFIX, [0, 41, 750, 20, 100], True),
+                                                      (pa.PA_MASK_CAUSAL, None, True)])
+def test_f2_masks_and_sinks(mask, prefixes, with_sinks):
+    b = workload.make_batch(MASK_Q, MASK_C, num_q_heads=16, num_kv_heads=8, page_size=16,
+                            seed=951, **F2)
+    masked_parity(b, mask, prefixes, "f2 mask %d sinks %s" % (mask, with_sinks),
+                  sinks=sink_logits(16, 5) if with_sinks else None)
+
+
+def test_f2_chunked_and_routed():
+    b = workload.make_batch([200, 1, 64], [20000, 30000, 9000], num_q_heads=4, num_kv_heads=4,
+                            page_size=16, seed=961, **F2)
+    chunked_parity(b, 4096, "f2 chunked long extend")
+    forward_parity(b, "f2 pa_forward routed through chunks")
+
+
+@pytest.mark.parametrize("Hq,Hkv,S", [(16, 4, 5), (16, 16, 1), (64, 2, 3)])
+def test_f2_decode_split(Hq, Hkv, S):
+    b = workload.make_batch([1] * 5, [300, 1, 2000, 77, 900], num_q_heads=Hq, num_kv_heads=Hkv,
+                            page_size=16, seed=971 + S, **F2)
+    g = b.to(DEV)
+    say("case f2 decode split Hq=%d Hkv=%d S=%d" % (Hq, Hkv, S))
+    po, pl = pa.pa_decode_split(g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens, b.scale, S)
+    lse = torch.empty(pl.shape[:2], dtype=torch.float32, device=DEV)
+    out = pa.pa_merge_lse(po, pl, lse=lse)
+    torch.cuda.synchronize()
+    rpo, rpl = oracle.decode_split(b.q, b.k_cache, b.v_cache, b.block_table, b.seq_lens, b.scale,
+                                   S, b.num_kv_heads, head_dim_v=128)
+    check_out(po.cpu().numpy(), rpo, torch.bfloat16, "f2 partials")
+    check_lse(pl.cpu().numpy(), rpl, "f2 partial lse")
+    ref, rlse = oracle_forward(b)
+    check_out(out.float().cpu().numpy(), ref, torch.bfloat16, "f2 split merged")
+    check_lse(lse.cpu().numpy(), rlse, "f2 split merged")
 
 
 def test_edge_empty_requests_single_keys_and_exact_pages():
