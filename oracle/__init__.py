@@ -30,6 +30,7 @@ _LIB = os.path.join(_HERE, "libpa_oracle.so")
 F32, BF16 = 0, 1
 LAYOUT_MHA, LAYOUT_MLA = 0, 1
 MASK_CAUSAL, MASK_FULL, MASK_PREFIX = 0, 1, 2
+ALIBI_NONE, ALIBI_LINEAR, ALIBI_SQRT = 0, 1, 2
 _ERRORS = {1: "invalid sizes", 2: "invalid request data (lengths or block table)",
            3: "out of memory"}
 
@@ -57,7 +58,8 @@ def _load():
             lib.orc_attention.argtypes = [p, p, p, i32, p, p, p] + [i32] * 9 + [f32, p, p, p, i32]
             lib.orc_attention.restype = i32
             lib.orc_attention_masked.argtypes = [p, p, p, i32, p, p, p] + [i32] * 9 + [f32, i32, p,
-                                                                                     p, p, p, p, i32]
+                                                                                     p, p, i32, p, p,
+                                                                                     p, i32]
             lib.orc_attention_masked.restype = i32
             lib.orc_decode_split.argtypes = [p, p, p, i32, p, p] + [i32] * 9 + [f32, i32, p, p, i32]
             lib.orc_decode_split.restype = i32
@@ -126,10 +128,12 @@ def _check(rc):
 
 def attention(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale,
               num_kv_heads, head_dim_v=None, layout=LAYOUT_MHA, rows=None,
-              nthreads=None, mask=MASK_CAUSAL, prefix_lens=None, sinks=None):
+              nthreads=None, mask=MASK_CAUSAL, prefix_lens=None, sinks=None,
+              alibi_slopes=None, alibi_mode=ALIBI_NONE):
     """Paged attention over a varlen batch, in fp64: causal, or MASK_FULL / MASK_PREFIX
     (prefix_lens int32 [B]) as defined in pa_oracle.c; sinks: optional float32 [Hq]
-    sink logits.
+    sink logits; alibi_mode ALIBI_LINEAR / ALIBI_SQRT with alibi_slopes float32 [Hq]:
+    the ALiBi bias of pa_oracle.c.
 
     q: [T, Hq, Dqk]; k_cache / v_cache in the layouts of pa_oracle.c
     (for LAYOUT_MLA pass the latent cache as both); block_table [B, max_pages];
@@ -159,7 +163,7 @@ def attention(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale
     if rows is not None:
         sel = np.ascontiguousarray(np.asarray(rows, dtype=np.uint8).reshape(T, Hq))
     nt = max_threads() if nthreads is None else int(nthreads)
-    if mask == MASK_CAUSAL and prefix_lens is None and sinks is None:
+    if mask == MASK_CAUSAL and prefix_lens is None and sinks is None and alibi_mode == ALIBI_NONE:
         rc = lib.orc_attention(_ptr(qa), _ptr(ka), _ptr(va), dt, _ptr(bt), _ptr(sl), _ptr(qs),
                                B, Hq, int(num_kv_heads), Dqk, Dv, P, num_pages, bt.shape[1],
                                layout, float(scale), _ptr(sel), _ptr(out), _ptr(lse), nt)
@@ -174,10 +178,16 @@ def attention(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale
             snk = np.ascontiguousarray(np.asarray(sinks, dtype=np.float32))
             if snk.shape != (Hq,):
                 raise ValueError("sinks must have Hq entries")
+        slp = None
+        if alibi_mode != ALIBI_NONE:
+            slp = np.ascontiguousarray(np.asarray(alibi_slopes, dtype=np.float32))
+            if slp.shape != (Hq,):
+                raise ValueError("alibi_slopes must have Hq entries")
         rc = lib.orc_attention_masked(_ptr(qa), _ptr(ka), _ptr(va), dt, _ptr(bt), _ptr(sl),
                                       _ptr(qs), B, Hq, int(num_kv_heads), Dqk, Dv, P, num_pages,
                                       bt.shape[1], layout, float(scale), int(mask), _ptr(pfx),
-                                      _ptr(snk), _ptr(sel), _ptr(out), _ptr(lse), nt)
+                                      _ptr(snk), _ptr(slp), int(alibi_mode), _ptr(sel),
+                                      _ptr(out), _ptr(lse), nt)
     _check(rc)
     return out, lse
 

@@ -36,6 +36,14 @@
  *     for GPT-OSS without a formula): a per-query-head logit sinks[h] joins
  *     the softmax of every row of head h as one more key whose value is
  *     zero, so it only adds e^{sinks[h]} to the denominator.
+ *   - ALiBi and its square-root variant (Triton deep dive, same list of use
+ *     cases: "ALiBi sqrt", used by a StepFun audio model; no formula there).
+ *     Reading: ALiBi as published by Press et al. ("Train Short, Test Long",
+ *     2022) adds -m_h * (p - t) to the logit of the query at position p and
+ *     the key at position t, with a fixed slope m_h per query head; the sqrt
+ *     variant adds -m_h * sqrt(p - t).  |p - t| is used, so that keys after
+ *     the query (full and prefix masks) are penalised by their distance too.
+ *     The slopes are an input (alibi_slopes[Hq]).
  *   - Split-KV partials and their log-sum-exp merge (Triton deep dive,
  *     section "Parallel tiled softmax (3D kernel)"; ROCm backends, bullet
  *     "Chunked context processing"): the key range is cut into contiguous
@@ -67,6 +75,7 @@
 enum { ORC_F32 = 0, ORC_BF16 = 1 };
 enum { ORC_LAYOUT_MHA = 0, ORC_LAYOUT_MLA = 1 };
 enum { ORC_MASK_CAUSAL = 0, ORC_MASK_FULL = 1, ORC_MASK_PREFIX = 2 };
+enum { ORC_ALIBI_NONE = 0, ORC_ALIBI_LINEAR = 1, ORC_ALIBI_SQRT = 2 };
 enum { ORC_OK = 0, ORC_ERR_ARG = 1, ORC_ERR_DATA = 2, ORC_ERR_NOMEM = 3 };
 
 /* Read element idx of an array of the given dtype, widened to double. */
@@ -114,14 +123,27 @@ static int gather(const void* kc, const void* vc, int dtype, int layout,
 }
 
 /*
+ * ALiBi bias of the key at position t for the query at position pos:
+ * -slope * |pos - t| (linear) or -slope * sqrt(|pos - t|) (sqrt); 0 without.
+ */
+static double alibi_bias(int mode, double slope, int pos, int t) {
+  const double dist = fabs((double)pos - (double)t);
+  if (mode == ORC_ALIBI_LINEAR) return -slope * dist;
+  if (mode == ORC_ALIBI_SQRT) return -slope * sqrt(dist);
+  return 0.0;
+}
+
+/*
  * Textbook attention of one query row over dense keys [t0, t1):
- *   s_t = sigma * q . k_t,  m = max s_t,  l = sum exp(s_t - m),
- *   out = sum exp(s_t - m) v_t / l,  lse = m + ln l.
+ *   s_t = sigma * q . k_t + bias_t,  m = max s_t,  l = sum exp(s_t - m),
+ *   out = sum exp(s_t - m) v_t / l,  lse = m + ln l,
+ * with bias_t = alibi_bias(alibi_mode, slope, pos, t).
  * An empty range gives out = 0 and lse = -inf.  `s` is scratch of size t1.
  */
-static void attend(const double* qrow, const double* Kd, const double* Vd,
-                   int t0, int t1, int Dqk, int Dv, double sigma, double* s,
-                   double* out, double* lse) {
+static void attend_biased(const double* qrow, const double* Kd, const double* Vd,
+                          int t0, int t1, int Dqk, int Dv, double sigma,
+                          int alibi_mode, double slope, int pos, double* s,
+                          double* out, double* lse) {
   for (int d = 0; d < Dv; ++d) out[d] = 0.0;
   if (t1 <= t0) {
     *lse = -INFINITY;
@@ -131,7 +153,7 @@ static void attend(const double* qrow, const double* Kd, const double* Vd,
   for (int t = t0; t < t1; ++t) {
     double dot = 0.0;
     for (int d = 0; d < Dqk; ++d) dot += qrow[d] * Kd[(size_t)t * Dqk + d];
-    s[t] = sigma * dot;
+    s[t] = sigma * dot + alibi_bias(alibi_mode, slope, pos, t);
     if (s[t] > m) m = s[t];
   }
   double l = 0.0;
@@ -142,6 +164,13 @@ static void attend(const double* qrow, const double* Kd, const double* Vd,
   }
   for (int d = 0; d < Dv; ++d) out[d] /= l;
   *lse = m + log(l);
+}
+
+/* attend_biased without a bias. */
+static void attend(const double* qrow, const double* Kd, const double* Vd,
+                   int t0, int t1, int Dqk, int Dv, double sigma, double* s,
+                   double* out, double* lse) {
+  attend_biased(qrow, Kd, Vd, t0, t1, Dqk, Dv, sigma, ORC_ALIBI_NONE, 0.0, 0, s, out, lse);
 }
 
 static int check_common(int B, int Hq, int Hkv, int Dqk, int Dv, int P,
@@ -157,7 +186,9 @@ static int check_common(int B, int Hq, int Hkv, int Dqk, int Dv, int P,
 
 /*
  * Paged attention over a varlen continuous batch, causal or with one of the
- * other masks above (mask; prefix_lens [B] is read for ORC_MASK_PREFIX only).
+ * other masks above (mask; prefix_lens [B] is read for ORC_MASK_PREFIX only),
+ * with optional sink logits (sinks [Hq] or NULL) and an optional ALiBi bias
+ * (alibi_mode ORC_ALIBI_LINEAR / ORC_ALIBI_SQRT with alibi_slopes [Hq]).
  *   q        [T, Hq, Dqk] (dtype), T = qsl[B]
  *   out      [T, Hq, Dv] double;  lse [T, Hq] double (may be NULL)
  *   row_sel  optional [T * Hq] bytes; when given, only rows with a nonzero
@@ -170,6 +201,7 @@ int orc_attention_masked(const void* q, const void* kc, const void* vc, int dtyp
                          const int32_t* qsl, int B, int Hq, int Hkv, int Dqk, int Dv,
                          int P, int num_pages, int max_pages, int layout, float scale,
                          int mask, const int32_t* prefix_lens, const float* sinks,
+                         const float* alibi_slopes, int alibi_mode,
                          const uint8_t* row_sel, double* out, double* lse,
                          int nthreads) {
   int rc = check_common(B, Hq, Hkv, Dqk, Dv, P, max_pages, layout);
@@ -177,6 +209,10 @@ int orc_attention_masked(const void* q, const void* kc, const void* vc, int dtyp
   if (mask != ORC_MASK_CAUSAL && mask != ORC_MASK_FULL && mask != ORC_MASK_PREFIX)
     return ORC_ERR_ARG;
   if (mask == ORC_MASK_PREFIX && !prefix_lens) return ORC_ERR_ARG;
+  if (alibi_mode != ORC_ALIBI_NONE && alibi_mode != ORC_ALIBI_LINEAR &&
+      alibi_mode != ORC_ALIBI_SQRT)
+    return ORC_ERR_ARG;
+  if (alibi_mode != ORC_ALIBI_NONE && !alibi_slopes) return ORC_ERR_ARG;
   const int g = Hq / Hkv;
   const double sigma = (double)scale;
   int err = ORC_OK;
@@ -234,8 +270,9 @@ int orc_attention_masked(const void* q, const void* kc, const void* vc, int dtyp
           if (mask == ORC_MASK_PREFIX && prefix_lens[b] > end)
             end = prefix_lens[b] < L ? prefix_lens[b] : L;
           double l_out;
-          attend(qrow, Kd, Vd, 0, end, Dqk, Dv, sigma, s,
-                 out + ((size_t)i * Hq + hh) * Dv, &l_out);
+          attend_biased(qrow, Kd, Vd, 0, end, Dqk, Dv, sigma, alibi_mode,
+                        alibi_mode ? (double)alibi_slopes[hh] : 0.0, pos, s,
+                        out + ((size_t)i * Hq + hh) * Dv, &l_out);
           if (sinks) {
             /* one more logit, sinks[hh], with a zero value: the row's weights
                shrink by e^{lse} / (e^{lse} + e^{sink}) */
@@ -266,8 +303,8 @@ int orc_attention(const void* q, const void* kc, const void* vc, int dtype,
                   int nthreads) {
   return orc_attention_masked(q, kc, vc, dtype, block_table, seq_lens, qsl, B,
                               Hq, Hkv, Dqk, Dv, P, num_pages, max_pages,
-                              layout, scale, ORC_MASK_CAUSAL, NULL, NULL, row_sel,
-                              out, lse, nthreads);
+                              layout, scale, ORC_MASK_CAUSAL, NULL, NULL, NULL,
+                              ORC_ALIBI_NONE, row_sel, out, lse, nthreads);
 }
 
 /*

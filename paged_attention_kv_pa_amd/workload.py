@@ -330,6 +330,24 @@ def deepseek_mha_prefill(case: int = 0, device="cpu", n_extend: int = 8, n_prefi
                       name="deepseek_mha_prefill/%d" % case)
 
 
+def alibi_slopes(num_heads: int) -> List[float]:
+    """The per-head ALiBi slopes published with ALiBi (Press et al., "Train Short,
+    Test Long", 2022): for n a power of two, the geometric sequence
+    2^(-8 (h + 1) / n), h = 0 .. n - 1; for other n, the n' = 2^floor(log2 n)
+    slopes of n' heads followed by every other slope (the 1st, 3rd, ...) of the
+    2 n' sequence, n - n' of them.  Inputs of the ALiBi calls (the kernels take
+    any slopes)."""
+    def pow2(n):
+        return [2.0 ** (-8.0 * (h + 1) / n) for h in range(n)]
+    n = int(num_heads)
+    if n <= 0:
+        return []
+    base = 1 << (n.bit_length() - 1)
+    if base == n:
+        return pow2(n)
+    return pow2(base) + pow2(2 * base)[0::2][:n - base]
+
+
 def algorithmic_bytes(b: Batch) -> int:
     """Bytes a perfect kernel moves: each visible K/V element once (the MLA latent
     once), q, out, lse (fp32) and 4 bytes per used block-table entry."""

@@ -56,9 +56,41 @@ def gqa_two_decodes():
                 query_start_loc=[0, 1, 2], expected_out=out, expected_lse=lse)
 
 
+def alibi_extend(mode):
+    # ALiBi reading: the logit of the key at position t for the query at position
+    # p gets -m_h |p - t| (linear) or -m_h sqrt|p - t| (sqrt).  One request, 2 new
+    # tokens on 1 cached key (positions 1 and 2), 2 query heads on 1 KV head with
+    # slopes m = 0.5 and 1.0, every query 0 (so q . k = 0 and the weights are the
+    # bias terms alone), values 8, 4, 2 (value dim 1).  Weights per visible key:
+    #   token 0 (p = 1), keys 0, 1:    e^{-m d(1)}, 1         (d(1) = 1 both modes)
+    #   token 1 (p = 2), keys 0, 1, 2: e^{-m d(2)}, e^{-m}, 1 (d(2) = 2 or sqrt 2)
+    # out = sum w v / sum w, lse = ln sum w.  Page size 2: logical page 0 (tokens
+    # 0, 1) -> physical 1, logical page 1 (token 2) -> physical 0.
+    d2 = 2.0 if mode == "linear" else math.sqrt(2.0)
+    vals = [8.0, 4.0, 2.0]
+    out, lse = [], []
+    for p, n in ((1, 2), (2, 3)):
+        orow, lrow = [], []
+        for m in (0.5, 1.0):
+            w = [math.exp(-m * 1.0), 1.0] if p == 1 else [math.exp(-m * d2), math.exp(-m), 1.0]
+            z = sum(w)
+            orow.append([sum(wi * vi for wi, vi in zip(w, vals[:n])) / z])
+            lrow.append(math.log(z))
+        out.append(orow)
+        lse.append(lrow)
+    k_cache = [[[[5, 6], [X, X]]], [[[1, 2], [3, 4]]]]
+    v_cache = [[[[2, X]]], [[[8, 4]]]]
+    return dict(name="alibi_%s_extend_two_heads" % mode, page_size=2, num_q_heads=2,
+                num_kv_heads=1, scale=1.0, q=[[[0, 0], [0, 0]], [[0, 0], [0, 0]]],
+                k_cache=k_cache, v_cache=v_cache, block_table=[[1, 0]], seq_lens=[3],
+                query_start_loc=[0, 2], alibi_mode=mode, alibi_slopes=[0.5, 1.0],
+                expected_out=out, expected_lse=lse)
+
+
 if __name__ == "__main__":
     doc = {"source": "hand-derived closed forms; the pages print no worked example",
-           "examples": [three_token_prefill(), gqa_two_decodes()]}
+           "examples": [three_token_prefill(), gqa_two_decodes(), alibi_extend("linear"),
+                        alibi_extend("sqrt")]}
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "worked_examples.json")
     with open(path, "w") as f:
         json.dump(doc, f, indent=1)

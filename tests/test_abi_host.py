@@ -281,3 +281,13 @@ def test_workload_shapes():
     assert int(m.query_start_loc[-1]) == m.num_tokens == m.q.shape[0]
     d = workload.deepseek_mla(0, batch=2, lo=70, hi=90)
     assert d.k_cache is d.v_cache and d.k_cache.shape[1:] == (64, 576)
+
+
+def test_standard_alibi_slopes():
+    # the geometric slopes published with ALiBi: 8 heads 1/2 .. 1/256, 16 heads
+    # 2^-0.5 .. 2^-8, and for 12 heads the 8-head slopes then 2^-0.5, 2^-1.5, 2^-2.5, 2^-3.5
+    assert workload.alibi_slopes(8) == [2.0 ** -k for k in range(1, 9)]
+    assert workload.alibi_slopes(16) == [2.0 ** (-0.5 * k) for k in range(1, 17)]
+    assert workload.alibi_slopes(12) == [2.0 ** -k for k in range(1, 9)] + \
+        [2.0 ** -0.5, 2.0 ** -1.5, 2.0 ** -2.5, 2.0 ** -3.5]
+    assert workload.alibi_slopes(1) == [2.0 ** -8]

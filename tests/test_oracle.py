@@ -461,6 +461,86 @@ def test_invalid_inputs_are_rejected():
         oracle.attention(c["q"], c["kc"], c["vc"], c["bt"], c["seq"], c["qsl"], 0.3, 3)
 
 
+def _alibi_bias(nq, L, slopes, mode, vis):
+    """[Hq, nq, L] additive bias for torch SDPA: the ALiBi term on visible keys
+    (positions: new token j at L - nq + j), -inf elsewhere."""
+    pos = (L - nq + torch.arange(nq, dtype=torch.float64)).unsqueeze(1)
+    dist = (pos - torch.arange(L, dtype=torch.float64).unsqueeze(0)).abs()
+    f = dist.sqrt() if mode == oracle.ALIBI_SQRT else dist
+    m = torch.as_tensor(np.asarray(slopes, np.float64)).view(-1, 1, 1)
+    bias = -m * f.unsqueeze(0)
+    return bias.masked_fill(~vis.unsqueeze(0), float("-inf"))
+
+
+def _sdpa_bias(q, K, V, scale, bias):
+    Hq, Hkv = q.shape[1], K.shape[1]
+    qd = q.double().permute(1, 0, 2).unsqueeze(0)
+    kd = K.double().permute(1, 0, 2).unsqueeze(0)
+    vd = V.double().permute(1, 0, 2).unsqueeze(0)
+    out = torch.nn.functional.scaled_dot_product_attention(qd, kd, vd, attn_mask=bias.unsqueeze(0),
+                                                           scale=scale, enable_gqa=True)
+    s = torch.matmul(qd, kd.repeat_interleave(Hq // Hkv, dim=1).transpose(-1, -2)) * scale
+    lse = torch.logsumexp(s + bias.unsqueeze(0), dim=-1)
+    return out[0].permute(1, 0, 2).numpy(), lse[0].permute(1, 0).numpy()
+
+
+ALIBI_SLOPES = np.array([0.5, 0.0625, 1.5, 0.25], dtype=np.float32)
+
+
+@pytest.mark.parametrize("mode", [oracle.ALIBI_LINEAR, oracle.ALIBI_SQRT])
+@pytest.mark.parametrize("mask,prefix", [(oracle.MASK_CAUSAL, None), (oracle.MASK_FULL, None),
+                                         (oracle.MASK_PREFIX, [2, 13, 13, 6, 33, 12])])
+def test_alibi_matches_sdpa_with_an_additive_bias(mode, mask, prefix):
+    """ALiBi (linear and sqrt) under every mask: torch SDPA with the bias as an
+    additive attention mask on dense, unpaged inputs."""
+    c = _build_case(53, MASK_SPECS, 4, 2, 8, 8, 4)
+    out, lse = oracle.attention(c["q"], c["kc"], c["vc"], c["bt"], c["seq"], c["qsl"], 0.45, 2,
+                                head_dim_v=8, mask=mask,
+                                prefix_lens=None if prefix is None else np.asarray(prefix, np.int32),
+                                alibi_slopes=ALIBI_SLOPES, alibi_mode=mode)
+    i0 = 0
+    for i, ((nq, ctx), q, K, V) in enumerate(zip(MASK_SPECS, c["qs"], c["Ks"], c["Vs"])):
+        L = nq + ctx
+        if mask == oracle.MASK_FULL:
+            vis = torch.ones(nq, L, dtype=torch.bool)
+        elif mask == oracle.MASK_PREFIX:
+            vis = prefix_mask(nq, L, prefix[i])
+        else:
+            vis = torch.arange(L).unsqueeze(0) <= (L - nq + torch.arange(nq)).unsqueeze(1)
+        ro, rl = _sdpa_bias(q, K, V, float(np.float32(0.45)), _alibi_bias(nq, L, ALIBI_SLOPES, mode, vis))
+        np.testing.assert_allclose(out[i0:i0 + nq], ro, atol=TOL, rtol=0)
+        np.testing.assert_allclose(lse[i0:i0 + nq], rl, atol=TOL, rtol=0)
+        i0 += nq
+
+
+def test_alibi_zero_slopes_change_nothing():
+    c = _build_case(55, MASK_SPECS, 4, 2, 8, 8, 4)
+    a = oracle.attention(c["q"], c["kc"], c["vc"], c["bt"], c["seq"], c["qsl"], 0.45, 2, head_dim_v=8)
+    for mode in (oracle.ALIBI_LINEAR, oracle.ALIBI_SQRT):
+        b = oracle.attention(c["q"], c["kc"], c["vc"], c["bt"], c["seq"], c["qsl"], 0.45, 2,
+                             head_dim_v=8, alibi_slopes=np.zeros(4, np.float32), alibi_mode=mode)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_alibi_decode_equals_last_prefill_row():
+    """Positions under ALiBi: a decode over L keys is the last row of a prefill of L
+    tokens, and an extend's rows are the matching prefill rows."""
+    gen = torch.Generator().manual_seed(57)
+    Hq, Hkv, D, P = 4, 2, 8, 4
+    q, K, V = dense_request(gen, 10, 0, Hq, Hkv, D, D, torch.float32)
+    kc, vc, bt = scatter_pages([K], [V], P, gen)
+    for mode in (oracle.ALIBI_LINEAR, oracle.ALIBI_SQRT):
+        def run(qpart, nq, L):
+            return oracle.attention(qpart, kc, vc, bt, np.array([L], np.int32),
+                                    np.array([0, nq], np.int32), 0.4, Hkv,
+                                    alibi_slopes=ALIBI_SLOPES, alibi_mode=mode)
+        full_o, full_l = run(q, 10, 10)
+        dec_o, dec_l = run(q[9:], 1, 10)
+        assert np.array_equal(dec_o[0], full_o[9]) and np.array_equal(dec_l[0], full_l[9])
+        ext_o, ext_l = run(q[6:], 4, 10)
+        assert np.array_equal(ext_o, full_o[6:]) and np.array_equal(ext_l, full_l[6:])
+
+
 def _load_golden():
     with open(os.path.join(HERE, "golden", "worked_examples.json")) as f:
         return json.load(f)["examples"]
@@ -476,7 +556,10 @@ def test_hand_worked_examples(ex):
     bt = np.array(ex["block_table"], dtype=np.int32)
     seq = np.array(ex["seq_lens"], dtype=np.int32)
     qsl = np.array(ex["query_start_loc"], dtype=np.int32)
+    mode = {"linear": oracle.ALIBI_LINEAR, "sqrt": oracle.ALIBI_SQRT}.get(ex.get("alibi_mode"),
+                                                                        oracle.ALIBI_NONE)
+    slopes = np.array(ex["alibi_slopes"], np.float32) if mode != oracle.ALIBI_NONE else None
     out, lse = oracle.attention(q, kc, vc, bt, seq, qsl, ex["scale"], Hkv,
-                                head_dim_v=vc.shape[2])
+                                head_dim_v=vc.shape[2], alibi_slopes=slopes, alibi_mode=mode)
     np.testing.assert_allclose(out, np.array(ex["expected_out"]), atol=1e-12, rtol=0)
     np.testing.assert_allclose(lse, np.array(ex["expected_lse"]), atol=1e-12, rtol=0)

@@ -30,7 +30,16 @@ MUTANTS = {
                                 "            end = prefix_lens[b] < L ? prefix_lens[b] : L - 1;"),
     "prefix_off_by_one": ("if (mask == ORC_MASK_PREFIX && prefix_lens[b] > end)\n            end = prefix_lens[b] < L ? prefix_lens[b] : L;",
                           "if (mask == ORC_MASK_PREFIX && prefix_lens[b] > end)\n            end = prefix_lens[b] + 1 < L ? prefix_lens[b] + 1 : L;"),
-    "scale_dropped": ("s[t] = sigma * dot;", "s[t] = dot;"),
+    "scale_dropped": ("s[t] = sigma * dot + alibi_bias(", "s[t] = dot + alibi_bias("),
+    "alibi_sign_flipped": ("if (mode == ORC_ALIBI_LINEAR) return -slope * dist;",
+                           "if (mode == ORC_ALIBI_LINEAR) return slope * dist;"),
+    "alibi_sqrt_dropped": ("if (mode == ORC_ALIBI_SQRT) return -slope * sqrt(dist);",
+                           "if (mode == ORC_ALIBI_SQRT) return -slope * dist;"),
+    "alibi_distance_off_by_one": ("fabs((double)pos - (double)t)", "fabs((double)pos - (double)t + 1.0)"),
+    "alibi_slope_of_kv_head": ("alibi_mode ? (double)alibi_slopes[hh] : 0.0",
+                               "alibi_mode ? (double)alibi_slopes[h] : 0.0"),
+    "alibi_token_index_for_position": ("alibi_mode ? (double)alibi_slopes[hh] : 0.0, pos, s,",
+                                       "alibi_mode ? (double)alibi_slopes[hh] : 0.0, j, s,"),
     "gqa_head_ignored": ("key_index(layout, page, slot, h, d, Hkv, P, Dqk)",
                          "key_index(layout, page, slot, 0, d, Hkv, P, Dqk)"),
     "value_layout_transposed": ("return (((size_t)page * Hkv + head) * Dv + d) * P + slot;",
@@ -68,12 +77,19 @@ def _battery():
         out.append(("prefix", lambda p=pf: pins.test_prefix_mask_matches_sdpa(p)))
     for C in (1, 3, 4, 16, 64):
         out.append(("chunked", lambda c=C: pins.test_chunked_then_merge_equals_unchunked(c)))
+    for mode in (real_oracle.ALIBI_LINEAR, real_oracle.ALIBI_SQRT):
+        for mask, pf in ((real_oracle.MASK_CAUSAL, None), (real_oracle.MASK_FULL, None),
+                         (real_oracle.MASK_PREFIX, [2, 13, 13, 6, 33, 12])):
+            out.append(("alibi", lambda m=mode, k=mask, p=pf:
+                        pins.test_alibi_matches_sdpa_with_an_additive_bias(m, k, p)))
     for name in ("test_page_permutation_is_bitwise_invariant",
                  "test_split_partials_match_sdpa_on_their_ranges",
                  "test_chunked_partials_match_sdpa_on_visible_keys",
                  "test_full_mask_equals_unmasked_sdpa",
                  "test_mask_special_cases_reduce_to_causal_or_full",
                  "test_sinks_match_sdpa_with_an_extra_zero_key",
+                 "test_alibi_zero_slopes_change_nothing",
+                 "test_alibi_decode_equals_last_prefill_row",
                  "test_minus_infinite_sinks_change_nothing",
                  "test_constant_value_rows_sum_to_one", "test_length_one_context_returns_v0",
                  "test_equal_keys_give_mean_of_visible_values",
