@@ -99,6 +99,19 @@ typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
  */
 typedef enum pa_mask { PA_MASK_CAUSAL = 0, PA_MASK_FULL = 1, PA_MASK_PREFIX = 2 } pa_mask;
 
+/*
+ * Position bias of pa_forward_masked ([TDD] section on the backend's use
+ * cases, which names "ALiBi sqrt", used by a StepFun audio model, without a
+ * formula; read as ALiBi, Press et al., "Train Short, Test Long", 2022).  With
+ * p the query's position and t the key's, the scaled score of query head h
+ * gets
+ *   PA_ALIBI_LINEAR  - alibi_slopes[h] * |p - t|
+ *   PA_ALIBI_SQRT    - alibi_slopes[h] * sqrt(|p - t|)
+ * before the softmax (the slopes are the caller's: ALiBi's own are the
+ * geometric sequence 2^(-8 (h + 1) / Hq) for Hq a power of two).
+ */
+typedef enum pa_alibi { PA_ALIBI_NONE = 0, PA_ALIBI_LINEAR = 1, PA_ALIBI_SQRT = 2 } pa_alibi;
+
 /* Shapes and host-side capacities of one call.  Capacities (max_*) size the
  * workspace and the launch grids without reading device memory. */
 typedef struct pa_dims {
@@ -166,14 +179,21 @@ PA_API pa_status pa_forward(const void* q, const void* k_cache, const void* v_ca
  * the units of the scaled scores, natural log) and a zero value, so
  *   out = sum_t e^{s_t} v_t / (e^{sinks[h]} + sum_t e^{s_t}),
  *   lse = ln(e^{sinks[h]} + sum_t e^{s_t});  -inf means no sink.
+ * alibi_mode is a pa_alibi; with PA_ALIBI_LINEAR or PA_ALIBI_SQRT,
+ * alibi_slopes is a float32 [Hq] device array of per-head slopes (else it must
+ * be NULL).  ALiBi needs Dqk <= 128 in bf16 (PA_ERR_UNSUPPORTED otherwise); an
+ * ALiBi call always runs on the persistent kernel, also where pa_forward would
+ * take the chunked route.
  * Everything else, including the workspace, is as for pa_forward, which is
- * this call with PA_MASK_CAUSAL and no sinks.  Returns PA_ERR_INVALID_ARG for
- * an unknown mask or a prefix_lens that does not match it.
+ * this call with PA_MASK_CAUSAL, no sinks and no ALiBi.  Returns
+ * PA_ERR_INVALID_ARG for an unknown mask or ALiBi mode, or a prefix_lens or
+ * alibi_slopes that does not match it.
  */
 PA_API pa_status pa_forward_masked(const void* q, const void* k_cache, const void* v_cache,
                                    const int32_t* block_table, const int32_t* seq_lens,
                                    const int32_t* query_start_loc, int32_t mask,
-                                   const int32_t* prefix_lens, const float* sinks, float scale,
+                                   const int32_t* prefix_lens, const float* sinks,
+                                   const float* alibi_slopes, int32_t alibi_mode, float scale,
                                    void* out, float* lse, const pa_dims* dims, void* workspace,
                                    size_t workspace_bytes, void* stream);
 

@@ -6,7 +6,8 @@ declared in ``include/pa.h``.  Functions carry the names of the C entry
 points.  The library is loaded on first use and a missing or unloadable
 library raises — there is no fallback.
 """
-from .binding import (PA_MASK_CAUSAL, PA_MASK_FULL, PA_MASK_PREFIX, PaError, pa_decode_split,
+from .binding import (PA_ALIBI_LINEAR, PA_ALIBI_NONE, PA_ALIBI_SQRT, PA_MASK_CAUSAL, PA_MASK_FULL,
+                      PA_MASK_PREFIX, PaError, pa_decode_split,
                       pa_forward, pa_forward_chunked, pa_forward_masked, pa_forward_noalloc,
                       pa_merge_lse, pa_noalloc_max_workspace,
                       pa_status_string,
@@ -16,6 +17,7 @@ from .binding import (PA_MASK_CAUSAL, PA_MASK_FULL, PA_MASK_PREFIX, PaError, pa_
 __all__ = ["PaError", "pa_forward", "pa_forward_masked", "pa_forward_chunked", "pa_decode_split",
            "pa_forward_noalloc", "pa_noalloc_max_workspace",
            "pa_merge_lse", "PA_MASK_CAUSAL", "PA_MASK_FULL", "PA_MASK_PREFIX",
+           "PA_ALIBI_NONE", "PA_ALIBI_LINEAR", "PA_ALIBI_SQRT",
            "mla_decode",
            "pa_workspace_size", "mla_workspace_size", "pa_validate", "pa_status_string",
            "library", "library_path", "make_dims"]

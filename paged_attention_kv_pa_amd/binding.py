@@ -60,7 +60,8 @@ def library():
             lib.pa_workspace_size.restype = sz
             lib.pa_forward.argtypes = [p, p, p, p, p, p, f32, p, p, dp, p, sz, p]
             lib.pa_forward.restype = i32
-            lib.pa_forward_masked.argtypes = [p, p, p, p, p, p, i32, p, p, f32, p, p, dp, p, sz, p]
+            lib.pa_forward_masked.argtypes = [p, p, p, p, p, p, i32, p, p, p, i32, f32, p, p, dp, p,
+                                              sz, p]
             lib.pa_forward_masked.restype = i32
             lib.pa_forward_noalloc.argtypes = [p, p, p, p, p, p, f32, p, p, dp, p]
             lib.pa_forward_noalloc.restype = i32
@@ -184,6 +185,7 @@ def mla_workspace_size(dims: PaDims, num_splits: int = 0) -> int:
 
 
 PA_MASK_CAUSAL, PA_MASK_FULL, PA_MASK_PREFIX = 0, 1, 2
+PA_ALIBI_NONE, PA_ALIBI_LINEAR, PA_ALIBI_SQRT = 0, 1, 2
 
 
 def pa_forward(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale, out=None,
@@ -195,28 +197,36 @@ def pa_forward(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scal
     Returns out ([T, Hq, D], allocated if not given).
     """
     return _forward(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale, out, lse,
-                    workspace, max_seq_len, max_q_len, stream, None, None, None)
+                    workspace, max_seq_len, max_q_len, stream, None, None, None, None, 0)
 
 
 def pa_forward_masked(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale, mask,
                       prefix_lens=None, sinks=None, out=None, lse=None, workspace=None,
-                      max_seq_len=None, max_q_len=None, stream=None):
+                      max_seq_len=None, max_q_len=None, stream=None, alibi_slopes=None,
+                      alibi_mode=None):
     """pa_forward with mask PA_MASK_CAUSAL, PA_MASK_FULL or PA_MASK_PREFIX (prefix_lens
-    int32 [B] on the device for the last) and optional sink logits (float32 [Hq] on the
-    device); see pa_forward_masked in include/pa.h."""
-    if sinks is not None:
-        _need(sinks.dtype == torch.float32 and sinks.is_contiguous() and sinks.device == q.device
-              and tuple(sinks.shape) == (int(q.shape[1]),), "sinks must be contiguous float32 [Hq]")
+    int32 [B] on the device for the last), optional sink logits (float32 [Hq] on the
+    device) and an optional ALiBi bias (alibi_slopes float32 [Hq] on the device;
+    alibi_mode PA_ALIBI_LINEAR or PA_ALIBI_SQRT, default PA_ALIBI_SQRT when slopes are
+    given); see pa_forward_masked in include/pa.h."""
+    for name, t in (("sinks", sinks), ("alibi_slopes", alibi_slopes)):
+        if t is not None:
+            _need(t.dtype == torch.float32 and t.is_contiguous() and t.device == q.device
+                  and tuple(t.shape) == (int(q.shape[1]),), "%s must be contiguous float32 [Hq]" % name)
+    if alibi_mode is None:
+        alibi_mode = PA_ALIBI_NONE if alibi_slopes is None else PA_ALIBI_SQRT
     if prefix_lens is not None:
         _need(prefix_lens.dtype == torch.int32 and prefix_lens.is_contiguous()
               and prefix_lens.device == q.device and tuple(prefix_lens.shape) == (int(seq_lens.shape[0]),),
               "prefix_lens must be contiguous int32 [B] on q's device")
     return _forward(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale, out, lse,
-                    workspace, max_seq_len, max_q_len, stream, int(mask), prefix_lens, sinks)
+                    workspace, max_seq_len, max_q_len, stream, int(mask), prefix_lens, sinks,
+                    alibi_slopes, int(alibi_mode))
 
 
 def _forward(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale, out, lse,
-             workspace, max_seq_len, max_q_len, stream, mask, prefix_lens, sinks):
+             workspace, max_seq_len, max_q_len, stream, mask, prefix_lens, sinks, alibi_slopes,
+             alibi_mode):
     _check_common(q, k_cache, v_cache, block_table, seq_lens)
     _need(query_start_loc.dtype == torch.int32 and query_start_loc.is_contiguous()
           and query_start_loc.device == q.device, "query_start_loc must be contiguous int32 on q's device")
@@ -245,8 +255,8 @@ def _forward(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale,
     else:
         st = library().pa_forward_masked(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
                                          _ptr(seq_lens), _ptr(query_start_loc), mask,
-                                         _ptr(prefix_lens), _ptr(sinks), float(scale), _ptr(out),
-                                         _ptr(lse),
+                                         _ptr(prefix_lens), _ptr(sinks), _ptr(alibi_slopes),
+                                         alibi_mode, float(scale), _ptr(out), _ptr(lse),
                                          ctypes.byref(dims), _ptr(workspace), nbytes,
                                          _stream(q.device, stream))
         _check(st, "pa_forward_masked")

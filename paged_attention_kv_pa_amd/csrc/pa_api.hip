@@ -251,8 +251,8 @@ pa_status pa_forward(const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* query_start_loc, float scale, void* out, float* lse,
                      const pa_dims* d, void* workspace, size_t workspace_bytes, void* stream) {
   return pa_forward_masked(q, k_cache, v_cache, block_table, seq_lens, query_start_loc,
-                           PA_MASK_CAUSAL, nullptr, nullptr, scale, out, lse, d, workspace,
-                           workspace_bytes, stream);
+                           PA_MASK_CAUSAL, nullptr, nullptr, nullptr, PA_ALIBI_NONE, scale, out,
+                           lse, d, workspace, workspace_bytes, stream);
 }
 
 static_assert(PA_MASK_CAUSAL == pa::kMaskCausal && PA_MASK_FULL == pa::kMaskFull &&
@@ -262,7 +262,8 @@ static_assert(PA_MASK_CAUSAL == pa::kMaskCausal && PA_MASK_FULL == pa::kMaskFull
 pa_status pa_forward_masked(const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* block_table, const int32_t* seq_lens,
                             const int32_t* query_start_loc, int32_t mask,
-                            const int32_t* prefix_lens, const float* sinks, float scale,
+                            const int32_t* prefix_lens, const float* sinks,
+                            const float* alibi_slopes, int32_t alibi_mode, float scale,
                             void* out, float* lse, const pa_dims* d, void* workspace,
                             size_t workspace_bytes, void* stream) {
   pa_status st = check_dims(d);
@@ -272,8 +273,13 @@ pa_status pa_forward_masked(const void* q, const void* k_cache, const void* v_ca
   if (mask != PA_MASK_CAUSAL && mask != PA_MASK_FULL && mask != PA_MASK_PREFIX)
     return PA_ERR_INVALID_ARG;
   if ((mask == PA_MASK_PREFIX) != (prefix_lens != nullptr)) return PA_ERR_INVALID_ARG;
+  if (alibi_mode != PA_ALIBI_NONE && alibi_mode != PA_ALIBI_LINEAR && alibi_mode != PA_ALIBI_SQRT)
+    return PA_ERR_INVALID_ARG;
+  if ((alibi_mode != PA_ALIBI_NONE) != (alibi_slopes != nullptr)) return PA_ERR_INVALID_ARG;
+  const bool alibi = alibi_mode != PA_ALIBI_NONE;
   st = check_mha_support(d);
   if (st != PA_OK) return st;
+  if (alibi && d->dtype == PA_BF16 && d->head_dim_qk > 128) return PA_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
   const int G = d->num_q_heads / d->num_kv_heads;
   if (d->num_seqs == 0 || d->num_tokens == 0) return PA_OK;
@@ -302,6 +308,8 @@ pa_status pa_forward_masked(const void* q, const void* k_cache, const void* v_ca
     a.mask = mask;
     a.prefix_lens = prefix_lens;
     a.sinks = sinks;
+    a.alibi = alibi_slopes;
+    a.alibi_sqrt = alibi_mode == PA_ALIBI_SQRT;
     hipError_t e = mark(g_ev_start, s);
     if (e == hipSuccess) e = pa::launch_f32_forward(a, s);
     if (e == hipSuccess) e = mark(g_ev_stop, s);
@@ -316,8 +324,9 @@ pa_status pa_forward_masked(const void* q, const void* k_cache, const void* v_ca
   const pa_status geo_st = fwd_geometry(d, &geo);
   const pa::FwdWorkspace w = pa::fwd_workspace_layout(
       d->num_seqs, d->num_kv_heads, d->head_dim_v, geo_st == PA_OK ? geo.target : INT32_MAX / 4);
+  // (ALiBi calls stay on the persistent path: the chunk kernel has no ALiBi term)
   const ChunkRoute route = chunk_route(d);
-  if (route.on) {
+  if (route.on && !alibi) {
     // few long requests: chunk partials and their merge instead of the
     // persistent kernel, whose prefill items alone could not fill the GPU
     if (!workspace || workspace_bytes < w.total + route.po_bytes + route.pl_bytes)
@@ -416,9 +425,11 @@ pa_status pa_forward_masked(const void* q, const void* k_cache, const void* v_ca
   a.mask = mask;
   a.prefix_lens = prefix_lens;
   a.sinks = sinks;
+  a.alibi = alibi_slopes;
+  a.alibi_sqrt = alibi_mode == PA_ALIBI_SQRT;
   if ((e = mark(g_ev_start, s)) != hipSuccess) return hip_fail(e);
-  e = fused ? pa::launch_mha_forward_fused(a, variant, grid, s)
-            : pa::launch_mha_forward(a, variant, decode_only, grid, s);
+  e = fused ? pa::launch_mha_forward_fused(a, variant, alibi, grid, s)
+            : pa::launch_mha_forward(a, variant, decode_only, alibi, grid, s);
   if (e != hipSuccess) return hip_fail(e);
   if ((e = mark(g_ev_stop, s)) != hipSuccess) return hip_fail(e);
   // the merge also leaves the queue counters zeroed for the next call; one
@@ -448,8 +459,8 @@ pa_status pa_forward_noalloc(const void* q, const void* k_cache, const void* v_c
   st = scratch_address(&ws);
   if (st != PA_OK) return st;
   return pa_forward_masked(q, k_cache, v_cache, block_table, seq_lens, query_start_loc,
-                           PA_MASK_CAUSAL, nullptr, nullptr, scale, out, lse, d, ws,
-                           kScratchBytes, stream);
+                           PA_MASK_CAUSAL, nullptr, nullptr, nullptr, PA_ALIBI_NONE, scale, out,
+                           lse, d, ws, kScratchBytes, stream);
 }
 
 pa_status pa_decode_split(const void* q, const void* k_cache, const void* v_cache,

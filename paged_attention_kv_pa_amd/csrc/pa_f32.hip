@@ -19,9 +19,10 @@ constexpr int kF32MaxD = 256;
 
 // One query row over keys [k0, k1) (k1 already capped by the row's visible limit).
 // Writes out[0..Dv) (normalised) and *lse; an empty range gives 0 and -inf.
-// sink: a sink logit folded into the row (-inf: none).
+// sink: a sink logit folded into the row (-inf: none).  alibi_slope (0: none):
+// the ALiBi term slope * f(|qpos - t|) is subtracted from the score of key t.
 __device__ void f32_row(const F32Args& a, int b, int kvh, const float* qrow, int k0, int k1,
-                        float* out, float* lse_out, float sink) {
+                        float* out, float* lse_out, float sink, float alibi_slope, int qpos) {
   __shared__ float qs[kF32MaxD];
   __shared__ float ps[64];
   const int lane = threadIdx.x;
@@ -42,6 +43,10 @@ __device__ void f32_row(const F32Args& a, int b, int kvh, const float* qrow, int
       float dot = 0.f;
       for (int d = 0; d < Dqk; ++d) dot = fmaf(qs[d], kr[d], dot);
       s = dot * a.scale;
+      if (alibi_slope != 0.f) {
+        const float d = fabsf((float)(qpos - t));
+        s -= alibi_slope * (a.alibi_sqrt ? sqrtf(d) : d);
+      }
     }
     const float mnew = fmaxf(m, wave_max(s));  // finite: key t0 < k1 is valid
     const float alpha = __expf(m - mnew);
@@ -94,7 +99,8 @@ __global__ __launch_bounds__(64) void f32_forward_kernel(F32Args a) {
   const int pfx = a.mask == kMaskPrefix ? a.prefix_lens[b] : 0;
   const int end = min(visible_end(a.mask, L - nq, i - a.qsl[b], pfx), L);
   f32_row(a, b, h / a.G, a.q + row * a.Dqk, 0, end, a.out + row * a.Dv,
-          a.lse ? a.lse + row : nullptr, a.sinks ? a.sinks[h] : kNegInf);
+          a.lse ? a.lse + row : nullptr, a.sinks ? a.sinks[h] : kNegInf,
+          a.alibi ? a.alibi[h] : 0.f, L - nq + (i - a.qsl[b]));
 }
 
 // pa_decode_split, fp32: one workgroup per (request, head, partition).
@@ -109,7 +115,8 @@ __global__ __launch_bounds__(64) void f32_split_kernel(F32Args a) {
   const long long per = (long long)a.P * ((pages + S - 1) / S);
   const long long a0 = per * s, a1 = a0 + per;
   const int t0 = a0 < L ? (int)a0 : L, t1 = a1 < L ? (int)a1 : L;
-  f32_row(a, b, h / a.G, a.q + bh * a.Dqk, t0, t1, a.part_o + id * a.Dv, a.part_lse + id, kNegInf);
+  f32_row(a, b, h / a.G, a.q + bh * a.Dqk, t0, t1, a.part_o + id * a.Dv, a.part_lse + id, kNegInf,
+          0.f, L - 1);
 }
 
 }  // namespace

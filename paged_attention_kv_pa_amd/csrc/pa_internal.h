@@ -39,6 +39,15 @@ __device__ __forceinline__ int visible_end(int mask, int ctx, int t, int prefix)
   return mask == kMaskPrefix ? (prefix > causal ? prefix : causal) : causal;
 }
 
+// ALiBi term of a score, in the units of the raw (unscaled) dot product:
+// m_raw * f(|d|) is subtracted, with m_raw = slope / scale and f the distance
+// (linear) or its square root (sqrt) between the query's and the key's
+// positions.  The caller scales the result like any raw score.
+__device__ __forceinline__ float alibi_term(float m_raw, int sqrt_mode, int dist) {
+  const float d = (float)(dist < 0 ? -dist : dist);
+  return m_raw * (sqrt_mode ? __builtin_amdgcn_sqrtf(d) : d);
+}
+
 // Folds a sink logit s (natural-log units, -inf for none) into a finished
 // row whose keys gave log-sum-exp *lse (-inf if it saw no key): the sink is
 // one more softmax key with a zero value.  Returns the factor the row's
@@ -79,6 +88,8 @@ struct MhaArgs {
   int32_t mask;              // kMaskCausal / kMaskFull / kMaskPrefix
   const int32_t* prefix_lens;  // [B], read under kMaskPrefix only
   const float* sinks;        // [Hq] sink logits or NULL (pa_forward_masked only)
+  const float* alibi;        // [Hq] ALiBi slopes (kernels built with ALiBi only)
+  int32_t alibi_sqrt;        // 1: square root of the distance, 0: the distance
 };
 
 struct PlanArgs {
@@ -110,6 +121,8 @@ struct F32Args {
   int32_t mask;                // forward mode: kMaskCausal / kMaskFull / kMaskPrefix
   const int32_t* prefix_lens;  // [B], read under kMaskPrefix only
   const float* sinks;          // forward mode: [Hq] sink logits or NULL
+  const float* alibi;          // forward mode: [Hq] ALiBi slopes or NULL
+  int32_t alibi_sqrt;          // 1: square root of the distance, 0: the distance
 };
 
 struct MlaArgs {
@@ -141,9 +154,11 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 // variant 0, 1, 2; mha_variant gives -1 for other pairs.
 constexpr int kMhaVariants = 3;
 int mha_variant(int dk, int dv);
-hipError_t launch_mha_forward(const MhaArgs& a, int variant, bool decode_only, int grid,
-                              hipStream_t s);
-hipError_t launch_mha_forward_fused(const MhaArgs& a, int variant, int grid, hipStream_t s);
+// alibi: launch the kernels built with the ALiBi term (variants 0 and 1 only).
+hipError_t launch_mha_forward(const MhaArgs& a, int variant, bool decode_only, bool alibi,
+                              int grid, hipStream_t s);
+hipError_t launch_mha_forward_fused(const MhaArgs& a, int variant, bool alibi, int grid,
+                                    hipStream_t s);
 hipError_t launch_mha_forward_merge(const MhaArgs& a, int Dv, int grid, hipStream_t s);
 hipError_t launch_mha_split(const MhaArgs& a, int variant, hipStream_t s);
 hipError_t launch_mha_chunked(const MhaArgs& a, int variant, hipStream_t s);

@@ -106,7 +106,8 @@ __device__ __forceinline__ void store_lse(const MhaArgs& a, const Dest& dst, int
 // `counter` (may be NULL): thread 0 takes the workgroup's next item index from
 // it once the keys are done, so the round trip overlaps the epilogue; the
 // index is returned in thread 0.
-template <int DK, int DV, int NW>
+// ALIBI: subtract the ALiBi term (alibi_term) from every score.
+template <int DK, int DV, int NW, bool ALIBI = false>
 __device__ int run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest& dst,
                                LdsDecode<DV, NW>& sm, int32_t* counter) {
   constexpr int KS = DK / 32, DT = DV / 16;
@@ -121,6 +122,11 @@ __device__ int run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest&
   const int head = kvh * G + (ridx - tok * G);
   const int pfx = a.mask == kMaskPrefix ? a.prefix_lens[b] : 0;
   const int lim = row_ok ? min(visible_end(a.mask, it.ctx, tok, pfx), kv_end) : it.kv_begin;
+  // ALiBi: the row's slope in raw-score units and its query position
+  float alibi_m = 0.f;
+  if constexpr (ALIBI) alibi_m = row_ok ? a.alibi[head] / a.scale : 0.f;
+  const int qpos = it.ctx + tok;
+  const int alibi_sqrt = ALIBI ? __builtin_amdgcn_readfirstlane(a.alibi_sqrt) : 0;
 
   bf16x8 qf[KS];
   {
@@ -218,7 +224,9 @@ __device__ int run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest&
     for (int j = 0; j < 8; ++j) {
       const int key = t0 + 8 * g + j;
       const float v = s[j >> 2][j & 3];
-      x[j] = key < lim ? v : kNegInf;
+      float vb = v;
+      if constexpr (ALIBI) vb -= alibi_term(alibi_m, alibi_sqrt, qpos - key);
+      x[j] = key < lim ? vb : kNegInf;
     }
     float tmax = x[0];
 #pragma unroll
@@ -414,7 +422,8 @@ struct alignas(16) LdsPrefill {
   char ring[PrefillLayout<DK, DV>::kRingBytes];
 };
 
-template <int DK, int DV>
+// ALIBI: subtract the ALiBi term (alibi_term) from every score.
+template <int DK, int DV, bool ALIBI = false>
 __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Dest& dst,
                                  LdsPrefill<DK, DV>& sm) {
   using LY = PrefillLayout<DK, DV>;
@@ -439,6 +448,8 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
   const bool row_ok = row < nrows;
   int64_t out_row;
   int lim;
+  float alibi_m = 0.f;  // ALiBi: the row's slope in raw-score units
+  int qpos;             // the row's query position
   bf16x8 qf[KS];  // B operand of S^T: Q[row][16 ks + 8 h .. +7]
   {
     const int rid = row0 + row;
@@ -446,6 +457,8 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
     const int head = kvh * G + (rid - t * G);
     out_row = (int64_t)(q0 + t) * a.Hq + head;
     lim = row_ok ? min(visible_end(mask, ctx, t, pfx), kv_end) : kv_begin;
+    qpos = ctx + t;
+    if constexpr (ALIBI) alibi_m = row_ok ? a.alibi[head] / a.scale : 0.f;
     const __bf16* qp = (const __bf16*)a.q + out_row * DK + 8 * h;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -615,6 +628,15 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
   auto softmax_phase = [&](int t) {
     if (t < 0 || t >= wave_tiles) return;
     const int t0 = kv_begin + t * kTK;
+    if constexpr (ALIBI) {
+      const int alibi_sqrt = __builtin_amdgcn_readfirstlane(a.alibi_sqrt);
+      const int d0 = qpos - t0 - 8 * h;  // distance to the key at offset 0 from t0 + 8 h
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          s[kb][v] -= alibi_term(alibi_m, alibi_sqrt, d0 - (32 * kb + 16 * (v >> 3) + (v & 7)));
+    }
     if (t0 + kTK > wave_min) {  // only tiles that reach past the smallest limit need masks
       const int rel = lim - t0 - 8 * h;  // visible iff the key's offset from t0 + 8 h is < rel
 #pragma unroll
@@ -792,12 +814,12 @@ __device__ WorkItem make_prefill_item(const MhaArgs& a, int idx) {
 // The decode item as a real call, for the kernel that also runs prefill
 // items: this keeps the decode code's register allocation out of the prefill
 // loop (a call costs little next to a decode item's key loads).
-template <int DK, int DV>
+template <int DK, int DV, bool ALIBI>
 __device__ __noinline__ int run_decode_item_outlined(const MhaArgs& a, const WorkItem& it,
                                                      const Dest& dst,
                                                      LdsDecode<DV, kPrefillWaves>& sm,
                                                      int32_t* counter) {
-  return run_decode_item<DK, DV, kPrefillWaves>(a, it, dst, sm, counter);
+  return run_decode_item<DK, DV, kPrefillWaves, ALIBI>(a, it, dst, sm, counter);
 }
 
 // ---------------------------------------------------------------------------
@@ -989,7 +1011,7 @@ __device__ WorkItem fused_item(const MhaArgs& a, const FusedPlan& fp, long long 
 // (Decode-only grids run two workgroups per compute unit, except with 192-wide
 // keys: their decode item's two steps of key operands in flight need more
 // registers than a half share of the register file.)
-template <int DK, int DV, bool DECODE_ONLY, bool FUSED = false>
+template <int DK, int DV, bool DECODE_ONLY, bool FUSED = false, bool ALIBI = false>
 __global__ __launch_bounds__(DECODE_ONLY ? kThreads : kPrefillThreads,
                              (DECODE_ONLY && DK <= 128) ? 2 : 1)
 void mha_forward_kernel(MhaArgs a) {
@@ -1095,14 +1117,15 @@ void mha_forward_kernel(MhaArgs a) {
     publish();
   } else {
     next();
-    for (; idx < n_pre && idx < n_items; next()) run_prefill_item<DK, DV>(a, it, dest(), sm.pre);
+    for (; idx < n_pre && idx < n_items; next())
+      run_prefill_item<DK, DV, ALIBI>(a, it, dest(), sm.pre);
   }
   // decode-mode items: each one claims its successor while its epilogue runs
   // (without the queue: the item gridDim.x further on)
   while (idx < n_items) {
     int j;
-    if constexpr (DECODE_ONLY) j = run_decode_item<DK, DV, 4>(a, it, dest(), sm, counter);
-    else j = run_decode_item_outlined<DK, DV>(a, it, dest(), sm.dec, counter);
+    if constexpr (DECODE_ONLY) j = run_decode_item<DK, DV, 4, ALIBI>(a, it, dest(), sm, counter);
+    else j = run_decode_item_outlined<DK, DV, ALIBI>(a, it, dest(), sm.dec, counter);
     if (threadIdx.x < 64)
       fetch_decode(queue ? __shfl(j, 0) + dec_base : idx - n_pre + (int)gridDim.x);
     publish();
@@ -1444,10 +1467,22 @@ hipError_t mha_occupancy(int variant, bool decode_only, int* blocks_per_cu) {
   });
 }
 
-hipError_t launch_mha_forward(const MhaArgs& a, int variant, bool decode_only, int grid,
-                              hipStream_t s) {
+hipError_t launch_mha_forward(const MhaArgs& a, int variant, bool decode_only, bool alibi,
+                              int grid, hipStream_t s) {
   return with_dims(variant, [&](auto dk, auto dv) {
     constexpr int DK = decltype(dk)::value, DV = decltype(dv)::value;
+    if (alibi) {
+      if constexpr (DK <= 128) {  // ALiBi kernels are built for head dims 64 and 128
+        if (decode_only)
+          hipLaunchKernelGGL((mha_forward_kernel<DK, DV, true, false, true>), dim3(grid),
+                             dim3(kThreads), 0, s, a);
+        else
+          hipLaunchKernelGGL((mha_forward_kernel<DK, DV, false, false, true>), dim3(grid),
+                             dim3(kPrefillThreads), 0, s, a);
+        return hipGetLastError();
+      }
+      return hipErrorInvalidValue;
+    }
     if (decode_only)
       hipLaunchKernelGGL((mha_forward_kernel<DK, DV, true>), dim3(grid), dim3(kThreads), 0, s, a);
     else
@@ -1457,9 +1492,18 @@ hipError_t launch_mha_forward(const MhaArgs& a, int variant, bool decode_only, i
   });
 }
 
-hipError_t launch_mha_forward_fused(const MhaArgs& a, int variant, int grid, hipStream_t s) {
+hipError_t launch_mha_forward_fused(const MhaArgs& a, int variant, bool alibi, int grid,
+                                    hipStream_t s) {
   return with_dims(variant, [&](auto dk, auto dv) {
     constexpr int DK = decltype(dk)::value, DV = decltype(dv)::value;
+    if (alibi) {
+      if constexpr (DK <= 128) {
+        hipLaunchKernelGGL((mha_forward_kernel<DK, DV, true, true, true>), dim3(grid),
+                           dim3(kThreads), 0, s, a);
+        return hipGetLastError();
+      }
+      return hipErrorInvalidValue;
+    }
     hipLaunchKernelGGL((mha_forward_kernel<DK, DV, true, true>), dim3(grid), dim3(kThreads), 0, s,
                        a);
     return hipGetLastError();

@@ -156,16 +156,26 @@ def test_masked_forward_argument_checks():
     lib = pa.library()
     d = _dims()
 
-    def call(mask, prefix, dd=d):
-        return lib.pa_forward_masked(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, mask, prefix, None, 0.1,
-                                     FAKE, None, ctypes.byref(dd), FAKE, 1 << 40, None)
+    def call(mask, prefix, dd=d, slopes=None, alibi=0):
+        return lib.pa_forward_masked(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, mask, prefix, None,
+                                     slopes, alibi, 0.1, FAKE, None, ctypes.byref(dd), FAKE,
+                                     1 << 40, None)
     bad = binding.PA_ERR_INVALID_ARG
     assert call(3, None) == bad and call(-1, None) == bad
     assert call(binding.PA_MASK_PREFIX, None) == bad   # prefix mask without prefix lengths
     assert call(binding.PA_MASK_FULL, FAKE) == bad     # prefix lengths with another mask
     assert call(binding.PA_MASK_CAUSAL, FAKE) == bad
+    # ALiBi: a known mode with slopes, or neither; bf16 keys up to 128 wide
+    assert call(binding.PA_MASK_CAUSAL, None, slopes=None, alibi=binding.PA_ALIBI_SQRT) == bad
+    assert call(binding.PA_MASK_CAUSAL, None, slopes=FAKE, alibi=binding.PA_ALIBI_NONE) == bad
+    assert call(binding.PA_MASK_CAUSAL, None, slopes=FAKE, alibi=3) == bad
+    f2 = _dims(head_dim_qk=192, head_dim_v=128)
+    assert call(binding.PA_MASK_CAUSAL, None, f2, slopes=FAKE, alibi=binding.PA_ALIBI_LINEAR) == \
+        binding.PA_ERR_UNSUPPORTED
     empty = _dims(num_seqs=0, num_tokens=0)
     assert call(binding.PA_MASK_FULL, None, empty) == binding.PA_OK
+    assert call(binding.PA_MASK_FULL, None, empty, slopes=FAKE, alibi=binding.PA_ALIBI_SQRT) == \
+        binding.PA_OK
     assert call(binding.PA_MASK_PREFIX, FAKE, empty) == binding.PA_OK
 
 

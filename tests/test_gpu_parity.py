@@ -203,22 +203,28 @@ def test_long_context_split_full_size(batch, S, lengths):
 
 # ------------------------------------------------------ full and prefix masks
 
-def masked_parity(b, mask, prefixes, what, sinks=None):
-    say("case %s: B=%d T=%d keys=%d mask=%d prefixes=%s sinks=%s" % (
-        what, b.num_seqs, b.num_tokens, sum(b.seq_lens_list), mask, prefixes, sinks is not None))
+def masked_parity(b, mask, prefixes, what, sinks=None, alibi=None, alibi_mode=pa.PA_ALIBI_NONE):
+    """pa_forward_masked against the oracle (alibi: the slopes, with alibi_mode)."""
+    say("case %s: B=%d T=%d keys=%d mask=%d prefixes=%s sinks=%s alibi=%d" % (
+        what, b.num_seqs, b.num_tokens, sum(b.seq_lens_list), mask, prefixes, sinks is not None,
+        alibi_mode))
     g = b.to(DEV)
     pl = None if prefixes is None else torch.tensor(prefixes, dtype=torch.int32, device=DEV)
     sk = None if sinks is None else torch.tensor(sinks, dtype=torch.float32, device=DEV)
+    al = None if alibi is None else torch.tensor(alibi, dtype=torch.float32, device=DEV)
     lse = torch.full((b.num_tokens, b.num_q_heads), float("nan"), dtype=torch.float32, device=DEV)
     out = pa.pa_forward_masked(g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens,
                                g.query_start_loc, b.scale, mask, prefix_lens=pl, sinks=sk, lse=lse,
                                max_seq_len=max(b.seq_lens_list + [1]),
-                               max_q_len=max(b.q_lens + [1]))
+                               max_q_len=max(b.q_lens + [1]), alibi_slopes=al,
+                               alibi_mode=alibi_mode)
     torch.cuda.synchronize()
     ref, rlse = oracle.attention(b.q, b.k_cache, b.v_cache, b.block_table, b.seq_lens,
                                  b.query_start_loc, b.scale, b.num_kv_heads, mask=mask,
                                  prefix_lens=None if prefixes is None else np.asarray(prefixes, np.int32),
-                                 sinks=sinks, head_dim_v=b.head_dim_v)
+                                 sinks=sinks, head_dim_v=b.head_dim_v,
+                                 alibi_slopes=None if alibi is None else np.asarray(alibi, np.float32),
+                                 alibi_mode=alibi_mode)
     got = out.float().cpu().numpy()
     check_out(got, ref, b.dtype, what)
     check_lse(lse.cpu().numpy(), rlse, what)
@@ -315,6 +321,45 @@ def test_sinks_f32():
     b = workload.make_batch([4, 1, 7], [20, 33, 0], num_q_heads=8, num_kv_heads=2, head_dim_qk=64,
                             page_size=16, dtype=torch.float32, seed=617)
     masked_parity(b, pa.PA_MASK_CAUSAL, None, "sinks fp32", sinks=sink_logits(8, 3))
+
+
+# ------------------------------------------------------------- ALiBi (sqrt)
+
+@pytest.mark.parametrize("mode", [pa.PA_ALIBI_SQRT, pa.PA_ALIBI_LINEAR])
+@pytest.mark.parametrize("mask,prefixes", [(pa.PA_MASK_CAUSAL, None), (pa.PA_MASK_FULL, None),
+                                           (pa.PA_MASK_PREFIX, [0, 41, 750, 20, 100])])
+def test_alibi_forward_matches_oracle(mode, mask, prefixes):
+    b = workload.make_batch(MASK_Q, MASK_C, num_q_heads=32, num_kv_heads=8, head_dim_qk=128,
+                            page_size=16, seed=1301)
+    masked_parity(b, mask, prefixes, "alibi", alibi=workload.alibi_slopes(32), alibi_mode=mode)
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,P,dtype", [(12, 4, 64, 16, torch.bfloat16),
+                                              (16, 16, 128, 32, torch.bfloat16),
+                                              (8, 2, 64, 16, torch.float32)])
+def test_alibi_shapes_and_fp32(Hq, Hkv, D, P, dtype):
+    b = workload.make_batch([3, 1, 270, 4], [50, 500, 260, 0], num_q_heads=Hq, num_kv_heads=Hkv,
+                            head_dim_qk=D, page_size=P, dtype=dtype, seed=1311 + Hq + D)
+    masked_parity(b, pa.PA_MASK_CAUSAL, None, "alibi sqrt Hq=%d D=%d %s" % (Hq, D, dtype),
+                  alibi=workload.alibi_slopes(Hq), alibi_mode=pa.PA_ALIBI_SQRT,
+                  sinks=sink_logits(Hq, 7))
+
+
+def test_alibi_decode_only_with_split_rows():
+    # long decode rows split over several partitions: the bias follows the key, not
+    # the partition
+    b = workload.llama_decode(3, batch=6)
+    masked_parity(b, pa.PA_MASK_CAUSAL, None, "alibi sqrt decode", alibi=workload.alibi_slopes(32),
+                  alibi_mode=pa.PA_ALIBI_SQRT)
+
+
+def test_alibi_stays_off_the_chunked_route():
+    # few long extends (pa_forward would take the chunked route): with ALiBi the call
+    # runs on the persistent kernel
+    b = workload.make_batch([100, 1, 30], [12000, 20000, 9000], num_q_heads=8, num_kv_heads=8,
+                            head_dim_qk=128, page_size=16, seed=1321)
+    masked_parity(b, pa.PA_MASK_CAUSAL, None, "alibi sqrt long extends",
+                  alibi=workload.alibi_slopes(8), alibi_mode=pa.PA_ALIBI_SQRT)
 
 
 def test_full_mask_qwen3_scaled():
