@@ -605,7 +605,7 @@ size_t mla_workspace_size(const pa_dims* d, int32_t num_splits) {
   if (num_splits == 0) {
     DevCfg cfg;
     if (device_config(&cfg) != PA_OK) return 0;
-    return mla_balanced_ws(d, cfg.cu_count).total;
+    return mla_balanced_ws(d, 2 * cfg.cu_count).total;
   }
   return mla_ws_bytes(d, num_splits);
 }
@@ -625,7 +625,7 @@ pa_status mla_decode(const void* q, const void* kv_cache, const int32_t* block_t
     DevCfg cfg;
     st = device_config(&cfg);
     if (st != PA_OK) return st;
-    const MlaBalancedWs w = mla_balanced_ws(d, cfg.cu_count);
+    const MlaBalancedWs w = mla_balanced_ws(d, 2 * cfg.cu_count);
     if (!workspace || workspace_bytes < w.total) return PA_ERR_WORKSPACE;
     char* ws = (char*)workspace;
     pa::MlaArgs a{};
@@ -645,9 +645,9 @@ pa_status mla_decode(const void* q, const void* kv_cache, const int32_t* block_t
     a.log2_page = __builtin_ctz((unsigned)d->page_size);
     a.max_pages = d->max_pages_per_seq;
     a.num_splits = 0;
-    a.max_pieces = cfg.cu_count;
+    a.max_pieces = 2 * cfg.cu_count;
     hipError_t e = mark(g_ev_start, s);
-    if (e == hipSuccess) e = pa::launch_mla_balanced(a, std::max(cfg.cu_count, d->num_seqs), s);
+    if (e == hipSuccess) e = pa::launch_mla_balanced(a, cfg.cu_count, s);
     if (e == hipSuccess) e = mark(g_ev_stop, s);
     if (e == hipSuccess) e = pa::launch_mla_balanced_merge(a, s);
     return e == hipSuccess ? PA_OK : hip_fail(e);

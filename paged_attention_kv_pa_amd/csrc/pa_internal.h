@@ -137,7 +137,7 @@ struct MlaArgs {
   int32_t* merge_info;       // balanced: [B, 2] first partial slot and piece count of each request
   float scale;
   int32_t B, Hq, P, log2_page, max_pages, num_splits;
-  int32_t max_pieces;        // balanced: pieces that run at once (one workgroup per compute unit)
+  int32_t max_pieces;        // balanced: partial slots (two per workgroup, one workgroup per CU)
 };
 
 // Workspace layout of pa_forward.

@@ -423,67 +423,39 @@ __device__ __forceinline__ long long mla_block_sum(long long v, long long* red) 
   return t;
 }
 
-__device__ __forceinline__ long long mla_block_max(long long v, long long* red) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o));
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  long long t = 0;
-#pragma unroll
-  for (int w = 0; w < kMlaThreads / 64; ++w) t = max(t, red[w]);
-  return t;
-}
-
-// Balanced schedule: every request is cut into pieces of at most c key tiles
-// (the last piece of a request may be shorter), c being the smallest cap the
-// search below finds for which all pieces fit in max_pieces workgroups (one
-// per compute unit), so that every workgroup streams at most c tiles whatever
-// the length mix.  Workgroup w takes piece w in request order; a request in
-// several pieces is finished by the merge kernel from the partial rows in
-// slots w0 .. w0 + n - 1, recorded in merge_info[2b] = w0, [2b + 1] = n.
-// When the requests outnumber the workgroups every request is one piece.
-// Each workgroup recomputes the (small) schedule from seq_lens.
+// Balanced schedule: the key tiles of all requests, taken in request order,
+// form one sequence of T tiles, cut into gridDim.x (one workgroup per compute
+// unit) contiguous ranges of ceil(T / gridDim.x) tiles.  Workgroup w walks its
+// range request by request: a request wholly inside the range is written to
+// the output, a request the range shares with a neighbour (cut) is written as
+// partial rows that the merge kernel combines.  A range cuts at most its first
+// and its last request, so workgroup w owns two partial slots: 2 w for its
+// first segment, 2 w + 1 for a later one.  A cut request b whose first tile
+// lies in range w0 and last tile in range w1 has its pieces in slots
+// merge_info[2 b] (2 w0 or 2 w0 + 1), then 2 (w0 + 1), ..., 2 w1;
+// merge_info[2 b + 1] is the piece count (1: not cut).  Every workgroup
+// recomputes the (small) schedule from seq_lens.  The tile loop (mla_keys)
+// runs once per segment on the same LDS ring; its LDS accesses stay LDS
+// instructions (the ring is addressed through the kernel's own shared array).
 __global__ __launch_bounds__(kMlaThreads) void mla_balanced_kernel(MlaArgs a) {
   extern __shared__ __align__(16) char mla_smem[];
   __shared__ long long s_red[kMlaThreads / 64];
-  __shared__ int s_b, s_j, s_n;
+  __shared__ int s_b;
+  __shared__ long long s_tb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const long long G = a.max_pieces;
-  long long T = 0, tmax = 1;
-  for (int b = tid; b < a.B; b += kMlaThreads) {
-    const long long t = mla_tiles(a.seq_lens[b]);
-    T += t;
-    tmax = max(tmax, t);
-  }
+  long long T = 0;
+  for (int b = tid; b < a.B; b += kMlaThreads) T += mla_tiles(a.seq_lens[b]);
   T = mla_block_sum(T, s_red);
-  tmax = mla_block_max(tmax, s_red);
-  // smallest cap found: start at the even share and raise it by the rounding
-  // overhead the last count showed (a handful of rounds)
-  long long c = (T + G - 1) / G;
-  if (c < 1) c = 1;
-  bool fits = false;
-  for (int round = 0; round < 32 && c < tmax; ++round) {
-    long long n = 0;
-    for (int b = tid; b < a.B; b += kMlaThreads) n += (mla_tiles(a.seq_lens[b]) + c - 1) / c;
-    n = mla_block_sum(n, s_red);
-    if (n <= G) {
-      fits = true;
-      break;
-    }
-    const long long extra = n - (T + c - 1) / c;
-    const long long next = G > extra ? (T + G - extra - 1) / (G - extra) : tmax;
-    c = next > c + 1 ? next : c + 1;
-  }
-  // no cap below the longest request found: one piece per request, none split
-  if (!fits || c > tmax) c = tmax;
-  // piece blockIdx.x: scan the per-request piece counts chunk by chunk
-  const long long w = blockIdx.x;
+  const long long G = gridDim.x, w = blockIdx.x;
+  const long long per = (T + G - 1) / G;
+  const long long start = w * per, end = min(start + per, T);
+  if (start >= end) return;  // uniform: no tile left for this workgroup
+  // first request of the range: the one whose tiles [ex, ex + n) hold `start`
   if (tid == 0) s_b = -1;
   long long run = 0;
   for (int base = 0; base < a.B; base += kMlaThreads) {
     const int b = base + tid;
-    const long long n = b < a.B ? (mla_tiles(a.seq_lens[b]) + c - 1) / c : 0;
+    const long long n = b < a.B ? mla_tiles(a.seq_lens[b]) : 0;
     long long incl = n;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -500,31 +472,37 @@ __global__ __launch_bounds__(kMlaThreads) void mla_balanced_kernel(MlaArgs a) {
       tot += s_red[v];
     }
     const long long ex = before + incl - n;
-    if (n > 0 && ex <= w && w < ex + n) {
+    if (n > 0 && ex <= start && start < ex + n) {
       s_b = b;
-      s_j = (int)(w - ex);
-      s_n = (int)n;
+      s_tb = ex;
     }
     run += tot;
-    if (run > w) break;  // uniform
+    if (run > start) break;  // uniform
   }
   __syncthreads();
-  const int b = s_b;
-  if (b < 0) return;  // no piece left for this workgroup
-  const int j = s_j, n = s_n;
-  const int L = a.seq_lens[b];
-  const long long k0 = (long long)j * c * kMTK, k1 = k0 + c * kMTK;
-  const int t0k = k0 < L ? (int)k0 : L, t1k = k1 < L ? (int)k1 : L;
-  if (tid == 0 && j == 0) {
-    a.merge_info[2 * b] = (int)w;
-    a.merge_info[2 * b + 1] = n;
+  int b = __builtin_amdgcn_readfirstlane(s_b);
+  long long tb = s_tb;  // first tile of request b in the sequence
+  for (int k = 0; b < a.B && tb < end; ++k, ++b) {
+    const int L = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
+    const long long n = mla_tiles(L);
+    const long long s0 = max(start, tb) - tb, s1 = min(end, tb + n) - tb;
+    const bool cut = s0 > 0 || s1 < n;
+    const int slot = 2 * (int)w + (k > 0 ? 1 : 0);
+    if (tid == 0 && s0 == 0) {  // the request's first tile is in this range
+      a.merge_info[2 * b] = slot;
+      a.merge_info[2 * b + 1] = cut ? (int)((tb + n - 1) / per - w + 1) : 1;
+    }
+    const long long k0 = s0 * kMTK, k1 = s1 * kMTK;
+    const int t0k = k0 < L ? (int)k0 : L, t1k = k1 < L ? (int)k1 : L;
+    mla_keys(a, mla_smem, tid, b, t0k, t1k, cut ? (int64_t)slot * a.Hq : -1, 1);
+    tb += n;
   }
-  mla_keys(a, mla_smem, threadIdx.x, b, t0k, t1k, n > 1 ? w * (int64_t)a.Hq : -1, 1);
 }
 
 // Rows of the requests the balanced schedule cut: workgroup (b, 16 heads),
 // 16 lanes per row with 32 columns each, folding the pieces' partial rows
-// with a running log-sum-exp.
+// (slots merge_info[2 b], then 2 (w0 + 1), 2 (w0 + 2), ... with w0 =
+// merge_info[2 b] / 2) with a running log-sum-exp.
 __global__ __launch_bounds__(kMlaThreads) void mla_balanced_merge_kernel(MlaArgs a) {
   const int hg_count = a.Hq / 16;
   const int b = blockIdx.x / hg_count, hg = blockIdx.x % hg_count;
@@ -538,7 +516,8 @@ __global__ __launch_bounds__(kMlaThreads) void mla_balanced_merge_kernel(MlaArgs
 #pragma unroll
   for (int c = 0; c < 32; ++c) o[c] = 0.f;
   for (int i = 0; i < np; ++i) {
-    const int64_t pi = (int64_t)(w0 + i) * a.Hq + head;
+    const int slot = i == 0 ? w0 : 2 * ((w0 >> 1) + i);
+    const int64_t pi = (int64_t)slot * a.Hq + head;
     const float ls = a.part_lse[pi];
     const floatx4* po = reinterpret_cast<const floatx4*>(a.part_o + pi * kDv + c0);
     floatx4 v[8];
