@@ -196,6 +196,22 @@ pa_status fwd_geometry(const pa_dims* d, FwdGeom* g) {
   return PA_OK;
 }
 
+// Partial rows x chunks of the requests pa_forward's planner may cut into
+// key chunks (prefill-mode requests of at least kLongKeys keys, "vLLM AMD ROCm
+// Attention Backend Optimization", bullet "Chunked context processing"):
+// zero unless the dims allow such a request on the persistent path (the
+// chunked route takes whole calls of few long requests instead), at most
+// kLongBudgetBytes of partials.
+int64_t long_rows(const pa_dims* d, const ChunkRoute& route) {
+  if (route.on || d->dtype != PA_BF16) return 0;
+  if (pa::mha_variant(d->head_dim_qk, d->head_dim_v) < 0) return 0;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if ((int64_t)d->max_q_len * G <= pa::kDecodeRows || d->max_seq_len < pa::kLongKeys) return 0;
+  const int64_t chunks = (d->max_seq_len + pa::kLongChunk - 1) / pa::kLongChunk;
+  const int64_t want = (int64_t)d->num_tokens * d->num_q_heads * chunks;
+  return std::min<int64_t>(want, pa::kLongBudgetBytes / (((int64_t)d->head_dim_v + 1) * 4));
+}
+
 pa_status check_mla(const pa_dims* d) {
   pa_status st = check_dims(d);
   if (st != PA_OK) return st;
@@ -242,7 +258,9 @@ size_t pa_workspace_size(const pa_dims* d) {
   FwdGeom geo;
   const int target = fwd_geometry(d, &geo) == PA_OK ? geo.target : INT32_MAX / 4;
   const ChunkRoute r = chunk_route(d);
-  return pa::fwd_workspace_layout(d->num_seqs, d->num_kv_heads, d->head_dim_v, target).total +
+  return pa::fwd_workspace_layout(d->num_seqs, d->num_kv_heads, d->head_dim_v, target,
+                                  long_rows(d, r))
+             .total +
          r.po_bytes + r.pl_bytes;
 }
 
@@ -322,10 +340,11 @@ pa_status pa_forward_masked(const void* q, const void* k_cache, const void* v_ca
   // host checks)
   FwdGeom geo;
   const pa_status geo_st = fwd_geometry(d, &geo);
-  const pa::FwdWorkspace w = pa::fwd_workspace_layout(
-      d->num_seqs, d->num_kv_heads, d->head_dim_v, geo_st == PA_OK ? geo.target : INT32_MAX / 4);
   // (ALiBi calls stay on the persistent path: the chunk kernel has no ALiBi term)
   const ChunkRoute route = chunk_route(d);
+  const pa::FwdWorkspace w =
+      pa::fwd_workspace_layout(d->num_seqs, d->num_kv_heads, d->head_dim_v,
+                               geo_st == PA_OK ? geo.target : INT32_MAX / 4, long_rows(d, route));
   if (route.on && !alibi) {
     // few long requests: chunk partials and their merge instead of the
     // persistent kernel, whose prefill items alone could not fill the GPU
@@ -391,6 +410,10 @@ pa_status pa_forward_masked(const void* q, const void* k_cache, const void* v_ca
   pl.P = d->page_size;
   pl.max_pages = d->max_pages_per_seq;
   pl.target_items = geo.target;
+  pl.cmerge = (int32_t*)(ws + w.cmerge_off);
+  pl.long_keys = w.crow_budget > 0 ? pa::kLongKeys : 0;
+  pl.chunk_keys = pa::kLongChunk;
+  pl.crow_budget = w.crow_budget;
   // decode-only calls of up to kFusedPlanMax requests: the persistent kernel
   // plans itself, so the call is two launches (attention kernel, merge)
   const bool fused = decode_only && d->num_seqs <= pa::kFusedPlanMax;
@@ -412,6 +435,10 @@ pa_status pa_forward_masked(const void* q, const void* k_cache, const void* v_ca
   a.pre_off = pre_off;
   a.dec_items = dec_items;
   a.merges = merges;
+  a.cmerge = (const int32_t*)(ws + w.cmerge_off);
+  a.cpart_o = (float*)(ws + w.cpo_off);
+  a.cpart_lse = (float*)(ws + w.cpl_off);
+  a.chunk_keys = pa::kLongChunk;
   a.ctrl = ctrl;
   a.scale = scale;
   a.num_seqs = d->num_seqs;
@@ -442,6 +469,11 @@ pa_status pa_forward_masked(const void* q, const void* k_cache, const void* v_ca
   e = pa::launch_mha_forward_merge(
       a, d->head_dim_v, (int)std::max<int64_t>(1, std::min<int64_t>(cfg.cu_count * 4, (units + 3) / 4)), s);
   if (e != hipSuccess) return hip_fail(e);
+  // rows of requests the planner cut into key chunks (dims that allow them only)
+  if (!fused && w.crow_budget > 0) {
+    e = pa::launch_mha_chunk_merge(a, d->head_dim_v, std::max(1, cfg.cu_count * 4), s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
   return PA_OK;
 }
 

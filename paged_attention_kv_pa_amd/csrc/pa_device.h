@@ -117,17 +117,42 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Lane exchanges within the VALU (v_permlane32_swap / v_permlane16_swap: no
+// LDS round trip, unlike a generic shuffle).  xor32_pair returns the values
+// of lanes l and l ^ 32 in a fixed order (lower half's first), so that both
+// lanes of a pair combine them into the same bits.
+struct LanePair {
+  float lo, hi;
+};
+__device__ __forceinline__ LanePair xor32_pair(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return LanePair{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+// The same for lanes l and l ^ 16 (16-lane rows 0 / 1 and 2 / 3 paired).
+__device__ __forceinline__ LanePair xor16_pair(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return LanePair{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ float xor32_max(float v) {
+  const LanePair p = xor32_pair(v);
+  return fmaxf(p.lo, p.hi);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const LanePair p = xor32_pair(v);
+  return p.lo + p.hi;
+}
+
 // Butterfly reductions across the 4 lane groups (lanes l, l^16, l^32, l^48)
 // that hold the same MFMA row.
 __device__ __forceinline__ float group_max4(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  const LanePair p = xor16_pair(v);
+  return xor32_max(fmaxf(p.lo, p.hi));
 }
 __device__ __forceinline__ float group_sum4(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  const LanePair p = xor16_pair(v);
+  return xor32_sum(p.lo + p.hi);
 }
 
 // Full 64-lane reductions.
@@ -167,10 +192,14 @@ struct WorkItem {
   int32_t nrows;     // rows in the item
   int32_t kv_begin;  // first key (multiple of 8)
   int32_t kv_end;    // one past the last key any row of the item may see
-  int32_t part;      // < 0: write the final output; >= 0: partial slot
+  int32_t part;      // < 0: write the final output; >= 0: partial slot, or for a
+                     // chunked prefill-mode item its request's first partial row
   int32_t q0;        // row of the request's first new token in q / out
   int32_t ctx;       // cached keys before the new tokens (seq_len - q_len)
-  int32_t pad[3];
+  int32_t nchunk;    // prefill-mode item of a request cut into key chunks: their
+                     // number (0 otherwise)
+  int32_t chunk;     // ... and this item's chunk
+  int32_t pad;
 };
 
 // Per-request plan written by the planner kernel of pa_forward.
@@ -182,7 +211,9 @@ struct ReqPlan {
   int32_t nsplit;  // decode-mode key partitions per KV head (0 for prefill-mode requests)
   int32_t per;     // keys per partition
   int32_t slot0;   // first partial slot (requests with nsplit > 1)
-  int32_t pad;
+  int32_t nchunk;  // prefill-mode key chunks (1: not cut)
+  int32_t pbase;   // first chunk-partial row (requests with nchunk > 1)
+  int32_t pad[3];
 };
 
 // Control block at the start of the pa_forward workspace.
@@ -202,7 +233,9 @@ struct Control {
   int32_t work_counter;     // decode-mode items claimed from the queue
   int32_t xcd_counter[8];   // next entry of each prefill-mode item queue
   uint32_t ready;           // kQueueReady: the counters above are zero
-  int32_t pad[51];
+  int32_t n_cmerge;         // prefill-mode requests cut into key chunks
+  int32_t n_crows;          // their output rows (new tokens x query heads)
+  int32_t pad[49];
 };
 
 }  // namespace pa

@@ -25,6 +25,9 @@ constexpr int kItemsPerWorkgroup = 4;  // decode work is cut into ~this many ite
 constexpr int kMaxSplits = 256;        // pa_decode_split / pa_merge_lse / mla_decode limit
 constexpr int kItemInts = 12;          // int32 words of one pa_forward work item
 constexpr int kFusedPlanMax = 1024;    // decode-only calls up to this many requests plan in-kernel
+constexpr int kLongKeys = 100000;      // prefill-mode requests of at least this many keys ...
+constexpr int kLongChunk = 32768;      // ... are cut into chunks of this many keys (a multiple of 64)
+constexpr int64_t kLongBudgetBytes = 256ll << 20;  // partials of such chunks, at most
 
 // Masks (pa_mask in include/pa.h).
 constexpr int kMaskCausal = 0, kMaskFull = 1, kMaskPrefix = 2;
@@ -87,6 +90,10 @@ struct MhaArgs {
   int32_t merge_groups;      // pa_forward's merge: groups of 4 rows of the widest split pair
   int32_t mask;              // kMaskCausal / kMaskFull / kMaskPrefix
   const int32_t* prefix_lens;  // [B], read under kMaskPrefix only
+  const int32_t* cmerge;     // pa_forward: chunked requests, 4 int32 each: request,
+                             // first output row among them, chunks, first partial row
+  float* cpart_o;            // pa_forward: chunk partials [rows, chunks, Dv] ...
+  float* cpart_lse;          // ... and their log-sum-exps
   const float* sinks;        // [Hq] sink logits or NULL (pa_forward_masked only)
   const float* alibi;        // [Hq] ALiBi slopes (kernels built with ALiBi only)
   int32_t alibi_sqrt;        // 1: square root of the distance, 0: the distance
@@ -99,10 +106,14 @@ struct PlanArgs {
   int32_t* pre_off;
   int32_t* dec_items;
   int32_t* merges;
+  int32_t* cmerge;           // chunked prefill-mode requests (see MhaArgs::cmerge)
   Control* ctrl;
   int32_t B, Hkv, G;
   int32_t P, max_pages;
   int32_t target_items;
+  int32_t long_keys;         // prefill-mode requests of >= long_keys keys are cut (0: never)
+  int32_t chunk_keys;        // ... into chunks of this many keys
+  int32_t crow_budget;       // ... while their partial rows x chunks stay within this
 };
 
 struct F32Args {
@@ -142,12 +153,15 @@ struct MlaArgs {
 
 // Workspace layout of pa_forward.
 struct FwdWorkspace {
-  size_t ctrl_off, req_off, pre_off, items_off, merges_off, plse_off, po_off, total;
+  size_t ctrl_off, req_off, pre_off, items_off, merges_off, plse_off, po_off;
+  size_t cmerge_off, cpl_off, cpo_off, total;
   int64_t cap_slots;
+  int32_t crow_budget;  // chunk partial rows x chunks the workspace holds (0: no chunking)
 };
 // target_items: the decode work of a call is cut into about this many items
 // (kItemsPerWorkgroup x the persistent grid).
-FwdWorkspace fwd_workspace_layout(int B, int Hkv, int D, int target_items);
+// long_rows: rows x chunks of per-request chunk partials to provide for (0: none).
+FwdWorkspace fwd_workspace_layout(int B, int Hkv, int D, int target_items, int64_t long_rows);
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 // bf16 MHA kernels exist for (Dqk, Dv) = (64, 64), (128, 128) and (192, 128):
@@ -160,6 +174,7 @@ hipError_t launch_mha_forward(const MhaArgs& a, int variant, bool decode_only, b
 hipError_t launch_mha_forward_fused(const MhaArgs& a, int variant, bool alibi, int grid,
                                     hipStream_t s);
 hipError_t launch_mha_forward_merge(const MhaArgs& a, int Dv, int grid, hipStream_t s);
+hipError_t launch_mha_chunk_merge(const MhaArgs& a, int Dv, int grid, hipStream_t s);
 hipError_t launch_mha_split(const MhaArgs& a, int variant, hipStream_t s);
 hipError_t launch_mha_chunked(const MhaArgs& a, int variant, hipStream_t s);
 hipError_t mha_occupancy(int variant, bool decode_only, int* blocks_per_cu);

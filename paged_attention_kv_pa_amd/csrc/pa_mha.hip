@@ -48,6 +48,8 @@ __device__ __forceinline__ int kperm(int mt, int m) { return 8 * (m >> 2) + 4 * 
 // part_lse[pl_base + row pl_row + out_row pl_out].
 struct Dest {
   bool partial;
+  float* po;                        // partial outputs and their log-sum-exps
+  float* pl;
   int64_t po_base, po_row, po_out;  // partial output offsets (elements)
   int64_t pl_base, pl_row, pl_out;
 };
@@ -67,7 +69,7 @@ __device__ __forceinline__ void store_row_chunk(const MhaArgs& a, const Dest& ds
                                                 int64_t out_row, int c0, const float* o) {
   static_assert(N == 2 || N == 4 || N == 8, "columns per store");
   if (dst.partial) {
-    float* p = a.part_o + dst.po_base + (int64_t)row * dst.po_row + out_row * dst.po_out + c0;
+    float* p = dst.po + dst.po_base + (int64_t)row * dst.po_row + out_row * dst.po_out + c0;
     if constexpr (N == 2) {
       *reinterpret_cast<u32x2*>(p) = u32x2{__float_as_uint(o[0]), __float_as_uint(o[1])};
     } else {
@@ -91,7 +93,7 @@ __device__ __forceinline__ void store_row_chunk(const MhaArgs& a, const Dest& ds
 __device__ __forceinline__ void store_lse(const MhaArgs& a, const Dest& dst, int row,
                                           int64_t out_row, float v) {
   if (dst.partial) {
-    a.part_lse[dst.pl_base + (int64_t)row * dst.pl_row + out_row * dst.pl_out] = v;
+    dst.pl[dst.pl_base + (int64_t)row * dst.pl_row + out_row * dst.pl_out] = v;
   } else if (a.lse) {
     a.lse[out_row] = v;
   }
@@ -645,12 +647,15 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
         for (int v = 0; v < 16; ++v)
           if (32 * kb + 16 * (v >> 3) + (v & 7) >= rel) s[kb][v] = kNegInf;
     }
-    float tmax = fmaxf(s[0][0], s[0][1]);
+    // row maximum: two independent chains (one per 32-key half), then the
+    // lane holding the row's other keys (lane ^ 32)
+    float tm0 = fmaxf(s[0][0], s[0][1]), tm1 = fmaxf(s[1][0], s[1][1]);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = (kb == 0 ? 2 : 0); v < 16; ++v) tmax = fmaxf(tmax, s[kb][v]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * sc;  // scale > 0
+    for (int v = 2; v < 16; ++v) {
+      tm0 = fmaxf(tm0, s[0][v]);
+      tm1 = fmaxf(tm1, s[1][v]);
+    }
+    const float tmax = xor32_max(fmaxf(tm0, tm1)) * sc;  // scale > 0
     // lazy rescale: move the reference maximum only when it grew by > 2^8
     const bool grow = tmax > m + 8.f;
     if (__any(grow)) {
@@ -664,15 +669,15 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
       m = mnew;
     }
     const float nmuse = m == kNegInf ? 0.f : -m;
-    float psum = 0.f;
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums: short dependency chains
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         s[kb][v] = fast_exp2(fmaf(s[kb][v], sc, nmuse));
-        psum += s[kb][v];
+        ps[v & 3] += s[kb][v];
       }
-    l += psum;
+    l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
     // bf16 probabilities: the B operand of O^T
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
@@ -739,7 +744,7 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
   __syncthreads();  // every wave is done with the ring before the next item
 
   // epilogue: element v of acc[dt] is O[row][32 dt + 8 (v / 4) + 4 h + v % 4]
-  const float lrow = l + __shfl_xor(l, 32);
+  const float lrow = xor32_sum(l);
   if (!row_ok) return;
   float lse = lrow > 0.f ? (m + __log2f(lrow)) * kLn2 : kNegInf;
   float inv = lrow > 0.f ? 1.f / lrow : 0.f;
@@ -787,27 +792,46 @@ __device__ __forceinline__ int find_request(const int32_t* off, int B, int idx) 
 static_assert(sizeof(WorkItem) == kItemInts * sizeof(int32_t), "work item size");
 
 // Prefill-mode work item `idx` of pa_forward, decoded from the planner's
-// per-request offsets; the heaviest row block of a request comes first.
+// per-request offsets: (KV head, key chunk, row block) in that order, so that
+// consecutive items read the same keys; the heaviest row block of a
+// (KV head, chunk) comes first.  A request the planner cut into key chunks
+// (long contexts, "vLLM AMD ROCm Attention Backend Optimization", bullet
+// "Chunked context processing") gets one item per chunk, over the chunk's
+// keys below the block's last key limit (possibly none: the item then writes
+// empty partials), writing partial rows that the chunk merge combines.
 __device__ WorkItem make_prefill_item(const MhaArgs& a, int idx) {
   WorkItem it;
   const int G = a.G;
   const int b = find_request(a.pre_off, a.num_seqs, idx);
   const ReqPlan rp = a.req[b];
-  const int local = idx - a.pre_off[b];
-  const int kvh = local / rp.nblk;
-  const int blk = rp.nblk - 1 - (local - kvh * rp.nblk);
+  int local = idx - a.pre_off[b];
+  const int blk = rp.nblk - 1 - local % rp.nblk;
+  local /= rp.nblk;
+  const int chunk = local % rp.nchunk;
+  const int kvh = local / rp.nchunk;
   const int rows = rp.nq * G;
   it.seq = b;
   it.kvh = kvh;
   it.row0 = blk * kPrefillRows;
   it.nrows = min(kPrefillRows, rows - it.row0);
   it.ctx = rp.L - rp.nq;
-  it.kv_begin = 0;
   const int pfx = a.mask == kMaskPrefix ? a.prefix_lens[b] : 0;
-  it.kv_end = min(rp.L, visible_end(a.mask, it.ctx, (it.row0 + it.nrows - 1) / G, pfx));
-  it.part = -1;
+  const int lim = min(rp.L, visible_end(a.mask, it.ctx, (it.row0 + it.nrows - 1) / G, pfx));
+  if (rp.nchunk > 1) {
+    const int c0 = chunk * a.chunk_keys;
+    it.kv_begin = c0;
+    it.kv_end = max(c0, min(lim, c0 + a.chunk_keys));
+    it.part = rp.pbase;
+    it.nchunk = rp.nchunk;
+    it.chunk = chunk;
+  } else {
+    it.kv_begin = 0;
+    it.kv_end = lim;
+    it.part = -1;
+    it.nchunk = it.chunk = 0;
+  }
   it.q0 = rp.q0;
-  it.pad[0] = it.pad[1] = it.pad[2] = 0;
+  it.pad = 0;
   return it;
 }
 
@@ -983,7 +1007,7 @@ __device__ WorkItem fused_item(const MhaArgs& a, const FusedPlan& fp, long long 
   it.part = nsplit > 1 ? fp.soff[b] + kvh * nsplit + sp : -1;
   it.q0 = q0;
   it.ctx = L - nq;
-  it.pad[0] = it.pad[1] = it.pad[2] = 0;
+  it.nchunk = it.chunk = it.pad = 0;
   return it;
 }
 
@@ -1104,12 +1128,28 @@ void mha_forward_kernel(MhaArgs a) {
   auto dest = [&]() {
     Dest dst;
     dst.partial = it.part >= 0;
-    dst.po_base = (int64_t)it.part * kDecodeRows * DV;
-    dst.po_row = DV;
-    dst.po_out = 0;
-    dst.pl_base = (int64_t)it.part * kDecodeRows;
-    dst.pl_row = 1;
-    dst.pl_out = 0;
+    if (it.nchunk > 1) {
+      // chunk partials of a cut request, row-major [token, head, chunk]:
+      // partial row pbase + (out_row - q0 Hq) nchunk + chunk
+      dst.po = a.cpart_o;
+      dst.pl = a.cpart_lse;
+      const int64_t r0 = (int64_t)it.part - (int64_t)it.q0 * a.Hq * it.nchunk + it.chunk;
+      dst.po_base = r0 * DV;
+      dst.po_row = 0;
+      dst.po_out = (int64_t)it.nchunk * DV;
+      dst.pl_base = r0;
+      dst.pl_row = 0;
+      dst.pl_out = it.nchunk;
+    } else {
+      dst.po = a.part_o;
+      dst.pl = a.part_lse;
+      dst.po_base = (int64_t)it.part * kDecodeRows * DV;
+      dst.po_row = DV;
+      dst.po_out = 0;
+      dst.pl_base = (int64_t)it.part * kDecodeRows;
+      dst.pl_row = 1;
+      dst.pl_out = 0;
+    }
     return dst;
   };
   if constexpr (DECODE_ONLY) {
@@ -1149,6 +1189,8 @@ void mha_split_kernel(MhaArgs a) {
   const int t0 = a0 < L ? (int)a0 : L, t1 = a1 < L ? (int)a1 : L;
   Dest dst;
   dst.partial = true;
+  dst.po = a.part_o;
+  dst.pl = a.part_lse;
   dst.po_base = ((int64_t)(b * a.Hq + kvh * a.G) * S + s) * D;
   dst.po_row = (int64_t)S * D;
   dst.po_out = 0;
@@ -1172,7 +1214,7 @@ void mha_split_kernel(MhaArgs a) {
   it.part = 0;
   it.q0 = b;
   it.ctx = L - 1;
-  it.pad[0] = it.pad[1] = it.pad[2] = 0;
+  it.nchunk = it.chunk = it.pad = 0;
   if constexpr (DEC) run_decode_item<DK, DV, 4>(a, it, dst, sm, nullptr);
   else run_prefill_item<DK, DV>(a, it, dst, sm);
 }
@@ -1228,6 +1270,8 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void mha_chunked_kernel(MhaArgs
   }
   Dest dst;
   dst.partial = true;
+  dst.po = a.part_o;
+  dst.pl = a.part_lse;
   dst.po_base = (int64_t)s * D;
   dst.po_row = 0;
   dst.po_out = (int64_t)S * D;
@@ -1244,7 +1288,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void mha_chunked_kernel(MhaArgs
   it.part = 0;
   it.q0 = q0;
   it.ctx = ctx;
-  it.pad[0] = it.pad[1] = it.pad[2] = 0;
+  it.nchunk = it.chunk = it.pad = 0;
   run_prefill_item<DK, DV>(a, it, dst, sm);
 }
 
@@ -1289,9 +1333,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 
   // pass 2: per-request counts, exclusive scans, plans
   int4 run = int4{0, 0, 0, 0};  // prefill items, decode items, partial slots, merge entries
+  // requests cut into key chunks: candidate partial rows, then chunked
+  // requests, their output rows and partial rows
+  long long run_cand = 0;
+  int4 run_c = int4{0, 0, 0, 0};
+  const int Hq = G * Hkv;
   for (int base = 0; base < a.B; base += kPlanThreads) {
     const int b = base + tid;
-    ReqPlan rp = {0, 0, 0, 0, 0, 0, 0, 0};
+    ReqPlan rp = {0, 0, 0, 0, 0, 0, 0, 1, 0, {0, 0, 0}};
     int4 cnt = int4{0, 0, 0, 0};
     if (b < a.B) {
       if (base == 0) {
@@ -1301,6 +1350,38 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       } else {
         request_shape(a, b, &rp.nq, &rp.L, &rp.q0);
       }
+    }
+    // A prefill-mode request of at least long_keys keys is cut into chunks of
+    // chunk_keys keys, in request order while the partial rows fit the budget.
+    int nchunk = 1;
+    if (b < a.B && a.long_keys > 0 && rp.nq > 0 && rp.nq * G > kDecodeRows &&
+        rp.L >= a.long_keys) {
+      const int n = (rp.L + a.chunk_keys - 1) / a.chunk_keys;
+      if (n > 1 && n <= kMaxSplits) nchunk = n;
+    }
+    const long long cand = nchunk > 1 ? (long long)rp.nq * Hq * nchunk : 0;
+    {
+      int4 tot_a;
+      // (capped at budget + 1: a capped prefix exceeds the budget exactly when
+      // the true one does, and 1024 capped values cannot overflow the scan)
+      const int cand_i = (int)min(cand, (long long)a.crow_budget + 1);
+      const int4 ex_a = block_exclusive_scan4<kPlanThreads>(int4{cand_i, 0, 0, 0}, sh, &tot_a);
+      if (nchunk > 1 && run_cand + ex_a.x + cand_i > a.crow_budget) nchunk = 1;
+      run_cand = min(run_cand + tot_a.x, (long long)a.crow_budget + 1);
+    }
+    rp.nchunk = nchunk;
+    {
+      int4 tot_c;
+      const int4 cc = nchunk > 1 ? int4{1, rp.nq * Hq, rp.nq * Hq * nchunk, 0} : int4{0, 0, 0, 0};
+      const int4 ex_c = block_exclusive_scan4<kPlanThreads>(cc, sh, &tot_c);
+      if (nchunk > 1) {
+        rp.pbase = run_c.z + ex_c.z;
+        reinterpret_cast<int4*>(a.cmerge)[run_c.x + ex_c.x] =
+            int4{b, run_c.y + ex_c.y, nchunk, rp.pbase};
+      }
+      run_c = int4{run_c.x + tot_c.x, run_c.y + tot_c.y, run_c.z + tot_c.z, 0};
+    }
+    if (b < a.B) {
       const int rows = rp.nq * G;
       if (rp.nq > 0 && rows <= kDecodeRows) {
         decode_split(rp.L, chunk, is_tail_request(b, a.B), &rp.per, &rp.nsplit);
@@ -1311,7 +1392,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         }
       } else if (rp.nq > 0) {
         rp.nblk = (rows + kPrefillRows - 1) / kPrefillRows;
-        cnt.x = Hkv * rp.nblk;
+        cnt.x = Hkv * rp.nblk * rp.nchunk;
       }
     }
     int4 tot;
@@ -1356,6 +1437,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     a.ctrl->n_pre = run.x;
     a.ctrl->n_items = run.x + run.y;
     a.ctrl->n_merge = run.w;
+    a.ctrl->n_cmerge = run_c.x;
+    a.ctrl->n_crows = run_c.y;
     a.ctrl->work_counter = 0;
 #pragma unroll
     for (int x = 0; x < 8; ++x) a.ctrl->xcd_counter[x] = 0;
@@ -1431,7 +1514,72 @@ __global__ __launch_bounds__(kThreads) void mha_forward_merge_kernel(MhaArgs a) 
   }
 }
 
+// Merge of the key chunks of the requests the planner cut: one wave per 4
+// output rows of the concatenated rows of those requests (16 lanes per row,
+// D / 16 consecutive columns each), folding the request's nchunk partial rows
+// with a running log-sum-exp, then the sink logit if any.
+template <int D>
+__global__ __launch_bounds__(kThreads) void mha_chunk_merge_kernel(MhaArgs a) {
+  constexpr int NC = D / 16;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int c0 = (lane & 15) * NC;
+  const int n_cm = a.ctrl->n_cmerge, n_rows = a.ctrl->n_crows;
+  const int4* cm = reinterpret_cast<const int4*>(a.cmerge);
+  const int stride = gridDim.x * (kThreads / 64);
+  for (int u = blockIdx.x * (kThreads / 64) + wv; 4 * u < n_rows; u += stride) {
+    const int r = 4 * u + (lane >> 4);
+    if (r >= n_rows) continue;
+    int lo = 0, hi = n_cm - 1;  // last entry whose first row is <= r
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (cm[mid].y <= r) lo = mid; else hi = mid - 1;
+    }
+    const int4 e = cm[lo];
+    const int lr = r - e.y, nchunk = e.z;
+    const int j = lr / a.Hq, head = lr - j * a.Hq;
+    const int64_t out_row = (int64_t)(a.req[e.x].q0 + j) * a.Hq + head;
+    const int64_t p0 = (int64_t)e.w + (int64_t)lr * nchunk;
+    float m = kNegInf, wsum = 0.f;
+    float o[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) o[c] = 0.f;
+#pragma unroll 4
+    for (int sp = 0; sp < nchunk; ++sp) {
+      const float ls = a.cpart_lse[p0 + sp];
+      const floatx4* po = reinterpret_cast<const floatx4*>(a.cpart_o + (p0 + sp) * D + c0);
+      floatx4 v[NC / 4];
+#pragma unroll
+      for (int c = 0; c < NC / 4; ++c) v[c] = po[c];
+      const float mn = fmaxf(m, ls);
+      const float f = mn == kNegInf ? 1.f : __expf(m - mn);
+      const float w = ls == kNegInf ? 0.f : __expf(ls - mn);
+      m = mn;
+      wsum = fmaf(wsum, f, w);
+#pragma unroll
+      for (int c = 0; c < NC / 4; ++c)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[4 * c + k] = fmaf(w, v[c][k], o[4 * c + k] * f);
+    }
+    float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    float lse = wsum > 0.f ? m + __logf(wsum) : kNegInf;
+    if (a.sinks) inv *= fold_sink(a.sinks[head], &lse);
+    __bf16* op = (__bf16*)a.out + out_row * D + c0;
+#pragma unroll
+    for (int c = 0; c < NC; c += 4)
+      *reinterpret_cast<u32x2*>(op + c) =
+          u32x2{pack_bf16x2(o[c] * inv, o[c + 1] * inv), pack_bf16x2(o[c + 2] * inv, o[c + 3] * inv)};
+    if ((lane & 15) == 0 && a.lse) a.lse[out_row] = lse;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_mha_chunk_merge(const MhaArgs& a, int Dv, int grid, hipStream_t s) {
+  if (Dv == 128) hipLaunchKernelGGL(mha_chunk_merge_kernel<128>, dim3(grid), dim3(kThreads), 0, s, a);
+  else if (Dv == 64) hipLaunchKernelGGL(mha_chunk_merge_kernel<64>, dim3(grid), dim3(kThreads), 0, s, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
@@ -1542,7 +1690,7 @@ hipError_t launch_mha_chunked(const MhaArgs& a, int variant, hipStream_t s) {
   });
 }
 
-FwdWorkspace fwd_workspace_layout(int B, int Hkv, int D, int target_items) {
+FwdWorkspace fwd_workspace_layout(int B, int Hkv, int D, int target_items, int64_t long_rows) {
   FwdWorkspace w;
   auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
   // Decode-mode items (and so partial slots) of one call: a (request, KV head)
@@ -1566,6 +1714,13 @@ FwdWorkspace fwd_workspace_layout(int B, int Hkv, int D, int target_items) {
   off = align(off + (size_t)w.cap_slots * kDecodeRows * sizeof(float));
   w.po_off = off;
   off = align(off + (size_t)w.cap_slots * kDecodeRows * D * sizeof(float));
+  w.crow_budget = (int32_t)std::min<int64_t>(std::max<int64_t>(long_rows, 0), INT32_MAX / 4);
+  w.cmerge_off = off;
+  off = align(off + (w.crow_budget > 0 ? (size_t)B * 4 * sizeof(int32_t) : 0));
+  w.cpl_off = off;
+  off = align(off + (size_t)w.crow_budget * sizeof(float));
+  w.cpo_off = off;
+  off = align(off + (size_t)w.crow_budget * D * sizeof(float));
   w.total = off;
   return w;
 }

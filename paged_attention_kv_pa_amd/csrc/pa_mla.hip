@@ -291,10 +291,13 @@ __device__ __forceinline__ void mla_keys(const MlaArgs& a, char* mla_smem, int t
         x[v] = key < t1k ? x[v] : kNegInf;
       }
     }
-    float tmax = x[0];
+    float tm0 = fmaxf(x[0], x[1]), tm1 = fmaxf(x[8], x[9]);  // two chains
 #pragma unroll
-    for (int v = 1; v < 16; ++v) tmax = fmaxf(tmax, x[v]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    for (int v = 2; v < 8; ++v) {
+      tm0 = fmaxf(tm0, x[v]);
+      tm1 = fmaxf(tm1, x[v + 8]);
+    }
+    const float tmax = xor32_max(fmaxf(tm0, tm1));
     const bool grow = (tmax - m) * sc > kLazyLog2;  // always true on the first tile
     if (__builtin_amdgcn_ballot_w64(grow)) {
       const float mnew = grow ? tmax : m;
@@ -316,12 +319,13 @@ __device__ __forceinline__ void mla_keys(const MlaArgs& a, char* mla_smem, int t
       m = mnew;
     }
     const float msc = (m == kNegInf ? 0.f : m) * sc;
-    float p[16];
+    float p[16], ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       p[v] = fast_exp2(fmaf(x[v], sc, -msc));
-      l += p[v];
+      ps[v & 3] += p[v];
     }
+    l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
     bf16x8 pf[2];  // B operand of O^T per 16-key step kk: keys 16 kk + 8h + i
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
@@ -362,7 +366,7 @@ __device__ __forceinline__ void mla_keys(const MlaArgs& a, char* mla_smem, int t
   // have retired before acc is read: the wait is tied to the last two tiles
   // (earlier tiles were written at least four instructions before the end).
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[DT - 1]), "+a"(acc[DT - 2]));
-  const float lrow = l + __shfl_xor(l, 32);
+  const float lrow = xor32_sum(l);
   if (!row_ok) return;
   const float inv = lrow > 0.f ? 1.f / lrow : 0.f;
   const float lse = lrow > 0.f ? m * a.scale + __log2f(lrow) * kLn2 : kNegInf;

@@ -311,6 +311,22 @@ def deepseek_mla(case: int = 0, device="cpu", batch: int = 64, lo: int = 1024,
                       name="deepseek_mla/%d" % case)
 
 
+def qwen3_mixed_with_long_extend(case: int = 0, device="cpu", new_tokens: int = 256,
+                                 cached: int = 131072, **mix) -> Batch:
+    """The Qwen3-235B mixed batch (keyword arguments as for qwen3_mixed) with one
+    more extend request after it: `new_tokens` new tokens on `cached` cached
+    ones (a context of at least 100K keys, which pa_forward cuts into key
+    chunks inside the batch)."""
+    base = qwen3_mixed(case, n_decode=mix.get("n_decode", 48), n_extend=mix.get("n_extend", 8),
+                       n_prefill=mix.get("n_prefill", 8), dec=mix.get("dec", (1024, 16384)),
+                       ext_q=mix.get("ext_q", (256, 2048)), ext_c=mix.get("ext_c", (4096, 32768)),
+                       pre_q=mix.get("pre_q", (512, 8192)))
+    return make_batch(base.q_lens + [new_tokens], base.ctx_lens + [cached], num_q_heads=64,
+                      num_kv_heads=4, head_dim_qk=128, page_size=16, dtype=BF16,
+                      seed=case_seed(4, 200 + case), device=device,
+                      name="qwen3_mixed_with_long_extend/%d" % case)
+
+
 def deepseek_mha_prefill(case: int = 0, device="cpu", n_extend: int = 8, n_prefill: int = 8,
                          ext_q=(256, 2048), ext_c=(4096, 32768), pre_q=(512, 8192),
                          heads: int = 128, page_size: int = 64) -> Batch:

@@ -491,6 +491,26 @@ def test_chunked_long_extend_full_size_all_rows():
     chunked_parity(b, 8192, "chunked long extend full size (all rows)", ref=ref, partials=False)
 
 
+LONG_MIX = dict(n_decode=6, n_extend=2, n_prefill=2, dec=(1024, 4096), ext_q=(256, 500),
+                ext_c=(4096, 8192), pre_q=(512, 1200))
+
+
+@pytest.mark.parametrize("mask,prefixes,with_sinks,alibi", [
+    (pa.PA_MASK_CAUSAL, None, False, False),
+    (pa.PA_MASK_FULL, None, True, False),
+    (pa.PA_MASK_PREFIX, [0] * 10 + [131000], False, False),
+    (pa.PA_MASK_CAUSAL, None, True, True)])
+def test_long_extend_cut_into_chunks_inside_a_mixed_batch(mask, prefixes, with_sinks, alibi):
+    # a scaled Qwen3 mixed batch plus one extend of 8 new tokens on 131072 cached
+    # ones: the planner cuts that request (>= 100K keys) into 32K-key chunks whose
+    # partial rows the chunk merge combines, inside the same persistent call
+    b = workload.qwen3_mixed_with_long_extend(1, new_tokens=8, cached=131072, **LONG_MIX)
+    masked_parity(b, mask, prefixes, "long extend in mixed batch mask %d" % mask,
+                  sinks=sink_logits(64, 13) if with_sinks else None,
+                  alibi=workload.alibi_slopes(64) if alibi else None,
+                  alibi_mode=pa.PA_ALIBI_SQRT if alibi else pa.PA_ALIBI_NONE)
+
+
 def padded_call(b, route_expected):
     """pa_forward with 7 padding rows past query_start_loc[B] in q, out and lse: the
     padding rows of out / lse must keep their sentinel bytes."""
