@@ -430,6 +430,30 @@ def main():
             "step": roof(workload.algorithmic_bytes(nab), nflops, n_step_ms, nab.num_tokens,
                          copy_gbs)}
         del nab
+        # the same prefill + extend sub-batch with the ALiBi-sqrt bias (standard slopes)
+        al = torch.tensor(workload.alibi_slopes(pre.num_q_heads), dtype=torch.float32, device=dev)
+        a_mo = torch.empty(pre.num_tokens, pre.num_q_heads, pre.head_dim_v, dtype=pre.dtype,
+                           device=dev)
+        a_dims = pa.make_dims(pre.q, pre.k_cache, pre.v_cache, pre.block_table, pre.seq_lens,
+                              pre.num_tokens, max_seq_len=max(pre.seq_lens_list),
+                              max_q_len=max(pre.q_lens))
+        a_ws = torch.empty(pa.pa_workspace_size(a_dims), dtype=torch.uint8, device=dev)
+
+        def astep():
+            pa.pa_forward_masked(pre.q, pre.k_cache, pre.v_cache, pre.block_table, pre.seq_lens,
+                                 pre.query_start_loc, pre.scale, pa.PA_MASK_CAUSAL, out=a_mo,
+                                 workspace=a_ws, max_seq_len=max(pre.seq_lens_list),
+                                 max_q_len=max(pre.q_lens), alibi_slopes=al,
+                                 alibi_mode=pa.PA_ALIBI_SQRT)
+
+        a_step_ms, a_kern_ms = time_steps(astep, psteps, 2, lib)
+        atf = flops / (a_kern_ms * 1e-3) / 1e12
+        result["prefill_alibi_sqrt"] = {
+            "workload": "the prefill + extend sub-batch above through pa_forward_masked with the "
+                        "ALiBi-sqrt bias (slopes 2^(-8(h+1)/64))",
+            "value": round(atf, 2), "unit": "TFLOP/s", "frac": round(atf / BF16_PEAK_TFLOPS, 4),
+            "kernel_ms": round(a_kern_ms, 4), "ms_per_step": round(a_step_ms, 4)}
+        del a_mo, a_ws, al
         m_step_ms, m_kern_ms = timed_forward(full, psteps)
         result["mixed_batch"] = {
             "workload": "Qwen3-235B-shaped mixed batch, all 64 requests [48 decode : 8 extend : "
@@ -438,7 +462,18 @@ def main():
             "new_tokens_per_s": round(full.num_tokens / (m_step_ms * 1e-3), 1),
             "step": roof(workload.algorithmic_bytes(full), workload.algorithmic_flops(full),
                          m_step_ms, full.num_tokens, copy_gbs)}
-        del full, pre
+        # the whole mixed batch plus one extend of 256 new tokens on 131072 cached
+        # ones, which pa_forward's planner cuts into 32K-key chunks inside the batch
+        lx = workload.qwen3_mixed_with_long_extend(0, device=dev)
+        x_step_ms, x_kern_ms = timed_forward(lx, psteps)
+        result["mixed_batch_with_long_extend"] = {
+            "workload": "the Qwen3-235B-shaped mixed batch above plus one extend of 256 new "
+                        "tokens on 131072 cached tokens (cut into 32K-key chunks by the planner) "
+                        "in one pa_forward call",
+            "ms_per_step": round(x_step_ms, 4), "kernel_ms": round(x_kern_ms, 4),
+            "step": roof(workload.algorithmic_bytes(lx), workload.algorithmic_flops(lx),
+                         x_step_ms, lx.num_tokens, copy_gbs)}
+        del lx, full, pre
 
     if not args.no_extra:
         xsteps = max(10, args.steps // 2)
