@@ -83,8 +83,21 @@ typedef enum pa_status {
   PA_ERR_UNSUPPORTED = 2,  /* valid but not implemented (head dim, page size ...) */
   PA_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than required            */
   PA_ERR_HIP = 4,          /* a HIP call or kernel launch failed                 */
-  PA_ERR_DEVICE_DATA = 5   /* pa_validate only: device contents are invalid      */
+  PA_ERR_DEVICE_DATA = 5   /* device contents are invalid (pa_validate, and the  */
+                           /* debug build below)                                 */
 } pa_status;
+
+/*
+ * Debug build.  libpa_debug.so is this library compiled with PA_DEBUG: its
+ * kernels check every block-table entry they read against [0, num_pages); an
+ * entry outside it is replaced by page 0 (so nothing outside the pool is
+ * read) and recorded in a per-GPU device flag.  Every call that reads a block
+ * table (pa_forward, pa_forward_masked, pa_forward_noalloc, pa_decode_split,
+ * pa_forward_chunked, mla_decode) then waits for its stream and returns
+ * PA_ERR_DEVICE_DATA if the flag was set (its outputs are then garbage).
+ * The release libpa.so does neither: block-table contents are the caller's
+ * contract there (pa_validate checks them on request).
+ */
 
 typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
 

@@ -12,7 +12,7 @@ from .binding import (PA_ALIBI_LINEAR, PA_ALIBI_NONE, PA_ALIBI_SQRT, PA_MASK_CAU
                       pa_merge_lse, pa_noalloc_max_workspace,
                       pa_status_string,
                       pa_validate, pa_workspace_size, mla_decode, mla_workspace_size,
-                      library, library_path, make_dims)
+                      library, library_path, make_dims, set_debug)
 
 __all__ = ["PaError", "pa_forward", "pa_forward_masked", "pa_forward_chunked", "pa_decode_split",
            "pa_forward_noalloc", "pa_noalloc_max_workspace",
@@ -20,4 +20,4 @@ __all__ = ["PaError", "pa_forward", "pa_forward_masked", "pa_forward_chunked", "
            "PA_ALIBI_NONE", "PA_ALIBI_LINEAR", "PA_ALIBI_SQRT",
            "mla_decode",
            "pa_workspace_size", "mla_workspace_size", "pa_validate", "pa_status_string",
-           "library", "library_path", "make_dims"]
+           "library", "library_path", "make_dims", "set_debug"]

@@ -16,7 +16,9 @@ from typing import Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_PKG, "libpa.so")
+_RELEASE_PATH = os.path.join(_PKG, "libpa.so")
+_DEBUG_PATH = os.path.join(_PKG, "libpa_debug.so")
+_LIB_PATH = _RELEASE_PATH
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_DEVICE_DATA = range(6)
 PA_F32, PA_BF16 = 0, 1
@@ -46,13 +48,25 @@ def library_path() -> str:
     return _LIB_PATH
 
 
+def set_debug(enabled: bool) -> None:
+    """Send later calls to libpa_debug.so (the PA_DEBUG build: block-table
+    entries outside the page pool are reported as PA_ERR_DEVICE_DATA) or back
+    to libpa.so."""
+    global _lib, _LIB_PATH
+    with _lock:
+        path = _DEBUG_PATH if enabled else _RELEASE_PATH
+        if path != _LIB_PATH:
+            _LIB_PATH, _lib = path, None
+
+
 def library():
-    """Load libpa.so (once).  Raises if it has not been built."""
+    """Load the selected library (once).  Raises if it has not been built."""
     global _lib
     with _lock:
         if _lib is None:
             if not os.path.exists(_LIB_PATH):
-                raise RuntimeError("libpa.so is not built (run paged_attention_kv_pa_amd.build.build())")
+                raise RuntimeError("%s is not built (run paged_attention_kv_pa_amd.build.build())"
+                                   % os.path.basename(_LIB_PATH))
             lib = ctypes.CDLL(_LIB_PATH)
             p, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
             dp = ctypes.POINTER(PaDims)

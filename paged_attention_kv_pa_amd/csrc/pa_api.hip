@@ -45,6 +45,49 @@ constexpr size_t kScratchBytes = 64ull << 20;
 __device__ __align__(256) char scratch[kScratchBytes];
 std::map<int, void*> g_scratch;  // device -> address of its copy (under g_mu)
 
+#ifdef PA_DEBUG
+// Debug builds: one flag per GPU, set by a kernel that met a block-table entry
+// outside the pool (checked_page).  It starts at zero; every call that reads
+// a block table waits for its stream, reads it and clears it when set.
+__device__ int32_t debug_bad_page;
+std::map<int, int32_t*> g_debug;  // device -> address of its flag (under g_mu)
+int32_t* debug_flag() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_debug.find(dev);
+  if (it == g_debug.end()) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(debug_bad_page)) != hipSuccess) return nullptr;
+    it = g_debug.emplace(dev, (int32_t*)ptr).first;
+  }
+  return it->second;
+}
+#else
+int32_t* debug_flag() { return nullptr; }
+#endif
+
+// Debug builds: after a call's launches, wait for its stream and report
+// PA_ERR_DEVICE_DATA if a kernel set the flag (then cleared again; it starts
+// at zero).  Release builds: nothing.
+pa_status debug_end(pa_status st, hipStream_t s) {
+#ifdef PA_DEBUG
+  if (st != PA_OK) return st;
+  int32_t* f = debug_flag();
+  if (!f) return PA_ERR_HIP;
+  int32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, f, sizeof(int32_t), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e == hipSuccess && v) e = hipMemsetAsync(f, 0, sizeof(int32_t), s);  // clear for the next call
+  if (e == hipSuccess && v) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e);
+  return v ? PA_ERR_DEVICE_DATA : PA_OK;
+#else
+  (void)s;
+  return st;
+#endif
+}
+
 pa_status scratch_address(void** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -277,7 +320,7 @@ static_assert(PA_MASK_CAUSAL == pa::kMaskCausal && PA_MASK_FULL == pa::kMaskFull
                   PA_MASK_PREFIX == pa::kMaskPrefix,
               "mask codes");
 
-pa_status pa_forward_masked(const void* q, const void* k_cache, const void* v_cache,
+static pa_status forward_masked_impl(const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* block_table, const int32_t* seq_lens,
                             const int32_t* query_start_loc, int32_t mask,
                             const int32_t* prefix_lens, const float* sinks,
@@ -322,6 +365,8 @@ pa_status pa_forward_masked(const void* q, const void* k_cache, const void* v_ca
     a.Dv = d->head_dim_v;
     a.P = d->page_size;
     a.max_pages = d->max_pages_per_seq;
+    a.num_pages = d->num_pages;
+    a.dbg = debug_flag();
     a.num_splits = 1;
     a.mask = mask;
     a.prefix_lens = prefix_lens;
@@ -367,6 +412,8 @@ pa_status pa_forward_masked(const void* q, const void* k_cache, const void* v_ca
     a.G = G;
     a.P = d->page_size;
     a.max_pages = d->max_pages_per_seq;
+    a.num_pages = d->num_pages;
+    a.dbg = debug_flag();
     a.num_splits = route.S;
     a.chunk_keys = route.C;
     a.row_blocks = route.row_blocks;
@@ -447,6 +494,8 @@ pa_status pa_forward_masked(const void* q, const void* k_cache, const void* v_ca
   a.G = G;
   a.P = d->page_size;
   a.max_pages = d->max_pages_per_seq;
+  a.num_pages = d->num_pages;
+  a.dbg = debug_flag();
   a.num_splits = 1;
   a.target_items = pl.target_items;
   a.mask = mask;
@@ -495,7 +544,7 @@ pa_status pa_forward_noalloc(const void* q, const void* k_cache, const void* v_c
                            lse, d, ws, kScratchBytes, stream);
 }
 
-pa_status pa_decode_split(const void* q, const void* k_cache, const void* v_cache,
+static pa_status decode_split_impl(const void* q, const void* k_cache, const void* v_cache,
                           const int32_t* block_table, const int32_t* seq_lens, float scale,
                           int32_t num_splits, float* part_out, float* part_lse,
                           const pa_dims* d, void* stream) {
@@ -535,6 +584,8 @@ pa_status pa_decode_split(const void* q, const void* k_cache, const void* v_cach
     a.Dv = d->head_dim_v;
     a.P = d->page_size;
     a.max_pages = d->max_pages_per_seq;
+    a.num_pages = d->num_pages;
+    a.dbg = debug_flag();
     a.num_splits = num_splits;
     e = pa::launch_f32_split(a, s);
   } else {
@@ -554,6 +605,8 @@ pa_status pa_decode_split(const void* q, const void* k_cache, const void* v_cach
     a.G = G;
     a.P = d->page_size;
     a.max_pages = d->max_pages_per_seq;
+    a.num_pages = d->num_pages;
+    a.dbg = debug_flag();
     a.num_splits = num_splits;
     e = pa::launch_mha_split(a, pa::mha_variant(d->head_dim_qk, d->head_dim_v), s);
   }
@@ -561,7 +614,7 @@ pa_status pa_decode_split(const void* q, const void* k_cache, const void* v_cach
   return e == hipSuccess ? PA_OK : hip_fail(e);
 }
 
-pa_status pa_forward_chunked(const void* q, const void* k_cache, const void* v_cache,
+static pa_status forward_chunked_impl(const void* q, const void* k_cache, const void* v_cache,
                              const int32_t* block_table, const int32_t* seq_lens,
                              const int32_t* query_start_loc, float scale, int32_t chunk_keys,
                              int32_t num_chunks, float* part_out, float* part_lse,
@@ -604,6 +657,8 @@ pa_status pa_forward_chunked(const void* q, const void* k_cache, const void* v_c
   a.G = G;
   a.P = d->page_size;
   a.max_pages = d->max_pages_per_seq;
+  a.num_pages = d->num_pages;
+  a.dbg = debug_flag();
   a.num_splits = num_chunks;
   a.chunk_keys = chunk_keys;
   a.row_blocks = (int32_t)row_blocks;
@@ -642,7 +697,7 @@ size_t mla_workspace_size(const pa_dims* d, int32_t num_splits) {
   return mla_ws_bytes(d, num_splits);
 }
 
-pa_status mla_decode(const void* q, const void* kv_cache, const int32_t* block_table,
+static pa_status mla_decode_impl(const void* q, const void* kv_cache, const int32_t* block_table,
                      const int32_t* seq_lens, float scale, void* out, float* lse,
                      int32_t num_splits, const pa_dims* d, void* workspace,
                      size_t workspace_bytes, void* stream) {
@@ -676,6 +731,8 @@ pa_status mla_decode(const void* q, const void* kv_cache, const int32_t* block_t
     a.P = d->page_size;
     a.log2_page = __builtin_ctz((unsigned)d->page_size);
     a.max_pages = d->max_pages_per_seq;
+    a.num_pages = d->num_pages;
+    a.dbg = debug_flag();
     a.num_splits = 0;
     a.max_pieces = 2 * cfg.cu_count;
     hipError_t e = mark(g_ev_start, s);
@@ -705,6 +762,8 @@ pa_status mla_decode(const void* q, const void* kv_cache, const int32_t* block_t
   a.P = d->page_size;
   a.log2_page = __builtin_ctz((unsigned)d->page_size);
   a.max_pages = d->max_pages_per_seq;
+  a.num_pages = d->num_pages;
+  a.dbg = debug_flag();
   a.num_splits = S;
   hipError_t e = mark(g_ev_start, s);
   if (e == hipSuccess) e = pa::launch_mla_split(a, s);
@@ -715,6 +774,51 @@ pa_status mla_decode(const void* q, const void* kv_cache, const int32_t* block_t
     if (e != hipSuccess) return hip_fail(e);
   }
   return PA_OK;
+}
+
+// The entry points that read a block table (debug builds check it there).
+pa_status pa_forward_masked(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_table, const int32_t* seq_lens,
+                            const int32_t* query_start_loc, int32_t mask,
+                            const int32_t* prefix_lens, const float* sinks,
+                            const float* alibi_slopes, int32_t alibi_mode, float scale,
+                            void* out, float* lse, const pa_dims* d, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return debug_end(forward_masked_impl(q, k_cache, v_cache, block_table, seq_lens,
+                                       query_start_loc, mask, prefix_lens, sinks, alibi_slopes,
+                                       alibi_mode, scale, out, lse, d, workspace, workspace_bytes,
+                                       stream),
+                   (hipStream_t)stream);
+}
+
+pa_status pa_decode_split(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, const int32_t* seq_lens, float scale,
+                          int32_t num_splits, float* part_out, float* part_lse,
+                          const pa_dims* d, void* stream) {
+  return debug_end(decode_split_impl(q, k_cache, v_cache, block_table, seq_lens, scale,
+                                     num_splits, part_out, part_lse, d, stream),
+                   (hipStream_t)stream);
+}
+
+pa_status pa_forward_chunked(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             const int32_t* query_start_loc, float scale, int32_t chunk_keys,
+                             int32_t num_chunks, float* part_out, float* part_lse,
+                             int32_t mask, const int32_t* prefix_lens, const pa_dims* d,
+                             void* stream) {
+  return debug_end(forward_chunked_impl(q, k_cache, v_cache, block_table, seq_lens,
+                                        query_start_loc, scale, chunk_keys, num_chunks, part_out,
+                                        part_lse, mask, prefix_lens, d, stream),
+                   (hipStream_t)stream);
+}
+
+pa_status mla_decode(const void* q, const void* kv_cache, const int32_t* block_table,
+                     const int32_t* seq_lens, float scale, void* out, float* lse,
+                     int32_t num_splits, const pa_dims* d, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  return debug_end(mla_decode_impl(q, kv_cache, block_table, seq_lens, scale, out, lse,
+                                   num_splits, d, workspace, workspace_bytes, stream),
+                   (hipStream_t)stream);
 }
 
 pa_status pa_validate(const int32_t* block_table, const int32_t* seq_lens,

@@ -38,7 +38,7 @@ __device__ void f32_row(const F32Args& a, int b, int kvh, const float* qrow, int
     const int t = t0 + lane;
     float s = kNegInf;
     if (t < k1) {
-      const int page = bt[t / P];
+      const int page = checked_page(bt[t / P], a.num_pages, a.dbg);
       const float* kr = a.k_cache + (((int64_t)page * a.Hkv + kvh) * P + (t % P)) * Dqk;
       float dot = 0.f;
       for (int d = 0; d < Dqk; ++d) dot = fmaf(qs[d], kr[d], dot);
@@ -60,7 +60,7 @@ __device__ void f32_row(const F32Args& a, int b, int kvh, const float* qrow, int
     for (int c = 0; c < kF32MaxD / 64; ++c) acc[c] *= alpha;
     for (int j = 0; j < n; ++j) {
       const int tt = t0 + j;
-      const int page = bt[tt / P];
+      const int page = checked_page(bt[tt / P], a.num_pages, a.dbg);
       const float* vp = a.v_cache + ((int64_t)page * a.Hkv + kvh) * Dv * P + (tt % P);
       const float pj = ps[j];
 #pragma unroll

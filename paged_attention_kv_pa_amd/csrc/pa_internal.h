@@ -42,6 +42,24 @@ __device__ __forceinline__ int visible_end(int mask, int ctx, int t, int prefix)
   return mask == kMaskPrefix ? (prefix > causal ? prefix : causal) : causal;
 }
 
+// Physical page read from a block table.  In a PA_DEBUG build an entry
+// outside [0, num_pages) is recorded in *dbg (kept nonzero) and replaced by
+// page 0, so the kernel only reads pages of the pool and the calling entry
+// point reports PA_ERR_DEVICE_DATA; in a release build the entry is used as
+// it is (device contents are the caller's contract).
+__device__ __forceinline__ int checked_page(int pg, int num_pages, int32_t* dbg) {
+#ifdef PA_DEBUG
+  if ((unsigned)pg >= (unsigned)num_pages) {
+    if (dbg) *dbg = 1;
+    return 0;
+  }
+#else
+  (void)num_pages;
+  (void)dbg;
+#endif
+  return pg;
+}
+
 // ALiBi term of a score, in the units of the raw (unscaled) dot product:
 // m_raw * f(|d|) is subtracted, with m_raw = slope / scale and f the distance
 // (linear) or its square root (sqrt) between the query's and the key's
@@ -97,6 +115,8 @@ struct MhaArgs {
   const float* sinks;        // [Hq] sink logits or NULL (pa_forward_masked only)
   const float* alibi;        // [Hq] ALiBi slopes (kernels built with ALiBi only)
   int32_t alibi_sqrt;        // 1: square root of the distance, 0: the distance
+  int32_t num_pages;         // pages in the pool (checked_page)
+  int32_t* dbg;              // PA_DEBUG builds: bad block-table entry flag (else NULL)
 };
 
 struct PlanArgs {
@@ -134,6 +154,8 @@ struct F32Args {
   const float* sinks;          // forward mode: [Hq] sink logits or NULL
   const float* alibi;          // forward mode: [Hq] ALiBi slopes or NULL
   int32_t alibi_sqrt;          // 1: square root of the distance, 0: the distance
+  int32_t num_pages;           // pages in the pool (checked_page)
+  int32_t* dbg;                // PA_DEBUG builds: bad block-table entry flag (else NULL)
 };
 
 struct MlaArgs {
@@ -149,6 +171,8 @@ struct MlaArgs {
   float scale;
   int32_t B, Hq, P, log2_page, max_pages, num_splits;
   int32_t max_pieces;        // balanced: partial slots (two per workgroup, one workgroup per CU)
+  int32_t num_pages;         // pages in the pool (checked_page)
+  int32_t* dbg;              // PA_DEBUG builds: bad block-table entry flag (else NULL)
 };
 
 // Workspace layout of pa_forward.

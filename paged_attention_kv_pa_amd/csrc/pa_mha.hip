@@ -179,7 +179,10 @@ __device__ int run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest&
       return min(pidx, last_pg);
     };
     const int i0 = min(pidx, last_pg), i1 = next_group(), i2 = next_group(), i3 = next_group();
-    const int pg0 = bt[i0], pg1 = bt[i1], pg2 = bt[i2], pg3 = bt[i3];
+    const int pg0 = checked_page(bt[i0], a.num_pages, a.dbg);
+    const int pg1 = checked_page(bt[i1], a.num_pages, a.dbg);
+    const int pg2 = checked_page(bt[i2], a.num_pages, a.dbg);
+    const int pg3 = checked_page(bt[i3], a.num_pages, a.dbg);
     // per-lane selects of the four scalars (written out: an indexed array
     // would live in scratch memory)
     auto pick = [](int j, int v0, int v1, int v2, int v3) {
@@ -521,8 +524,8 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
     const int ts = __builtin_amdgcn_readfirstlane(t0);
     const int i0 = min(ts + 16 * kgroup, kv_end - 1) / P;
     const int i1 = min(ts + 16 * kgroup + 8, kv_end - 1) / P;
-    tp.pg0 = cbt[i0];
-    tp.pg1 = cbt[i1];
+    tp.pg0 = checked_page(cbt[i0], a.num_pages, a.dbg);
+    tp.pg1 = checked_page(cbt[i1], a.num_pages, a.dbg);
     tp.first0 = i0 * P;
     tp.first1 = i1 * P;
     return tp;

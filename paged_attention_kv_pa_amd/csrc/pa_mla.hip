@@ -155,7 +155,7 @@ __device__ __forceinline__ void mla_keys(const MlaArgs& a, char* mla_smem, int t
     if (P >= kMTK && t0 + kMTK <= t1k) {
       // all 32 keys real and in one page: a scalar page base plus a fixed
       // per-lane offset
-      const int page = bt[t0 >> lp];
+      const int page = checked_page(bt[t0 >> lp], a.num_pages, a.dbg);
       src = kv + (((int64_t)page << lp) + (t0 & (P - 1))) * (kDqk * 2) + lane_src;
     } else {
       const int key = min(t0 + dkey, t1k - 1);  // clamped: real data, masked later
@@ -164,13 +164,13 @@ __device__ __forceinline__ void mla_keys(const MlaArgs& a, char* mla_smem, int t
       const int pg0 = __builtin_amdgcn_readfirstlane(t0 >> lp);
       int page;
       if (P >= kMTK) {
-        page = bt[pg0];
+        page = checked_page(bt[pg0], a.num_pages, a.dbg);
       } else {
         const int j = (key >> lp) - pg0;  // 0 .. 32 / P - 1
-        const int p0 = bt[pg0];
-        const int p1 = bt[min(pg0 + 1, last_pg)];
-        const int p2 = bt[min(pg0 + 2, last_pg)];
-        const int p3 = bt[min(pg0 + 3, last_pg)];
+        const int p0 = checked_page(bt[pg0], a.num_pages, a.dbg);
+        const int p1 = checked_page(bt[min(pg0 + 1, last_pg)], a.num_pages, a.dbg);
+        const int p2 = checked_page(bt[min(pg0 + 2, last_pg)], a.num_pages, a.dbg);
+        const int p3 = checked_page(bt[min(pg0 + 3, last_pg)], a.num_pages, a.dbg);
         page = j == 0 ? p0 : (j == 1 ? p1 : (j == 2 ? p2 : p3));
       }
       src = kv + (((int64_t)page << lp) + (key & (P - 1))) * (kDqk * 2) + dchunk * 16;

@@ -35,6 +35,22 @@ def test_library_loads_and_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
+def test_debug_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(binding._DEBUG_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_set_debug_switches_the_library():
+    try:
+        pa.set_debug(True)
+        assert pa.library_path().endswith("libpa_debug.so")
+        assert pa.library().pa_workspace_size(None) == 0
+    finally:
+        pa.set_debug(False)
+    assert pa.library_path().endswith("libpa.so")
+
+
 def test_status_strings():
     for code in range(6):
         s = pa.pa_status_string(code)
