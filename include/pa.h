@@ -356,8 +356,9 @@ PA_API pa_status pa_validate(const int32_t* block_table, const int32_t* seq_lens
  */
 PA_API pa_status pa_set_kernel_events(void* start, void* stop);
 
-/* Static, human-readable name of a status code. */
-PA_API const char* pa_status_string(pa_status status);
+/* Static, human-readable name of a status code (any integer: values that are
+ * no pa_status give "unknown status"). */
+PA_API const char* pa_status_string(int32_t status);
 
 /* hipError_t of the last PA_ERR_HIP returned on this thread (0 if none). */
 PA_API int32_t pa_last_hip_error(void);

@@ -52,8 +52,11 @@ def _load():
     global _lib
     with _lock:
         if _lib is None:
-            build(force=False)
-            lib = ctypes.CDLL(_LIB)
+            # PA_ORACLE_LIB: another build of pa_oracle.c (a sanitizer build, say)
+            path = os.environ.get("PA_ORACLE_LIB")
+            if not path:
+                path = build(force=False)
+            lib = ctypes.CDLL(path)
             p, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
             lib.orc_attention.argtypes = [p, p, p, i32, p, p, p] + [i32] * 9 + [f32, p, p, p, i32]
             lib.orc_attention.restype = i32

@@ -16,7 +16,9 @@ from typing import Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-_RELEASE_PATH = os.path.join(_PKG, "libpa.so")
+# PA_LIBRARY names another build of the same library (a sanitizer build of
+# the host code, for instance) to load in place of the in-tree libpa.so.
+_RELEASE_PATH = os.environ.get("PA_LIBRARY") or os.path.join(_PKG, "libpa.so")
 _DEBUG_PATH = os.path.join(_PKG, "libpa_debug.so")
 _LIB_PATH = _RELEASE_PATH
 

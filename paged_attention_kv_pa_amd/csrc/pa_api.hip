@@ -273,8 +273,8 @@ pa_status check_mla(const pa_dims* d) {
 
 extern "C" {
 
-const char* pa_status_string(pa_status s) {
-  switch (s) {
+const char* pa_status_string(int32_t status) {
+  switch (status) {
     case PA_OK: return "ok";
     case PA_ERR_INVALID_ARG: return "invalid argument";
     case PA_ERR_UNSUPPORTED: return "unsupported configuration";
