@@ -264,6 +264,10 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only time a plain 2 GiB device-to-device copy (HBM reference and the "
                          "byte-counter calibration kernel)")
+    ap.add_argument("--gather-calibration", action="store_true",
+                    help="only run a gather of 131072 random 4 KiB rows of a 1 GiB pool (a second "
+                         "byte-counter calibration with the decode kernel's access pattern: "
+                         "scattered 4 KiB blocks, one K or V page of one KV head)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -287,6 +291,19 @@ def main():
         n = 2 << 30
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": round(ms, 4),
                           "read_plus_write_GBs": round(gbs, 1)}), flush=True)
+        return
+    if args.gather_calibration:
+        row_bytes, rows = 4096, (1 << 30) // 4096
+        pool = torch.empty(rows, row_bytes // 2, dtype=torch.bfloat16, device=dev).fill_(1)
+        gen = torch.Generator(device="cpu").manual_seed(7)
+        idx = torch.randperm(rows, generator=gen)[: rows // 2].to(dev)
+        gout = torch.empty(rows // 2, row_bytes // 2, dtype=torch.bfloat16, device=dev)
+        for _ in range(max(args.steps, 1)):
+            torch.index_select(pool, 0, idx, out=gout)
+        torch.cuda.synchronize()
+        print(json.dumps({"gather_rows": rows // 2, "row_bytes": row_bytes,
+                          "bytes_read": rows // 2 * row_bytes + idx.numel() * idx.element_size(),
+                          "bytes_written": rows // 2 * row_bytes}), flush=True)
         return
     sha = source_sha256()
     copy_ms, copy_gbs = copy_bandwidth(torch, dev)
