@@ -387,7 +387,7 @@ def main():
 
     # ---- prefill half of the metric: the prefill + extend requests of the Qwen3-235B
     # mixed batch (requests 48..63); the decode share (requests 0..47); the whole batch
-    if not args.no_prefill:
+    if not args.no_prefill and not args.no_extra:
         full = workload.qwen3_mixed(0, device=dev)
         psteps = max(3, args.steps // 3)
         pre = workload.sub_batch(full, range(48, 64))
