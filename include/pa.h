@@ -25,13 +25,16 @@
  *    launched; a failed check returns an error code and launches nothing.
  *    A launch failure returns PA_ERR_HIP (pa_last_hip_error() gives the
  *    hipError_t).  Nothing throws across this boundary.
- *  - DEVICE CONTENTS ARE NOT CHECKED by the compute calls (a block-table entry
- *    outside [0, num_pages), seq_len < q_len, a non-monotone
- *    query_start_loc ...): they are undefined behaviour there.  pa_validate()
- *    checks them synchronously.
+ *  - DEVICE CONTENTS ARE NOT CHECKED by the compute calls of libpa.so (a
+ *    block-table entry outside [0, num_pages), seq_len < q_len, a
+ *    non-monotone query_start_loc ...): they are undefined behaviour there.
+ *    pa_validate() checks them synchronously; the debug build libpa_debug.so
+ *    checks block-table entries as it reads them (see "Debug build" below).
  *  - Calls are graph-capture safe: each call is a fixed sequence of kernel
  *    launches whose grids depend only on the pa_dims capacities, never on
- *    device contents, and no call issues a memset or a host synchronisation.
+ *    device contents, and no call issues a memset or a host synchronisation
+ *    (in libpa.so; the debug build waits for its stream after every call
+ *    that reads a block table).
  *    A captured call may be replayed after the caller rewrites seq_lens,
  *    query_start_loc and block_table in place (within the capacities).
  *
