@@ -869,13 +869,23 @@ __device__ __forceinline__ void shape_of(const int32_t* qsl, const int32_t* seq_
   *L = l;
 }
 
+// Smallest decode partition of a call with dec_reqs decode-mode requests.
+// When the (request, KV head) pairs alone give every workgroup of the grid
+// about two items (target_items is kItemsPerWorkgroup per workgroup), cutting
+// short requests only adds partial rows and a merge: the floor is then
+// kMinChunkWide.  Fewer pairs need the cuts for parallelism: kMinChunk.
+__device__ __forceinline__ long long decode_min_chunk(int dec_reqs, int Hkv, int target_items) {
+  const long long pairs = (long long)dec_reqs * Hkv;
+  return pairs * 2 * kItemsPerWorkgroup >= target_items ? kMinChunkWide : kMinChunk;
+}
+
 // Keys per decode partition: the decode work (keys x KV heads) spread over
-// about target_items items, at least kMinChunk keys, a multiple of 64.
+// about target_items items, at least minc keys, a multiple of 64.
 __device__ __forceinline__ long long decode_chunk(unsigned long long dec_keys, int Hkv,
-                                                  int target_items) {
+                                                  int target_items, long long minc) {
   const unsigned long long work = dec_keys * (unsigned long long)Hkv;
   long long chunk = (long long)((work + target_items - 1) / (unsigned long long)target_items);
-  chunk = chunk < kMinChunk ? kMinChunk : chunk;
+  chunk = chunk < minc ? minc : chunk;
   return (chunk + 63) & ~63LL;
 }
 
@@ -883,12 +893,12 @@ __device__ __forceinline__ long long decode_chunk(unsigned long long dec_keys, i
 // request order, so the last requests' items run last: cutting those finer
 // shortens the tail where workgroups finish at different times (the extra
 // partial rows stay few).
-__device__ __forceinline__ void decode_split(int L, long long chunk, bool tail, int* per,
-                                             int* nsplit) {
+__device__ __forceinline__ void decode_split(int L, long long chunk, long long minc, bool tail,
+                                             int* per, int* nsplit) {
   long long ck = chunk;
   if (tail) {
     ck = (chunk / kTailDivisor + 63) & ~63LL;
-    ck = ck < kMinChunk ? kMinChunk : ck;
+    ck = ck < minc ? minc : ck;
   }
   long long sp = (L + ck - 1) / ck;
   sp = sp < 1 ? 1 : (sp > kMaxFwdSplits ? kMaxFwdSplits : sp);
@@ -937,23 +947,38 @@ struct FusedPlan {
   int soff[kFusedPlanMax + 1];  // first partial slot
   int4 wsum[kThreads / 64];
   unsigned long long keys;
+  int reqs;       // decode-mode requests
+  long long minc;  // smallest partition (decode_min_chunk)
 };
 
 __device__ long long fused_plan(const MhaArgs& a, FusedPlan& fp) {
   const int tid = threadIdx.x;
-  if (tid == 0) fp.keys = 0;
+  if (tid == 0) {
+    fp.keys = 0;
+    fp.reqs = 0;
+  }
   __syncthreads();
   unsigned long long my_keys = 0;
+  int my_reqs = 0;
   for (int b = tid; b < a.num_seqs; b += kThreads) {
     int nq, L, q0;
     shape_of(a.qsl, a.seq_lens, a.max_pages, a.P, b, &nq, &L, &q0);
-    if (nq > 0) my_keys += (unsigned long long)L;
+    if (nq > 0) {
+      my_keys += (unsigned long long)L;
+      ++my_reqs;
+    }
   }
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) my_keys += __shfl_xor(my_keys, o);
+  for (int o = 32; o >= 1; o >>= 1) {
+    my_keys += __shfl_xor(my_keys, o);
+    my_reqs += __shfl_xor(my_reqs, o);
+  }
   if ((tid & 63) == 0 && my_keys) atomicAdd(&fp.keys, my_keys);
+  if ((tid & 63) == 0 && my_reqs) atomicAdd(&fp.reqs, my_reqs);
   __syncthreads();
-  const long long chunk = decode_chunk(fp.keys, a.Hkv, a.target_items);
+  const long long minc = decode_min_chunk(fp.reqs, a.Hkv, a.target_items);
+  const long long chunk = decode_chunk(fp.keys, a.Hkv, a.target_items, minc);
+  if (tid == 0) fp.minc = minc;  // read after the barrier at the end
   int4 run = int4{0, 0, 0, 0};  // decode items, partial slots, merge entries
   for (int base = 0; base < a.num_seqs; base += kThreads) {
     const int b = base + tid;
@@ -962,7 +987,7 @@ __device__ long long fused_plan(const MhaArgs& a, FusedPlan& fp) {
     if (b < a.num_seqs) {
       shape_of(a.qsl, a.seq_lens, a.max_pages, a.P, b, &nq, &L, &q0);
       if (nq > 0) {
-        decode_split(L, chunk, is_tail_request(b, a.num_seqs), &per, &nsplit);
+        decode_split(L, chunk, minc, is_tail_request(b, a.num_seqs), &per, &nsplit);
         cnt.x = a.Hkv * nsplit;
         if (nsplit > 1) {
           cnt.y = a.Hkv * nsplit;
@@ -997,7 +1022,7 @@ __device__ WorkItem fused_item(const MhaArgs& a, const FusedPlan& fp, long long 
   const int b = find_request(fp.doff, a.num_seqs, j);
   int nq, L, q0, per, nsplit;
   shape_of(a.qsl, a.seq_lens, a.max_pages, a.P, b, &nq, &L, &q0);
-  decode_split(L, chunk, is_tail_request(b, a.num_seqs), &per, &nsplit);
+  decode_split(L, chunk, fp.minc, is_tail_request(b, a.num_seqs), &per, &nsplit);
   const int local = j - fp.doff[b];
   const int kvh = local / nsplit, sp = local - kvh * nsplit;
   WorkItem it;
@@ -1309,14 +1334,19 @@ __device__ __forceinline__ void request_shape(const PlanArgs& a, int b, int* nq,
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ int4 sh[kPlanThreads / 64];
   __shared__ unsigned long long s_dec_keys;
+  __shared__ int s_dec_reqs;
   __shared__ int s_doff[kPlanThreads + 1];
   __shared__ ReqPlan s_plan[kPlanThreads];
   const int tid = threadIdx.x;
   const int G = a.G, Hkv = a.Hkv;
-  if (tid == 0) s_dec_keys = 0;
+  if (tid == 0) {
+    s_dec_keys = 0;
+    s_dec_reqs = 0;
+  }
   __syncthreads();
-  // pass 1: total decode-mode keys, which sets the partition size
+  // pass 1: total decode-mode keys and requests, which set the partition size
   unsigned long long my_keys = 0;
+  int my_reqs = 0;
   int nq_first = 0, L_first = 0, q0_first = 0;  // request tid, reused by pass 2
   for (int b = tid; b < a.B; b += kPlanThreads) {
     int nq, L, q0;
@@ -1326,13 +1356,21 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       L_first = L;
       q0_first = q0;
     }
-    if (nq > 0 && nq * G <= kDecodeRows) my_keys += (unsigned long long)L;
+    if (nq > 0 && nq * G <= kDecodeRows) {
+      my_keys += (unsigned long long)L;
+      ++my_reqs;
+    }
   }
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) my_keys += __shfl_xor(my_keys, o);
+  for (int o = 32; o >= 1; o >>= 1) {
+    my_keys += __shfl_xor(my_keys, o);
+    my_reqs += __shfl_xor(my_reqs, o);
+  }
   if ((tid & 63) == 0 && my_keys) atomicAdd(&s_dec_keys, my_keys);
+  if ((tid & 63) == 0 && my_reqs) atomicAdd(&s_dec_reqs, my_reqs);
   __syncthreads();
-  const long long chunk = decode_chunk(s_dec_keys, Hkv, a.target_items);
+  const long long minc = decode_min_chunk(s_dec_reqs, Hkv, a.target_items);
+  const long long chunk = decode_chunk(s_dec_keys, Hkv, a.target_items, minc);
 
   // pass 2: per-request counts, exclusive scans, plans
   int4 run = int4{0, 0, 0, 0};  // prefill items, decode items, partial slots, merge entries
@@ -1387,7 +1425,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     if (b < a.B) {
       const int rows = rp.nq * G;
       if (rp.nq > 0 && rows <= kDecodeRows) {
-        decode_split(rp.L, chunk, is_tail_request(b, a.B), &rp.per, &rp.nsplit);
+        decode_split(rp.L, chunk, minc, is_tail_request(b, a.B), &rp.per, &rp.nsplit);
         cnt.y = Hkv * rp.nsplit;
         if (rp.nsplit > 1) {
           cnt.z = Hkv * rp.nsplit;
