@@ -1090,7 +1090,11 @@ void mha_forward_kernel(MhaArgs a) {
   // by the previous call's merge kernel, or else takes a fixed item sequence
   // (see Control).  `ready` is not written while this kernel runs, so every
   // workgroup reads the same value.
-  const bool queue = !FUSED || __builtin_amdgcn_readfirstlane(a.ctrl->ready) == kQueueReady;
+  // A decode-only call with no more items than workgroups has nothing to
+  // hand out: its workgroups skip the claim (an atomic round trip on the
+  // path of the call's last item).
+  const bool queue = (!DECODE_ONLY || n_dec > (int)gridDim.x) &&
+                     (!FUSED || __builtin_amdgcn_readfirstlane(a.ctrl->ready) == kQueueReady);
   int32_t* const counter = queue ? &a.ctrl->work_counter : nullptr;
   int idx;
   WorkItem it;
