@@ -402,10 +402,10 @@ struct PrefillLayout {
   static constexpr int kKBytes = kTK * DK * 2;           // K tile
   static constexpr int kVBytes = kTK * DV * 2;           // V^T tile
   static constexpr int kRingBytes = kKStages * kKBytes + kVStages * kVBytes;
-  static constexpr int kKCopies = kChunks / 8;           // K copies per wave per tile
-  static constexpr int kVCopies = DV / 64;               // V copies per wave per tile
+  static constexpr int kKCopies = kChunks / 4;           // K copies per wave per tile
+  static constexpr int kVCopies = DV / 32;               // V copies per wave per tile
   static constexpr int kCopies = kKCopies + kVCopies;    // copy instructions per thread per tile
-  static_assert(kChunks % 8 == 0 && DV % 64 == 0, "head dims");
+  static_assert(kChunks % 8 == 0 && DV % 32 == 0, "head dims");
   // byte offsets of tile t's K and V^T stages in the ring
   __device__ static __forceinline__ int kstage(int t) { return (t % kKStages) * kKBytes; }
   __device__ static __forceinline__ int vstage(int t) {
@@ -418,8 +418,12 @@ struct PrefillLayout {
     return (((((k >> 4) * (kChunks / 4) + (c >> 2)) * 16 + (k & 15)) * 4) +
             ((c & 3) ^ ((k >> 2) & 3))) * 16;
   }
-  // byte offset of key chunk c (keys 8c .. 8c + 7), column d in the V^T tile
-  __device__ static __forceinline__ int voff(int c, int d) { return (c * DV + d) * 16; }
+  // byte offset of key chunk c (keys 8c .. 8c + 7), column d in the V^T tile:
+  // per 16-key group, column-major, the group's two 8-key chunks of a column
+  // side by side (the 32 bytes one column of a 16-key page row holds)
+  __device__ static __forceinline__ int voff(int c, int d) {
+    return (((c >> 1) * DV + d) * 2 + (c & 1)) * 16;
+  }
 };
 
 template <int DK, int DV>
@@ -536,33 +540,34 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
     const int ts = __builtin_amdgcn_readfirstlane(t0);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {  // the two 8-key halves of the group
-      {
-        // four consecutive lanes copy 64 contiguous bytes of one key row (in
-        // swizzled order), so a copy instruction reads 16 whole 64-byte pieces
-        const int k16 = lane >> 2;
-        const int cl = (lane & 3) ^ ((k16 >> 2) & 3);
-        const bool hi = k16 >= 8;
-        const int key = min(ts + 16 * kgroup + k16, kv_end - 1);
-        const int c0 = half * (LY::kChunks / 2);  // first column chunk of this half
-        const char* page0 = kbase + (int64_t)tp.pg0 * kpage_elems * 2;
-        const char* page1 = kbase + (int64_t)tp.pg1 * kpage_elems * 2;
-        const int off = ((key - (hi ? tp.first1 : tp.first0)) * DK + 8 * (c0 + cl)) * 2;
-        const char* src = (hi ? page1 : page0) + off;
+      // four consecutive lanes copy 64 contiguous bytes of one key row (in
+      // swizzled order), so a copy instruction reads 16 whole 64-byte pieces
+      const int k16 = lane >> 2;
+      const int cl = (lane & 3) ^ ((k16 >> 2) & 3);
+      const bool hi = k16 >= 8;
+      const int key = min(ts + 16 * kgroup + k16, kv_end - 1);
+      const int c0 = half * (LY::kChunks / 2);  // first column chunk of this half
+      const char* page0 = kbase + (int64_t)tp.pg0 * kpage_elems * 2;
+      const char* page1 = kbase + (int64_t)tp.pg1 * kpage_elems * 2;
+      const int off = ((key - (hi ? tp.first1 : tp.first0)) * DK + 8 * (c0 + cl)) * 2;
+      const char* src = (hi ? page1 : page0) + off;
 #pragma unroll
-        for (int j = 0; j < LY::kKCopies; ++j)
-          lds_dma16_m0(src + 64 * j, kst + LY::koff(16 * kgroup, c0 + 4 * j));
-      }
-      {
-        const bool hi = half;
-        const int vch = 2 * kgroup + half;  // the 8-key chunk
-        const int cs = min(ts + 8 * vch, (kv_end - 1) & ~7);
-        const int pg = hi ? tp.pg1 : tp.pg0;
-        const int slot = cs - (hi ? tp.first1 : tp.first0);
-        const char* vpage = vbase + ((int64_t)pg * vpage_elems + slot) * 2;
+      for (int j = 0; j < LY::kKCopies / 2; ++j)
+        lds_dma16_m0(src + 64 * j, kst + LY::koff(16 * kgroup, c0 + 4 * j));
+    }
+    {
+      // V^T: lanes 2j and 2j + 1 copy the two 8-key chunks of column 32 i + j
+      // for the group's 16 keys; where one page holds all 16 (P >= 16) the
+      // pair reads 32 contiguous bytes, and at P = 16 a copy instruction
+      // reads 1 KiB in one piece
+      const int hv = lane & 1;
+      const int cs = min(ts + 8 * (2 * kgroup + hv), (kv_end - 1) & ~7);
+      const int pg = hv ? tp.pg1 : tp.pg0;
+      const int slot = cs - (hv ? tp.first1 : tp.first0);
+      const char* vsrc = vbase + ((int64_t)pg * vpage_elems + (int64_t)(lane >> 1) * P + slot) * 2;
 #pragma unroll
-        for (int i = 0; i < LY::kVCopies; ++i)
-          lds_dma16_m0(vpage + (64 * i + lane) * P * 2, vst + LY::voff(vch, 64 * i));
-      }
+      for (int i = 0; i < LY::kVCopies; ++i)
+        lds_dma16_m0(vsrc + (int64_t)(32 * i) * P * 2, vst + LY::voff(2 * kgroup, 32 * i));
     }
   };
 
@@ -704,7 +709,7 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
   if (ntiles > 0) issue_tile(kv_begin, 0, load_pages(kv_begin));
   if (ntiles > 1) {
     issue_tile(kv_begin + kTK, 1, load_pages(kv_begin + kTK));
-    if (copier) wait_vmcnt<2 * LY::kCopies>();
+    if (copier) wait_vmcnt<LY::kCopies>();
   } else {
     wait_vmcnt<0>();
   }
@@ -738,7 +743,7 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
     else softmax_phase(t);
     // this thread's part of tile t + 1 is in LDS (tile t + 2 may stay in flight)
     if (t + 2 < ntiles) {
-      if (copier) wait_vmcnt<2 * LY::kCopies>();
+      if (copier) wait_vmcnt<LY::kCopies>();
     } else {
       wait_vmcnt<0>();
     }
