@@ -362,8 +362,9 @@ __device__ int run_decode_item(const MhaArgs& a, const WorkItem& it, const Dest&
 //       — one copy instruction moves 4 column chunks of 16 keys, four
 //       consecutive lanes reading 64 contiguous bytes of a key row; the
 //       swizzle puts the 16 lanes of a read phase on 16 distinct bank groups;
-//   V^T [key chunk][column]          — one copy instruction moves 64 columns
-//       of one 8-key chunk (one page); operand reads are consecutive.
+//   V^T [16-key group][column][8-key half] — one copy instruction moves 32
+//       columns of a 16-key group, a lane pair reading the 32 contiguous
+//       bytes of one column; operand reads are consecutive.
 // The online softmax rescales the accumulator only when a row maximum grows by
 // more than 2^8 (exact either way: numerator and denominator share the stale
 // maximum).
