@@ -509,8 +509,9 @@ static pa_status forward_masked_impl(const void* q, const void* k_cache, const v
   if (e != hipSuccess) return hip_fail(e);
   if ((e = mark(g_ev_stop, s)) != hipSuccess) return hip_fail(e);
   // the merge also leaves the queue counters zeroed for the next call; one
-  // wave per 4 rows of a (request, KV head) pair with split rows (at most
-  // B * Hkv pairs of up to 16 rows), four waves per workgroup
+  // wave per 4 rows of each (request, KV head) pair (B * Hkv pairs of up to
+  // 16 rows; the waves of unsplit pairs stop at the pair's entry), four waves
+  // per workgroup
   const int64_t pairs = (int64_t)d->num_seqs * d->num_kv_heads;
   a.merge_groups =
       (int)((std::min<int64_t>(std::max(1, d->max_q_len) * (int64_t)G, pa::kDecodeRows) + 3) / 4);

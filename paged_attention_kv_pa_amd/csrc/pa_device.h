@@ -229,7 +229,7 @@ constexpr uint32_t kQueueReady = 0x51a9e7c3u;
 struct Control {
   int32_t n_pre;            // prefill-mode items; item indices [0, n_pre)
   int32_t n_items;          // all items; decode-mode items are [n_pre, n_items)
-  int32_t n_merge;          // (request, KV head) pairs whose decode rows were split
+  int32_t unused0;          // (free; keeps the layout)
   int32_t work_counter;     // decode-mode items claimed from the queue
   int32_t xcd_counter[8];   // next entry of each prefill-mode item queue
   uint32_t ready;           // kQueueReady: the counters above are zero

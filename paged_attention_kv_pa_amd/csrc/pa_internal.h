@@ -96,7 +96,8 @@ struct MhaArgs {
   const ReqPlan* req;        // pa_forward planner output
   const int32_t* pre_off;    // [B + 1] first prefill-mode item of each request
   const int32_t* dec_items;  // decode-mode items (relative to n_pre), kItemInts int32 each
-  int32_t* merges;           // merge entries, 4 int32 each: first slot, S | nrows << 16, q0, kvh
+  int32_t* merges;           // merge entry of each (request, KV head) pair, 4 int32 each:
+                             // first slot, S | nrows << 16, q0, kvh (S <= 1: not split)
                              // (written by the kernel that plans the call)
   Control* ctrl;
   float scale;

@@ -1006,19 +1006,18 @@ __device__ long long fused_plan(const MhaArgs& a, FusedPlan& fp) {
     if (b < a.num_seqs) {
       fp.doff[b] = run.x + ex.x;
       fp.soff[b] = run.y + ex.y;
-      if (blockIdx.x == 0 && nsplit > 1) {
-        int4* me = reinterpret_cast<int4*>(a.merges) + run.z + ex.z;
+      if (blockIdx.x == 0) {
+        // one merge entry per (request, KV head) pair, split or not
+        int4* me = reinterpret_cast<int4*>(a.merges) + (int64_t)b * a.Hkv;
         const int slot0 = run.y + ex.y;
         for (int kvh = 0; kvh < a.Hkv; ++kvh)
-          me[kvh] = int4{slot0 + kvh * nsplit, nsplit | (nq * a.G) << 16, q0, kvh};
+          me[kvh] = nsplit > 1 ? int4{slot0 + kvh * nsplit, nsplit | (nq * a.G) << 16, q0, kvh}
+                               : int4{0, 0, 0, kvh};
       }
     }
     run = int4{run.x + tot.x, run.y + tot.y, run.z + tot.z, 0};
   }
-  if (tid == 0) {
-    fp.doff[a.num_seqs] = run.x;
-    if (blockIdx.x == 0) a.ctrl->n_merge = run.z;
-  }
+  if (tid == 0) fp.doff[a.num_seqs] = run.x;
   __syncthreads();
   return chunk;
 }
@@ -1452,12 +1451,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       rp.slot0 = run.z + ex.z;
       a.req[b] = rp;
       a.pre_off[b] = run.x + ex.x;
-      // merge entries of the request's split (request, KV head) pairs
-      if (rp.nsplit > 1) {
-        int4* me = reinterpret_cast<int4*>(a.merges) + run.w + ex.w;
-        for (int kvh = 0; kvh < Hkv; ++kvh)
-          me[kvh] = int4{rp.slot0 + kvh * rp.nsplit, rp.nsplit | (rp.nq * G) << 16, rp.q0, kvh};
-      }
+      // one merge entry per (request, KV head) pair; S <= 1: nothing to merge
+      int4* me = reinterpret_cast<int4*>(a.merges) + (int64_t)b * Hkv;
+      for (int kvh = 0; kvh < Hkv; ++kvh)
+        me[kvh] = rp.nsplit > 1 ? int4{rp.slot0 + kvh * rp.nsplit, rp.nsplit | (rp.nq * G) << 16,
+                                       rp.q0, kvh}
+                                : int4{0, 0, 0, kvh};
     }
     // Decode-mode items of this chunk of requests, written by all threads:
     // item i of the chunk belongs to the last request whose first item is at
@@ -1487,7 +1486,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     a.pre_off[a.B] = run.x;
     a.ctrl->n_pre = run.x;
     a.ctrl->n_items = run.x + run.y;
-    a.ctrl->n_merge = run.w;
     a.ctrl->n_cmerge = run_c.x;
     a.ctrl->n_crows = run_c.y;
     a.ctrl->work_counter = 0;
@@ -1497,9 +1495,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 }
 
 // Merge of pa_forward's split decode rows.  One wave takes 4 rows of a
-// (request, KV head) pair whose rows were split (unit e = pair x
-// merge_groups + row group; a pair has at most merge_groups x 4 <= 16 rows,
-// fixed on the host from max_q_len): 16 lanes per row, each with
+// (request, KV head) pair (unit e = pair x merge_groups + row group; a pair
+// has at most merge_groups x 4 <= 16 rows, fixed on the host from
+// max_q_len); the pair's entry, indexed by the pair itself so that no count
+// has to be read first, says whether its rows were split: 16 lanes per row, each with
 // D / 16 consecutive columns, folding the partitions in one pass with a
 // running log-sum-exp (max, rescaled weight sum, rescaled sum); the loads of
 // several partitions are in flight together.
@@ -1508,7 +1507,6 @@ __global__ __launch_bounds__(kThreads) void mha_forward_merge_kernel(MhaArgs a) 
   constexpr int NC = D / 16;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int rsub = lane >> 4, c0 = (lane & 15) * NC;
-  const int n_merge = a.ctrl->n_merge;
   // The attention kernel of this call is done with the queue counters: zero
   // them for the next call and mark them so (see Control).
   if (blockIdx.x == 0 && threadIdx.x < 64) {
@@ -1518,9 +1516,11 @@ __global__ __launch_bounds__(kThreads) void mha_forward_merge_kernel(MhaArgs a) 
   }
   const int groups = a.merge_groups;
   const int stride = gridDim.x * (kThreads / 64);
-  for (int e = blockIdx.x * (kThreads / 64) + wv; e < n_merge * groups; e += stride) {
+  const int64_t units = (int64_t)a.num_seqs * a.Hkv * groups;
+  for (int64_t e = blockIdx.x * (kThreads / 64) + wv; e < units; e += stride) {
     const int4 me = reinterpret_cast<const int4*>(a.merges)[e / groups];
     const int slot0 = me.x, S = me.y & 0xffff, nrows = me.y >> 16, q0 = me.z, kvh = me.w;
+    if (S <= 1) continue;  // the pair's rows were written whole
     {
       const int row = 4 * (e % groups) + rsub;
       if (row >= nrows) continue;
