@@ -360,6 +360,8 @@ __device__ __forceinline__ void mla_keys(const MlaArgs& a, char* mla_smem, int t
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  // every wave is done with the ring before a later segment's copies refill it
+  __syncthreads();
 
   // epilogue: lane holds O[head][32 dt + 8 (v / 4) + 4h + v % 4].  The last
   // matrix instructions (inline assembly, issued in column-tile order) must
@@ -396,9 +398,266 @@ __device__ __forceinline__ void mla_keys(const MlaArgs& a, char* mla_smem, int t
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Wide variant of the tile loop: 8 waves, two per SIMD, wave w owning heads
+// 16 w .. 16 w + 15 on v_mfma_f32_16x16x32_bf16 (lane layouts in
+// pa_device.h).  A wave's output tile is 16 heads x 512 columns, 128
+// accumulator registers, so two waves fit on a SIMD and one runs its matrix
+// products while the other waits on LDS or runs its softmax.  Every wave
+// reads the whole key tile and value tile from LDS (twice the LDS reads of
+// the 4-wave loop per key tile); the ring and the copies (waves 0-3) are
+// those of the 4-wave loop.
+//   * S^T = K Q^T: M-row r of key block kb (0, 1) holds key 8 (r / 4) + 4 kb
+//     + r % 4, so lane (r, g) ends with keys 8 g .. 8 g + 7 of head r: the
+//     B operand (P^T) of the value product, in order;
+//   * O^T = V^T P^T: one instruction per 16 columns, its V^T operand (8 keys
+//     of one column per lane) read with two transposing LDS reads.
+// Chunk swizzle: chosen by measurement (the LDS bank-conflict counter over
+// every invertible linear map of key bits 1, 3 and 4 onto the 3 chunk bits)
+// among those with no conflicts for both the key-operand reads and the
+// transposing value reads; LDS bank selection on this part is not a plain
+// function of the low address bits, so the choice is not derived here.
+// ---------------------------------------------------------------------------
+constexpr int kWThreads = 512;
+constexpr int kWSteps = kDqk / 32;                       // 18 K-steps of 32 columns
+constexpr int kWQRegSteps = 14;                          // query K-steps held in registers
+constexpr int kWQLdsSteps = kWSteps - kWQRegSteps;       // the rest in LDS
+constexpr int kWQLdsStride = kWQLdsSteps * 32 * 2 + 16;  // bytes per head row (padded)
+constexpr int kWQLdsBytes = 128 * kWQLdsStride;
+constexpr size_t kWLdsBytes = (size_t)kStages * kStageBytes + kWQLdsBytes;
+
+__device__ __forceinline__ int swz_w(int k) {
+  const int k1 = (k >> 1) & 1, k3 = (k >> 3) & 1, k4 = (k >> 4) & 1;
+  return k1 | ((k1 ^ k3) << 1) | ((k3 ^ k4) << 2);
+}
+__device__ __forceinline__ int chunk_off_w(int k, int c) {
+  return (((c >> 3) * kMTK + k) * 8 + ((c & 7) ^ swz_w(k))) * 16;
+}
+
+// Keys [t0k, t1k) of request b for all its heads, by one workgroup of
+// kWThreads; the same contract as mla_keys.
+__device__ __forceinline__ void mla_keys_wide(const MlaArgs& a, char* mla_smem, int tid, int b,
+                                              int t0k, int t1k, int64_t pbase, int pstride) {
+  constexpr int DT = kDv / 16;  // 32 column tiles of O^T
+  const int wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const int P = a.P, lp = a.log2_page;
+  const int ntiles = (t1k - t0k + kMTK - 1) / kMTK;
+
+  typedef const __attribute__((address_space(4))) int32_t* ConstI32Ptr;
+  const ConstI32Ptr bt =
+      (ConstI32Ptr)uniform_ptr(a.block_table + (int64_t)__builtin_amdgcn_readfirstlane(b) * a.max_pages);
+  const char* kv = uniform_ptr((const char*)a.kv);
+
+  // copies by waves 0-3 (one per SIMD): thread t copies key t / 8, chunk
+  // slot t % 8 of each of the 9 groups, as in mla_keys
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const bool copier = wave_s < 4;
+  const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(lds_cchar*)mla_smem + (wave_s & 3) * 64 * 16);
+  auto issue_tile = [&](int ti, int st) {
+    int lane_now = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    asm volatile("" : "+v"(lane_now));
+    const int dt = (wave_s & 3) * 64 + lane_now;
+    const int dkey = dt >> 3;
+    const int dchunk = (dt & 7) ^ swz_w(dkey);
+    const int lane_src = dkey * (kDqk * 2) + dchunk * 16;
+    const int t0 = t0k + ti * kMTK;
+    const char* src;
+    if (P >= kMTK && t0 + kMTK <= t1k) {
+      const int page = checked_page(bt[t0 >> lp], a.num_pages, a.dbg);
+      src = kv + (((int64_t)page << lp) + (t0 & (P - 1))) * (kDqk * 2) + lane_src;
+    } else {
+      const int key = min(t0 + dkey, t1k - 1);  // clamped: real data, masked later
+      const int last_pg = (t1k - 1) >> lp;
+      const int pg0 = __builtin_amdgcn_readfirstlane(t0 >> lp);
+      int page;
+      if (P >= kMTK) {
+        page = checked_page(bt[pg0], a.num_pages, a.dbg);
+      } else {
+        const int j = (key >> lp) - pg0;  // 0 .. 32 / P - 1
+        const int p0 = checked_page(bt[pg0], a.num_pages, a.dbg);
+        const int p1 = checked_page(bt[min(pg0 + 1, last_pg)], a.num_pages, a.dbg);
+        const int p2 = checked_page(bt[min(pg0 + 2, last_pg)], a.num_pages, a.dbg);
+        const int p3 = checked_page(bt[min(pg0 + 3, last_pg)], a.num_pages, a.dbg);
+        page = j == 0 ? p0 : (j == 1 ? p1 : (j == 2 ? p2 : p3));
+      }
+      src = kv + (((int64_t)page << lp) + (key & (P - 1))) * (kDqk * 2) + dchunk * 16;
+    }
+    const uint32_t dst = lds_wave + st * kStageBytes;
+#pragma unroll
+    for (int j = 0; j < kGroups; ++j) lds_dma16_m0(src + 128 * j, dst + j * kMTK * 8 * 16);
+  };
+
+  // query: K-steps [0, kWQRegSteps) in registers, the rest in LDS after the
+  // ring (each wave writes and reads only its own heads' rows)
+  const int head = 16 * wave + r;
+  const bool row_ok = head < a.Hq;
+  char* qlds = mla_smem + kStages * kStageBytes;
+  lds_cchar* qlds3 = (lds_cchar*)mla_smem + kStages * kStageBytes;
+  bf16x8 qf[kWQRegSteps];  // B operand of S^T: Q[head][32 ks + 8 g .. +7]
+  {
+    const __bf16* qp = (const __bf16*)a.q + ((int64_t)b * a.Hq + head) * kDqk + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < kWQRegSteps; ++ks)
+      qf[ks] = row_ok ? as_bf16x8(load16(qp + 32 * ks)) : as_bf16x8(u32x4{0, 0, 0, 0});
+#pragma unroll
+    for (int ks = kWQRegSteps; ks < kWSteps; ++ks) {
+      const u32x4 v = row_ok ? load16(qp + 32 * ks) : u32x4{0, 0, 0, 0};
+      store16(qlds + head * kWQLdsStride + (32 * (ks - kWQRegSteps) + 8 * g) * 2, v);
+    }
+  }
+  wait_vmcnt<0>();
+  if (copier && ntiles > 0) issue_tile(0, 0);
+
+  const float sc = a.scale * kLog2e;
+  float m = kNegInf, l = 0.f;  // l: this lane's share of the head's sum
+  floatx4 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // K operand offsets: K-step ks = 2 j + u reads chunk 4 ks + g = 8 j + 4 u + g
+  int koff[2][2];  // [kb][u]; chunk group j adds 4 KiB
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      koff[kb][u] = chunk_off_w(8 * (r >> 2) + 4 * kb + (r & 3), 4 * u + g);
+  // V^T operand: in 16-lane group g, source lane r of read hh addresses key
+  // 8 g + 4 hh + r / 4, columns 16 dt + 4 (r % 4) .. +3 (chunk 2 dt + (r / 2)
+  // % 2, half r % 2); lane r of the group receives column 16 dt + r
+  int voff[2][4];  // [hh][dt % 4]; chunk group dt / 4 adds 4 KiB
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int d4 = 0; d4 < 4; ++d4)
+      voff[hh][d4] = chunk_off_w(8 * g + 4 * hh + (r >> 2), 2 * d4 + ((r >> 1) & 1)) + 8 * (r & 1);
+
+  for (int ti = 0; ti < ntiles; ++ti) {
+    if (copier) wait_vmcnt<0>();
+    __syncthreads();  // tile ti is in LDS; stage (ti + 1) % 2 is no longer read
+    if (copier && ti + 1 < ntiles) issue_tile(ti + 1, (ti + 1) % kStages);
+    const int t0 = t0k + ti * kMTK;
+    lds_cchar* stage = (lds_cchar*)mla_smem + (ti % kStages) * kStageBytes;
+
+    // S^T: instruction i = 2 ks + kb; operand reads kAhead instructions ahead
+    constexpr int kAhead = 4;
+    auto kread = [&](int i) {
+      const int ks = i >> 1, kb = i & 1;
+      const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+          stage + koff[kb][ks & 1] + (ks >> 1) * (kMTK * 8 * 16));
+      return as_bf16x8(v);
+    };
+    auto qread = [&](int ks) {
+      const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+          qlds3 + head * kWQLdsStride + (32 * (ks - kWQRegSteps) + 8 * g) * 2);
+      return as_bf16x8(v);
+    };
+    floatx4 s0 = floatx4{0.f, 0.f, 0.f, 0.f}, s1 = floatx4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 kbuf[kAhead], qbuf[4];
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) kbuf[i] = kread(i);
+#pragma unroll
+    for (int i = 0; i < 2 * kWSteps; ++i) {
+      const int ks = i >> 1, kb = i & 1;
+      // LDS query steps, two K-steps ahead of their use
+      if (kb == 0 && ks + 2 >= kWQRegSteps && ks + 2 < kWSteps) qbuf[(ks + 2) & 3] = qread(ks + 2);
+      const bf16x8 qv = ks < kWQRegSteps ? qf[ks < kWQRegSteps ? ks : 0] : qbuf[ks & 3];
+      if (kb == 0) s0 = mfma_bf16(kbuf[i % kAhead], qv, s0);
+      else s1 = mfma_bf16(kbuf[i % kAhead], qv, s1);
+      if (i + kAhead < 2 * kWSteps) kbuf[i % kAhead] = kread(i + kAhead);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // lane (r, g) holds S[head][t0 + 8 g + j] in x[j]
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[j] = s0[j];
+      x[4 + j] = s1[j];
+    }
+    if (t0 + kMTK > t1k) {  // the last tile of the range: mask the keys past its end
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = t0 + 8 * g + j < t1k ? x[j] : kNegInf;
+    }
+    float tm0 = fmaxf(x[0], x[1]), tm1 = fmaxf(x[4], x[5]);
+    tm0 = fmaxf(tm0, fmaxf(x[2], x[3]));
+    tm1 = fmaxf(tm1, fmaxf(x[6], x[7]));
+    const float tmax = group_max4(fmaxf(tm0, tm1));
+    const bool grow = (tmax - m) * sc > kLazyLog2;  // always true on the first tile
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float mnew = grow ? tmax : m;
+      const float alpha = grow ? fast_exp2((m - mnew) * sc) : 1.f;  // 0 while m = -inf
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+      m = mnew;
+    }
+    const float msc = (m == kNegInf ? 0.f : m) * sc;
+    float p[8], ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      p[j] = fast_exp2(fmaf(x[j], sc, -msc));
+      if (j & 1) ps1 += p[j];
+      else ps0 += p[j];
+    }
+    l += ps0 + ps1;
+    const bf16x8 pf = __builtin_bit_cast(
+        bf16x8, u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                      pack_bf16x2(p[6], p[7])});
+
+    // O^T += V^T P^T, operand reads kAheadV instructions ahead
+    constexpr int kAheadV = 4;
+    auto vread = [&](int dt) {
+      const int goff = (dt >> 2) * (kMTK * 8 * 16);
+      const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_short4*)(stage + voff[0][dt & 3] + goff));
+      const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_short4*)(stage + voff[1][dt & 3] + goff));
+      const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+      return __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
+    };
+    bf16x8 vbuf[kAheadV];
+#pragma unroll
+    for (int i = 0; i < kAheadV; ++i) vbuf[i] = vread(i);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      acc[dt] = mfma_bf16(vbuf[dt % kAheadV], pf, acc[dt]);
+      if (dt + kAheadV < DT) vbuf[dt % kAheadV] = vread(dt + kAheadV);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // every wave is done with the ring before a later segment's copies refill it
+  __syncthreads();
+
+  // epilogue: lane (r, g) holds O[head][16 dt + 4 g + v] in acc[dt][v]
+  const float lrow = group_sum4(l);
+  if (!row_ok) return;
+  const float inv = lrow > 0.f ? 1.f / lrow : 0.f;
+  const float lse = lrow > 0.f ? m * a.scale + __log2f(lrow) * kLn2 : kNegInf;
+  const int64_t bh = (int64_t)b * a.Hq + head;
+  if (pbase < 0) {
+    __bf16* op = (__bf16*)a.out + bh * kDv + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<u32x2*>(op + 16 * dt) =
+          u32x2{pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv),
+                pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv)};
+    if (g == 0 && a.lse) a.lse[bh] = lse;
+  } else {
+    const int64_t pi = pbase + (int64_t)head * pstride;
+    float* op = a.part_o + pi * kDv + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      store16(op + 16 * dt, __builtin_bit_cast(u32x4, acc[dt] * inv));
+    if (g == 0) a.part_lse[pi] = lse;
+  }
+}
+
 // pa_decode_split-style partitions: workgroup (b, s) takes the s-th of
 // num_splits page-aligned key ranges of request b.
-__global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
+template <bool WIDE>
+__global__ __launch_bounds__(WIDE ? kWThreads : kMlaThreads) void mla_split_kernel(MlaArgs a) {
   extern __shared__ __align__(16) char mla_smem[];
   const int S = a.num_splits;
   const int s = blockIdx.x % S, b = blockIdx.x / S;
@@ -407,7 +666,9 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
   const long long per = (long long)P * ((pages + S - 1) / S);
   const long long a0 = per * s, a1 = a0 + per;
   const int t0k = a0 < L ? (int)a0 : L, t1k = a1 < L ? (int)a1 : L;
-  mla_keys(a, mla_smem, threadIdx.x, b, t0k, t1k, S > 1 ? (int64_t)b * a.Hq * S + s : -1, S);
+  const int64_t pbase = S > 1 ? (int64_t)b * a.Hq * S + s : -1;
+  if constexpr (WIDE) mla_keys_wide(a, mla_smem, threadIdx.x, b, t0k, t1k, pbase, S);
+  else mla_keys(a, mla_smem, threadIdx.x, b, t0k, t1k, pbase, S);
 }
 
 // Tiles a request contributes to the balanced schedule (an empty request
@@ -415,6 +676,7 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
 __device__ __forceinline__ int mla_tiles(int L) { return L > kMTK ? (L + kMTK - 1) / kMTK : 1; }
 
 // Sum / maximum over the workgroup (every thread gets the result).
+template <int NT>
 __device__ __forceinline__ long long mla_block_sum(long long v, long long* red) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
@@ -423,7 +685,7 @@ __device__ __forceinline__ long long mla_block_sum(long long v, long long* red) 
   __syncthreads();
   long long t = 0;
 #pragma unroll
-  for (int w = 0; w < kMlaThreads / 64; ++w) t += red[w];
+  for (int w = 0; w < NT / 64; ++w) t += red[w];
   return t;
 }
 
@@ -441,15 +703,17 @@ __device__ __forceinline__ long long mla_block_sum(long long v, long long* red) 
 // recomputes the (small) schedule from seq_lens.  The tile loop (mla_keys)
 // runs once per segment on the same LDS ring; its LDS accesses stay LDS
 // instructions (the ring is addressed through the kernel's own shared array).
-__global__ __launch_bounds__(kMlaThreads) void mla_balanced_kernel(MlaArgs a) {
+template <bool WIDE>
+__global__ __launch_bounds__(WIDE ? kWThreads : kMlaThreads) void mla_balanced_kernel(MlaArgs a) {
+  constexpr int NT = WIDE ? kWThreads : kMlaThreads;
   extern __shared__ __align__(16) char mla_smem[];
-  __shared__ long long s_red[kMlaThreads / 64];
+  __shared__ long long s_red[NT / 64];
   __shared__ int s_b;
   __shared__ long long s_tb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   long long T = 0;
-  for (int b = tid; b < a.B; b += kMlaThreads) T += mla_tiles(a.seq_lens[b]);
-  T = mla_block_sum(T, s_red);
+  for (int b = tid; b < a.B; b += NT) T += mla_tiles(a.seq_lens[b]);
+  T = mla_block_sum<NT>(T, s_red);
   const long long G = gridDim.x, w = blockIdx.x;
   const long long per = (T + G - 1) / G;
   const long long start = w * per, end = min(start + per, T);
@@ -457,7 +721,7 @@ __global__ __launch_bounds__(kMlaThreads) void mla_balanced_kernel(MlaArgs a) {
   // first request of the range: the one whose tiles [ex, ex + n) hold `start`
   if (tid == 0) s_b = -1;
   long long run = 0;
-  for (int base = 0; base < a.B; base += kMlaThreads) {
+  for (int base = 0; base < a.B; base += NT) {
     const int b = base + tid;
     const long long n = b < a.B ? mla_tiles(a.seq_lens[b]) : 0;
     long long incl = n;
@@ -471,7 +735,7 @@ __global__ __launch_bounds__(kMlaThreads) void mla_balanced_kernel(MlaArgs a) {
     __syncthreads();
     long long before = run, tot = 0;
 #pragma unroll
-    for (int v = 0; v < kMlaThreads / 64; ++v) {
+    for (int v = 0; v < NT / 64; ++v) {
       if (v < wave) before += s_red[v];
       tot += s_red[v];
     }
@@ -498,7 +762,9 @@ __global__ __launch_bounds__(kMlaThreads) void mla_balanced_kernel(MlaArgs a) {
     }
     const long long k0 = s0 * kMTK, k1 = s1 * kMTK;
     const int t0k = k0 < L ? (int)k0 : L, t1k = k1 < L ? (int)k1 : L;
-    mla_keys(a, mla_smem, tid, b, t0k, t1k, cut ? (int64_t)slot * a.Hq : -1, 1);
+    const int64_t pbase = cut ? (int64_t)slot * a.Hq : -1;
+    if constexpr (WIDE) mla_keys_wide(a, mla_smem, tid, b, t0k, t1k, pbase, 1);
+    else mla_keys(a, mla_smem, tid, b, t0k, t1k, pbase, 1);
     tb += n;
   }
 }
@@ -562,14 +828,19 @@ hipError_t allow_lds_once(const void* kernel, std::atomic<uint64_t>& done, size_
 
 std::atomic<uint64_t> g_lds_balanced{0}, g_lds_split{0};
 
+// The tile loop the MLA kernels run: the 8-wave one (two waves per SIMD) or
+// the 4-wave one.
+constexpr bool kMlaWide = true;
+constexpr int kMlaLaunchThreads = kMlaWide ? kWThreads : kMlaThreads;
+constexpr size_t kMlaLds = kMlaWide ? kWLdsBytes : (size_t)kStages * kStageBytes + kQLdsBytes;
+
 }  // namespace
 
 hipError_t launch_mla_balanced(const MlaArgs& a, int grid, hipStream_t s) {
   if (a.B <= 0 || grid <= 0) return hipSuccess;
-  const size_t lds = (size_t)kStages * kStageBytes + kQLdsBytes;
-  hipError_t e = allow_lds_once((const void*)mla_balanced_kernel, g_lds_balanced, lds);
+  hipError_t e = allow_lds_once((const void*)mla_balanced_kernel<kMlaWide>, g_lds_balanced, kMlaLds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mla_balanced_kernel, dim3(grid), dim3(kMlaThreads), lds, s, a);
+  hipLaunchKernelGGL(mla_balanced_kernel<kMlaWide>, dim3(grid), dim3(kMlaLaunchThreads), kMlaLds, s, a);
   return hipGetLastError();
 }
 
@@ -582,10 +853,9 @@ hipError_t launch_mla_balanced_merge(const MlaArgs& a, hipStream_t s) {
 hipError_t launch_mla_split(const MlaArgs& a, hipStream_t s) {
   const int64_t blocks = (int64_t)a.B * a.num_splits;
   if (blocks <= 0) return hipSuccess;
-  const size_t lds = (size_t)kStages * kStageBytes + kQLdsBytes;
-  hipError_t e = allow_lds_once((const void*)mla_split_kernel, g_lds_split, lds);
+  hipError_t e = allow_lds_once((const void*)mla_split_kernel<kMlaWide>, g_lds_split, kMlaLds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mla_split_kernel, dim3(blocks), dim3(kMlaThreads), lds, s, a);
+  hipLaunchKernelGGL(mla_split_kernel<kMlaWide>, dim3(blocks), dim3(kMlaLaunchThreads), kMlaLds, s, a);
   return hipGetLastError();
 }
 
