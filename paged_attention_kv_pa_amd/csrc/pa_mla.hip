@@ -5,30 +5,32 @@
 // ("vLLM AMD ROCm Attention Backend Optimization", sections "AITER MLA
 // backend" and "Hybrid processing strategy").  With 128 heads on one latent
 // head the work per cached byte is high (about 240 flop per byte), so one
-// workgroup of 4 waves takes all heads of one request — wave w owns heads
-// 32w .. 32w+31 as one 32-row MFMA tile — and every latent tile is read from
-// HBM exactly once.
+// workgroup takes all heads of one request and every latent tile is read
+// from HBM exactly once.  The workgroup has 8 waves, two per SIMD; wave w
+// owns heads 16 w .. 16 w + 15 on v_mfma_f32_16x16x32_bf16 (lane layouts in
+// pa_device.h).  A wave's output tile (16 heads x 512 columns) is 128
+// accumulator registers, so two waves fit on a SIMD and one runs its matrix
+// products while the other waits on LDS or runs its softmax.
 //
 // Per 32-key tile:
-//   * HBM -> LDS by direct-to-LDS copies (16 bytes per lane, no registers)
-//     into a 2-stage ring with one barrier per tile, each tile's copies
-//     issued one tile ahead (two tiles ahead in a 3-stage ring measured
-//     about 5% slower: the copy latency is covered either way).  The tile is stored
+//   * HBM -> LDS by direct-to-LDS copies (16 bytes per lane, no registers),
+//     issued by waves 0-3, into a 2-stage ring with one barrier per tile,
+//     each tile's copies issued one tile ahead.  The tile is stored
 //     "chunk-group major": [9 groups of 8 sixteen-byte chunks][32 keys][8],
 //     with the chunk index inside a group XOR-swizzled by the key, so that a
 //     thread's 9 copies of a tile are 128 bytes apart in HBM (one address
-//     register) and the operand reads of different keys hit different banks;
-//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (32 keys x 32 heads x 16
-//     columns per instruction).  The 32 M-rows of the K operand are permuted
-//     so that lanes l and l + 32 end up holding keys 8h .. 8h+7 and
-//     16 + 8h .. 16 + 8h+7 (h = l / 32) of head l % 32 — exactly the slots
-//     they must supply as the B operand (P^T) of the value product;
-//   * O^T = V^T P^T on the same instruction (32 columns x 32 heads x 16 keys):
-//     the V^T operand (8 consecutive keys of one column per lane) is read from
-//     the row-major tile with the LDS transpose read ds_read_b64_tr_b16;
+//     register) and the operand reads hit distinct banks;
+//   * S^T = K Q^T: M-row r of key block kb (0, 1) holds key 8 (r / 4) + 4 kb
+//     + r % 4, so lane (r, g) ends with keys 8 g .. 8 g + 7 of head r — the
+//     B operand (P^T) of the value product, in order;
+//   * O^T = V^T P^T: one instruction per 16 columns; its V^T operand (8 keys
+//     of one column per lane) is read from the row-major tile with two LDS
+//     transpose reads (ds_read_b64_tr_b16);
 //   * online softmax in base 2 with lazy rescaling: the running max of a head
-//     only moves when a tile would push probabilities above 2^8, so the
-//     accumulator (256 registers per lane) is rarely touched by vector ALUs.
+//     only moves when a tile would push probabilities above 2^8.
+// Every wave reads the whole key and value tile from LDS: the 8-wave loop
+// reads twice the LDS bytes per key tile that a 4-wave loop of 32 heads per
+// wave would, and the second wave per SIMD is worth more.
 // The keys of a request are cut into page-aligned partitions, one workgroup
 // each, combined by the log-sum-exp merge in a second launch.
 #include <atomic>
@@ -40,7 +42,8 @@ namespace pa {
 
 namespace {
 
-constexpr int kMlaThreads = 256;
+constexpr int kMlaThreads = 512;           // 8 waves, two per SIMD
+constexpr int kMergeThreads = 256;
 constexpr int kDqk = 576, kDv = 512;
 constexpr int kMTK = 32;                   // keys per tile
 constexpr int kRowChunks = kDqk / 8;       // 16-byte chunks per latent row (72)
@@ -48,64 +51,34 @@ constexpr int kGroups = kRowChunks / 8;    // chunk groups per row (9)
 constexpr int kStages = 2;
 constexpr int kStageBytes = kMTK * kDqk * 2;  // 36 KiB
 constexpr float kLazyLog2 = 8.f;           // rescale when probabilities would exceed 2^8
-// The query's trailing kQLdsSteps K-steps (16 columns each) are kept in LDS
-// instead of registers: the 256 accumulator registers plus the whole query
-// would not fit in one wave's register budget.
-constexpr int kQRegSteps = 25;
-constexpr int kQLdsSteps = kDqk / 16 - kQRegSteps;  // 11
-constexpr int kQLdsCols = 16 * kQLdsSteps;          // 176
-constexpr int kQLdsStride = kQLdsCols * 2 + 16;     // bytes per head row (padded: 368)
+constexpr int kKSteps = kDqk / 32;                       // 18 K-steps of 32 columns
+// The query's trailing K-steps are kept in LDS: the 128 accumulator
+// registers plus the whole query would not fit in a wave's half of the
+// register file.
+constexpr int kQRegSteps = 14;                           // query K-steps held in registers
+constexpr int kQLdsSteps = kKSteps - kQRegSteps;         // the rest in LDS
+constexpr int kQLdsStride = kQLdsSteps * 32 * 2 + 16;    // bytes per head row (padded)
 constexpr int kQLdsBytes = 128 * kQLdsStride;
+constexpr size_t kMlaLds = (size_t)kStages * kStageBytes + kQLdsBytes;
 
 typedef __attribute__((ext_vector_type(4))) short short4v;
 typedef __attribute__((address_space(3))) short4v lds_short4;
 typedef __attribute__((address_space(3))) const char lds_cchar;
 
-// Swizzle of the chunk index inside its group of 8, by key.
-__device__ __forceinline__ int swz(int k) { return (k >> 1) & 7; }
+// Swizzle of the chunk index inside its group of 8, by key.  Chosen by
+// measurement (the LDS bank-conflict counter over every invertible linear
+// map of key bits 1, 3 and 4 onto the 3 chunk bits) among those with no
+// conflicts for both the key-operand reads and the transposing value reads:
+// LDS bank selection on this part is not a plain function of the low
+// address bits, so the choice is not derived here.
+__device__ __forceinline__ int swz(int k) {
+  const int k1 = (k >> 1) & 1, k3 = (k >> 3) & 1, k4 = (k >> 4) & 1;
+  return k1 | ((k1 ^ k3) << 1) | ((k3 ^ k4) << 2);
+}
 
 // Byte offset of 16-byte chunk c (0..71) of key k (0..31) inside a stage.
 __device__ __forceinline__ int chunk_off(int k, int c) {
   return (((c >> 3) * kMTK + k) * 8 + ((c & 7) ^ swz(k))) * 16;
-}
-
-// x *= alpha for a value the caller keeps in an accumulation register (AGPR).
-__device__ __forceinline__ void agpr_scale(float& x, float alpha) {
-  float t;
-  asm volatile(
-      "v_accvgpr_read_b32 %1, %0\n\ts_nop 1\n\tv_mul_f32 %1, %1, %2\n\ts_nop 1\n\t"
-      "v_accvgpr_write_b32 %0, %1"
-      : "+a"(x), "=&v"(t)
-      : "v"(alpha));
-}
-
-// acc += A B on v_mfma_f32_32x32x16_bf16 with acc pinned in AGPRs (inline
-// assembly: the accumulators of all 16 column tiles fill the AGPR file, and
-// pinning them keeps the allocator from parking other values there).  The
-// caller pads hazards: vector writes of a or b need 2 wait states before this
-// instruction, and reads of acc need the instruction to have retired.
-__device__ __forceinline__ void mfma32_acc_agpr(floatx16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-
-// s += A B (or s = A B) on v_mfma_f32_32x32x16_bf16 with s in vector
-// registers.  Written as inline assembly because, once the output
-// accumulators are pinned to AGPRs, the compiler selects the AGPR form for
-// every builtin matrix instruction: the score tiles then took AGPRs 0..31
-// and two output tiles were moved out to vector registers and back around
-// every key tile.  The caller pads hazards as for mfma32_acc_agpr, and reads
-// s only after the last instruction has retired.
-__device__ __forceinline__ void mfma32_vgpr(floatx16& s, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma32_vgpr_first(floatx16& s, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "v"(b));
-}
-
-// Key held by M-row m of the K operand (see the file comment).
-__device__ __forceinline__ int kperm32(int m) {
-  const int q = m >> 3, h = (m >> 2) & 1, w = m & 3;
-  return 16 * (q >> 1) + 8 * h + 4 * (q & 1) + w;
 }
 
 // Keys [t0k, t1k) of request b for all its heads, by one workgroup.  The
@@ -114,31 +87,29 @@ __device__ __forceinline__ int kperm32(int m) {
 // the workgroup calls this together; LDS is free on entry and on return.
 __device__ __forceinline__ void mla_keys(const MlaArgs& a, char* mla_smem, int tid, int b,
                                          int t0k, int t1k, int64_t pbase, int pstride) {
-  constexpr int KS = kDqk / 16;  // 36 K-steps of S^T
-  constexpr int DT = kDv / 32;   // 16 column tiles of O^T
+  constexpr int DT = kDv / 16;  // 32 column tiles of O^T
   const int wave = tid >> 6, lane = tid & 63;
-  const int n = lane & 31, h = lane >> 5;
+  const int r = lane & 15, g = lane >> 4;
   const int P = a.P, lp = a.log2_page;
   const int ntiles = (t1k - t0k + kMTK - 1) / kMTK;
 
   // The block table is read-only for the whole call: reading it through the
   // constant address space lets the uniform reads become scalar loads (a
-  // vector load would make the compiler wait for every copy in flight).
+  // vector load would make the compiler wait for every copy in flight).  The
+  // request's table row and the cache base are workgroup-uniform: kept in
+  // scalar registers, nothing on the copy path is reloaded from spill slots.
   typedef const __attribute__((address_space(4))) int32_t* ConstI32Ptr;
-  // The request's table row and the cache base are workgroup-uniform: kept
-  // in scalar registers, the page lookups are scalar loads and nothing on
-  // the copy path has to be reloaded from spill slots (a vector reload there
-  // would wait for every copy in flight).
   const ConstI32Ptr bt =
       (ConstI32Ptr)uniform_ptr(a.block_table + (int64_t)__builtin_amdgcn_readfirstlane(b) * a.max_pages);
   const char* kv = uniform_ptr((const char*)a.kv);
 
-  // DMA of tile ti into stage st: thread tid copies key tid / 8, chunk slot
-  // tid % 8 of each of the 9 groups; one wave instruction fills 64
-  // consecutive chunk positions of a group.
+  // DMA of tile ti into stage st by waves 0-3 (one per SIMD): thread t of
+  // them copies key t / 8, chunk slot t % 8 of each of the 9 groups; one
+  // wave instruction fills 64 consecutive chunk positions of a group.
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const bool copier = wave_s < 4;
   const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(lds_cchar*)mla_smem + wave_s * 64 * 16);
+      (uint32_t)(uintptr_t)(lds_cchar*)mla_smem + (wave_s & 3) * 64 * 16);
   auto issue_tile = [&](int ti, int st) {
     // The thread's key and chunk are recomputed from the lane index at every
     // call (the empty asm keeps the compiler from hoisting them out of the
@@ -146,10 +117,10 @@ __device__ __forceinline__ void mla_keys(const MlaArgs& a, char* mla_smem, int t
     // reload would wait for the copies in flight.
     int lane_now = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
     asm volatile("" : "+v"(lane_now));
-    const int dt = wave_s * 64 + lane_now;
+    const int dt = (wave_s & 3) * 64 + lane_now;
     const int dkey = dt >> 3;
     const int dchunk = (dt & 7) ^ swz(dkey);
-    const int lane_src = dkey * (kDqk * 2) + dchunk * 16;  // within a tile of one page
+    const int lane_src = dkey * (kDqk * 2) + dchunk * 16;
     const int t0 = t0k + ti * kMTK;
     const char* src;
     if (P >= kMTK && t0 + kMTK <= t1k) {
@@ -159,7 +130,6 @@ __device__ __forceinline__ void mla_keys(const MlaArgs& a, char* mla_smem, int t
       src = kv + (((int64_t)page << lp) + (t0 & (P - 1))) * (kDqk * 2) + lane_src;
     } else {
       const int key = min(t0 + dkey, t1k - 1);  // clamped: real data, masked later
-      // pages of this tile, read through scalar loads (uniform indices)
       const int last_pg = (t1k - 1) >> lp;
       const int pg0 = __builtin_amdgcn_readfirstlane(t0 >> lp);
       int page;
@@ -180,332 +150,22 @@ __device__ __forceinline__ void mla_keys(const MlaArgs& a, char* mla_smem, int t
     for (int j = 0; j < kGroups; ++j) lds_dma16_m0(src + 128 * j, dst + j * kMTK * 8 * 16);
   };
 
-  // query fragments first (plain loads, waited for before the copies start):
-  // K-steps [0, kQRegSteps) in registers, the rest in LDS after the KV ring
-  const int head = 32 * wave + n;
-  const bool row_ok = head < a.Hq;
-  char* qlds = mla_smem + kStages * kStageBytes;
-  lds_cchar* qlds3 = (lds_cchar*)mla_smem + kStages * kStageBytes;
-  bf16x8 qf[kQRegSteps];  // B operand of S^T: Q[head][16 ks + 8h .. +7]
-  {
-    const __bf16* qp = (const __bf16*)a.q + ((int64_t)b * a.Hq + head) * kDqk + 8 * h;
-#pragma unroll
-    for (int ks = 0; ks < kQRegSteps; ++ks)
-      qf[ks] = row_ok ? as_bf16x8(load16(qp + 16 * ks)) : as_bf16x8(u32x4{0, 0, 0, 0});
-#pragma unroll
-    for (int ks = kQRegSteps; ks < KS; ++ks) {
-      const u32x4 v = row_ok ? load16(qp + 16 * ks) : u32x4{0, 0, 0, 0};
-      store16(qlds + head * kQLdsStride + (16 * (ks - kQRegSteps) + 8 * h) * 2, v);
-    }
-  }
-  wait_vmcnt<0>();
-  if (ntiles > 0) issue_tile(0, 0);
-
-  const float sc = a.scale * kLog2e;
-  float m = kNegInf, l = 0.f;
-  floatx16 acc[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[dt][v] = 0.f;
-
-  // K operand: M-row n reads key kperm32(n), columns 16 ks + 8h (chunk 2 ks + h)
-  const int krow = kperm32(n);
-  int koff[4];  // offset of chunk 2 u + h (u = ks % 4); chunk group ks / 4 adds 4 KiB each
-#pragma unroll
-  for (int u = 0; u < 4; ++u) koff[u] = chunk_off(krow, 2 * u + h);
-  // V^T operand via transpose reads.  16-lane group G = lane / 16 of the wave
-  // serves columns 32 dt + 16 (G & 1) + .. and keys 16 kk + 8 (G >> 1) + ..;
-  // its source lane k' reads key 16 kk + 8 (G >> 1) + 4 hh + (k' >> 2),
-  // columns 32 dt + 16 (G & 1) + 4 (k' & 3) .. +3 (chunk 4 dt + 2 (G & 1) +
-  // ((k' & 3) >> 1), half (k' & 1)).
-  const int G = lane >> 4, kq = lane & 15;
-  int voff[2][2][2];  // [kk][hh][dt & 1]; the group index dt >> 1 adds a constant
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int d2 = 0; d2 < 2; ++d2) {
-        const int key = 16 * kk + 8 * (G >> 1) + 4 * hh + (kq >> 2);
-        const int c = 4 * d2 + 2 * (G & 1) + ((kq & 3) >> 1);
-        voff[kk][hh][d2] = chunk_off(key, c) + 8 * (kq & 1);
-      }
-
-  for (int ti = 0; ti < ntiles; ++ti) {
-    wait_vmcnt<0>();
-    __syncthreads();  // tile ti is in LDS; stage (ti + 1) % 2 is no longer read
-    if (ti + 1 < ntiles) issue_tile(ti + 1, (ti + 1) % kStages);
-    const int t0 = t0k + ti * kMTK;
-    // the stage as an LDS address: operand addresses stay 32-bit and their
-    // constant parts fold into the instructions' offsets
-    lds_cchar* stage = (lds_cchar*)mla_smem + (ti % kStages) * kStageBytes;
-
-    // S^T (two accumulation chains: even / odd K-steps, each started by an
-    // instruction with a zero addend)
-    floatx16 sa, sb;
-    // operand reads run kAhead K-steps ahead of the matrix instructions (by
-    // hand: left alone, the scheduler sinks each read next to its use)
-    constexpr int kAhead = 4;
-    auto kread = [&](int ks) {  // chunk 2 ks + h lives in group (2 ks + h) >> 3 = ks >> 2
-      const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-          stage + koff[ks & 3] + (ks >> 2) * (kMTK * 8 * 16));
-      return as_bf16x8(v);
-    };
-    auto qread = [&](int ks) {
-      const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-          qlds3 + head * kQLdsStride + (16 * (ks - kQRegSteps) + 8 * h) * 2);
-      return as_bf16x8(v);
-    };
-    bf16x8 kbuf[kAhead], qbuf[kAhead];
-#pragma unroll
-    for (int i = 0; i < kAhead; ++i) {
-      kbuf[i] = kread(i);
-      if (i >= kQRegSteps) qbuf[i] = qread(i);
-    }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 kf = kbuf[ks % kAhead];
-      const bf16x8 qv = ks < kQRegSteps ? qf[ks < kQRegSteps ? ks : 0] : qbuf[ks % kAhead];
-      if (ks == 0) mfma32_vgpr_first(sa, kf, qv);
-      else if (ks == 1) mfma32_vgpr_first(sb, kf, qv);
-      else if (ks & 1) mfma32_vgpr(sb, kf, qv);
-      else mfma32_vgpr(sa, kf, qv);
-      if (ks + kAhead < KS) {
-        kbuf[ks % kAhead] = kread(ks + kAhead);
-        if (ks + kAhead >= kQRegSteps) qbuf[ks % kAhead] = qread(ks + kAhead);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // the last two matrix instructions (one per chain) must have retired
-    // before vector instructions read their results
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(sa), "+v"(sb));
-    // lane holds S[head][key] for keys 8h + v (v < 8) and 16 + 8h + (v - 8)
-    float x[16];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) x[v] = sa[v] + sb[v];
-    if (t0 + kMTK > t1k) {  // the last tile of the range: mask the keys past its end
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = t0 + (v < 8 ? 8 * h + v : 16 + 8 * h + (v - 8));
-        x[v] = key < t1k ? x[v] : kNegInf;
-      }
-    }
-    float tm0 = fmaxf(x[0], x[1]), tm1 = fmaxf(x[8], x[9]);  // two chains
-#pragma unroll
-    for (int v = 2; v < 8; ++v) {
-      tm0 = fmaxf(tm0, x[v]);
-      tm1 = fmaxf(tm1, x[v + 8]);
-    }
-    const float tmax = xor32_max(fmaxf(tm0, tm1));
-    const bool grow = (tmax - m) * sc > kLazyLog2;  // always true on the first tile
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-      const float mnew = grow ? tmax : m;
-      const float alpha = grow ? fast_exp2((m - mnew) * sc) : 1.f;  // 0 while m = -inf
-      l *= alpha;
-      // acc lives in AGPRs; scale it there (read, multiply, write back) so
-      // that the allocator never has to hold it in vector registers.  The
-      // last matrix instruction that wrote it must have retired first.
-      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float x = acc[dt][v];
-          agpr_scale(x, alpha);
-          acc[dt][v] = x;
-        }
-      asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");  // settle before the next MFMA reads acc
-      m = mnew;
-    }
-    const float msc = (m == kNegInf ? 0.f : m) * sc;
-    float p[16], ps[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      p[v] = fast_exp2(fmaf(x[v], sc, -msc));
-      ps[v & 3] += p[v];
-    }
-    l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-    bf16x8 pf[2];  // B operand of O^T per 16-key step kk: keys 16 kk + 8h + i
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-      pf[kk] = __builtin_bit_cast(
-          bf16x8, u32x4{pack_bf16x2(p[8 * kk + 0], p[8 * kk + 1]),
-                        pack_bf16x2(p[8 * kk + 2], p[8 * kk + 3]),
-                        pack_bf16x2(p[8 * kk + 4], p[8 * kk + 5]),
-                        pack_bf16x2(p[8 * kk + 6], p[8 * kk + 7])});
-    // the matrix instructions below are inline assembly, which the compiler
-    // does not pad against hazards: let the vector writes of pf settle (the
-    // operands keep those writes before this point)
-    asm volatile("s_nop 4" : "+v"(pf[0]), "+v"(pf[1]));
-    // V^T operands: two transposing reads each, kAheadV instructions ahead
-    constexpr int kAheadV = 4;
-    auto vread = [&](int i) {  // i = 2 dt + kk
-      const int dt = i >> 1, kk = i & 1;
-      const int goff = (dt >> 1) * (kMTK * 8 * 16);  // chunk group of columns 32 dt ..
-      const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_short4*)(stage + voff[kk][0][dt & 1] + goff));
-      const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_short4*)(stage + voff[kk][1][dt & 1] + goff));
-      const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-      return __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
-    };
-    bf16x8 vbuf[kAheadV];
-#pragma unroll
-    for (int i = 0; i < kAheadV; ++i) vbuf[i] = vread(i);
-#pragma unroll
-    for (int i = 0; i < 2 * DT; ++i) {
-      mfma32_acc_agpr(acc[i >> 1], vbuf[i % kAheadV], pf[i & 1]);
-      if (i + kAheadV < 2 * DT) vbuf[i % kAheadV] = vread(i + kAheadV);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-  // every wave is done with the ring before a later segment's copies refill it
-  __syncthreads();
-
-  // epilogue: lane holds O[head][32 dt + 8 (v / 4) + 4h + v % 4].  The last
-  // matrix instructions (inline assembly, issued in column-tile order) must
-  // have retired before acc is read: the wait is tied to the last two tiles
-  // (earlier tiles were written at least four instructions before the end).
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[DT - 1]), "+a"(acc[DT - 2]));
-  const float lrow = xor32_sum(l);
-  if (!row_ok) return;
-  const float inv = lrow > 0.f ? 1.f / lrow : 0.f;
-  const float lse = lrow > 0.f ? m * a.scale + __log2f(lrow) * kLn2 : kNegInf;
-  const int64_t bh = (int64_t)b * a.Hq + head;
-  if (pbase < 0) {
-    __bf16* op = (__bf16*)a.out + bh * kDv + 4 * h;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * q) =
-            u32x2{pack_bf16x2(acc[dt][4 * q] * inv, acc[dt][4 * q + 1] * inv),
-                  pack_bf16x2(acc[dt][4 * q + 2] * inv, acc[dt][4 * q + 3] * inv)};
-    if (h == 0 && a.lse) a.lse[bh] = lse;
-  } else {
-    const int64_t pi = pbase + (int64_t)head * pstride;
-    float* op = a.part_o + pi * kDv + 4 * h;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        store16(op + 32 * dt + 8 * q,
-                __builtin_bit_cast(u32x4, floatx4{acc[dt][4 * q] * inv, acc[dt][4 * q + 1] * inv,
-                                                  acc[dt][4 * q + 2] * inv,
-                                                  acc[dt][4 * q + 3] * inv}));
-    if (h == 0) a.part_lse[pi] = lse;
-  }
-}
-
-
-// ---------------------------------------------------------------------------
-// Wide variant of the tile loop: 8 waves, two per SIMD, wave w owning heads
-// 16 w .. 16 w + 15 on v_mfma_f32_16x16x32_bf16 (lane layouts in
-// pa_device.h).  A wave's output tile is 16 heads x 512 columns, 128
-// accumulator registers, so two waves fit on a SIMD and one runs its matrix
-// products while the other waits on LDS or runs its softmax.  Every wave
-// reads the whole key tile and value tile from LDS (twice the LDS reads of
-// the 4-wave loop per key tile); the ring and the copies (waves 0-3) are
-// those of the 4-wave loop.
-//   * S^T = K Q^T: M-row r of key block kb (0, 1) holds key 8 (r / 4) + 4 kb
-//     + r % 4, so lane (r, g) ends with keys 8 g .. 8 g + 7 of head r: the
-//     B operand (P^T) of the value product, in order;
-//   * O^T = V^T P^T: one instruction per 16 columns, its V^T operand (8 keys
-//     of one column per lane) read with two transposing LDS reads.
-// Chunk swizzle: chosen by measurement (the LDS bank-conflict counter over
-// every invertible linear map of key bits 1, 3 and 4 onto the 3 chunk bits)
-// among those with no conflicts for both the key-operand reads and the
-// transposing value reads; LDS bank selection on this part is not a plain
-// function of the low address bits, so the choice is not derived here.
-// ---------------------------------------------------------------------------
-constexpr int kWThreads = 512;
-constexpr int kWSteps = kDqk / 32;                       // 18 K-steps of 32 columns
-constexpr int kWQRegSteps = 14;                          // query K-steps held in registers
-constexpr int kWQLdsSteps = kWSteps - kWQRegSteps;       // the rest in LDS
-constexpr int kWQLdsStride = kWQLdsSteps * 32 * 2 + 16;  // bytes per head row (padded)
-constexpr int kWQLdsBytes = 128 * kWQLdsStride;
-constexpr size_t kWLdsBytes = (size_t)kStages * kStageBytes + kWQLdsBytes;
-
-__device__ __forceinline__ int swz_w(int k) {
-  const int k1 = (k >> 1) & 1, k3 = (k >> 3) & 1, k4 = (k >> 4) & 1;
-  return k1 | ((k1 ^ k3) << 1) | ((k3 ^ k4) << 2);
-}
-__device__ __forceinline__ int chunk_off_w(int k, int c) {
-  return (((c >> 3) * kMTK + k) * 8 + ((c & 7) ^ swz_w(k))) * 16;
-}
-
-// Keys [t0k, t1k) of request b for all its heads, by one workgroup of
-// kWThreads; the same contract as mla_keys.
-__device__ __forceinline__ void mla_keys_wide(const MlaArgs& a, char* mla_smem, int tid, int b,
-                                              int t0k, int t1k, int64_t pbase, int pstride) {
-  constexpr int DT = kDv / 16;  // 32 column tiles of O^T
-  const int wave = tid >> 6, lane = tid & 63;
-  const int r = lane & 15, g = lane >> 4;
-  const int P = a.P, lp = a.log2_page;
-  const int ntiles = (t1k - t0k + kMTK - 1) / kMTK;
-
-  typedef const __attribute__((address_space(4))) int32_t* ConstI32Ptr;
-  const ConstI32Ptr bt =
-      (ConstI32Ptr)uniform_ptr(a.block_table + (int64_t)__builtin_amdgcn_readfirstlane(b) * a.max_pages);
-  const char* kv = uniform_ptr((const char*)a.kv);
-
-  // copies by waves 0-3 (one per SIMD): thread t copies key t / 8, chunk
-  // slot t % 8 of each of the 9 groups, as in mla_keys
-  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-  const bool copier = wave_s < 4;
-  const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(lds_cchar*)mla_smem + (wave_s & 3) * 64 * 16);
-  auto issue_tile = [&](int ti, int st) {
-    int lane_now = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-    asm volatile("" : "+v"(lane_now));
-    const int dt = (wave_s & 3) * 64 + lane_now;
-    const int dkey = dt >> 3;
-    const int dchunk = (dt & 7) ^ swz_w(dkey);
-    const int lane_src = dkey * (kDqk * 2) + dchunk * 16;
-    const int t0 = t0k + ti * kMTK;
-    const char* src;
-    if (P >= kMTK && t0 + kMTK <= t1k) {
-      const int page = checked_page(bt[t0 >> lp], a.num_pages, a.dbg);
-      src = kv + (((int64_t)page << lp) + (t0 & (P - 1))) * (kDqk * 2) + lane_src;
-    } else {
-      const int key = min(t0 + dkey, t1k - 1);  // clamped: real data, masked later
-      const int last_pg = (t1k - 1) >> lp;
-      const int pg0 = __builtin_amdgcn_readfirstlane(t0 >> lp);
-      int page;
-      if (P >= kMTK) {
-        page = checked_page(bt[pg0], a.num_pages, a.dbg);
-      } else {
-        const int j = (key >> lp) - pg0;  // 0 .. 32 / P - 1
-        const int p0 = checked_page(bt[pg0], a.num_pages, a.dbg);
-        const int p1 = checked_page(bt[min(pg0 + 1, last_pg)], a.num_pages, a.dbg);
-        const int p2 = checked_page(bt[min(pg0 + 2, last_pg)], a.num_pages, a.dbg);
-        const int p3 = checked_page(bt[min(pg0 + 3, last_pg)], a.num_pages, a.dbg);
-        page = j == 0 ? p0 : (j == 1 ? p1 : (j == 2 ? p2 : p3));
-      }
-      src = kv + (((int64_t)page << lp) + (key & (P - 1))) * (kDqk * 2) + dchunk * 16;
-    }
-    const uint32_t dst = lds_wave + st * kStageBytes;
-#pragma unroll
-    for (int j = 0; j < kGroups; ++j) lds_dma16_m0(src + 128 * j, dst + j * kMTK * 8 * 16);
-  };
-
-  // query: K-steps [0, kWQRegSteps) in registers, the rest in LDS after the
+  // query: K-steps [0, kQRegSteps) in registers, the rest in LDS after the
   // ring (each wave writes and reads only its own heads' rows)
   const int head = 16 * wave + r;
   const bool row_ok = head < a.Hq;
   char* qlds = mla_smem + kStages * kStageBytes;
   lds_cchar* qlds3 = (lds_cchar*)mla_smem + kStages * kStageBytes;
-  bf16x8 qf[kWQRegSteps];  // B operand of S^T: Q[head][32 ks + 8 g .. +7]
+  bf16x8 qf[kQRegSteps];  // B operand of S^T: Q[head][32 ks + 8 g .. +7]
   {
     const __bf16* qp = (const __bf16*)a.q + ((int64_t)b * a.Hq + head) * kDqk + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < kWQRegSteps; ++ks)
+    for (int ks = 0; ks < kQRegSteps; ++ks)
       qf[ks] = row_ok ? as_bf16x8(load16(qp + 32 * ks)) : as_bf16x8(u32x4{0, 0, 0, 0});
 #pragma unroll
-    for (int ks = kWQRegSteps; ks < kWSteps; ++ks) {
+    for (int ks = kQRegSteps; ks < kKSteps; ++ks) {
       const u32x4 v = row_ok ? load16(qp + 32 * ks) : u32x4{0, 0, 0, 0};
-      store16(qlds + head * kWQLdsStride + (32 * (ks - kWQRegSteps) + 8 * g) * 2, v);
+      store16(qlds + head * kQLdsStride + (32 * (ks - kQRegSteps) + 8 * g) * 2, v);
     }
   }
   wait_vmcnt<0>();
@@ -523,7 +183,7 @@ __device__ __forceinline__ void mla_keys_wide(const MlaArgs& a, char* mla_smem, 
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int u = 0; u < 2; ++u)
-      koff[kb][u] = chunk_off_w(8 * (r >> 2) + 4 * kb + (r & 3), 4 * u + g);
+      koff[kb][u] = chunk_off(8 * (r >> 2) + 4 * kb + (r & 3), 4 * u + g);
   // V^T operand: in 16-lane group g, source lane r of read hh addresses key
   // 8 g + 4 hh + r / 4, columns 16 dt + 4 (r % 4) .. +3 (chunk 2 dt + (r / 2)
   // % 2, half r % 2); lane r of the group receives column 16 dt + r
@@ -532,7 +192,7 @@ __device__ __forceinline__ void mla_keys_wide(const MlaArgs& a, char* mla_smem, 
   for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
     for (int d4 = 0; d4 < 4; ++d4)
-      voff[hh][d4] = chunk_off_w(8 * g + 4 * hh + (r >> 2), 2 * d4 + ((r >> 1) & 1)) + 8 * (r & 1);
+      voff[hh][d4] = chunk_off(8 * g + 4 * hh + (r >> 2), 2 * d4 + ((r >> 1) & 1)) + 8 * (r & 1);
 
   for (int ti = 0; ti < ntiles; ++ti) {
     if (copier) wait_vmcnt<0>();
@@ -551,7 +211,7 @@ __device__ __forceinline__ void mla_keys_wide(const MlaArgs& a, char* mla_smem, 
     };
     auto qread = [&](int ks) {
       const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-          qlds3 + head * kWQLdsStride + (32 * (ks - kWQRegSteps) + 8 * g) * 2);
+          qlds3 + head * kQLdsStride + (32 * (ks - kQRegSteps) + 8 * g) * 2);
       return as_bf16x8(v);
     };
     floatx4 s0 = floatx4{0.f, 0.f, 0.f, 0.f}, s1 = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -559,14 +219,14 @@ __device__ __forceinline__ void mla_keys_wide(const MlaArgs& a, char* mla_smem, 
 #pragma unroll
     for (int i = 0; i < kAhead; ++i) kbuf[i] = kread(i);
 #pragma unroll
-    for (int i = 0; i < 2 * kWSteps; ++i) {
+    for (int i = 0; i < 2 * kKSteps; ++i) {
       const int ks = i >> 1, kb = i & 1;
       // LDS query steps, two K-steps ahead of their use
-      if (kb == 0 && ks + 2 >= kWQRegSteps && ks + 2 < kWSteps) qbuf[(ks + 2) & 3] = qread(ks + 2);
-      const bf16x8 qv = ks < kWQRegSteps ? qf[ks < kWQRegSteps ? ks : 0] : qbuf[ks & 3];
+      if (kb == 0 && ks + 2 >= kQRegSteps && ks + 2 < kKSteps) qbuf[(ks + 2) & 3] = qread(ks + 2);
+      const bf16x8 qv = ks < kQRegSteps ? qf[ks < kQRegSteps ? ks : 0] : qbuf[ks & 3];
       if (kb == 0) s0 = mfma_bf16(kbuf[i % kAhead], qv, s0);
       else s1 = mfma_bf16(kbuf[i % kAhead], qv, s1);
-      if (i + kAhead < 2 * kWSteps) kbuf[i % kAhead] = kread(i + kAhead);
+      if (i + kAhead < 2 * kKSteps) kbuf[i % kAhead] = kread(i + kAhead);
       __builtin_amdgcn_sched_barrier(0);
     }
     // lane (r, g) holds S[head][t0 + 8 g + j] in x[j]
@@ -656,8 +316,7 @@ __device__ __forceinline__ void mla_keys_wide(const MlaArgs& a, char* mla_smem, 
 
 // pa_decode_split-style partitions: workgroup (b, s) takes the s-th of
 // num_splits page-aligned key ranges of request b.
-template <bool WIDE>
-__global__ __launch_bounds__(WIDE ? kWThreads : kMlaThreads) void mla_split_kernel(MlaArgs a) {
+__global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
   extern __shared__ __align__(16) char mla_smem[];
   const int S = a.num_splits;
   const int s = blockIdx.x % S, b = blockIdx.x / S;
@@ -667,8 +326,7 @@ __global__ __launch_bounds__(WIDE ? kWThreads : kMlaThreads) void mla_split_kern
   const long long a0 = per * s, a1 = a0 + per;
   const int t0k = a0 < L ? (int)a0 : L, t1k = a1 < L ? (int)a1 : L;
   const int64_t pbase = S > 1 ? (int64_t)b * a.Hq * S + s : -1;
-  if constexpr (WIDE) mla_keys_wide(a, mla_smem, threadIdx.x, b, t0k, t1k, pbase, S);
-  else mla_keys(a, mla_smem, threadIdx.x, b, t0k, t1k, pbase, S);
+  mla_keys(a, mla_smem, threadIdx.x, b, t0k, t1k, pbase, S);
 }
 
 // Tiles a request contributes to the balanced schedule (an empty request
@@ -703,9 +361,8 @@ __device__ __forceinline__ long long mla_block_sum(long long v, long long* red) 
 // recomputes the (small) schedule from seq_lens.  The tile loop (mla_keys)
 // runs once per segment on the same LDS ring; its LDS accesses stay LDS
 // instructions (the ring is addressed through the kernel's own shared array).
-template <bool WIDE>
-__global__ __launch_bounds__(WIDE ? kWThreads : kMlaThreads) void mla_balanced_kernel(MlaArgs a) {
-  constexpr int NT = WIDE ? kWThreads : kMlaThreads;
+__global__ __launch_bounds__(kMlaThreads) void mla_balanced_kernel(MlaArgs a) {
+  constexpr int NT = kMlaThreads;
   extern __shared__ __align__(16) char mla_smem[];
   __shared__ long long s_red[NT / 64];
   __shared__ int s_b;
@@ -763,8 +420,7 @@ __global__ __launch_bounds__(WIDE ? kWThreads : kMlaThreads) void mla_balanced_k
     const long long k0 = s0 * kMTK, k1 = s1 * kMTK;
     const int t0k = k0 < L ? (int)k0 : L, t1k = k1 < L ? (int)k1 : L;
     const int64_t pbase = cut ? (int64_t)slot * a.Hq : -1;
-    if constexpr (WIDE) mla_keys_wide(a, mla_smem, tid, b, t0k, t1k, pbase, 1);
-    else mla_keys(a, mla_smem, tid, b, t0k, t1k, pbase, 1);
+    mla_keys(a, mla_smem, tid, b, t0k, t1k, pbase, 1);
     tb += n;
   }
 }
@@ -773,7 +429,7 @@ __global__ __launch_bounds__(WIDE ? kWThreads : kMlaThreads) void mla_balanced_k
 // 16 lanes per row with 32 columns each, folding the pieces' partial rows
 // (slots merge_info[2 b], then 2 (w0 + 1), 2 (w0 + 2), ... with w0 =
 // merge_info[2 b] / 2) with a running log-sum-exp.
-__global__ __launch_bounds__(kMlaThreads) void mla_balanced_merge_kernel(MlaArgs a) {
+__global__ __launch_bounds__(kMergeThreads) void mla_balanced_merge_kernel(MlaArgs a) {
   const int hg_count = a.Hq / 16;
   const int b = blockIdx.x / hg_count, hg = blockIdx.x % hg_count;
   const int w0 = a.merge_info[2 * b], np = a.merge_info[2 * b + 1];
@@ -828,34 +484,29 @@ hipError_t allow_lds_once(const void* kernel, std::atomic<uint64_t>& done, size_
 
 std::atomic<uint64_t> g_lds_balanced{0}, g_lds_split{0};
 
-// The tile loop the MLA kernels run: the 8-wave one (two waves per SIMD) or
-// the 4-wave one.
-constexpr bool kMlaWide = true;
-constexpr int kMlaLaunchThreads = kMlaWide ? kWThreads : kMlaThreads;
-constexpr size_t kMlaLds = kMlaWide ? kWLdsBytes : (size_t)kStages * kStageBytes + kQLdsBytes;
 
 }  // namespace
 
 hipError_t launch_mla_balanced(const MlaArgs& a, int grid, hipStream_t s) {
   if (a.B <= 0 || grid <= 0) return hipSuccess;
-  hipError_t e = allow_lds_once((const void*)mla_balanced_kernel<kMlaWide>, g_lds_balanced, kMlaLds);
+  hipError_t e = allow_lds_once((const void*)mla_balanced_kernel, g_lds_balanced, kMlaLds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mla_balanced_kernel<kMlaWide>, dim3(grid), dim3(kMlaLaunchThreads), kMlaLds, s, a);
+  hipLaunchKernelGGL(mla_balanced_kernel, dim3(grid), dim3(kMlaThreads), kMlaLds, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_mla_balanced_merge(const MlaArgs& a, hipStream_t s) {
   if (a.B <= 0) return hipSuccess;
-  hipLaunchKernelGGL(mla_balanced_merge_kernel, dim3(a.B * (a.Hq / 16)), dim3(kMlaThreads), 0, s, a);
+  hipLaunchKernelGGL(mla_balanced_merge_kernel, dim3(a.B * (a.Hq / 16)), dim3(kMergeThreads), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_mla_split(const MlaArgs& a, hipStream_t s) {
   const int64_t blocks = (int64_t)a.B * a.num_splits;
   if (blocks <= 0) return hipSuccess;
-  hipError_t e = allow_lds_once((const void*)mla_split_kernel<kMlaWide>, g_lds_split, kMlaLds);
+  hipError_t e = allow_lds_once((const void*)mla_split_kernel, g_lds_split, kMlaLds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mla_split_kernel<kMlaWide>, dim3(blocks), dim3(kMlaLaunchThreads), kMlaLds, s, a);
+  hipLaunchKernelGGL(mla_split_kernel, dim3(blocks), dim3(kMlaThreads), kMlaLds, s, a);
   return hipGetLastError();
 }
 
