@@ -62,6 +62,50 @@ __device__ __forceinline__ void lds_dma16_m0(const void* gsrc, uint32_t lds_wave
       : "memory");
 }
 
+// N copies as lds_dma16_m0, issued back to back with m0 saved once before
+// them and restored once after them (two scalar instructions per copy fewer
+// than N single calls).  gsrc[i] goes to lds_wave_base[i].
+__device__ __forceinline__ void lds_dma16_m0_x2(const void* g0, const void* g1, uint32_t l0,
+                                                uint32_t l1) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %4\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g0), "v"(g1), "s"(l0), "s"(l1)
+      : "memory");
+}
+__device__ __forceinline__ void lds_dma16_m0_x4(const void* g0, const void* g1, const void* g2,
+                                                const void* g3, uint32_t l0, uint32_t l1,
+                                                uint32_t l2, uint32_t l3) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %5\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %6\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %7\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %3, off\n\t"
+      "s_mov_b32 m0, %8\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %4, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g0), "v"(g1), "v"(g2), "v"(g3), "s"(l0), "s"(l1), "s"(l2), "s"(l3)
+      : "memory");
+}
+// The N copies gsrc[0..N) -> lds_wave_base[0..N) in groups of 4, 2 and 1.
+template <int N>
+__device__ __forceinline__ void lds_dma16_m0_seq(const void* const* g, const uint32_t* l) {
+  if constexpr (N >= 4) {
+    lds_dma16_m0_x4(g[0], g[1], g[2], g[3], l[0], l[1], l[2], l[3]);
+    lds_dma16_m0_seq<N - 4>(g + 4, l + 4);
+  } else if constexpr (N >= 2) {
+    lds_dma16_m0_x2(g[0], g[1], l[0], l[1]);
+    lds_dma16_m0_seq<N - 2>(g + 2, l + 2);
+  } else if constexpr (N == 1) {
+    lds_dma16_m0(g[0], l[0]);
+  }
+}
+
 // A pointer every lane holds the same value of, made visibly uniform (scalar
 // registers): loads through it with uniform indices become scalar loads,
 // which the copy waits do not count.

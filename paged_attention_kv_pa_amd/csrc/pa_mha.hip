@@ -552,9 +552,15 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
       const char* page1 = kbase + (int64_t)tp.pg1 * kpage_elems * 2;
       const int off = ((key - (hi ? tp.first1 : tp.first0)) * DK + 8 * (c0 + cl)) * 2;
       const char* src = (hi ? page1 : page0) + off;
+      // (each half's copies back to back, m0 saved once for them)
+      const void* gsrc[LY::kKCopies / 2];
+      uint32_t ldst[LY::kKCopies / 2];
 #pragma unroll
-      for (int j = 0; j < LY::kKCopies / 2; ++j)
-        lds_dma16_m0(src + 64 * j, kst + LY::koff(16 * kgroup, c0 + 4 * j));
+      for (int j = 0; j < LY::kKCopies / 2; ++j) {
+        gsrc[j] = src + 64 * j;
+        ldst[j] = kst + LY::koff(16 * kgroup, c0 + 4 * j);
+      }
+      lds_dma16_m0_seq<LY::kKCopies / 2>(gsrc, ldst);
     }
     {
       // V^T: lanes 2j and 2j + 1 copy the two 8-key chunks of column 32 i + j
@@ -567,8 +573,10 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
       const int slot = cs - (hv ? tp.first1 : tp.first0);
       const char* vsrc = vbase + ((int64_t)pg * vpage_elems + (int64_t)(lane >> 1) * P + slot) * 2;
 #pragma unroll
-      for (int i = 0; i < LY::kVCopies; ++i)
-        lds_dma16_m0(vsrc + (int64_t)(32 * i) * P * 2, vst + LY::voff(2 * kgroup, 32 * i));
+      for (int i = 0; i < LY::kVCopies; i += 2) {
+        lds_dma16_m0_x2(vsrc + (int64_t)(32 * i) * P * 2, vsrc + (int64_t)(32 * i + 32) * P * 2,
+                        vst + LY::voff(2 * kgroup, 32 * i), vst + LY::voff(2 * kgroup, 32 * i + 32));
+      }
     }
   };
 

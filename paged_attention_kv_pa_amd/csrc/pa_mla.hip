@@ -146,8 +146,14 @@ __device__ __forceinline__ void mla_keys(const MlaArgs& a, char* mla_smem, int t
       src = kv + (((int64_t)page << lp) + (key & (P - 1))) * (kDqk * 2) + dchunk * 16;
     }
     const uint32_t dst = lds_wave + st * kStageBytes;
+    const void* gsrc[kGroups];
+    uint32_t ldst[kGroups];
 #pragma unroll
-    for (int j = 0; j < kGroups; ++j) lds_dma16_m0(src + 128 * j, dst + j * kMTK * 8 * 16);
+    for (int j = 0; j < kGroups; ++j) {
+      gsrc[j] = src + 128 * j;
+      ldst[j] = dst + j * kMTK * 8 * 16;
+    }
+    lds_dma16_m0_seq<kGroups>(gsrc, ldst);
   };
 
   // query: K-steps [0, kQRegSteps) in registers, the rest in LDS after the
