@@ -57,7 +57,8 @@ constexpr int kKSteps = kDqk / 32;                       // 18 K-steps of 32 col
 // register file.
 constexpr int kQRegSteps = 14;                           // query K-steps held in registers
 constexpr int kQLdsSteps = kKSteps - kQRegSteps;         // the rest in LDS
-constexpr int kQLdsStride = kQLdsSteps * 32 * 2 + 16;    // bytes per head row (padded)
+constexpr int kQLdsStride = kQLdsSteps * 32 * 2 + 32;    // bytes per head row (padded: 288
+                                                         // measured conflict-free, 272 2-way)
 constexpr int kQLdsBytes = 128 * kQLdsStride;
 constexpr size_t kMlaLds = (size_t)kStages * kStageBytes + kQLdsBytes;
 
