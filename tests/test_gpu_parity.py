@@ -603,8 +603,9 @@ def test_mla_balanced_many_short_requests():
     mla_parity(b, "mla balanced, 600 short requests", S=0)
 
 
-@pytest.mark.parametrize("page,heads", [(16, 64), (8, 16), (256, 128)])
+@pytest.mark.parametrize("page,heads", [(16, 64), (8, 16), (256, 128), (32, 48), (64, 112)])
 def test_mla_balanced_pages_and_heads(page, heads):
+    # (head counts that leave some of the 16-head waves without rows)
     # fewer tiles than workgroups: most requests spread over several workgroups
     lens = [1, 33, 700, 5, 2000, 64, 63, 32, 31]
     b = workload.make_batch([1] * len(lens), [x - 1 for x in lens], num_q_heads=heads,
