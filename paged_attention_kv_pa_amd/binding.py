@@ -124,6 +124,27 @@ def _stream(device, stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+# pa_forward leaves its work-queue state in the first bytes of its workspace
+# for the next call on it; a workspace that is new (or was written by others
+# since) makes the call take a fixed item order instead, which balances worse.
+# Calls that pass no workspace therefore share one per (device, stream),
+# grown when a call needs more.  Work on one stream is ordered, so calls on it
+# never use the shared workspace at the same time.  Calls made while a graph is
+# being captured get a workspace of their own, which the graph keeps.
+_ws_cache = {}
+
+
+def _shared_workspace(device, need, stream):
+    if torch.cuda.is_current_stream_capturing():
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    key = (device.index, _stream(device, stream).value)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return PA_BF16
@@ -210,7 +231,8 @@ def pa_forward(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scal
 
     q [T, Hq, D]; k_cache [pages, Hkv, P, D]; v_cache [pages, Hkv, D, P];
     block_table int32 [B, max_pages]; seq_lens int32 [B]; query_start_loc int32 [B+1].
-    Returns out ([T, Hq, D], allocated if not given).
+    Returns out ([T, Hq, D], allocated if not given).  Without `workspace`, calls on one
+    (device, stream) share a workspace the binding keeps (see _shared_workspace).
     """
     return _forward(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale, out, lse,
                     workspace, max_seq_len, max_q_len, stream, None, None, None, None, 0)
@@ -260,7 +282,7 @@ def _forward(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale,
               "bad lse tensor")
     need = pa_workspace_size(dims)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = _shared_workspace(q.device, need, stream)
     nbytes = workspace.numel() * workspace.element_size()
     if mask is None:
         st = library().pa_forward(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),

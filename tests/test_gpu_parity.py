@@ -796,6 +796,27 @@ def test_decode_workspace_state_between_calls(fill):
     check_out(outs[0].float().cpu().numpy(), ref, b.dtype, "decode, workspace filled 0x%02x" % fill)
 
 
+def test_forward_without_workspace_shares_one_per_stream():
+    # calls that pass no workspace reuse one kept by the binding, so the second
+    # call finds the queue marker the first one left; the bits do not change
+    b = workload.llama_decode(3, batch=24)
+    g = b.to(DEV)
+    kw = dict(max_seq_len=max(b.seq_lens_list), max_q_len=1)
+    from paged_attention_kv_pa_amd import binding
+    binding._ws_cache.clear()
+    o1 = pa.pa_forward(g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens, g.query_start_loc,
+                       b.scale, **kw)
+    assert len(binding._ws_cache) == 1
+    ws = next(iter(binding._ws_cache.values()))
+    o2 = pa.pa_forward(g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens, g.query_start_loc,
+                       b.scale, **kw)
+    torch.cuda.synchronize()
+    assert next(iter(binding._ws_cache.values())) is ws
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    ref, _ = oracle_forward(b)
+    check_out(o2.float().cpu().numpy(), ref, b.dtype, "decode, shared workspace")
+
+
 def test_page_permutation_invariance_bitwise():
     a = workload.make_batch([1, 9, 70], [400, 33, 0], num_q_heads=32, num_kv_heads=8,
                             head_dim_qk=128, page_size=16, seed=5)
