@@ -498,6 +498,14 @@ static pa_status forward_masked_impl(const void* q, const void* k_cache, const v
   a.dbg = debug_flag();
   a.num_splits = 1;
   a.target_items = pl.target_items;
+  // A decode-only call whose requests all fit one smallest partition and
+  // whose (request, KV head) pairs do not outnumber the workgroups splits no
+  // row and claims nothing from the queue (every workgroup runs at most its
+  // first item): with the partition floor set to that size, the merge launch
+  // has no rows to merge and no counters to reset, so it is left out.
+  const bool single_launch = fused && d->max_seq_len <= pa::kMinChunkWide &&
+                             (int64_t)d->num_seqs * d->num_kv_heads <= grid;
+  a.min_chunk = single_launch ? pa::kMinChunkWide : 0;
   a.mask = mask;
   a.prefix_lens = prefix_lens;
   a.sinks = sinks;
@@ -512,6 +520,7 @@ static pa_status forward_masked_impl(const void* q, const void* k_cache, const v
   // wave per 4 rows of each (request, KV head) pair (B * Hkv pairs of up to
   // 16 rows; the waves of unsplit pairs stop at the pair's entry), four waves
   // per workgroup
+  if (single_launch) return PA_OK;
   const int64_t pairs = (int64_t)d->num_seqs * d->num_kv_heads;
   a.merge_groups =
       (int)((std::min<int64_t>(std::max(1, d->max_q_len) * (int64_t)G, pa::kDecodeRows) + 3) / 4);

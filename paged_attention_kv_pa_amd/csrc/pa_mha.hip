@@ -990,7 +990,8 @@ __device__ long long fused_plan(const MhaArgs& a, FusedPlan& fp) {
   if ((tid & 63) == 0 && my_keys) atomicAdd(&fp.keys, my_keys);
   if ((tid & 63) == 0 && my_reqs) atomicAdd(&fp.reqs, my_reqs);
   __syncthreads();
-  const long long minc = decode_min_chunk(fp.reqs, a.Hkv, a.target_items);
+  long long minc = decode_min_chunk(fp.reqs, a.Hkv, a.target_items);
+  if (a.min_chunk > minc) minc = a.min_chunk;  // the host's floor (see pa_forward)
   const long long chunk = decode_chunk(fp.keys, a.Hkv, a.target_items, minc);
   if (tid == 0) fp.minc = minc;  // read after the barrier at the end
   int4 run = int4{0, 0, 0, 0};  // decode items, partial slots, merge entries
