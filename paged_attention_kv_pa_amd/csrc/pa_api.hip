@@ -498,14 +498,15 @@ static pa_status forward_masked_impl(const void* q, const void* k_cache, const v
   a.dbg = debug_flag();
   a.num_splits = 1;
   a.target_items = pl.target_items;
-  // A decode-only call whose requests all fit one smallest partition and
-  // whose (request, KV head) pairs do not outnumber the workgroups splits no
-  // row and claims nothing from the queue (every workgroup runs at most its
-  // first item): with the partition floor set to that size, the merge launch
-  // has no rows to merge and no counters to reset, so it is left out.
+  // A decode-only call whose requests are no longer than the smallest
+  // partition the plan would make for a filled grid, and whose (request, KV
+  // head) pairs do not outnumber the workgroups, needs neither a plan nor a
+  // split nor the queue: workgroup j runs pair j over all its keys.  The merge
+  // launch then has no rows to merge and no counters to reset, so it is left
+  // out and the call is one launch.
   const bool single_launch = fused && d->max_seq_len <= pa::kMinChunkWide &&
                              (int64_t)d->num_seqs * d->num_kv_heads <= grid;
-  a.min_chunk = single_launch ? pa::kMinChunkWide : 0;
+  a.single_pass = single_launch ? 1 : 0;
   a.mask = mask;
   a.prefix_lens = prefix_lens;
   a.sinks = sinks;

@@ -105,7 +105,8 @@ struct MhaArgs {
   int32_t Hq, Hkv, G, P, max_pages;
   int32_t num_splits;        // pa_decode_split: partitions; pa_forward_chunked: chunks
   int32_t target_items;      // pa_forward decode-only calls planned in the kernel
-  int32_t min_chunk;         // ... and their smallest partition (0: the kernel's own rule)
+  int32_t single_pass;       // ... 1: one item per (request, KV head) over all its keys,
+                             // no plan, no split, no queue (see pa_forward)
   int32_t chunk_keys;        // pa_forward_chunked: keys per chunk
   int32_t row_blocks;        // pa_forward_chunked: row blocks of the longest request
   int32_t merge_groups;      // pa_forward's merge: groups of 4 rows of the widest split pair

@@ -990,8 +990,7 @@ __device__ long long fused_plan(const MhaArgs& a, FusedPlan& fp) {
   if ((tid & 63) == 0 && my_keys) atomicAdd(&fp.keys, my_keys);
   if ((tid & 63) == 0 && my_reqs) atomicAdd(&fp.reqs, my_reqs);
   __syncthreads();
-  long long minc = decode_min_chunk(fp.reqs, a.Hkv, a.target_items);
-  if (a.min_chunk > minc) minc = a.min_chunk;  // the host's floor (see pa_forward)
+  const long long minc = decode_min_chunk(fp.reqs, a.Hkv, a.target_items);
   const long long chunk = decode_chunk(fp.keys, a.Hkv, a.target_items, minc);
   if (tid == 0) fp.minc = minc;  // read after the barrier at the end
   int4 run = int4{0, 0, 0, 0};  // decode items, partial slots, merge entries
@@ -1053,6 +1052,26 @@ __device__ WorkItem fused_item(const MhaArgs& a, const FusedPlan& fp, long long 
   return it;
 }
 
+// Item j of a single-pass call: request j / Hkv, KV head j % Hkv, all its
+// keys (an empty request gets an empty key range and writes nothing).
+__device__ WorkItem pair_item(const MhaArgs& a, int j) {
+  const int b = j / a.Hkv;
+  int nq, L, q0;
+  shape_of(a.qsl, a.seq_lens, a.max_pages, a.P, b, &nq, &L, &q0);
+  WorkItem it;
+  it.seq = b;
+  it.kvh = j - b * a.Hkv;
+  it.row0 = 0;
+  it.nrows = nq * a.G;
+  it.kv_begin = 0;
+  it.kv_end = nq > 0 ? L : 0;
+  it.part = -1;
+  it.q0 = q0;
+  it.ctx = L - nq;
+  it.nchunk = it.chunk = it.pad = 0;
+  return it;
+}
+
 // Persistent forward kernel: a fixed grid; each workgroup takes items from
 // device counters until the planner's item count is reached.
 //
@@ -1089,9 +1108,13 @@ void mha_forward_kernel(MhaArgs a) {
   long long chunk = 0;
   int n_items, n_pre;
   if constexpr (FUSED) {
-    chunk = fused_plan(a, fp);
     n_pre = 0;
-    n_items = __builtin_amdgcn_readfirstlane(fp.doff[a.num_seqs]);
+    if (a.single_pass) {
+      n_items = a.num_seqs * a.Hkv;  // no plan: item j is (request, KV head) pair j
+    } else {
+      chunk = fused_plan(a, fp);
+      n_items = __builtin_amdgcn_readfirstlane(fp.doff[a.num_seqs]);
+    }
   } else {
     n_items = a.ctrl->n_items;
     n_pre = a.ctrl->n_pre;
@@ -1119,7 +1142,7 @@ void mha_forward_kernel(MhaArgs a) {
     const int lane = threadIdx.x;
     if constexpr (FUSED) {
       if (j < n_dec) {
-        const WorkItem w = fused_item(a, fp, chunk, j);
+        const WorkItem w = a.single_pass ? pair_item(a, j) : fused_item(a, fp, chunk, j);
         if (lane == 0) s_item = w;
       }
     } else {
