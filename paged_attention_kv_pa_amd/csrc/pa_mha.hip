@@ -959,6 +959,9 @@ __device__ int4 block_exclusive_scan4(int4 v, int4* wsum, int4* total) {
 struct FusedPlan {
   int doff[kFusedPlanMax + 1];  // first decode item of each request; [B] = item count
   int soff[kFusedPlanMax + 1];  // first partial slot
+  int nq[kFusedPlanMax];        // each request's shape (shape_of), loaded once
+  int L[kFusedPlanMax];
+  int q0[kFusedPlanMax];
   int4 wsum[kThreads / 64];
   unsigned long long keys;
   int reqs;       // decode-mode requests
@@ -977,6 +980,9 @@ __device__ long long fused_plan(const MhaArgs& a, FusedPlan& fp) {
   for (int b = tid; b < a.num_seqs; b += kThreads) {
     int nq, L, q0;
     shape_of(a.qsl, a.seq_lens, a.max_pages, a.P, b, &nq, &L, &q0);
+    fp.nq[b] = nq;  // read after the barrier below, by the second pass and fused_item
+    fp.L[b] = L;
+    fp.q0[b] = q0;
     if (nq > 0) {
       my_keys += (unsigned long long)L;
       ++my_reqs;
@@ -999,7 +1005,9 @@ __device__ long long fused_plan(const MhaArgs& a, FusedPlan& fp) {
     int4 cnt = int4{0, 0, 0, 0};
     int nq = 0, L = 0, q0 = 0, per = 0, nsplit = 0;
     if (b < a.num_seqs) {
-      shape_of(a.qsl, a.seq_lens, a.max_pages, a.P, b, &nq, &L, &q0);
+      nq = fp.nq[b];
+      L = fp.L[b];
+      q0 = fp.q0[b];
       if (nq > 0) {
         decode_split(L, chunk, minc, is_tail_request(b, a.num_seqs), &per, &nsplit);
         cnt.x = a.Hkv * nsplit;
@@ -1033,8 +1041,8 @@ __device__ long long fused_plan(const MhaArgs& a, FusedPlan& fp) {
 // Decode item j of the kernel's own plan (the planner kernel's item layout).
 __device__ WorkItem fused_item(const MhaArgs& a, const FusedPlan& fp, long long chunk, int j) {
   const int b = find_request(fp.doff, a.num_seqs, j);
-  int nq, L, q0, per, nsplit;
-  shape_of(a.qsl, a.seq_lens, a.max_pages, a.P, b, &nq, &L, &q0);
+  int per, nsplit;
+  const int nq = fp.nq[b], L = fp.L[b], q0 = fp.q0[b];
   decode_split(L, chunk, fp.minc, is_tail_request(b, a.num_seqs), &per, &nsplit);
   const int local = j - fp.doff[b];
   const int kvh = local / nsplit, sp = local - kvh * nsplit;
