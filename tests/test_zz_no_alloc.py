@@ -46,16 +46,18 @@ def test_noalloc_matches_pa_forward_on_two_calls():
 
 
 def test_noalloc_refuses_calls_beyond_its_workspace():
-    # 256 new tokens on 131072 cached ones: pa_forward would run it as chunk
-    # partials far larger than the library's 64 MiB array
-    b = workload.llama_long_extend(0, new_tokens=256, cached=131072)
+    # 1024 decode requests on 8 KV heads: room for pa_forward's split partials
+    # of that many (request, KV head) pairs is about 100 MB, more than the
+    # library's 64 MiB array
+    n = 1024
+    b = workload.make_batch([1] * n, [47] * n, num_q_heads=32, num_kv_heads=8,
+                            head_dim_qk=128, page_size=16, seed=7, name="noalloc_big")
     g = b.to(DEV)
     dims = pa.make_dims(g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens, b.num_tokens,
-                        max_seq_len=max(b.seq_lens_list), max_q_len=256)
+                        max_seq_len=48, max_q_len=1)
     assert pa.pa_workspace_size(dims) > pa.pa_noalloc_max_workspace()
     out = torch.empty(b.num_tokens, b.num_q_heads, b.head_dim_v, dtype=b.dtype, device=DEV)
     with pytest.raises(pa.PaError) as e:
         pa.pa_forward_noalloc(g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens,
-                              g.query_start_loc, b.scale, out, max_seq_len=max(b.seq_lens_list),
-                              max_q_len=256)
+                              g.query_start_loc, b.scale, out, max_seq_len=48, max_q_len=1)
     assert e.value.status == pa.binding.PA_ERR_WORKSPACE
