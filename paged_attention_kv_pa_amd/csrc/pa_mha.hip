@@ -430,6 +430,7 @@ struct PrefillLayout {
 template <int DK, int DV>
 struct alignas(16) LdsPrefill {
   char ring[PrefillLayout<DK, DV>::kRingBytes];
+  float alibi_tab[kPrefillWaves][128];  // per wave: sqrt of the tile's distances (ALiBi-sqrt)
 };
 
 // ALIBI: subtract the ALiBi term (alibi_term) from every score.
@@ -469,6 +470,15 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
     lim = row_ok ? min(visible_end(mask, ctx, t, pfx), kv_end) : kv_begin;
     qpos = ctx + t;
     if constexpr (ALIBI) alibi_m = row_ok ? a.alibi[head] / a.scale : 0.f;
+  }
+  // ALiBi-sqrt: the wave's 32 rows cover at most 32 consecutive query
+  // positions from qmin (lane 0's), so with the 64 keys of a tile they span
+  // at most 95 distances; the tile's square roots are taken once per wave into
+  // a table (two per lane) instead of once per score.  Entry i of the table is
+  // for distance qmin - t0 - 63 + i; the lane's entries start at tab_lb.
+  const int qmin = __builtin_amdgcn_readfirstlane(qpos);
+  const int tab_lb = qpos - qmin + 8 - 8 * h;  // (qpos - qmin) + 63 - 8 h - 55, >= 0
+  {
     const __bf16* qp = (const __bf16*)a.q + out_row * DK + 8 * h;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -649,12 +659,30 @@ __device__ void run_prefill_item(const MhaArgs& a, const WorkItem& it, const Des
     const int t0 = kv_begin + t * kTK;
     if constexpr (ALIBI) {
       const int alibi_sqrt = __builtin_amdgcn_readfirstlane(a.alibi_sqrt);
-      const int d0 = qpos - t0 - 8 * h;  // distance to the key at offset 0 from t0 + 8 h
+      if (alibi_sqrt) {
+        float* tab = sm.alibi_tab[wave];
+        const int dbase = qmin - t0 - 63;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int i = 0; i < 2; ++i) {
+          const int d = dbase + lane + 64 * i;
+          tab[lane + 64 * i] = __builtin_amdgcn_sqrtf((float)(d < 0 ? -d : d));
+        }
+        // the key at offset o = 8 h + 32 kb + 16 (v / 8) + v % 8 from t0 is at
+        // distance qpos - t0 - o, entry tab_lb + 55 - (o - 8 h)
+        const float* tp = tab + tab_lb;
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          s[kb][v] -= alibi_term(alibi_m, alibi_sqrt, d0 - (32 * kb + 16 * (v >> 3) + (v & 7)));
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            s[kb][v] -= alibi_m * tp[55 - (32 * kb + 16 * (v >> 3) + (v & 7))];
+      } else {
+        const int d0 = qpos - t0 - 8 * h;  // distance to the key at offset 0 from t0 + 8 h
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            s[kb][v] -= alibi_term(alibi_m, 0, d0 - (32 * kb + 16 * (v >> 3) + (v & 7)));
+      }
     }
     if (t0 + kTK > wave_min) {  // only tiles that reach past the smallest limit need masks
       const int rel = lim - t0 - 8 * h;  // visible iff the key's offset from t0 + 8 h is < rel
