@@ -485,10 +485,15 @@ def test_forward_long_extend_full_size_all_rows():
     forward_parity(b, "pa_forward long extend full size (all rows)", ref=ref)
 
 
-def test_chunked_long_extend_full_size_all_rows():
-    # partials are compared at smaller sizes (test_chunked_long_context_extend)
+@pytest.mark.parametrize("chunks", [8, 17])
+def test_chunked_long_extend_full_size_all_rows(chunks):
+    # partials are compared at smaller sizes (test_chunked_long_context_extend);
+    # 8 chunks (one work item per compute unit) is the configuration the bench times
     b, ref = long_extend_case()
-    chunked_parity(b, 8192, "chunked long extend full size (all rows)", ref=ref, partials=False)
+    L = max(b.seq_lens_list)
+    C = ((L + chunks - 1) // chunks + 63) // 64 * 64
+    chunked_parity(b, C, "chunked long extend full size, %d chunks (all rows)" % chunks, ref=ref,
+                   partials=False)
 
 
 LONG_MIX = dict(n_decode=6, n_extend=2, n_prefill=2, dec=(1024, 4096), ext_q=(256, 500),
