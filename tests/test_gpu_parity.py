@@ -353,6 +353,37 @@ def test_alibi_decode_only_with_split_rows():
                   alibi_mode=pa.PA_ALIBI_SQRT)
 
 
+# Decode-only calls of at most 512 keys whose (request, KV head) pairs fit the
+# grid run one workgroup per pair over all its keys (no plan, no split, no merge
+# launch): that path with every option of pa_forward_masked and every head shape.
+SINGLE_Q, SINGLE_C = [1, 1, 1, 1, 1], [0, 37, 255, 400, 511]
+
+
+@pytest.mark.parametrize("feature", ["causal", "full", "prefix", "sinks", "alibi_sqrt",
+                                     "alibi_linear"])
+def test_single_pass_decode_options(feature):
+    b = workload.make_batch(SINGLE_Q, SINGLE_C, num_q_heads=32, num_kv_heads=8, head_dim_qk=128,
+                            page_size=16, seed=1401)
+    mask = {"full": pa.PA_MASK_FULL, "prefix": pa.PA_MASK_PREFIX}.get(feature, pa.PA_MASK_CAUSAL)
+    prefixes = [0, 10, 300, 1000, 5] if feature == "prefix" else None
+    sinks = sink_logits(32, 21) if feature == "sinks" else None
+    mode = {"alibi_sqrt": pa.PA_ALIBI_SQRT, "alibi_linear": pa.PA_ALIBI_LINEAR}.get(
+        feature, pa.PA_ALIBI_NONE)
+    alibi = workload.alibi_slopes(32) if mode != pa.PA_ALIBI_NONE else None
+    masked_parity(b, mask, prefixes, "single-pass decode %s" % feature, sinks=sinks, alibi=alibi,
+                  alibi_mode=mode)
+
+
+@pytest.mark.parametrize("Hq,Hkv,Dqk,Dv,P", [(64, 4, 128, 128, 16), (32, 8, 64, 64, 8),
+                                             (16, 16, 192, 128, 64), (128, 8, 128, 128, 32)])
+def test_single_pass_decode_shapes(Hq, Hkv, Dqk, Dv, P):
+    b = workload.make_batch(SINGLE_Q, SINGLE_C, num_q_heads=Hq, num_kv_heads=Hkv,
+                            head_dim_qk=Dqk, head_dim_v=Dv, page_size=P, seed=1403 + Hq + Dqk)
+    forward_parity(b, "single-pass decode Hq=%d Hkv=%d D=%d/%d P=%d" % (Hq, Hkv, Dqk, Dv, P))
+    masked_parity(b, pa.PA_MASK_CAUSAL, None, "single-pass decode sinks Hq=%d D=%d/%d" % (
+        Hq, Dqk, Dv), sinks=sink_logits(Hq, 23))
+
+
 def test_alibi_stays_off_the_chunked_route():
     # few long extends (pa_forward would take the chunked route): with ALiBi the call
     # runs on the persistent kernel
