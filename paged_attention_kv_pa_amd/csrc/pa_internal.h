@@ -22,7 +22,9 @@ constexpr int kMinChunk = 256;         // smallest key partition pa_forward make
 constexpr int kMinChunkWide = 512;     // ... or, for calls whose (request, KV head) pairs fill the grid, this
 constexpr int kTailFraction = 8;       // the last 1 / kTailFraction of the requests ...
 constexpr int kTailDivisor = 2;        // ... get decode partitions kTailDivisor times smaller
-constexpr int kItemsPerWorkgroup = 4;  // decode work is cut into ~this many items per workgroup
+constexpr int kItemsPerWorkgroup = 4;  // decode work is cut into ~this many items per workgroup,
+constexpr int kItemsPerWorkgroupWide = 2;  // or this many in decode-only calls of more than 8
+                                           // rows per (request, KV head) pair
 constexpr int kMaxSplits = 256;        // pa_decode_split / pa_merge_lse / mla_decode limit
 constexpr int kItemInts = 12;          // int32 words of one pa_forward work item
 constexpr int kFusedPlanMax = 1024;    // decode-only calls up to this many requests plan in-kernel
@@ -187,7 +189,7 @@ struct FwdWorkspace {
   int32_t crow_budget;  // chunk partial rows x chunks the workspace holds (0: no chunking)
 };
 // target_items: the decode work of a call is cut into about this many items
-// (kItemsPerWorkgroup x the persistent grid).
+// (kItemsPerWorkgroup, or kItemsPerWorkgroupWide, x the persistent grid).
 // long_rows: rows x chunks of per-request chunk partials to provide for (0: none).
 FwdWorkspace fwd_workspace_layout(int B, int Hkv, int D, int target_items, int64_t long_rows);
 

@@ -912,9 +912,10 @@ __device__ __forceinline__ void shape_of(const int32_t* qsl, const int32_t* seq_
 }
 
 // Smallest decode partition of a call with dec_reqs decode-mode requests.
-// When the (request, KV head) pairs alone give every workgroup of the grid
-// about two items (target_items is kItemsPerWorkgroup per workgroup), cutting
-// short requests only adds partial rows and a merge: the floor is then
+// When the (request, KV head) pairs are many next to the items aimed at
+// (pairs x 2 x kItemsPerWorkgroup >= target_items: at least one pair per two
+// workgroups at the usual target, one per four at the wide one), cutting short
+// requests only adds partial rows and a merge: the floor is then
 // kMinChunkWide.  Fewer pairs need the cuts for parallelism: kMinChunk.
 __device__ __forceinline__ long long decode_min_chunk(int dec_reqs, int Hkv, int target_items) {
   const long long pairs = (long long)dec_reqs * Hkv;
