@@ -20,7 +20,7 @@ constexpr int kXcdRun = 32;           // consecutive prefill-mode items per queu
 constexpr int kMaxFwdSplits = 64;      // key partitions per decode row in pa_forward
 constexpr int kMinChunk = 256;         // smallest key partition pa_forward makes ...
 constexpr int kMinChunkWide = 512;     // ... or, for calls whose (request, KV head) pairs fill the grid, this
-constexpr int kTailFraction = 8;       // the last 1 / kTailFraction of the requests ...
+constexpr int kTailFraction = 4;       // the last 1 / kTailFraction of the requests ...
 constexpr int kTailDivisor = 2;        // ... get decode partitions kTailDivisor times smaller
 constexpr int kItemsPerWorkgroup = 4;  // decode work is cut into ~this many items per workgroup,
 constexpr int kItemsPerWorkgroupWide = 2;  // or this many in decode-only calls of more than 8
